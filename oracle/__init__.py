@@ -1,0 +1,164 @@
+"""CPU oracle for mass-matrix assembly: ctypes wrapper around ``mm_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the GPU product path must not.
+
+The C library is a plain fp64 direct per-particle scatter of Eq. (6) of
+Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+Particle-In-Cell Methods" (Sec. 2.1), with the B-spline weights of Sec. 2.3
+and the compact stencil storage of Sec. 3.4. See the header of
+``mm_oracle.c`` for every reading it takes where the page is silent.
+
+Arrays are numpy float64 (positions ``[np, 3]``, weights ``[np]``, magnetic
+field ``[np, 3]``); the output layout is ``[nnodes, noff, ncomp]`` with
+``ncomp`` = 1 (scalar) or 9 (3x3 tensorial, row-major).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mm_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (OpenMP, no FP contraction)."""
+    tmp = LIB_PATH + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC",
+         "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    lib.oracle_alpha.argtypes = [P, D, P]
+    lib.oracle_support.argtypes = [I, I, P, P, P, P, P, P]
+    lib.oracle_assemble.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I, P, I]
+    lib.oracle_bin.argtypes = [I, I, P, P, P, I64, P, P, P]
+    lib.oracle_bilinear.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, P, P, P]
+    lib.oracle_rows.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I64, P, P]
+    lib.oracle_max_threads.argtypes = []
+    for f in (lib.oracle_alpha, lib.oracle_support, lib.oracle_assemble, lib.oracle_bin,
+              lib.oracle_bilinear, lib.oracle_rows, lib.oracle_max_threads):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _grid_args(n, origin, h):
+    return (np.ascontiguousarray(n, dtype=np.int32), np.ascontiguousarray(origin, dtype=np.float64),
+            np.ascontiguousarray(h, dtype=np.float64))
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def noff(order: int) -> int:
+    return (2 * order + 1) ** 3
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def alpha(B, beta: float) -> np.ndarray:
+    """3x3 magnetic response tensor of one particle (row-major)."""
+    B = _f64(B)
+    out = np.empty(9)
+    _check(_load().oracle_alpha(_ptr(B), float(beta), _ptr(out)), "alpha")
+    return out.reshape(3, 3)
+
+
+def support(order, n, origin, h, x, prec32=False):
+    """First support node (wrapped) and per-dimension 1D weights ``[3, 3]``."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    x = _f64(x)
+    first = np.empty(3, dtype=np.int32)
+    w1d = np.empty(9)
+    _check(_load().oracle_support(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), _ptr(x), _ptr(first),
+                                  _ptr(w1d)), "support")
+    return first, w1d.reshape(3, 3)
+
+
+def assemble(order, n, origin, h, pos, w, B=None, beta=0.0, sigma=1.0, M=None, accumulate=False,
+             prec32=False, nthreads=0) -> np.ndarray:
+    """Mass matrix ``[nnodes, noff, ncomp]`` by direct scatter (scalar if ``B is None``)."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos, w, B = _f64(pos), _f64(w), _f64(B)
+    npart = 0 if pos is None else pos.reshape(-1, 3).shape[0]
+    ncomp = 1 if B is None else 9
+    nnodes = int(np.prod(n_.astype(np.int64)))
+    shape = (nnodes, noff(order), ncomp)
+    if M is None:
+        M = np.zeros(shape)
+        accumulate = False
+    assert M.shape == shape and M.dtype == np.float64 and M.flags.c_contiguous
+    _check(_load().oracle_assemble(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
+                                   _ptr(B), float(beta), float(sigma), int(bool(accumulate)), _ptr(M),
+                                   int(nthreads)), "assemble")
+    return M
+
+
+def bin_particles(order, n, origin, h, pos, prec32=False):
+    """Stable counting sort by first support node: ``(bin_start[nbins+1], perm[np])``."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos = _f64(pos)
+    npart = pos.reshape(-1, 3).shape[0]
+    nbins = int(np.prod(n_.astype(np.int64)))
+    bin_start = np.empty(nbins + 1, dtype=np.int32)
+    perm = np.empty(max(npart, 1), dtype=np.int32)
+    _check(_load().oracle_bin(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(bin_start),
+                              _ptr(perm)), "bin")
+    return bin_start, perm[:npart]
+
+
+def bilinear(order, n, origin, h, pos, w, u, v, B=None, beta=0.0, sigma=1.0, prec32=False) -> float:
+    """``sigma * sum_p (W_p u)^T s_p (W_p v)``; u, v are ``[nnodes, 3]`` (tensorial) or ``[nnodes]``."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos, w, B, u, v = _f64(pos), _f64(w), _f64(B), _f64(u), _f64(v)
+    npart = pos.reshape(-1, 3).shape[0]
+    out = np.zeros(1)
+    _check(_load().oracle_bilinear(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
+                                   _ptr(B), float(beta), float(sigma), _ptr(u), _ptr(v), _ptr(out)), "bilinear")
+    return float(out[0])
+
+
+def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32=False) -> np.ndarray:
+    """Exact stencil rows ``[len(nodes), noff, ncomp]`` for selected nodes."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos, w, B = _f64(pos), _f64(w), _f64(B)
+    nodes = np.ascontiguousarray(nodes, dtype=np.int64)
+    npart = pos.reshape(-1, 3).shape[0]
+    ncomp = 1 if B is None else 9
+    out = np.zeros((len(nodes), noff(order), ncomp))
+    _check(_load().oracle_rows(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
+                               float(beta), float(sigma), len(nodes), _ptr(nodes), _ptr(out)), "rows")
+    return out
