@@ -1,0 +1,143 @@
+/*
+ * mm.h - C ABI of the MI355X (gfx950) particle-to-grid mass-matrix library.
+ *
+ * The operation is the implicit-PIC mass matrix of Pennati & Markidis,
+ * "Mass Matrix Assembly on Tensor Cores for Implicit Particle-In-Cell
+ * Methods", Sec. 2.1 Eq. (6):
+ *
+ *     M^{ij}_{g g'} = sigma * sum_p s_p^{ij} W_pg W_pg'
+ *
+ * with tensor-product B-spline weights W_pg (Sec. 2.3 Eq. 12) of order 1
+ * (CIC, 8 support nodes) or 2 (TSC, 27 support nodes), assembled cell by
+ * cell as batched small matrix products (Sec. 3.1-3.2, Eq. 15) on the matrix
+ * cores, and stored in the compact stencil format of Sec. 3.4.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Grid:    periodic, n[d] cells per axis and as many nodes; node k sits at
+ *           origin[d] + k*h[d]. Node index g = x + n0*(y + n1*z).
+ *  Support: per axis u = (x - origin)/h (IEEE division), j = floor(u),
+ *           xi = u - j. CIC: nodes j, j+1 with weights (1-xi, xi). TSC: the
+ *           stencil is centred on the nearest node m (m = j if xi < 1/2, else
+ *           j+1, the tie going up as in Sec. 2.3), nodes m-1, m, m+1 with the
+ *           quadratic B-spline weights. Node ids wrap modulo n.
+ *  Output:  M[node][offset][comp], node-major. offset = (dx+R) + (2R+1)*((dy+R)
+ *           + (2R+1)*(dz+R)) for the node-pair displacement d = g' - g in
+ *           [-R,R]^3 (27 offsets for CIC, 125 for TSC). comp = 3*i + j
+ *           (tensorial, 9 per entry, row i of alpha) or a single scalar.
+ *           The full stencil is stored (both g->g' and g'->g).
+ *  dtype:   MM_F64: pos, w, B and M are double. MM_F32: all four are float,
+ *           the cell decision, weights and matrix-core accumulation run in
+ *           fp32 (sigma and beta are rounded to fp32).
+ *  Memory:  every array argument is a device pointer (hipMalloc or an
+ *           allocator on top of it, e.g. torch) on the current device,
+ *           owned by the caller. The library allocates nothing and keeps no
+ *           mutable global state; calls are reentrant.
+ *  Streams: all work is enqueued asynchronously on `stream` (a hipStream_t,
+ *           NULL = default stream); no call synchronizes the host.
+ *  Workspace (CUB style): call with ws == NULL to receive the required byte
+ *           count in *ws_bytes (nothing is enqueued, MM_OK is returned); then
+ *           call again with a device buffer of at least that many bytes.
+ *  Errors:  arguments are validated on the host before any HIP call;
+ *           a failed launch returns MM_ERR_HIP. Positions must be finite and
+ *           |(x - origin)/h| < 2^31; that precondition is not checked.
+ */
+#ifndef MM_H
+#define MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MM_OK = 0,
+  MM_ERR_NULL = 1,        /* a required pointer is NULL */
+  MM_ERR_ARG = 2,         /* order, dtype, grid, sigma/beta or algo out of range */
+  MM_ERR_UNSUPPORTED = 3, /* np or node count at or above 2^31 */
+  MM_ERR_WORKSPACE = 4,   /* *ws_bytes smaller than required */
+  MM_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} mm_status;
+
+typedef enum { MM_F64 = 0, MM_F32 = 1 } mm_dtype;
+
+/* Assembly algorithm. */
+typedef enum {
+  MM_ALGO_MFMA = 0,          /* per-bin matrix-core contraction + the library's default deposit */
+  MM_ALGO_ATOMIC = 1,        /* conventional per-particle atomic scatter (comparison kernel);
+                                ignores bin_start/perm, which may be NULL */
+  MM_ALGO_MFMA_ATOMIC = 2    /* per-bin matrix-core contraction, global-atomic deposit */
+} mm_algo;
+
+typedef struct {
+  int32_t n[3];      /* cells (= nodes) per axis; each >= 2*order + 1 */
+  double origin[3];  /* position of node (0,0,0) */
+  double h[3];       /* node spacing, > 0 and finite */
+} mm_grid;
+
+/* Opaque stream handle: pass a hipStream_t (or NULL). */
+typedef void* mm_stream_t;
+
+/*
+ * mm_bin_particles - counting sort of particles by support set.
+ *
+ * Groups particles whose B-spline supports coincide (the support-group
+ * partition of Sec. 3.3; for CIC this is the cell, Sec. 2.3), keyed by the
+ * linear index of the support's first node, which is a prerequisite of the
+ * cell-wise assembly (Sec. 4.2 sorts particles by cell).
+ *
+ *  pos        [np][3] device array of dtype dt.
+ *  bin_start  [n0*n1*n2 + 1] int32 output: bin k holds particles
+ *             perm[bin_start[k] .. bin_start[k+1]-1]; bin_start[nbins] = np.
+ *  perm       [np] int32 output: particle indices, bin by bin, ascending
+ *             within a bin (a stable sort, so the result is unique).
+ *  np == 0 fills bin_start with zeros. perm may be NULL when np == 0.
+ */
+mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                           int32_t* bin_start, int32_t* perm, void* ws, size_t* ws_bytes, mm_stream_t stream);
+
+/*
+ * mm_assemble_scalar - scalar mass matrix M_gg' = sigma * sum_p w_p W_pg W_pg'
+ * (Eq. 6 with s_p = w_p; the scalar case of Sec. 3, as in FLIP/MPM, Sec. 1).
+ *
+ *  pos [np][3], w [np]: particle positions and weights (dtype dt).
+ *  bin_start, perm: output of mm_bin_particles for the same grid, order,
+ *             dtype and positions (required for the MFMA algorithms).
+ *  M [nnodes][noff] output (dtype dt). accumulate == 0 overwrites M,
+ *             accumulate != 0 adds to it (several species into one M).
+ */
+mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                             const void* w, const int32_t* bin_start, const int32_t* perm, double sigma,
+                             int accumulate, mm_algo algo, void* M, void* ws, size_t* ws_bytes,
+                             mm_stream_t stream);
+
+/*
+ * mm_assemble_ecsim - 3x3 tensorial ECSIM mass matrix
+ *   M^{ij}_gg' = sigma * sum_p w_p alpha_p^{ij} W_pg W_pg'
+ * with the per-particle magnetic response of the implicit-midpoint push,
+ *   alpha_p = (I + beta^2 B_p B_p^T - beta [B_p]x) / (1 + beta^2 |B_p|^2),
+ * [B]x u = B x u, beta = q dt / (2 m) of the species (Sec. 2.1 Eq. 6;
+ * the page cites alpha as Eq. 5 in Sec. 4.1).
+ *
+ *  B [np][3]: magnetic field at each particle (dtype dt).
+ *  M [nnodes][noff][3][3] output (dtype dt), row i of alpha first.
+ *  Other arguments as for mm_assemble_scalar.
+ */
+mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                            const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                            double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                            size_t* ws_bytes, mm_stream_t stream);
+
+/* Static description of a status code. */
+const char* mm_status_string(mm_status s);
+
+/* Library version string. */
+const char* mm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM_H */

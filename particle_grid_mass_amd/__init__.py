@@ -1,0 +1,8 @@
+"""MI355X (gfx950) particle-to-grid mass-matrix assembly.
+
+The computation lives in ``libmm.so`` (hand-written HIP kernels behind the C
+ABI of ``include/mm.h``); this package is its thin torch binding.
+"""
+from .api import MMError, assemble_ecsim, assemble_scalar, bin_particles, noff  # noqa: F401
+
+__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "noff", "MMError"]

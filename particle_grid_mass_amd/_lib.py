@@ -1,0 +1,72 @@
+"""ctypes loader for ``libmm.so`` (the gfx950 HIP library). Fails loudly if absent."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmm.so")
+
+MM_OK, MM_ERR_NULL, MM_ERR_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP = range(6)
+MM_F64, MM_F32 = 0, 1
+ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
+
+# Every symbol the public header include/mm.h declares.
+EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_status_string", "mm_version")
+
+
+class MMGrid(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32 * 3), ("origin", ctypes.c_double * 3), ("h", ctypes.c_double * 3)]
+
+
+class MMError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load():
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m particle_grid_mass_amd.build` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    SZ = ctypes.POINTER(ctypes.c_size_t)
+    G = ctypes.POINTER(MMGrid)
+    lib.mm_bin_particles.argtypes = [G, I, I, I64, P, P, P, P, SZ, P]
+    lib.mm_assemble_scalar.argtypes = [G, I, I, I64, P, P, P, P, D, I, I, P, P, SZ, P]
+    lib.mm_assemble_ecsim.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, P, SZ, P]
+    for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim):
+        f.restype = ctypes.c_int
+    lib.mm_status_string.argtypes = [ctypes.c_int]
+    lib.mm_status_string.restype = ctypes.c_char_p
+    lib.mm_version.argtypes = []
+    lib.mm_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().mm_status_string(int(status)).decode()
+    except ImportError:
+        return "library not loaded"
+
+
+def make_grid(n, origin=(0.0, 0.0, 0.0), h=(1.0, 1.0, 1.0)) -> MMGrid:
+    g = MMGrid()
+    for d in range(3):
+        g.n[d] = int(n[d])
+        g.origin[d] = float(origin[d])
+        g.h[d] = float(h[d])
+    return g

@@ -1,0 +1,148 @@
+"""Thin torch-facing binding of the C ABI in ``include/mm.h``.
+
+Argument marshalling only: tensors are checked for device, dtype and
+layout, output and workspace buffers are allocated with torch on the
+tensors' device, and the call is enqueued on the current torch stream.
+Every step of the computation runs in the HIP kernels of ``libmm.so``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MMError
+
+_DT = {torch.float64: _lib.MM_F64, torch.float32: _lib.MM_F32}
+
+
+def _grid_of(grid) -> _lib.MMGrid:
+    if isinstance(grid, _lib.MMGrid):
+        return grid
+    if hasattr(grid, "n"):
+        return _lib.make_grid(grid.n, getattr(grid, "origin", (0, 0, 0)), getattr(grid, "h", (1, 1, 1)))
+    n, origin, h = grid
+    return _lib.make_grid(n, origin, h)
+
+
+def _nnodes(g: _lib.MMGrid) -> int:
+    return int(g.n[0]) * int(g.n[1]) * int(g.n[2])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype, shape_tail=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU device")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(fn, what, *args):
+    st = fn(*args)
+    if st != _lib.MM_OK:
+        raise MMError(st, what)
+
+
+def _workspace(fn, what, args_before_ws, device, stream):
+    """Query, allocate and return the workspace tensor and its size pointer."""
+    nbytes = ctypes.c_size_t(0)
+    _call(fn, what + " (workspace query)", *args_before_ws, None, ctypes.byref(nbytes), stream)
+    ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def noff(order: int) -> int:
+    return (2 * order + 1) ** 3
+
+
+def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch.Tensor] = None,
+                  perm: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable counting sort by first support node -> ``(bin_start[nbins+1], perm[np])`` (int32)."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    dt = pos.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor(pos, "pos", dt)
+    npart = pos.numel() // 3
+    dev = pos.device
+    if bin_start is None:
+        bin_start = torch.empty(_nnodes(g) + 1, dtype=torch.int32, device=dev)
+    if perm is None:
+        perm = torch.empty(max(npart, 1), dtype=torch.int32, device=dev)
+    _check_tensor(bin_start, "bin_start", torch.int32)
+    _check_tensor(perm, "perm", torch.int32)
+    s = _stream(dev)
+    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(bin_start), _ptr(perm))
+    ws, nbytes = _workspace(lib.mm_bin_particles, "mm_bin_particles", head, dev, s)
+    _call(lib.mm_bin_particles, "mm_bin_particles", *head, _ptr(ws), ctypes.byref(nbytes), s)
+    return bin_start, perm[:npart]
+
+
+def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo):
+    lib = _lib.load()
+    g = _grid_of(grid)
+    dt = pos.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor(pos, "pos", dt)
+    _check_tensor(w, "w", dt)
+    if B is not None:
+        _check_tensor(B, "B", dt)
+    npart = pos.numel() // 3
+    if w.numel() != npart or (B is not None and B.numel() != 3 * npart):
+        raise ValueError("pos, w and B disagree on the particle count")
+    if algo not in _lib.ALGOS:
+        raise ValueError(f"unknown algo {algo!r}; expected one of {sorted(_lib.ALGOS)}")
+    if _lib.ALGOS[algo] != _lib.ALGOS["atomic"]:
+        if bin_start is None or perm is None:
+            raise ValueError("the matrix-core algorithms need bin_start and perm from bin_particles")
+        _check_tensor(bin_start, "bin_start", torch.int32)
+        _check_tensor(perm, "perm", torch.int32)
+    ncomp = 9 if kind == "ecsim" else 1
+    shape = (_nnodes(g), noff(order), ncomp) if ncomp == 9 else (_nnodes(g), noff(order))
+    dev = pos.device
+    if M is None:
+        M = torch.empty(shape, dtype=dt, device=dev)
+        accumulate = False
+    _check_tensor(M, "M", dt)
+    if M.numel() != _nnodes(g) * noff(order) * ncomp:
+        raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * noff(order) * ncomp}")
+    s = _stream(dev)
+    a = _lib.ALGOS[algo]
+    if kind == "ecsim":
+        fn, name = lib.mm_assemble_ecsim, "mm_assemble_ecsim"
+        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
+                float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
+    else:
+        fn, name = lib.mm_assemble_scalar, "mm_assemble_scalar"
+        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(bin_start), _ptr(perm),
+                float(sigma), int(bool(accumulate)), a, _ptr(M))
+    ws, nbytes = _workspace(fn, name, head, dev, s)
+    _call(fn, name, *head, _ptr(ws), ctypes.byref(nbytes), s)
+    return M
+
+
+def assemble_scalar(grid, order: int, pos, w, bin_start=None, perm=None, sigma: float = 1.0,
+                    M: Optional[torch.Tensor] = None, accumulate: bool = False, algo: str = "mfma") -> torch.Tensor:
+    """Scalar mass matrix ``[nnodes, noff]``."""
+    return _assemble("scalar", grid, order, pos, w, None, bin_start, perm, 0.0, sigma, M, accumulate, algo)
+
+
+def assemble_ecsim(grid, order: int, pos, w, B, bin_start=None, perm=None, beta: float = 0.0, sigma: float = 1.0,
+                   M: Optional[torch.Tensor] = None, accumulate: bool = False, algo: str = "mfma") -> torch.Tensor:
+    """3x3 tensorial ECSIM mass matrix ``[nnodes, noff, 9]``."""
+    return _assemble("ecsim", grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo)

@@ -1,0 +1,145 @@
+// C ABI of the mass-matrix library: host-side validation, workspace planning
+// and kernel dispatch. Every argument error is reported before any HIP call.
+#include <math.h>
+
+#include "../../include/mm.h"
+#include "mm_internal.h"
+
+using namespace mmk;
+
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647LL;
+
+bool finite(double v) { return isfinite(v) != 0; }
+
+mm_status check_grid(const mm_grid* g, int order, int64_t* nnodes) {
+  if (!g) return MM_ERR_NULL;
+  if (order != 1 && order != 2) return MM_ERR_ARG;
+  int64_t nn = 1;
+  for (int d = 0; d < 3; ++d) {
+    if (g->n[d] < 2 * order + 1) return MM_ERR_ARG;
+    if (!(g->h[d] > 0.0) || !finite(g->h[d]) || !finite(g->origin[d])) return MM_ERR_ARG;
+    nn *= g->n[d];
+  }
+  if (nn >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  *nnodes = nn;
+  return MM_OK;
+}
+
+GridDev to_dev(const mm_grid* g) {
+  GridDev d;
+  d.n0 = g->n[0];
+  d.n1 = g->n[1];
+  d.n2 = g->n[2];
+  d.o0 = g->origin[0];
+  d.o1 = g->origin[1];
+  d.o2 = g->origin[2];
+  d.h0 = g->h[0];
+  d.h1 = g->h[1];
+  d.h2 = g->h[2];
+  return d;
+}
+
+mm_status hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
+
+// Shared argument checks of the two assembly entry points.
+mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
+                          const void* B, bool tensorial, const int32_t* bin_start, const int32_t* perm, double beta,
+                          double sigma, mm_algo algo, void* M, void* ws, size_t* ws_bytes, mm_stream_t stream,
+                          int accumulate) {
+  if (!ws_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC) return MM_ERR_ARG;
+  if (!finite(sigma) || !finite(beta)) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!M) return MM_ERR_NULL;
+  const bool mfma = algo != MM_ALGO_ATOMIC;
+  if (np > 0) {
+    if (!pos || !w || (tensorial && !B)) return MM_ERR_NULL;
+    if (mfma && (!bin_start || !perm)) return MM_ERR_NULL;
+  }
+  const size_t need = 0;  // the atomic deposits need no workspace
+  if (!ws) {
+    *ws_bytes = need;
+    return MM_OK;
+  }
+  if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+
+  const bool f32 = dt == MM_F32;
+  const int noff = order == 1 ? 27 : 125;
+  const size_t count = (size_t)nnodes * noff * (tensorial ? 9 : 1);
+  hipStream_t s = (hipStream_t)stream;
+  GridDev g = to_dev(grid);
+  hipError_t e = hipSuccess;
+  if (!accumulate) e = launch_fill_zero(M, count, f32, s);
+  if (e != hipSuccess) return MM_ERR_HIP;
+  if (np == 0) return MM_OK;
+  Particles P{pos, w, tensorial ? B : nullptr, (int)np};
+  if (algo == MM_ALGO_ATOMIC)
+    e = launch_atomic_scatter(g, order, f32, P, beta, sigma, M, s);
+  else
+    e = launch_mfma_atomic(g, order, f32, P, bin_start, perm, beta, sigma, M, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                           int32_t* bin_start, int32_t* perm, void* ws, size_t* ws_bytes, mm_stream_t stream) {
+  if (!ws_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!bin_start) return MM_ERR_NULL;
+  if (np > 0 && (!pos || !perm)) return MM_ERR_NULL;
+  const size_t need = np > 0 ? bin_workspace_bytes(np, nnodes) : 0;
+  if (!ws) {
+    *ws_bytes = need;
+    return MM_OK;
+  }
+  if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+  return hip_status(launch_bin(to_dev(grid), order, dt == MM_F32, pos, (int)np, (int)nnodes, bin_start, perm, ws,
+                               (hipStream_t)stream));
+}
+
+mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                             const void* w, const int32_t* bin_start, const int32_t* perm, double sigma,
+                             int accumulate, mm_algo algo, void* M, void* ws, size_t* ws_bytes,
+                             mm_stream_t stream) {
+  return assemble_common(grid, order, dt, np, pos, w, nullptr, false, bin_start, perm, 0.0, sigma, algo, M, ws,
+                         ws_bytes, stream, accumulate);
+}
+
+mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                            const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                            double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                            size_t* ws_bytes, mm_stream_t stream) {
+  return assemble_common(grid, order, dt, np, pos, w, B, true, bin_start, perm, beta, sigma, algo, M, ws, ws_bytes,
+                         stream, accumulate);
+}
+
+const char* mm_status_string(mm_status s) {
+  switch (s) {
+    case MM_OK: return "ok";
+    case MM_ERR_NULL: return "a required pointer is NULL";
+    case MM_ERR_ARG: return "argument out of range (order, dtype, grid, sigma/beta or algo)";
+    case MM_ERR_UNSUPPORTED: return "particle or node count at or above 2^31";
+    case MM_ERR_WORKSPACE: return "workspace smaller than required";
+    case MM_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mm_version(void) { return "mm 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side launcher interface between the C ABI (mm_abi.hip) and the kernel
+// translation units. Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mm_device.h"
+
+namespace mmk {
+
+struct Particles {
+  const void* pos;  // [np][3]
+  const void* w;    // [np]
+  const void* B;    // [np][3] or NULL (scalar)
+  int np;
+};
+
+// M <- 0 (a fill kernel, so the stream stays capturable).
+hipError_t launch_fill_zero(void* M, size_t count, bool f32, hipStream_t s);
+
+// Conventional per-particle atomic scatter (comparison kernel).
+hipError_t launch_atomic_scatter(const GridDev& g, int order, bool f32, const Particles& P, double beta,
+                                 double sigma, void* M, hipStream_t s);
+
+// Per-bin matrix-core contraction with a global-atomic deposit.
+hipError_t launch_mfma_atomic(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
+                              const int32_t* perm, double beta, double sigma, void* M, hipStream_t s);
+
+// Binning: stable LSD radix sort of first-support-node keys.
+size_t bin_workspace_bytes(int64_t np, int64_t nbins);
+hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, int np, int nbins, int32_t* bin_start,
+                      int32_t* perm, void* ws, hipStream_t s);
+
+}  // namespace mmk

@@ -1,0 +1,120 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+public header declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes. Workspace queries (ws == NULL) also
+return without touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from particle_grid_mass_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mm.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mm_status|const char\*)\s+(mm_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_symbols() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_all_symbols():
+    lib = _lib.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.mm_version().decode().startswith("mm ")
+    for code in range(6):
+        assert lib.mm_status_string(code)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails (or sizes are returned) first
+
+
+def _bin(grid, order=1, dt=_lib.MM_F64, np_=10, pos=FAKE, bs=FAKE, perm=FAKE, ws=None):
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(0)
+    st = lib.mm_bin_particles(ctypes.byref(grid) if grid is not None else None, order, dt, np_, pos, bs, perm, ws,
+                              ctypes.byref(nbytes), None)
+    return st, nbytes.value
+
+
+def _ecsim(grid, order=1, dt=_lib.MM_F64, np_=10, pos=FAKE, w=FAKE, B=FAKE, bs=FAKE, perm=FAKE, beta=0.5,
+           sigma=1.0, algo=0, M=FAKE, ws=None, nbytes=0):
+    lib = _lib.load()
+    nb = ctypes.c_size_t(nbytes)
+    st = lib.mm_assemble_ecsim(ctypes.byref(grid) if grid is not None else None, order, dt, np_, pos, w, B, bs, perm,
+                               beta, sigma, 0, algo, M, ws, ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def _scalar(grid, order=1, np_=10, w=FAKE, algo=0, M=FAKE):
+    lib = _lib.load()
+    nb = ctypes.c_size_t(0)
+    return lib.mm_assemble_scalar(ctypes.byref(grid), order, _lib.MM_F64, np_, FAKE, w, FAKE, FAKE, 1.0, 0, algo, M,
+                                  None, ctypes.byref(nb), None)
+
+
+G8 = _lib.make_grid((8, 8, 8))
+
+
+def test_workspace_queries():
+    st, nb = _bin(G8, np_=100000)
+    assert st == _lib.MM_OK and nb >= 3 * 100000 * 4
+    st, nb0 = _bin(G8, np_=0, pos=None, perm=None)
+    assert st == _lib.MM_OK and nb0 == 0
+    st, _ = _ecsim(G8)
+    assert st == _lib.MM_OK
+
+
+def test_bin_validation():
+    assert _bin(None)[0] == _lib.MM_ERR_NULL
+    assert _bin(G8, order=3)[0] == _lib.MM_ERR_ARG
+    assert _bin(G8, order=0)[0] == _lib.MM_ERR_ARG
+    assert _bin(G8, dt=7)[0] == _lib.MM_ERR_ARG
+    assert _bin(_lib.make_grid((2, 8, 8)))[0] == _lib.MM_ERR_ARG          # n < 2R+1 for CIC
+    assert _bin(_lib.make_grid((4, 8, 8)), order=2)[0] == _lib.MM_ERR_ARG  # n < 2R+1 for TSC
+    assert _bin(_lib.make_grid((8, 8, 8), h=(1, 0, 1)))[0] == _lib.MM_ERR_ARG
+    assert _bin(_lib.make_grid((8, 8, 8), h=(1, float("inf"), 1)))[0] == _lib.MM_ERR_ARG
+    assert _bin(_lib.make_grid((8, 8, 8), origin=(float("nan"), 0, 0)))[0] == _lib.MM_ERR_ARG
+    assert _bin(G8, np_=-1)[0] == _lib.MM_ERR_ARG
+    assert _bin(G8, np_=2 ** 31)[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _bin(_lib.make_grid((2048, 1024, 1024)))[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _bin(G8, pos=None)[0] == _lib.MM_ERR_NULL
+    assert _bin(G8, perm=None)[0] == _lib.MM_ERR_NULL
+    assert _bin(G8, bs=None)[0] == _lib.MM_ERR_NULL
+
+
+def test_bin_workspace_too_small():
+    lib = _lib.load()
+    nbytes = ctypes.c_size_t(16)
+    st = lib.mm_bin_particles(ctypes.byref(G8), 1, _lib.MM_F64, 1000, FAKE, FAKE, FAKE, FAKE, ctypes.byref(nbytes),
+                              None)
+    assert st == _lib.MM_ERR_WORKSPACE
+
+
+def test_assemble_validation():
+    assert _ecsim(None)[0] == _lib.MM_ERR_NULL
+    assert _ecsim(G8, order=5)[0] == _lib.MM_ERR_ARG
+    assert _ecsim(G8, dt=-1)[0] == _lib.MM_ERR_ARG
+    assert _ecsim(G8, algo=9)[0] == _lib.MM_ERR_ARG
+    assert _ecsim(G8, beta=float("nan"))[0] == _lib.MM_ERR_ARG
+    assert _ecsim(G8, sigma=float("inf"))[0] == _lib.MM_ERR_ARG
+    assert _ecsim(G8, np_=2 ** 31)[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _ecsim(G8, M=None)[0] == _lib.MM_ERR_NULL
+    assert _ecsim(G8, B=None)[0] == _lib.MM_ERR_NULL
+    assert _ecsim(G8, pos=None)[0] == _lib.MM_ERR_NULL
+    assert _ecsim(G8, bs=None)[0] == _lib.MM_ERR_NULL           # MFMA needs the binning
+    assert _ecsim(G8, bs=None, perm=None, algo=1)[0] == _lib.MM_OK  # the atomic scatter does not
+    assert _ecsim(G8, np_=0, pos=None, w=None, B=None, bs=None, perm=None)[0] == _lib.MM_OK
+    assert _scalar(G8, w=None) == _lib.MM_ERR_NULL
+    assert _scalar(G8, order=2) == _lib.MM_OK
+
+
+def test_scalar_tsc_grid_bounds():
+    assert _scalar(_lib.make_grid((5, 5, 5)), order=2) == _lib.MM_OK
+    assert _scalar(_lib.make_grid((4, 5, 5)), order=2) == _lib.MM_ERR_ARG
