@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the mass-matrix hot path on one MI355X.
+
+Metric: particles/s assembled (ECSIM 3x3 mass matrix, fp64), with the
+roofline fraction of the dominant kernel. One step is the whole hot path for
+every species of the workload: binning (stable counting sort by support
+group), per-bin matrix-core contraction, and stencil deposition. Inputs are
+seeded synthetic particles already resident in HBM when timing starts.
+
+Default workload: CIC ECSIM fp64 on a 32^3 periodic grid with 64 particles
+per cell (2,097,152 particles), beta = 0.5, sigma = 1.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--kind K]
+                    [--dtype f64|f32] [--shuffled] [--algo A] [--no-cpu-baseline]
+
+Prints one JSON line. ``--gpus`` above 1 is rejected: this build runs on a
+single GPU (see the design doc for how the path would shard).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "particles/s assembled (ECSIM 3x3 mass matrix, fp64) + % MFMA/HBM roofline"
+PEAK_FP64_MFMA = 78.6e12
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12
+PMC_FILE = os.path.join(ROOT, "profiles", "contract_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "particle_grid_mass_amd", "csrc", f) for f in
+                  ("k_contract.hip", "mm_device.h", "mm_contract.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def flops_per_particle(order: int, tensorial: bool) -> int:
+    n = (order + 1) ** 3
+    return 2 * n * n * (9 if tensorial else 1)
+
+
+def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int) -> int:
+    """Algorithmic HBM bytes of one contraction launch: each particle's
+    position, weight (and field) and permutation entry read once, bin bounds
+    read once, one packed upper-triangle record written per bin."""
+    n = (order + 1) ** 3
+    per_particle = (3 + 1 + (3 if tensorial else 0)) * elem + 4
+    record = n * (n + 1) // 2 * (9 if tensorial else 1) * elem
+    return np_ * per_particle + (nbins + 1) * 4 + nbins * record
+
+
+def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool) -> int:
+    """Algorithmic HBM bytes of one deposition launch: every record read once,
+    every stencil entry written once (read too when accumulating)."""
+    n = (order + 1) ** 3
+    noff = (2 * order + 1) ** 3
+    nc = 9 if tensorial else 1
+    out = nbins * noff * nc * elem
+    return nbins * n * (n + 1) // 2 * nc * elem + out * (2 if accumulate else 1)
+
+
+def workload_name(case) -> str:
+    n = case.grid.n
+    kind = "ECSIM 3x3" if case.kind == "ecsim" else "scalar"
+    order = "CIC" if case.order == 1 else "TSC"
+    return (f"{order} {kind} {case.dtype}, {n[0]}x{n[1]}x{n[2]} periodic cells, {case.np_total:,} particles "
+            f"({len(case.species)} species), {case.name}")
+
+
+def pmc_traffic(kernel_hash: str, config: int, launches_per_step: int):
+    """HBM bytes per contraction launch from the committed rocprofv3 counter runs,
+    or None when they were taken on a different kernel or workload."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != kernel_hash or d.get("config") != config:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle as it stands, on the host cores, on a bounded sample."""
+    import numpy as np
+    import oracle
+    sp = case.species[0]
+    # whole species if it fits the budget estimate, else a cell-sorted prefix (a slab of cells)
+    sample = sp.np
+    t0 = time.perf_counter()
+    probe = min(sp.np, 200_000)
+    oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:probe], sp.w[:probe],
+                    sp.B[:probe] if case.kind == "ecsim" else None, sp.beta, case.sigma,
+                    prec32=case.dtype == "f32")
+    rate_guess = probe / max(time.perf_counter() - t0, 1e-6)
+    if sp.np / rate_guess > budget_s:
+        sample = int(rate_guess * budget_s)
+    reps, total_t, Mref = 0, 0.0, None
+    while True:
+        t0 = time.perf_counter()
+        Mref = oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:sample],
+                               sp.w[:sample], sp.B[:sample] if case.kind == "ecsim" else None, sp.beta, case.sigma,
+                               prec32=case.dtype == "f32")
+        total_t += time.perf_counter() - t0
+        reps += 1
+        if total_t >= min(budget_s, 3.0) or reps >= 5:
+            break
+    value = sample * reps / total_t
+    desc = (f"species 0 of the workload, {'all' if sample == sp.np else 'first'} {sample:,} particles"
+            f"{'' if sample == sp.np else ' (cell-sorted prefix: a slab of cells)'}, {reps} run(s)")
+    return {"value": value, "unit": "particles/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": desc}, (Mref if sample == sp.np else None)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--kind", default=None, help="scalar|ecsim where the config offers both (config 4)")
+    ap.add_argument("--dtype", default="f64")
+    ap.add_argument("--shuffled", action="store_true", help="config 3: randomly shuffled particle order")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work at most")
+    ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but this build runs on exactly one "
+              f"GPU; the multi-GPU decomposition is described in DESIGN.md and not implemented.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import particle_grid_mass_amd as mm
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    case = make_config(args.config, kind=args.kind, dtype=args.dtype, shuffled=args.shuffled)
+    tdt = torch.float64 if case.dtype == "f64" else torch.float32
+    elem = 8 if case.dtype == "f64" else 4
+    tensorial = case.kind == "ecsim"
+    order = case.order
+    nbins = case.grid.ncells
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=tdt)
+
+    spec = []
+    for sp in case.species:
+        spec.append(dict(pos=to_dev(sp.pos), w=to_dev(sp.w), B=to_dev(sp.B) if tensorial else None, beta=sp.beta,
+                         bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
+                         perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
+    ncomp = 9 if tensorial else 1
+    M = torch.empty(nbins * mm.noff(order) * ncomp, dtype=tdt, device=dev)
+    rec = None
+    if args.algo == "mfma":
+        s0 = spec[0]
+        bs0, perm0 = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"])
+        rec = mm.contract_bins(case.grid, order, s0["pos"], s0["w"], s0["B"], bs0, perm0, s0["beta"], case.sigma)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    phases = ("bin", "contract", "deposit")
+
+    def step(evs):
+        for si, s in enumerate(spec):
+            if evs is not None:
+                evs[si][0].record(stream)
+            if args.algo == "atomic":
+                if tensorial:
+                    mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], None, None, s["beta"], case.sigma,
+                                      M=M, accumulate=si > 0, algo="atomic")
+                else:
+                    mm.assemble_scalar(case.grid, order, s["pos"], s["w"], None, None, case.sigma, M=M,
+                                       accumulate=si > 0, algo="atomic")
+                if evs is not None:
+                    for k in (1, 2, 3):
+                        evs[si][k].record(stream)
+                continue
+            bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"])
+            if evs is not None:
+                evs[si][1].record(stream)
+            if args.algo == "mfma":
+                mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec)
+                if evs is not None:
+                    evs[si][2].record(stream)
+                mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0)
+            else:
+                if tensorial:
+                    mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma,
+                                      M=M, accumulate=si > 0, algo=args.algo)
+                else:
+                    mm.assemble_scalar(case.grid, order, s["pos"], s["w"], bs, perm, case.sigma, M=M,
+                                       accumulate=si > 0, algo=args.algo)
+                if evs is not None:
+                    evs[si][2].record(stream)
+            if evs is not None:
+                evs[si][3].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in spec] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    phase_ms = {p: 0.0 for p in phases}
+    for k in range(args.steps):
+        for si in range(len(spec)):
+            for pi, p in enumerate(phases):
+                phase_ms[p] += ev[k][si][pi].elapsed_time(ev[k][si][pi + 1])
+    launches = args.steps * len(spec)
+    phase_per_launch_ms = {p: phase_ms[p] / launches for p in phases}
+    if args.algo == "atomic":  # one kernel per species: the per-particle atomic scatter
+        phase_per_launch_ms = {"atomic_scatter": phase_per_launch_ms["bin"]}
+        phase_ms = {"bin": 0.0, "contract": phase_ms["bin"], "deposit": 0.0}
+    np_total = case.np_total
+    value = np_total / (ms_step * 1e-3)
+
+    # roofline of the dominant kernel
+    if args.algo == "mfma":
+        dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
+        t_dom = phase_per_launch_ms[dom] * 1e-3
+    else:
+        dom = "contract"
+        t_dom = phase_ms["contract"] / launches * 1e-3
+    np_launch = np_total / len(spec)
+    khash = kernel_source_hash()
+    if dom == "contract":
+        flops = flops_per_particle(order, tensorial) * np_launch
+        peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
+        roof = {"kernel": "k_contract (per-bin MFMA contraction)", "bound": "mfma", "achieved": flops / t_dom / 1e12,
+                "peak": peak / 1e12, "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["algorithmic_flops_per_launch"] = flops
+        traffic = pmc_traffic(khash, args.config, 1)
+        roof["traffic"] = traffic
+        roof["algorithmic_bytes_per_launch"] = contract_bytes(order, tensorial, elem, int(np_launch), nbins)
+    else:
+        byts = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
+        roof = {"kernel": "k_gather (stencil deposition of bin records)", "bound": "hbm",
+                "achieved": byts / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["algorithmic_bytes_per_launch"] = byts
+    roof["avg_launch_ms"] = t_dom * 1e3
+    if args.algo != "mfma":
+        roof["kernel"] = {"atomic": "k_atomic_scatter (comparison)", "mfma_atomic": "k_contract, atomic deposit"}.get(
+            args.algo, args.algo)
+    roof["kernel_source_hash"] = khash
+
+    # parity of this run's output against the oracle (and the CPU baseline timing)
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, Mref = cpu_baseline(case, args.cpu_budget)
+        if Mref is not None and len(spec) == 1:
+            got = M.double().cpu().numpy().reshape(Mref.shape)
+            parity = float(np.linalg.norm(got - Mref) / np.linalg.norm(Mref))
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "particles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload_name(case), "config_id": args.config, "grid": list(case.grid.n),
+                   "order": order, "kind": case.kind, "np": np_total, "species": len(spec), "algo": args.algo,
+                   "step": "bin + contract + deposit per species" if args.algo == "mfma" else
+                   ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
+        "phases_ms_per_launch": phase_per_launch_ms,
+        "assembly_only_particles_per_s": np_total / ((phase_ms["contract"] + phase_ms["deposit"]) / args.steps * 1e-3)
+        if args.algo != "atomic" else value,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_rel_fro_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -130,6 +130,29 @@ mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t
                             double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
                             size_t* ws_bytes, mm_stream_t stream);
 
+/*
+ * The two phases of mm_assemble_* with MM_ALGO_MFMA, for callers that time,
+ * overlap or reuse them. Calling both is the same as one MFMA assembly call.
+ *
+ * mm_contract_bins - the per-bin local matrices (Sec. 3.1 Eq. 15, batched as
+ * in Sec. 3.2, one per support group of Sec. 3.3):
+ *   rec[bin][pair(a,b)][comp] = sigma * sum_{p in bin} t_p^comp W_pa W_pb,
+ * for support rows a <= b (upper triangle, pair(a,b) = a*N - a(a-1)/2 + b - a,
+ * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp).
+ *  rec       device buffer of *rec_bytes bytes (query with rec == NULL).
+ *  Other arguments as for mm_assemble_ecsim; bin_start/perm are required.
+ *
+ * mm_deposit_records - the sparse stencil deposition of Sec. 3.4: every
+ * M[g][o][comp] is set (accumulate == 0) or incremented by the sum, in a fixed
+ * order, of the records of all bins whose support holds both g and g+o.
+ *  tensorial  1 for the 3x3 records of mm_contract_bins with B != NULL, else 0.
+ */
+mm_status mm_contract_bins(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
+                           const void* B, const int32_t* bin_start, const int32_t* perm, double beta, double sigma,
+                           void* rec, size_t* rec_bytes, mm_stream_t stream);
+mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
+                             int accumulate, void* M, mm_stream_t stream);
+
 /* Static description of a status code. */
 const char* mm_status_string(mm_status s);
 

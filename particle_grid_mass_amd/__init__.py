@@ -3,6 +3,7 @@
 The computation lives in ``libmm.so`` (hand-written HIP kernels behind the C
 ABI of ``include/mm.h``); this package is its thin torch binding.
 """
-from .api import MMError, assemble_ecsim, assemble_scalar, bin_particles, noff  # noqa: F401
+from .api import (MMError, assemble_ecsim, assemble_scalar, bin_particles, contract_bins,  # noqa: F401
+                  deposit_records, noff)
 
-__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "noff", "MMError"]
+__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "contract_bins", "deposit_records", "noff", "MMError"]

@@ -146,3 +146,45 @@ def assemble_ecsim(grid, order: int, pos, w, B, bin_start=None, perm=None, beta:
                    M: Optional[torch.Tensor] = None, accumulate: bool = False, algo: str = "mfma") -> torch.Tensor:
     """3x3 tensorial ECSIM mass matrix ``[nnodes, noff, 9]``."""
     return _assemble("ecsim", grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo)
+
+
+def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.0, sigma: float = 1.0,
+                  rec: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Phase 1 of the matrix-core assembly: packed per-bin local matrices (uint8 buffer)."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    dt = pos.dtype
+    for t, name in ((pos, "pos"), (w, "w")):
+        _check_tensor(t, name, dt)
+    if B is not None:
+        _check_tensor(B, "B", dt)
+    _check_tensor(bin_start, "bin_start", torch.int32)
+    _check_tensor(perm, "perm", torch.int32)
+    npart = pos.numel() // 3
+    s = _stream(pos.device)
+    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
+            float(beta), float(sigma))
+    nbytes = ctypes.c_size_t(0)
+    _call(lib.mm_contract_bins, "mm_contract_bins (size query)", *head, None, ctypes.byref(nbytes), s)
+    if rec is None:
+        rec = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=pos.device)
+    else:
+        nbytes = ctypes.c_size_t(rec.numel() * rec.element_size())
+    _call(lib.mm_contract_bins, "mm_contract_bins", *head, _ptr(rec), ctypes.byref(nbytes), s)
+    return rec
+
+
+def deposit_records(grid, order: int, rec: torch.Tensor, M: torch.Tensor, tensorial: bool,
+                    accumulate: bool = False) -> torch.Tensor:
+    """Phase 2: stencil deposition of the packed records into ``M``."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    _check_tensor(M, "M", None)
+    if M.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {M.dtype}")
+    ncomp = 9 if tensorial else 1
+    if M.numel() != _nnodes(g) * noff(order) * ncomp:
+        raise ValueError("M has the wrong number of elements")
+    _call(lib.mm_deposit_records, "mm_deposit_records", ctypes.byref(g), int(order), _DT[M.dtype], int(bool(tensorial)),
+          _ptr(rec), int(bool(accumulate)), _ptr(M), _stream(M.device))
+    return M

@@ -1,0 +1,497 @@
+// Per-bin matrix-core contraction of the mass matrix (gfx950 MFMA), phase 1.
+//
+// Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+// Particle-In-Cell Methods": within one support group (one bin of particles
+// sharing their first support node, Sec. 3.3) the local matrix is
+//   Mhat^{c}_{ab} = sum_p t_p^c W_pa W_pb            (Sec. 3.1, Eq. 15)
+// i.e. A^c B with A^c = W diag(t^c), B = W^T (Sec. 3.1, Eq. 14), evaluated as
+// batched products whose inner dimension is a batch of particles (Sec. 3.2)
+// and using the spatial symmetry Mhat_ab = Mhat_ba to skip the lower
+// off-diagonal tile (Table 1). t^c = sigma w_p alpha_p^c (Eq. 6).
+//
+// Wave organisation (one wave owns a bin at a time, persistent over bins):
+//  * particle preparation runs one particle per lane: 64 particles are loaded
+//    with one gather each, their support weights W_a (Eq. 12) and
+//    coefficients t^c are computed once and staged in LDS columns;
+//  * the matrix instructions then read their operands from LDS:
+//    CIC fp64 - v_mfma_f64_4x4x4, 4 blocks; the 8 support rows split by az into
+//      two halves (quadrants Q00, Q01, Q11; Q10 = Q01^T); one instruction is one
+//      (component, quadrant) product for four different 4-particle batches
+//      (block = batch), so no block is padded; the 4 block partials are summed
+//      across lanes once per bin. 16 particles per round.
+//    CIC fp32 - v_mfma_f32_4x4x1, 16 blocks, one particle per block.
+//    TSC      - 27 rows padded to 32, tiles (0,0), (0,1), (1,1) of
+//      v_mfma_{f64,f32}_16x16x4, 4 particles per batch.
+//  * the next chunk's particle index and data are fetched while the current
+//    chunk computes.
+//
+// Output of a bin (MODE):
+//  MODE_RECORD - the upper triangle (a <= b) of the local matrix is written as
+//    one compact record rec[bin][pair(a,b)][comp]; a second kernel (k_gather)
+//    sums records into the stencil matrix (deterministic, every output entry
+//    written once, no atomics);
+//  MODE_ATOMIC - every local entry is added into the stencil matrix with a
+//    hardware atomic ((a,b) and (b,a) for off-diagonal tiles).
+#include "mm_contract.h"
+
+namespace mmk {
+
+template <int R>
+struct Geo {
+  static constexpr int NS = R + 1;
+  static constexpr int N = NS * NS * NS;
+  static constexpr int NPAIR = N * (N + 1) / 2;
+  static constexpr int NO = 2 * R + 1;
+  static constexpr int NOFF = NO * NO * NO;
+};
+
+// Position of the pair (a, b), a <= b, in the packed upper triangle.
+template <int N>
+__device__ __forceinline__ int pair_index(int a, int b) {
+  return a * N - (a * (a - 1)) / 2 + (b - a);
+}
+
+__device__ __forceinline__ size_t support_node(int fx, int fy, int fz, int ax, int ay, int az, const GridDev& g) {
+  int x = fx + ax, y = fy + ay, z = fz + az;
+  x = x >= g.n0 ? x - g.n0 : x;
+  y = y >= g.n1 ? y - g.n1 : y;
+  z = z >= g.n2 ? z - g.n2 : z;
+  return (size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * (size_t)z);
+}
+
+// Bin output for local entry (a, b) of component c (value v).
+template <typename T, int R, int NC, int MODE>
+struct Sink {
+  T* out;
+  int bin, fx, fy, fz;
+  GridDev g;
+  __device__ __forceinline__ void atomic_entry(int a, int b, int c, T v) const {
+    constexpr int NS = Geo<R>::NS, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF;
+    int ax = a % NS, ay = (a / NS) % NS, az = a / (NS * NS);
+    int bx = b % NS, by = (b / NS) % NS, bz = b / (NS * NS);
+    size_t node = support_node(fx, fy, fz, ax, ay, az, g);
+    int o = (bx - ax + R) + NO * ((by - ay + R) + NO * (bz - az + R));
+    atomic_add(out + (node * NOFF + o) * NC + c, v);
+  }
+  // Diagonal-tile entry: stored once as (a,b) with a <= b (record) or added as is (atomic).
+  __device__ __forceinline__ void diag_tile(int a, int b, int c, T v) const {
+    if (MODE == MODE_RECORD) {
+      if (a <= b) out[((size_t)bin * Geo<R>::NPAIR + pair_index<Geo<R>::N>(a, b)) * NC + c] = v;
+    } else {
+      atomic_entry(a, b, c, v);
+    }
+  }
+  // Off-diagonal-tile entry with a < b: stands for both (a,b) and (b,a).
+  __device__ __forceinline__ void off_tile(int a, int b, int c, T v) const {
+    if (MODE == MODE_RECORD) {
+      out[((size_t)bin * Geo<R>::NPAIR + pair_index<Geo<R>::N>(a, b)) * NC + c] = v;
+    } else {
+      atomic_entry(a, b, c, v);
+      atomic_entry(b, a, c, v);
+    }
+  }
+};
+
+// Raw data of the particle a lane prepares.
+template <typename T>
+struct Raw {
+  T x, y, z, w, bx, by, bz;
+  bool valid;
+};
+
+template <typename T, int NC>
+__device__ __forceinline__ Raw<T> load_raw(const T* __restrict__ pos, const T* __restrict__ w,
+                                           const T* __restrict__ Bf, int p, int np) {
+  Raw<T> r;
+  r.valid = (unsigned)p < (unsigned)np;
+  r.x = r.y = r.z = r.w = r.bx = r.by = r.bz = T(0);
+  if (r.valid) {
+    r.x = pos[3 * (size_t)p];
+    r.y = pos[3 * (size_t)p + 1];
+    r.z = pos[3 * (size_t)p + 2];
+    r.w = w[p];
+    if (NC == 9) {
+      r.bx = Bf[3 * (size_t)p];
+      r.by = Bf[3 * (size_t)p + 1];
+      r.bz = Bf[3 * (size_t)p + 2];
+    }
+  }
+  return r;
+}
+
+// One particle per lane: weights W[a] (a = ax + NS*(ay + NS*az)) into sW[a][lane],
+// coefficients t^c into sT[c][lane]; zeros for an empty lane.
+template <typename T, int R, int NC>
+__device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g, T beta, T sigma, T* sW, T* sT,
+                                               int lane) {
+  constexpr int NS = Geo<R>::NS, N = Geo<R>::N;
+  T wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) t[c] = T(0);
+  if (r.valid) {
+    axis_support<T, R>(r.x, (T)g.o0, (T)g.h0, g.n0, wx);
+    axis_support<T, R>(r.y, (T)g.o1, (T)g.h1, g.n1, wy);
+    axis_support<T, R>(r.z, (T)g.o2, (T)g.h2, g.n2, wz);
+    T f = sigma * r.w;
+    if (NC == 9)
+      response<T>(r.bx, r.by, r.bz, beta, f, t);
+    else
+      t[0] = f;
+  }
+#pragma unroll
+  for (int az = 0; az < NS; ++az)
+#pragma unroll
+    for (int ay = 0; ay < NS; ++ay)
+#pragma unroll
+      for (int ax = 0; ax < NS; ++ax) sW[(ax + NS * (ay + NS * az)) * 64 + lane] = (wx[ax] * wy[ay]) * wz[az];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) sT[c * 64 + lane] = t[c];
+  static_assert(N == NS * NS * NS, "support size");
+}
+
+// ---------------------------------------------------------------- accumulators
+// CIC fp64: 3 quadrants x NC components, one double each (4x4x4, 4 blocks).
+template <int NC>
+struct AccCicF64 {
+  double q[NC][3];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][0] = q[c][1] = q[c][2] = 0.0;
+  }
+  // Rounds of 16 particles from LDS columns [0, cnt).
+  __device__ __forceinline__ void accumulate(const double* sW, const double* sT, int cnt, int lane) {
+    const int slot = (lane >> 2) & 3, r4 = lane & 3, kq = lane >> 4;
+    for (int r0 = 0; r0 < cnt; r0 += 16) {
+      const int pl = r0 + 4 * slot + kq;
+      const double wlo = sW[r4 * 64 + pl], whi = sW[(4 + r4) * 64 + pl];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const double tc = sT[c * 64 + pl];
+        const double alo = tc * wlo, ahi = tc * whi;
+        q[c][0] = mfma_f64_4x4x4(alo, wlo, q[c][0]);
+        q[c][1] = mfma_f64_4x4x4(alo, whi, q[c][1]);
+        q[c][2] = mfma_f64_4x4x4(ahi, whi, q[c][2]);
+      }
+    }
+  }
+  template <int MODE>
+  __device__ __forceinline__ void finish(const Sink<double, 1, NC, MODE>& sk, int lane) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        double v = q[c][k];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        q[c][k] = v;
+      }
+    // D_blk[i][j] at lane (i<<4)|(blk<<2)|j; every block lane now holds the sum.
+    const int i = lane >> 4, slot = (lane >> 2) & 3, j = lane & 3;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (slot == 0) sk.diag_tile(i, j, c, q[c][0]);
+      if (slot == 1) sk.off_tile(i, 4 + j, c, q[c][1]);
+      if (slot == 2) sk.diag_tile(4 + i, 4 + j, c, q[c][2]);
+    }
+  }
+};
+
+// CIC fp32: 3 quadrants x NC components, 4 floats each (4x4x1, 16 blocks).
+template <int NC>
+struct AccCicF32 {
+  v4f q[NC][3];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) q[c][k] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void accumulate(const float* sW, const float* sT, int cnt, int lane) {
+    const int blk = lane >> 2, r4 = lane & 3;
+    for (int r0 = 0; r0 < cnt; r0 += 16) {
+      const int pl = r0 + blk;
+      const float wlo = sW[r4 * 64 + pl], whi = sW[(4 + r4) * 64 + pl];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float tc = sT[c * 64 + pl];
+        const float alo = tc * wlo, ahi = tc * whi;
+        q[c][0] = mfma_f32_4x4x1(alo, wlo, q[c][0]);
+        q[c][1] = mfma_f32_4x4x1(alo, whi, q[c][1]);
+        q[c][2] = mfma_f32_4x4x1(ahi, whi, q[c][2]);
+      }
+    }
+  }
+  template <int MODE>
+  __device__ __forceinline__ void finish(const Sink<float, 1, NC, MODE>& sk, int lane) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = q[c][k][r];
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          q[c][k][r] = v;
+        }
+    // D_blk[i][j] at lane 4 blk + j, register i; all blocks hold the sum.
+    const int blk = lane >> 2, j = lane & 3;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (blk == 0) sk.diag_tile(i, j, c, q[c][0][i]);
+        if (blk == 1) sk.off_tile(i, 4 + j, c, q[c][1][i]);
+        if (blk == 2) sk.diag_tile(4 + i, 4 + j, c, q[c][2][i]);
+      }
+  }
+};
+
+// TSC: tiles (0,0), (0,1), (1,1) of 16x16 per component.
+template <typename T>
+struct TscOps;
+template <>
+struct TscOps<double> {
+  typedef v4d V;
+  static __device__ __forceinline__ V mma(double a, double b, V c) { return mfma_f64_16x16x4(a, b, c); }
+  static __device__ __forceinline__ int row(int l, int r) { return 4 * r + (l >> 4); }
+};
+template <>
+struct TscOps<float> {
+  typedef v4f V;
+  static __device__ __forceinline__ V mma(float a, float b, V c) { return mfma_f32_16x16x4(a, b, c); }
+  static __device__ __forceinline__ int row(int l, int r) { return 4 * (l >> 4) + r; }
+};
+
+template <typename T, int NC>
+struct AccTsc {
+  typedef typename TscOps<T>::V V;
+  V q[NC][3];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) q[c][k] = V{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ void accumulate(const T* sW, const T* sT, int cnt, int lane) {
+    const int i16 = lane & 15, kq = lane >> 4;
+    const bool hi_ok = 16 + i16 < 27;
+    for (int b0 = 0; b0 < cnt; b0 += 4) {
+      const int pl = b0 + kq;
+      const T w0 = sW[i16 * 64 + pl];
+      const T w1 = hi_ok ? sW[(16 + i16) * 64 + pl] : T(0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const T tc = sT[c * 64 + pl];
+        const T a0 = tc * w0, a1 = tc * w1;
+        q[c][0] = TscOps<T>::mma(a0, w0, q[c][0]);
+        q[c][1] = TscOps<T>::mma(a0, w1, q[c][1]);
+        q[c][2] = TscOps<T>::mma(a1, w1, q[c][2]);
+      }
+    }
+  }
+  template <int MODE>
+  __device__ __forceinline__ void finish(const Sink<T, 2, NC, MODE>& sk, int lane) {
+    const int j = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = TscOps<T>::row(lane, r);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sk.diag_tile(i, j, c, q[c][0][r]);
+        if (16 + j < 27) sk.off_tile(i, 16 + j, c, q[c][1][r]);
+        if (16 + i < 27 && 16 + j < 27) sk.diag_tile(16 + i, 16 + j, c, q[c][2][r]);
+      }
+    }
+  }
+};
+
+template <typename T, int R, int NC>
+struct AccSel;
+template <int NC>
+struct AccSel<double, 1, NC> {
+  typedef AccCicF64<NC> A;
+};
+template <int NC>
+struct AccSel<float, 1, NC> {
+  typedef AccCicF32<NC> A;
+};
+template <typename T, int NC>
+struct AccSel<T, 2, NC> {
+  typedef AccTsc<T, NC> A;
+};
+
+// ---------------------------------------------------------------- kernel
+constexpr int CT_WAVES = 4;  // waves per block; each wave works alone
+
+template <typename T, int R, int NC, int MODE>
+__global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const T* __restrict__ pos,
+                                                            const T* __restrict__ w, const T* __restrict__ Bf,
+                                                            const int32_t* __restrict__ bin_start,
+                                                            const int32_t* __restrict__ perm, int np, int nbins,
+                                                            T beta, T sigma, T* __restrict__ out) {
+  constexpr int N = Geo<R>::N;
+  __shared__ T smem[CT_WAVES][(N + NC) * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  T* sW = smem[wv];
+  T* sT = smem[wv] + N * 64;
+  const int nwaves = gridDim.x * CT_WAVES;
+  int b = blockIdx.x * CT_WAVES + wv;
+  if (b >= nbins) return;
+
+  typename AccSel<T, R, NC>::A acc;
+  acc.zero();
+
+  int s = bin_start[b], e = bin_start[b + 1];
+  s = s < 0 ? 0 : s;
+  e = e > np ? np : e;
+  int c0 = s;
+  Raw<T> cur = load_raw<T, NC>(pos, w, Bf, c0 + lane < e ? perm[c0 + lane] : -1, np);
+
+  while (true) {
+    // Next chunk: the rest of this bin, else the wave's next bin.
+    int nb = b, ns = s, ne = e, nc0 = c0 + 64;
+    if (nc0 >= e) {
+      nb = b + nwaves;
+      if (nb < nbins) {
+        ns = bin_start[nb];
+        ne = bin_start[nb + 1];
+        ns = ns < 0 ? 0 : ns;
+        ne = ne > np ? np : ne;
+        nc0 = ns;
+      }
+    }
+    const bool more = nb < nbins;
+    const int pnext = (more && nc0 + lane < ne) ? perm[nc0 + lane] : -1;
+
+    stage_particle<T, R, NC>(cur, g, beta, sigma, sW, sT, lane);
+    Raw<T> nxt = load_raw<T, NC>(pos, w, Bf, pnext, np);
+    const int cnt = e - c0 < 64 ? (e - c0 > 0 ? e - c0 : 0) : 64;
+    acc.accumulate(sW, sT, cnt, lane);
+
+    if (c0 + 64 >= e) {  // bin complete
+      const int fx = b % g.n0, fy = (b / g.n0) % g.n1, fz = b / (g.n0 * g.n1);
+      Sink<T, R, NC, MODE> sk{out, b, fx, fy, fz, g};
+      if (MODE == MODE_RECORD || e > s) acc.template finish<MODE>(sk, lane);
+      acc.zero();
+    }
+    if (!more) break;
+    b = nb;
+    s = ns;
+    e = ne;
+    c0 = nc0;
+    cur = nxt;
+  }
+}
+
+template <typename T, int R, int NC, int MODE>
+static hipError_t contract_launch(const GridDev& g, const Particles& P, const int32_t* bin_start,
+                                  const int32_t* perm, double beta, double sigma, void* out, int waves_per_cu,
+                                  hipStream_t s) {
+  const int nbins = g.n0 * g.n1 * g.n2;
+  int blocks = (nbins + CT_WAVES - 1) / CT_WAVES;
+  int cap = 256 * waves_per_cu / CT_WAVES;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((k_contract<T, R, NC, MODE>), dim3(blocks), dim3(64 * CT_WAVES), 0, s, g, (const T*)P.pos,
+                     (const T*)P.w, (const T*)P.B, bin_start, perm, P.np, nbins, (T)beta, (T)sigma, (T*)out);
+  return hipGetLastError();
+}
+
+template <typename T, int MODE>
+static hipError_t contract_t(const GridDev& g, int order, const Particles& P, const int32_t* bin_start,
+                             const int32_t* perm, double beta, double sigma, void* out, hipStream_t s) {
+  const bool ten = P.B != nullptr;
+  // resident waves per CU that the register/LDS budget of each variant allows
+  if (order == 1)
+    return ten ? contract_launch<T, 1, 9, MODE>(g, P, bin_start, perm, beta, sigma, out, 16, s)
+               : contract_launch<T, 1, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 32, s);
+  return ten ? contract_launch<T, 2, 9, MODE>(g, P, bin_start, perm, beta, sigma, out, 4, s)
+             : contract_launch<T, 2, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 16, s);
+}
+
+hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
+                           const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
+  if (mode == MODE_RECORD)
+    return f32 ? contract_t<float, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s)
+               : contract_t<double, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s);
+  return f32 ? contract_t<float, MODE_ATOMIC>(g, order, P, bin_start, perm, beta, sigma, out, s)
+             : contract_t<double, MODE_ATOMIC>(g, order, P, bin_start, perm, beta, sigma, out, s);
+}
+
+size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
+  const int npair = order == 1 ? Geo<1>::NPAIR : Geo<2>::NPAIR;
+  return (size_t)nbins * npair * (tensorial ? 9 : 1) * (f32 ? 4 : 8);
+}
+
+// ---------------------------------------------------------------- phase 2
+// M[g][o][c] = sum over the bins k = g - a whose support holds both g and
+// g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
+template <typename T, int R, int NC>
+__global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
+                                                T* __restrict__ M, size_t total) {
+  constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
+  const size_t e = (size_t)xcd_remap(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % NC);
+  const size_t r = e / NC;
+  const int o = (int)(r % NOFF);
+  const int node = (int)(r / NOFF);
+  const int gx = node % g.n0, gy = (node / g.n0) % g.n1, gz = node / (g.n0 * g.n1);
+  const int ox = o % NO - R, oy = (o / NO) % NO - R, oz = o / (NO * NO) - R;
+  T sum = T(0);
+#pragma unroll
+  for (int az = 0; az < NS; ++az) {
+    const int bz = az + oz;
+    if (bz < 0 || bz > R) continue;
+    int kz = gz - az;
+    kz = kz < 0 ? kz + g.n2 : kz;
+#pragma unroll
+    for (int ay = 0; ay < NS; ++ay) {
+      const int by = ay + oy;
+      if (by < 0 || by > R) continue;
+      int ky = gy - ay;
+      ky = ky < 0 ? ky + g.n1 : ky;
+#pragma unroll
+      for (int ax = 0; ax < NS; ++ax) {
+        const int bx = ax + ox;
+        if (bx < 0 || bx > R) continue;
+        int kx = gx - ax;
+        kx = kx < 0 ? kx + g.n0 : kx;
+        const size_t k = (size_t)kx + (size_t)g.n0 * ((size_t)ky + (size_t)g.n1 * (size_t)kz);
+        const int a = ax + NS * (ay + NS * az), bb = bx + NS * (by + NS * bz);
+        const int pi = a <= bb ? pair_index<N>(a, bb) : pair_index<N>(bb, a);
+        sum += rec[(k * NPAIR + pi) * NC + c];
+      }
+    }
+  }
+  M[e] = accumulate ? M[e] + sum : sum;
+}
+
+template <typename T, int R, int NC>
+static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
+  const size_t total = (size_t)g.n0 * g.n1 * g.n2 * Geo<R>::NOFF * NC;
+  const size_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL((k_gather<T, R, NC>), dim3((unsigned)blocks), dim3(256), 0, s, g, (const T*)rec, accumulate,
+                     (T*)M, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
+                         void* M, hipStream_t s) {
+  if (f32) {
+    if (order == 1)
+      return tensorial ? gather_launch<float, 1, 9>(g, rec, accumulate, M, s)
+                       : gather_launch<float, 1, 1>(g, rec, accumulate, M, s);
+    return tensorial ? gather_launch<float, 2, 9>(g, rec, accumulate, M, s)
+                     : gather_launch<float, 2, 1>(g, rec, accumulate, M, s);
+  }
+  if (order == 1)
+    return tensorial ? gather_launch<double, 1, 9>(g, rec, accumulate, M, s)
+                     : gather_launch<double, 1, 1>(g, rec, accumulate, M, s);
+  return tensorial ? gather_launch<double, 2, 9>(g, rec, accumulate, M, s)
+                   : gather_launch<double, 2, 1>(g, rec, accumulate, M, s);
+}
+
+}  // namespace mmk

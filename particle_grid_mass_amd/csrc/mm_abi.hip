@@ -3,7 +3,7 @@
 #include <math.h>
 
 #include "../../include/mm.h"
-#include "mm_internal.h"
+#include "mm_contract.h"
 
 using namespace mmk;
 
@@ -11,7 +11,7 @@ namespace {
 
 constexpr int64_t kMaxI32 = 2147483647LL;
 
-bool finite(double v) { return isfinite(v) != 0; }
+bool is_finite_d(double v) { return isfinite(v) != 0; }
 
 mm_status check_grid(const mm_grid* g, int order, int64_t* nnodes) {
   if (!g) return MM_ERR_NULL;
@@ -19,7 +19,7 @@ mm_status check_grid(const mm_grid* g, int order, int64_t* nnodes) {
   int64_t nn = 1;
   for (int d = 0; d < 3; ++d) {
     if (g->n[d] < 2 * order + 1) return MM_ERR_ARG;
-    if (!(g->h[d] > 0.0) || !finite(g->h[d]) || !finite(g->origin[d])) return MM_ERR_ARG;
+    if (!(g->h[d] > 0.0) || !is_finite_d(g->h[d]) || !is_finite_d(g->origin[d])) return MM_ERR_ARG;
     nn *= g->n[d];
   }
   if (nn >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -54,7 +54,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (st != MM_OK) return st;
   if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
   if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC) return MM_ERR_ARG;
-  if (!finite(sigma) || !finite(beta)) return MM_ERR_ARG;
+  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
   if (!M) return MM_ERR_NULL;
@@ -63,27 +63,34 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     if (!pos || !w || (tensorial && !B)) return MM_ERR_NULL;
     if (mfma && (!bin_start || !perm)) return MM_ERR_NULL;
   }
-  const size_t need = 0;  // the atomic deposits need no workspace
+  const bool f32 = dt == MM_F32;
+  // The two-phase deposit keeps one packed record per bin; the atomic
+  // deposits need no workspace.
+  const bool records = algo == MM_ALGO_MFMA && np > 0;
+  const size_t need = records ? record_bytes(order, f32, tensorial, nnodes) : 0;
   if (!ws) {
     *ws_bytes = need;
     return MM_OK;
   }
   if (*ws_bytes < need) return MM_ERR_WORKSPACE;
 
-  const bool f32 = dt == MM_F32;
   const int noff = order == 1 ? 27 : 125;
   const size_t count = (size_t)nnodes * noff * (tensorial ? 9 : 1);
   hipStream_t s = (hipStream_t)stream;
   GridDev g = to_dev(grid);
   hipError_t e = hipSuccess;
-  if (!accumulate) e = launch_fill_zero(M, count, f32, s);
-  if (e != hipSuccess) return MM_ERR_HIP;
-  if (np == 0) return MM_OK;
   Particles P{pos, w, tensorial ? B : nullptr, (int)np};
+  if (records) {
+    e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
+    if (e == hipSuccess) e = launch_gather(g, order, f32, tensorial, ws, accumulate, M, s);
+    return hip_status(e);
+  }
+  if (!accumulate) e = launch_fill_zero(M, count, f32, s);
+  if (e != hipSuccess || np == 0) return hip_status(e);
   if (algo == MM_ALGO_ATOMIC)
     e = launch_atomic_scatter(g, order, f32, P, beta, sigma, M, s);
   else
-    e = launch_mfma_atomic(g, order, f32, P, bin_start, perm, beta, sigma, M, s);
+    e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_ATOMIC, M, s);
   return hip_status(e);
 }
 
@@ -126,6 +133,41 @@ mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t
                             size_t* ws_bytes, mm_stream_t stream) {
   return assemble_common(grid, order, dt, np, pos, w, B, true, bin_start, perm, beta, sigma, algo, M, ws, ws_bytes,
                          stream, accumulate);
+}
+
+mm_status mm_contract_bins(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
+                           const void* B, const int32_t* bin_start, const int32_t* perm, double beta, double sigma,
+                           void* rec, size_t* rec_bytes, mm_stream_t stream) {
+  if (!rec_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
+  const bool f32 = dt == MM_F32;
+  const size_t need = record_bytes(order, f32, B != nullptr, nnodes);
+  if (!rec) {
+    *rec_bytes = need;
+    return MM_OK;
+  }
+  if (*rec_bytes < need) return MM_ERR_WORKSPACE;
+  Particles P{pos, w, B, (int)np};
+  return hip_status(
+      launch_contract(to_dev(grid), order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, (hipStream_t)stream));
+}
+
+mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
+                             int accumulate, void* M, mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!rec || !M) return MM_ERR_NULL;
+  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, M,
+                                  (hipStream_t)stream));
 }
 
 const char* mm_status_string(mm_status s) {

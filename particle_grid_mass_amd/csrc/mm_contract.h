@@ -1,0 +1,24 @@
+// Launchers of the per-bin matrix-core contraction (phase 1) and the record
+// gather (phase 2). Not part of the public API.
+#pragma once
+
+#include "mm_internal.h"
+
+namespace mmk {
+
+enum { MODE_RECORD = 0, MODE_ATOMIC = 1 };
+
+// Phase 1: per-bin local matrices. MODE_RECORD writes packed upper-triangle
+// records to `out` (record_bytes() long); MODE_ATOMIC adds into the stencil
+// matrix `out` with hardware atomics.
+hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
+                           const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s);
+
+// Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
+size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
+
+// Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o.
+hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
+                         void* M, hipStream_t s);
+
+}  // namespace mmk

@@ -24,10 +24,6 @@ hipError_t launch_fill_zero(void* M, size_t count, bool f32, hipStream_t s);
 hipError_t launch_atomic_scatter(const GridDev& g, int order, bool f32, const Particles& P, double beta,
                                  double sigma, void* M, hipStream_t s);
 
-// Per-bin matrix-core contraction with a global-atomic deposit.
-hipError_t launch_mfma_atomic(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
-                              const int32_t* perm, double beta, double sigma, void* M, hipStream_t s);
-
 // Binning: stable LSD radix sort of first-support-node keys.
 size_t bin_workspace_bytes(int64_t np, int64_t nbins);
 hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, int np, int nbins, int32_t* bin_start,
