@@ -37,7 +37,8 @@
  *           NULL = default stream); no call synchronizes the host.
  *  Workspace (CUB style): call with ws == NULL to receive the required byte
  *           count in *ws_bytes (nothing is enqueued, MM_OK is returned); then
- *           call again with a device buffer of at least that many bytes.
+ *           call again with a device buffer of at least that many bytes,
+ *           aligned to 16 bytes (else MM_ERR_ARG).
  *  Errors:  arguments are validated on the host before any HIP call;
  *           a failed launch returns MM_ERR_HIP. Positions must be finite and
  *           |(x - origin)/h| < 2^31; that precondition is not checked.
@@ -139,7 +140,8 @@ mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t
  *   rec[bin][pair(a,b)][comp] = sigma * sum_{p in bin} t_p^comp W_pa W_pb,
  * for support rows a <= b (upper triangle, pair(a,b) = a*N - a(a-1)/2 + b - a,
  * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp).
- *  rec       device buffer of *rec_bytes bytes (query with rec == NULL).
+ *  rec       device buffer of *rec_bytes bytes (query with rec == NULL),
+ *            16-byte aligned (else MM_ERR_ARG).
  *  Other arguments as for mm_assemble_ecsim; bin_start/perm are required.
  *
  * mm_deposit_records - the sparse stencil deposition of Sec. 3.4: every

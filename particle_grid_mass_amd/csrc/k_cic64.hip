@@ -1,0 +1,252 @@
+// First-order (CIC) fp64 per-bin contraction on v_mfma_f64_4x4x4_4b, phase 1
+// of the two-phase assembly.
+//
+// Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+// Particle-In-Cell Methods": every particle of a CIC cell touches the same
+// 8 corner nodes (Sec. 2.3), so the cell's local matrix is
+//   Mhat^c_ab = sum_p t_p^c W_pa W_pb                       (Sec. 3.1, Eq. 15)
+// accumulated over batches of K_t particles (Sec. 3.2); the lower off-diagonal
+// quadrant is skipped by the spatial symmetry Mhat_ab = Mhat_ba (Table 1).
+//
+// gfx950 mapping. One wave owns a group of four consecutive bins and gives
+// each bin one of the four 4x4x4 blocks of the instruction, so the block
+// results are final (no cross-block reduction). The 8 support rows split by
+// the z corner into two halves; per component three instructions form the
+// quadrants Q00, Q01, Q11 for four particles of each of the four bins (K_t = 4).
+// Per 16 particles: 27 instructions (ECSIM) or 3 (scalar).
+//
+//  * Particle preparation runs one particle per lane (16 per bin per chunk):
+//    the support weights W_a (Eq. 12) and the coefficients t^c = sigma w alpha^c
+//    are computed once and staged in LDS, W interleaved so that the two rows a
+//    lane feeds (r and 4 + r) are one 16-byte read.
+//  * The permutation entries of the chunk after next and the particle data of
+//    the next chunk are in flight while the current chunk is contracted.
+//  * A finished group stages its four packed upper-triangle records in LDS and
+//    writes them with 16-byte stores (the records of consecutive bins are
+//    contiguous).
+#include "mm_contract.h"
+
+namespace mmk {
+
+namespace {
+
+constexpr int NB = 4;          // bins per wave group (= 4x4x4 blocks)
+constexpr int CH = 16;         // particles per bin per chunk
+constexpr int SW = 10;         // staged doubles per particle for W (8 used)
+constexpr int NPAIR = 36;      // packed upper triangle of 8 x 8
+
+template <int NC>
+struct Cfg {
+  static constexpr int ST = NC == 9 ? 10 : 2;                 // staged doubles per particle for t
+  static constexpr int STAGE = 64 * (SW + ST);                 // doubles of particle staging
+  static constexpr int REC = NB * NPAIR * NC;                  // doubles of one group's records
+  static constexpr int SMEM = STAGE > REC ? STAGE : REC;
+};
+
+// A group is bins 4g .. 4g+3. Prep lane l serves bin 4g + (l >> 4): `s` and
+// `n` are that bin's start in perm and particle count; `maxn` is the largest
+// count of the group (wave-uniform).
+struct Group {
+  int s, n;
+  int maxn;
+  int nchunks;
+};
+
+__device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int nbins, int np,
+                                            int lane) {
+  Group G;
+  const int bin = NB * g + (lane >> 4);
+  int s = 0, e = 0;
+  if (bin < nbins) {
+    s = bin_start[bin];
+    e = bin_start[bin + 1];
+    s = s < 0 ? 0 : (s > np ? np : s);
+    e = e < s ? s : (e > np ? np : e);
+  }
+  G.s = s;
+  G.n = e - s;
+  int m = __builtin_amdgcn_readlane(G.n, 0);
+  m = max(m, __builtin_amdgcn_readlane(G.n, 16));
+  m = max(m, __builtin_amdgcn_readlane(G.n, 32));
+  m = max(m, __builtin_amdgcn_readlane(G.n, 48));
+  G.maxn = m;
+  G.nchunks = m > 0 ? (m + CH - 1) / CH : 1;  // an empty group still writes zero records
+  return G;
+}
+
+// Permutation entry that prep lane `lane` loads for chunk j of group G (-1: none).
+__device__ __forceinline__ int chunk_perm(const int32_t* __restrict__ perm, const Group& G, int j, int lane) {
+  const int q = j * CH + (lane & 15);
+  return q < G.n ? perm[G.s + q] : -1;
+}
+
+struct Raw {
+  double x, y, z, w, bx, by, bz;
+  bool valid;
+};
+
+template <int NC>
+__device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
+                                        const double* __restrict__ Bf, int p, int np) {
+  Raw r{0, 0, 0, 0, 0, 0, 0, false};
+  if ((unsigned)p < (unsigned)np) {
+    r.valid = true;
+    r.x = pos[3 * (size_t)p];
+    r.y = pos[3 * (size_t)p + 1];
+    r.z = pos[3 * (size_t)p + 2];
+    r.w = w[p];
+    if (NC == 9) {
+      r.bx = Bf[3 * (size_t)p];
+      r.by = Bf[3 * (size_t)p + 1];
+      r.bz = Bf[3 * (size_t)p + 2];
+    }
+  }
+  return r;
+}
+
+// Weights and coefficients of the lane's particle into LDS slot `lane` (zeros
+// for a lane without a particle). W_a, a = ax + 2 ay + 4 az, is stored at
+// 2 (a & 3) + (a >> 2).
+template <int NC>
+__device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, double* sm,
+                                      int lane) {
+  double wx[2] = {0, 0}, wy[2] = {0, 0}, wz[2] = {0, 0}, t[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) t[c] = 0.0;
+  if (r.valid) {
+    axis_support<double, 1>(r.x, g.o0, g.h0, g.n0, wx);
+    axis_support<double, 1>(r.y, g.o1, g.h1, g.n1, wy);
+    axis_support<double, 1>(r.z, g.o2, g.h2, g.n2, wz);
+    const double f = sigma * r.w;
+    if (NC == 9)
+      response<double>(r.bx, r.by, r.bz, beta, f, t);
+    else
+      t[0] = f;
+  }
+  double* sw = sm + lane * SW;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const double wxy = wx[r4 & 1] * wy[r4 >> 1];
+    double2 v;
+    v.x = wxy * wz[0];
+    v.y = wxy * wz[1];
+    *reinterpret_cast<double2*>(sw + 2 * r4) = v;
+  }
+  double* st = sm + 64 * SW + lane * Cfg<NC>::ST;
+  if (NC == 9) {
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) *reinterpret_cast<double2*>(st + c) = double2{t[c], t[c + 1]};
+    st[8] = t[NC - 1];
+  } else {
+    st[0] = t[0];
+  }
+}
+
+template <int NC>
+struct Acc {
+  double q[NC][3];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c][0] = q[c][1] = q[c][2] = 0.0;
+  }
+};
+
+}  // namespace
+
+template <int NC>
+__global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restrict__ pos,
+                                              const double* __restrict__ w, const double* __restrict__ Bf,
+                                              const int32_t* __restrict__ bin_start,
+                                              const int32_t* __restrict__ perm, int np, int nbins, double beta,
+                                              double sigma, double* __restrict__ rec) {
+  __shared__ __attribute__((aligned(16))) double sm[Cfg<NC>::SMEM];
+  const int lane = threadIdx.x;
+  const int ngroups = (nbins + NB - 1) / NB;
+  const int grp = blockIdx.x;
+  if (grp >= ngroups) return;
+  const Group G = load_group(bin_start, grp, nbins, np, lane);
+
+  // MFMA lane roles: particle k of the K_t batch, block (= bin) mb, row/column mr.
+  const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
+
+  Raw raw = load_raw<NC>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  int pnext = chunk_perm(perm, G, 1, lane);
+  Acc<NC> acc;
+  acc.zero();
+
+  for (int j = 0; j < G.nchunks; ++j) {
+    stage<NC>(raw, g, beta, sigma, sm, lane);
+    __syncthreads();
+    // In flight during this chunk's rounds: the next chunk's particle data and
+    // the permutation entries of the chunk after it.
+    raw = load_raw<NC>(pos, w, Bf, pnext, np);
+    const int p2 = chunk_perm(perm, G, j + 2, lane);
+
+    const int left = G.maxn - j * CH;
+    const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
+    for (int rd = 0; rd < nr; ++rd) {
+      const int slot = CH * mb + 4 * rd + mk;
+      const double2 wv = *reinterpret_cast<const double2*>(sm + slot * SW + 2 * mr);
+      const double* st = sm + 64 * SW + slot * Cfg<NC>::ST;
+      double tv[NC];
+      if (NC == 9) {
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+          const double2 tt = *reinterpret_cast<const double2*>(st + c);
+          tv[c] = tt.x;
+          tv[c + 1] = tt.y;
+        }
+        tv[NC - 1] = st[8];
+      } else {
+        tv[0] = st[0];
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const double alo = tv[c] * wv.x, ahi = tv[c] * wv.y;
+        acc.q[c][0] = mfma_f64_4x4x4(alo, wv.x, acc.q[c][0]);
+        acc.q[c][1] = mfma_f64_4x4x4(alo, wv.y, acc.q[c][1]);
+        acc.q[c][2] = mfma_f64_4x4x4(ahi, wv.y, acc.q[c][2]);
+      }
+    }
+    __syncthreads();
+    pnext = p2;
+  }
+
+  // D_blk[i][j] sits in lane (i << 4) | (blk << 2) | j. Stage the packed
+  // records rec[bin][pair(a, b)][c] (a <= b, pair(a, b) = 8a - a(a-1)/2 + b - a)
+  // of the group's bins in LDS, then write them with 16-byte stores.
+  const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
+  double* sr = sm + db * NPAIR * NC;
+  const int p00 = di * 8 - (di * (di - 1)) / 2 + (dj - di);
+  const int p01 = di * 8 - (di * (di - 1)) / 2 + (4 + dj - di);
+  const int a1 = 4 + di;
+  const int p11 = a1 * 8 - (a1 * (a1 - 1)) / 2 + (dj - di);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (di <= dj) sr[p00 * NC + c] = acc.q[c][0];
+    sr[p01 * NC + c] = acc.q[c][1];
+    if (di <= dj) sr[p11 * NC + c] = acc.q[c][2];
+  }
+  __syncthreads();
+  const int b0 = NB * grp;
+  const int nvalid = nbins - b0 < NB ? nbins - b0 : NB;
+  const int n2 = nvalid * NPAIR * NC / 2;  // NPAIR is even, so whole 16-byte words
+  double2* dst = reinterpret_cast<double2*>(rec + (size_t)b0 * NPAIR * NC);
+  const double2* src = reinterpret_cast<const double2*>(sm);
+  for (int i = lane; i < n2; i += 64) dst[i] = src[i];
+}
+
+hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s) {
+  const int nbins = g.n0 * g.n1 * g.n2;
+  const int ngroups = (nbins + NB - 1) / NB;  // one single-wave workgroup per group of four bins
+  if (P.B)
+    hipLaunchKernelGGL(k_cic64<9>, dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos, (const double*)P.w,
+                       (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  else
+    hipLaunchKernelGGL(k_cic64<1>, dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos, (const double*)P.w,
+                       (const double*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  return hipGetLastError();
+}
+
+}  // namespace mmk

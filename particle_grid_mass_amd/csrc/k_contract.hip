@@ -413,6 +413,8 @@ static hipError_t contract_t(const GridDev& g, int order, const Particles& P, co
 
 hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
+  if (mode == MODE_RECORD && order == 1 && !f32)
+    return launch_cic64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
   if (mode == MODE_RECORD)
     return f32 ? contract_t<float, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s)
                : contract_t<double, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s);

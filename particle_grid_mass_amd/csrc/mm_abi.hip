@@ -73,6 +73,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     return MM_OK;
   }
   if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+  if (need > 0 && ((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
 
   const int noff = order == 1 ? 27 : 125;
   const size_t count = (size_t)nnodes * noff * (tensorial ? 9 : 1);
@@ -154,6 +155,7 @@ mm_status mm_contract_bins(const mm_grid* grid, int order, mm_dtype dt, int64_t 
     return MM_OK;
   }
   if (*rec_bytes < need) return MM_ERR_WORKSPACE;
+  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
   Particles P{pos, w, B, (int)np};
   return hip_status(
       launch_contract(to_dev(grid), order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, (hipStream_t)stream));

@@ -14,6 +14,10 @@ enum { MODE_RECORD = 0, MODE_ATOMIC = 1 };
 hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s);
 
+// Phase 1 for CIC fp64 records: four bins per wave, one per 4x4x4 block.
+hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s);
+
 // Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 
