@@ -8,186 +8,235 @@
 // makes each key one support group (for CIC: the cell), so one bin = one
 // group with a single local matrix.
 //
-// Pipeline (all on the caller's stream):
-//   k_keys          key[p] = first support node of particle p
-//   per 8-bit digit: k_radix_hist (per-tile digit counts, digit-major)
-//                    exclusive scan of the counts (multi-level)
-//                    k_radix_scatter (stable in-tile ranks by wave ballots)
-//   k_bin_bounds    bin_start[k] = lower_bound(sorted keys, k)
+// Pipeline (all on the caller's stream), 8-bit digits, npass = ceil(bits/8):
+//   k_keys_hist   key[p] = first support node of particle p, and per tile of
+//                 4096 particles the counts of the first digit
+//   per pass d:   k_hist (d > 0: per-tile counts of digit d in the order the
+//                 previous pass left), k_scan_cols (exclusive scan of each
+//                 digit's column over the tiles, plus the column totals),
+//                 k_scatter (stable in-tile ranks: each wave ranks its 1024
+//                 particles in index order with wave-private digit counters;
+//                 position = digit base + tile prefix + wave prefix + rank)
+//   k_bounds      bin_start[k] = first sorted position whose key is >= k
 #include "mm_internal.h"
 
 namespace mmk {
 
-constexpr int RS_THREADS = 256;
-constexpr int RS_ITEMS = 16;
-constexpr int RS_TILE = RS_THREADS * RS_ITEMS;  // elements per block
-constexpr int SCAN_THREADS = 256;
-constexpr int SCAN_ITEMS = 8;
-constexpr int SCAN_TILE = SCAN_THREADS * SCAN_ITEMS;
+namespace {
 
-template <typename T, int R>
-__global__ void k_keys(GridDev g, const T* __restrict__ pos, int np, uint32_t* __restrict__ keys) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < np) keys[i] = (uint32_t)particle_key<T, R>(pos + 3 * (size_t)i, g);
+constexpr int BT = 256;                // threads per block
+constexpr int BI = 16;                 // items per thread
+constexpr int TILE = BT * BI;          // particles per tile
+constexpr int NWV = BT / 64;           // waves per block
+constexpr int WITEMS = TILE / NWV;     // particles per wave in the scatter
+
+__device__ __forceinline__ unsigned long long lanemask_lt() { return __lanemask_lt(); }
+
+// Lanes of the wave whose 8-bit digit equals this lane's (among `valid` lanes).
+__device__ __forceinline__ unsigned long long match_digit(int d, bool valid) {
+  unsigned long long peers = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (d >> b) & 1;
+    const unsigned long long m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
 }
 
-__global__ __launch_bounds__(RS_THREADS) void k_radix_hist(const uint32_t* __restrict__ keys, int n, int shift,
-                                                           int32_t* __restrict__ ghist, int nblocks) {
+}  // namespace
+
+// Adds this wave's digits to the LDS histogram h. Consecutive lanes hold
+// consecutive particles and the valid lanes are a prefix of the wave, so equal
+// digits of a cell-sorted input form runs; each run is one LDS atomic.
+__device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int lane) {
+  const int end = __popcll(__ballot(valid));
+  const int dprev = __shfl_up(d, 1);
+  const bool head = valid && (lane == 0 || d != dprev);
+  const unsigned long long heads = __ballot(head);
+  if (head) {
+    const unsigned long long after = lane == 63 ? 0ull : (heads >> (lane + 1));
+    const int next = after ? lane + 1 + __ffsll((long long)after) - 1 : end;
+    atomicAdd(&h[d], next - lane);
+  }
+}
+
+// Keys, and per tile of TILE particles the counts of the first digit.
+template <typename T, int R>
+__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np,
+                                                  uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
+                                                  int ntiles) {
   __shared__ int h[256];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   h[tid] = 0;
   __syncthreads();
-  const int base = blockIdx.x * RS_TILE;
-  for (int it = 0; it < RS_ITEMS; ++it) {
-    int idx = base + it * RS_THREADS + tid;
-    if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & 255], 1);
-  }
-  __syncthreads();
-  ghist[(size_t)tid * nblocks + blockIdx.x] = h[tid];
-}
-
-// Stable scatter: elements are ranked in index order (round, wave, lane).
-__global__ __launch_bounds__(RS_THREADS) void k_radix_scatter(const uint32_t* __restrict__ keys_in,
-                                                              const int32_t* __restrict__ vals_in, int n, int shift,
-                                                              const int32_t* __restrict__ goff, int nblocks,
-                                                              uint32_t* __restrict__ keys_out,
-                                                              int32_t* __restrict__ vals_out) {
-  __shared__ int cnt[256];
-  __shared__ int wcnt[RS_THREADS / 64][256];
-  __shared__ int boff[256];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  cnt[tid] = 0;
-  boff[tid] = goff[(size_t)tid * nblocks + blockIdx.x];
-#pragma unroll
-  for (int wv = 0; wv < RS_THREADS / 64; ++wv) wcnt[wv][tid] = 0;
-  __syncthreads();
-  const unsigned long long lt = __lanemask_lt();
-  const int base = blockIdx.x * RS_TILE;
-  for (int it = 0; it < RS_ITEMS; ++it) {
-    const int idx = base + it * RS_THREADS + tid;
-    const bool valid = idx < n;
-    uint32_t key = valid ? keys_in[idx] : 0u;
-    int32_t val = valid ? (vals_in ? vals_in[idx] : idx) : 0;
-    int d = (int)((key >> shift) & 255u);
-    unsigned long long peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      bool bit = (d >> b) & 1;
-      unsigned long long m = __ballot(valid && bit);
-      peers &= bit ? m : ~m;
-    }
-    int rank = __popcll(peers & lt);
-    if (valid && rank == 0) wcnt[wave][d] = __popcll(peers);
-    __syncthreads();
+  const int tile = blockIdx.x;
+  const size_t base = (size_t)tile * TILE;
+  for (int it = 0; it < BI; ++it) {
+    const size_t idx = base + (size_t)it * BT + tid;
+    const bool valid = idx < (size_t)np;
+    uint32_t key = 0;
     if (valid) {
-      int pos = boff[d] + cnt[d] + rank;
-      for (int wv = 0; wv < wave; ++wv) pos += wcnt[wv][d];
-      keys_out[pos] = key;
-      vals_out[pos] = val;
+      key = (uint32_t)particle_key<T, R>(pos + 3 * idx, g);
+      keys[idx] = key;
     }
-    __syncthreads();
-    int tot = 0;
-#pragma unroll
-    for (int wv = 0; wv < RS_THREADS / 64; ++wv) {
-      tot += wcnt[wv][tid];
-      wcnt[wv][tid] = 0;
-    }
-    cnt[tid] += tot;
-    __syncthreads();
+    count_digit_runs(h, (int)(key & 255u), valid, lane);
   }
+  __syncthreads();
+  ghist[(size_t)tid * ntiles + tile] = h[tid];
 }
 
-// Exclusive scan of one tile per block; tile totals go to sums[block].
-__global__ __launch_bounds__(SCAN_THREADS) void k_scan_tile(const int32_t* in, int32_t* out, int n,
-                                                            int32_t* sums) {
-  __shared__ int wsum[SCAN_THREADS / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t base = (size_t)blockIdx.x * SCAN_TILE + (size_t)tid * SCAN_ITEMS;
-  int v[SCAN_ITEMS];
-  int run = 0;
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    size_t idx = base + i;
-    v[i] = idx < (size_t)n ? in[idx] : 0;
-    run += v[i];
+// Per-tile counts of the digit at `shift` of keys in their current order.
+__global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, int np, int shift,
+                                             int32_t* __restrict__ ghist, int ntiles) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  h[tid] = 0;
+  __syncthreads();
+  const int tile = blockIdx.x;
+  const size_t base = (size_t)tile * TILE;
+  for (int it = 0; it < BI; ++it) {
+    const size_t idx = base + (size_t)it * BT + tid;
+    const bool valid = idx < (size_t)np;
+    const uint32_t key = valid ? keys[idx] : 0u;
+    count_digit_runs(h, (int)((key >> shift) & 255u), valid, lane);
   }
-  // inclusive wave scan of thread totals
-  int incl = run;
+  __syncthreads();
+  ghist[(size_t)tid * ntiles + tile] = h[tid];
+}
+
+// One block per digit column: exclusive scan over the tiles in place, column
+// total to totals[digit].
+__global__ __launch_bounds__(256) void k_scan_cols(int32_t* __restrict__ ghist, int ntiles,
+                                                   int32_t* __restrict__ totals) {
+  __shared__ int wsum[4];
+  const int col = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* c = ghist + (size_t)col * ntiles;
+  int carry = 0;
+  for (int b0 = 0; b0 < ntiles; b0 += 256 * 8) {
+    int v[8], run = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = b0 + tid * 8 + i;
+      v[i] = idx < ntiles ? c[idx] : 0;
+      run += v[i];
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) wbase += wsum[w];
+      total += wsum[w];
+    }
+    int excl = carry + wbase + incl - run;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = b0 + tid * 8 + i;
+      if (idx < ntiles) c[idx] = excl;
+      excl += v[i];
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) totals[col] = carry;
+}
+
+// Stable scatter of one 8-bit digit pass. vals_in == NULL means the identity.
+__global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ keys_in,
+                                                const int32_t* __restrict__ vals_in, int np, int shift,
+                                                const int32_t* __restrict__ ghist, const int32_t* __restrict__ totals,
+                                                int ntiles, uint32_t* __restrict__ keys_out,
+                                                int32_t* __restrict__ vals_out) {
+  __shared__ int wcnt[NWV][256];
+  __shared__ int wpre[NWV][256];
+  __shared__ int dsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x;
+
+  // digit base of this tile: exclusive prefix of the pass totals over digits
+  // plus this tile's prefix within the digit's column
+  const int tot = totals[tid];
+  int incl = tot;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(incl, off);
+    const int y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
-  if (lane == 63) wsum[wave] = incl;
+  if (lane == 63) dsum[wave] = incl;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) wcnt[w][tid] = 0;
   __syncthreads();
-  int wbase = 0, total = 0;
+  int dbase = incl - tot;
+  for (int w = 0; w < wave; ++w) dbase += dsum[w];
+  dbase += ghist[(size_t)tid * ntiles + tile];
+
+  // rank this wave's particles in index order
+  const size_t base = (size_t)tile * TILE + (size_t)wave * WITEMS;
+  const unsigned long long lt = lanemask_lt();
+  uint32_t k[BI];
+  int32_t v[BI];
+  int rk[BI];
 #pragma unroll
-  for (int wv = 0; wv < SCAN_THREADS / 64; ++wv) {
-    if (wv < wave) wbase += wsum[wv];
-    total += wsum[wv];
+  for (int r = 0; r < BI; ++r) {
+    const size_t idx = base + (size_t)r * 64 + lane;
+    const bool valid = idx < (size_t)np;
+    k[r] = valid ? keys_in[idx] : 0u;
+    v[r] = valid ? (vals_in ? vals_in[idx] : (int32_t)idx) : 0;
+    const int d = (int)((k[r] >> shift) & 255u);
+    const unsigned long long peers = match_digit(d, valid);
+    const int rank = __popcll(peers & lt);
+    const int cnt = wcnt[wave][d];
+    rk[r] = valid ? cnt + rank : -1;
+    if (valid && rank == 0) wcnt[wave][d] = cnt + __popcll(peers);
   }
-  int excl = wbase + incl - run;
+  __syncthreads();
+  {
+    int run = dbase;
 #pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    size_t idx = base + i;
-    if (idx < (size_t)n) out[idx] = excl;
-    excl += v[i];
+    for (int w = 0; w < NWV; ++w) {
+      wpre[w][tid] = run;
+      run += wcnt[w][tid];
+    }
   }
-  if (tid == 0) sums[blockIdx.x] = total;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < BI; ++r) {
+    if (rk[r] >= 0) {
+      const int d = (int)((k[r] >> shift) & 255u);
+      const int dst = wpre[wave][d] + rk[r];
+      if ((unsigned)dst < (unsigned)np) {  // always true for consistent inputs; guards the writes
+        keys_out[dst] = k[r];
+        vals_out[dst] = v[r];
+      }
+    }
+  }
 }
 
-__global__ __launch_bounds__(SCAN_THREADS) void k_scan_add(int32_t* out, int n, const int32_t* sums) {
-  const int add = sums[blockIdx.x];
-  const size_t base = (size_t)blockIdx.x * SCAN_TILE;
-  for (int i = threadIdx.x; i < SCAN_TILE; i += SCAN_THREADS) {
-    size_t idx = base + i;
-    if (idx < (size_t)n) out[idx] += add;
-  }
-}
-
-static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-
-static size_t scan_tmp_ints(size_t n) {
-  size_t total = 0;
-  while (n > 1) {
-    size_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
-    total += align256(nb * 4) / 4;
-    n = nb;
-  }
-  return total + 64;
-}
-
-static hipError_t scan_exclusive(const int32_t* in, int32_t* out, int n, int32_t* tmp, hipStream_t s) {
-  int nb = (n + SCAN_TILE - 1) / SCAN_TILE;
-  hipLaunchKernelGGL(k_scan_tile, dim3(nb), dim3(SCAN_THREADS), 0, s, in, out, n, tmp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nb <= 1) return e;
-  int32_t* next = tmp + align256((size_t)nb * 4) / 4;
-  e = scan_exclusive(tmp, tmp, nb, next, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_add, dim3(nb), dim3(SCAN_THREADS), 0, s, out, n, (const int32_t*)tmp);
-  return hipGetLastError();
-}
-
-// bin_start[k] = number of sorted keys < k, for k in [0, nbins].
-__global__ void k_bin_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start) {
-  int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k > nbins) return;
-  int lo = 0, hi = np;
-  while (lo < hi) {
-    int mid = lo + ((hi - lo) >> 1);
-    if (skeys[mid] < (uint32_t)k)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  bin_start[k] = lo;
+// bin_start[k] = lower bound of k in the sorted keys, for k in [0, nbins]:
+// thread i (0 <= i <= np) writes i for every k in (skeys[i-1], skeys[i]]
+// (with skeys[-1] = -1 and skeys[np] = nbins), so each entry is written once.
+__global__ void k_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i > np) return;
+  const int lo = i == 0 ? -1 : (int)skeys[i - 1];
+  int hi = i == np ? nbins : (int)skeys[i];
+  hi = hi > nbins ? nbins : hi;
+  for (int k = lo + 1; k <= hi; ++k) bin_start[k] = i;
 }
 
 __global__ void k_fill_i32(int32_t* p, int n, int v) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static int digit_passes(int64_t nbins) {
   int bits = 0;
@@ -201,17 +250,16 @@ struct BinWs {
   uint32_t* keysB;
   int32_t* vtmp;
   int32_t* ghist;
-  int32_t* scan_tmp;
+  int32_t* totals;
   size_t bytes;
 };
 
 static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
-  (void)nbins;
   BinWs w;
   size_t off = 0;
   char* b = (char*)base;
-  size_t nblocks = (size_t)((np + RS_TILE - 1) / RS_TILE);
-  size_t nh = 256 * (nblocks > 0 ? nblocks : 1);
+  (void)nbins;
+  const size_t ntiles = (size_t)((np + TILE - 1) / TILE);
   w.keysA = (uint32_t*)(b + off);
   off += align256((size_t)np * 4);
   w.keysB = (uint32_t*)(b + off);
@@ -219,9 +267,9 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
   w.vtmp = (int32_t*)(b + off);
   off += align256((size_t)np * 4);
   w.ghist = (int32_t*)(b + off);
-  off += align256(nh * 4);
-  w.scan_tmp = (int32_t*)(b + off);
-  off += align256(scan_tmp_ints(nh) * 4);
+  off += align256((size_t)256 * (ntiles > 0 ? ntiles : 1) * 4);
+  w.totals = (int32_t*)(b + off);
+  off += align256((size_t)256 * 4);
   w.bytes = off;
   return w;
 }
@@ -229,12 +277,12 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
 size_t bin_workspace_bytes(int64_t np, int64_t nbins) { return bin_layout(nullptr, np, nbins).bytes; }
 
 template <typename T>
-static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, uint32_t* keys, hipStream_t s) {
-  dim3 grid((np + 255) / 256), block(256);
+static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, uint32_t* keys, int32_t* ghist,
+                         int ntiles, hipStream_t s) {
   if (order == 1)
-    hipLaunchKernelGGL((k_keys<T, 1>), grid, block, 0, s, g, (const T*)pos, np, keys);
+    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles);
   else
-    hipLaunchKernelGGL((k_keys<T, 2>), grid, block, 0, s, g, (const T*)pos, np, keys);
+    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles);
   return hipGetLastError();
 }
 
@@ -245,29 +293,31 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
     return hipGetLastError();
   }
   BinWs w = bin_layout(ws, np, nbins);
-  hipError_t e = f32 ? keys_t<float>(g, order, pos, np, w.keysA, s) : keys_t<double>(g, order, pos, np, w.keysA, s);
+  const int npass = digit_passes(nbins);
+  const int ntiles = (np + TILE - 1) / TILE;
+  hipError_t e = f32 ? keys_t<float>(g, order, pos, np, w.keysA, w.ghist, ntiles, s)
+                     : keys_t<double>(g, order, pos, np, w.keysA, w.ghist, ntiles, s);
   if (e != hipSuccess) return e;
-  const int passes = digit_passes(nbins);
-  const int nblocks = (np + RS_TILE - 1) / RS_TILE;
-  const int nh = 256 * nblocks;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;
   const int32_t* vin = nullptr;
-  for (int p = 0; p < passes; ++p) {
-    int32_t* vout = ((passes - 1 - p) % 2 == 0) ? perm : w.vtmp;
-    hipLaunchKernelGGL(k_radix_hist, dim3(nblocks), dim3(RS_THREADS), 0, s, (const uint32_t*)kin, np, 8 * p, w.ghist,
-                       nblocks);
+  for (int p = 0; p < npass; ++p) {
+    if (p > 0) {
+      hipLaunchKernelGGL(k_hist, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, np, 8 * p, w.ghist, ntiles);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_scan_cols, dim3(256), dim3(256), 0, s, w.ghist, ntiles, w.totals);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = scan_exclusive(w.ghist, w.ghist, nh, w.scan_tmp, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_radix_scatter, dim3(nblocks), dim3(RS_THREADS), 0, s, (const uint32_t*)kin, vin, np, 8 * p,
-                       (const int32_t*)w.ghist, nblocks, kout, vout);
+    int32_t* vout = ((npass - 1 - p) % 2 == 0) ? perm : w.vtmp;
+    hipLaunchKernelGGL(k_scatter, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, vin, np, 8 * p,
+                       (const int32_t*)w.ghist, (const int32_t*)w.totals, ntiles, kout, vout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vin = vout;
     uint32_t* t = kin;
     kin = kout;
     kout = t;
   }
-  hipLaunchKernelGGL(k_bin_bounds, dim3((nbins + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
+  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
                      bin_start);
   return hipGetLastError();
 }

@@ -430,17 +430,22 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 // ---------------------------------------------------------------- phase 2
 // M[g][o][c] = sum over the bins k = g - a whose support holds both g and
 // g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
+// One thread per output entry. Each block covers part of one row of nodes
+// (fixed y, z), so the row decomposition is wave-uniform (scalar) and the
+// per-thread index arithmetic divides only by compile-time constants.
 template <typename T, int R, int NC>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
-                                                T* __restrict__ M, size_t total) {
+                                                T* __restrict__ M, int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
-  const size_t e = (size_t)xcd_remap(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int c = (int)(e % NC);
-  const size_t r = e / NC;
-  const int o = (int)(r % NOFF);
-  const int node = (int)(r / NOFF);
-  const int gx = node % g.n0, gy = (node / g.n0) % g.n1, gz = node / (g.n0 * g.n1);
+  constexpr int ROW = NOFF * NC;  // outputs per node
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int row = blk / blocks_per_row;          // y + n1 * z
+  const int t = (blk - row * blocks_per_row) * 256 + threadIdx.x;
+  if (t >= g.n0 * ROW) return;
+  const int gy = row % g.n1, gz = row / g.n1;
+  const int gx = t / ROW;
+  const int rr = t - gx * ROW;
+  const int o = rr / NC, c = rr - o * NC;
   const int ox = o % NO - R, oy = (o / NO) % NO - R, oz = o / (NO * NO) - R;
   T sum = T(0);
 #pragma unroll
@@ -468,15 +473,19 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
       }
     }
   }
+  const size_t e = ((size_t)row * g.n0) * ROW + t;
   M[e] = accumulate ? M[e] + sum : sum;
 }
 
 template <typename T, int R, int NC>
 static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
-  const size_t total = (size_t)g.n0 * g.n1 * g.n2 * Geo<R>::NOFF * NC;
-  const size_t blocks = (total + 255) / 256;
+  const size_t row_len = (size_t)g.n0 * Geo<R>::NOFF * NC;
+  if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
+  const int bpr = (int)((row_len + 255) / 256);
+  const size_t blocks = (size_t)bpr * g.n1 * g.n2;
+  if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gather<T, R, NC>), dim3((unsigned)blocks), dim3(256), 0, s, g, (const T*)rec, accumulate,
-                     (T*)M, total);
+                     (T*)M, bpr);
   return hipGetLastError();
 }
 
