@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work at most")
     ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +220,13 @@ def main():
 
     for _ in range(args.warmup):
         step(None)
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 8
+        src = torch.ones(n, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in spec] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)

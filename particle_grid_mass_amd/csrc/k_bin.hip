@@ -61,26 +61,36 @@ __device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int 
   }
 }
 
-// Keys, and per tile of TILE particles the counts of the first digit.
+// Keys, and per tile of TILE particles the counts of the first digit. The
+// positions of KB items per thread are loaded before any is processed.
 template <typename T, int R>
 __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np,
                                                   uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
                                                   int ntiles) {
+  constexpr int KB = 8;
   __shared__ int h[256];
   const int tid = threadIdx.x, lane = tid & 63;
   h[tid] = 0;
   __syncthreads();
   const int tile = blockIdx.x;
   const size_t base = (size_t)tile * TILE;
-  for (int it = 0; it < BI; ++it) {
-    const size_t idx = base + (size_t)it * BT + tid;
-    const bool valid = idx < (size_t)np;
-    uint32_t key = 0;
-    if (valid) {
-      key = (uint32_t)particle_key<T, R>(pos + 3 * idx, g);
-      keys[idx] = key;
+  for (int i0 = 0; i0 < BI; i0 += KB) {
+    T x[KB][3];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      size_t idx = base + (size_t)(i0 + i) * BT + tid;
+      idx = idx < (size_t)np ? idx : (size_t)np - 1;  // clamped: loads are unconditional
+#pragma unroll
+      for (int d = 0; d < 3; ++d) x[i][d] = pos[3 * idx + d];
     }
-    count_digit_runs(h, (int)(key & 255u), valid, lane);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const size_t idx = base + (size_t)(i0 + i) * BT + tid;
+      const bool valid = idx < (size_t)np;
+      const uint32_t key = (uint32_t)particle_key<T, R>(x[i], g);
+      if (valid) keys[idx] = key;
+      count_digit_runs(h, (int)(key & 255u), valid, lane);
+    }
   }
   __syncthreads();
   ghist[(size_t)tid * ntiles + tile] = h[tid];
@@ -92,14 +102,19 @@ __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, 
   __shared__ int h[256];
   const int tid = threadIdx.x, lane = tid & 63;
   h[tid] = 0;
-  __syncthreads();
   const int tile = blockIdx.x;
   const size_t base = (size_t)tile * TILE;
+  uint32_t kk[BI];
+#pragma unroll
   for (int it = 0; it < BI; ++it) {
     const size_t idx = base + (size_t)it * BT + tid;
-    const bool valid = idx < (size_t)np;
-    const uint32_t key = valid ? keys[idx] : 0u;
-    count_digit_runs(h, (int)((key >> shift) & 255u), valid, lane);
+    kk[it] = keys[idx < (size_t)np ? idx : (size_t)np - 1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < BI; ++it) {
+    const size_t idx = base + (size_t)it * BT + tid;
+    count_digit_runs(h, (int)((kk[it] >> shift) & 255u), idx < (size_t)np, lane);
   }
   __syncthreads();
   ghist[(size_t)tid * ntiles + tile] = h[tid];
@@ -184,11 +199,16 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
   int32_t v[BI];
   int rk[BI];
 #pragma unroll
+  for (int r = 0; r < BI; ++r) {  // loads first (clamped index, unconditional)
+    const size_t idx = base + (size_t)r * 64 + lane;
+    const size_t ci = idx < (size_t)np ? idx : (size_t)np - 1;
+    k[r] = keys_in[ci];
+    v[r] = vals_in ? vals_in[ci] : (int32_t)idx;
+  }
+#pragma unroll
   for (int r = 0; r < BI; ++r) {
     const size_t idx = base + (size_t)r * 64 + lane;
     const bool valid = idx < (size_t)np;
-    k[r] = valid ? keys_in[idx] : 0u;
-    v[r] = valid ? (vals_in ? vals_in[idx] : (int32_t)idx) : 0;
     const int d = (int)((k[r] >> shift) & 255u);
     const unsigned long long peers = match_digit(d, valid);
     const int rank = __popcll(peers & lt);

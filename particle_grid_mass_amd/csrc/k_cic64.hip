@@ -114,9 +114,9 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
 #pragma unroll
   for (int c = 0; c < NC; ++c) t[c] = 0.0;
   if (r.valid) {
-    axis_support<double, 1>(r.x, g.o0, g.h0, g.n0, wx);
-    axis_support<double, 1>(r.y, g.o1, g.h1, g.n1, wy);
-    axis_support<double, 1>(r.z, g.o2, g.h2, g.n2, wz);
+    axis_support<double, 1>(grid_coord<double, 0>(r.x, g), g.n0, wx);
+    axis_support<double, 1>(grid_coord<double, 1>(r.y, g), g.n1, wy);
+    axis_support<double, 1>(grid_coord<double, 2>(r.z, g), g.n2, wz);
     const double f = sigma * r.w;
     if (NC == 9)
       response<double>(r.bx, r.by, r.bz, beta, f, t);

@@ -129,9 +129,9 @@ __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g
 #pragma unroll
   for (int c = 0; c < NC; ++c) t[c] = T(0);
   if (r.valid) {
-    axis_support<T, R>(r.x, (T)g.o0, (T)g.h0, g.n0, wx);
-    axis_support<T, R>(r.y, (T)g.o1, (T)g.h1, g.n1, wy);
-    axis_support<T, R>(r.z, (T)g.o2, (T)g.h2, g.n2, wz);
+    axis_support<T, R>(grid_coord<T, 0>(r.x, g), g.n0, wx);
+    axis_support<T, R>(grid_coord<T, 1>(r.y, g), g.n1, wy);
+    axis_support<T, R>(grid_coord<T, 2>(r.z, g), g.n2, wz);
     T f = sigma * r.w;
     if (NC == 9)
       response<T>(r.bx, r.by, r.bz, beta, f, t);
@@ -430,56 +430,73 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 // ---------------------------------------------------------------- phase 2
 // M[g][o][c] = sum over the bins k = g - a whose support holds both g and
 // g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
-// One thread per output entry. Each block covers part of one row of nodes
-// (fixed y, z), so the row decomposition is wave-uniform (scalar) and the
-// per-thread index arithmetic divides only by compile-time constants.
+// One thread per (node, offset, group of CPT components): the CPT values of a
+// record entry are contiguous, and the threads of one entry cover it without
+// gaps. Each block covers part of one row of nodes (fixed y, z), so the row
+// decomposition is wave-uniform and the per-thread index arithmetic divides
+// only by compile-time constants.
 template <typename T, int R, int NC>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
                                                 T* __restrict__ M, int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
-  constexpr int ROW = NOFF * NC;  // outputs per node
+  constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
+  constexpr int TPE = NC / CPT;         // threads per (node, offset)
+  constexpr int ROWT = NOFF * TPE;      // threads per node
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int row = blk / blocks_per_row;          // y + n1 * z
+  const int row = blk / blocks_per_row;  // y + n1 * z
   const int t = (blk - row * blocks_per_row) * 256 + threadIdx.x;
-  if (t >= g.n0 * ROW) return;
+  if (t >= g.n0 * ROWT) return;
   const int gy = row % g.n1, gz = row / g.n1;
-  const int gx = t / ROW;
-  const int rr = t - gx * ROW;
-  const int o = rr / NC, c = rr - o * NC;
+  const int gx = t / ROWT;
+  const int rr = t - gx * ROWT;
+  const int o = rr / TPE, c0 = (rr - o * TPE) * CPT;
   const int ox = o % NO - R, oy = (o / NO) % NO - R, oz = o / (NO * NO) - R;
-  T sum = T(0);
+  const int dlin = ox + NS * (oy + NS * oz);  // b - a in support-linear numbering
+  // bin coordinates g - a per axis (wrapped)
+  int kx[NS], kyz[NS][NS];
+#pragma unroll
+  for (int a = 0; a < NS; ++a) kx[a] = gx - a < 0 ? gx - a + g.n0 : gx - a;
 #pragma unroll
   for (int az = 0; az < NS; ++az) {
-    const int bz = az + oz;
-    if (bz < 0 || bz > R) continue;
-    int kz = gz - az;
-    kz = kz < 0 ? kz + g.n2 : kz;
+    const int kz = gz - az < 0 ? gz - az + g.n2 : gz - az;
 #pragma unroll
     for (int ay = 0; ay < NS; ++ay) {
-      const int by = ay + oy;
-      if (by < 0 || by > R) continue;
-      int ky = gy - ay;
-      ky = ky < 0 ? ky + g.n1 : ky;
+      const int ky = gy - ay < 0 ? gy - ay + g.n1 : gy - ay;
+      kyz[az][ay] = g.n0 * (ky + g.n1 * kz);
+    }
+  }
+  T sum[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) sum[j] = T(0);
+#pragma unroll
+  for (int az = 0; az < NS; ++az) {
+    if (az + oz < 0 || az + oz > R) continue;
+#pragma unroll
+    for (int ay = 0; ay < NS; ++ay) {
+      if (ay + oy < 0 || ay + oy > R) continue;
 #pragma unroll
       for (int ax = 0; ax < NS; ++ax) {
-        const int bx = ax + ox;
-        if (bx < 0 || bx > R) continue;
-        int kx = gx - ax;
-        kx = kx < 0 ? kx + g.n0 : kx;
-        const size_t k = (size_t)kx + (size_t)g.n0 * ((size_t)ky + (size_t)g.n1 * (size_t)kz);
-        const int a = ax + NS * (ay + NS * az), bb = bx + NS * (by + NS * bz);
-        const int pi = a <= bb ? pair_index<N>(a, bb) : pair_index<N>(bb, a);
-        sum += rec[(k * NPAIR + pi) * NC + c];
+        if (ax + ox < 0 || ax + ox > R) continue;
+        const int a = ax + NS * (ay + NS * az);
+        const int b = a + dlin;
+        // pair(lo, hi) = lo * N - lo (lo - 1) / 2 + hi - lo
+        const int lo = a < b ? a : b, hi = a < b ? b : a;
+        const int pi = lo * (2 * N - lo - 1) / 2 + hi;
+        const unsigned k = (unsigned)(kx[ax] + kyz[az][ay]);
+        const T* src = rec + ((size_t)k * NPAIR + pi) * NC + c0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) sum[j] += src[j];
       }
     }
   }
-  const size_t e = ((size_t)row * g.n0) * ROW + t;
-  M[e] = accumulate ? M[e] + sum : sum;
+  T* dst = M + ((size_t)row * g.n0 + gx) * (NOFF * NC) + o * NC + c0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) dst[j] = accumulate ? dst[j] + sum[j] : sum[j];
 }
 
 template <typename T, int R, int NC>
 static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
-  const size_t row_len = (size_t)g.n0 * Geo<R>::NOFF * NC;
+  const size_t row_len = (size_t)g.n0 * Geo<R>::NOFF * (NC == 9 ? 3 : 1);  // threads per row of nodes
   if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;

@@ -38,6 +38,17 @@ GridDev to_dev(const mm_grid* g) {
   d.h0 = g->h[0];
   d.h1 = g->h[1];
   d.h2 = g->h[2];
+  d.i0 = 1.0 / g->h[0];
+  d.i1 = 1.0 / g->h[1];
+  d.i2 = 1.0 / g->h[2];
+  d.exact = 0;
+  for (int k = 0; k < 3; ++k) {
+    // a power of two well inside the fp32 range: multiplying by 1/h is then
+    // exact in fp64 and in fp32 alike
+    int ex = 0;
+    const double m = frexp(g->h[k], &ex);
+    if (m == 0.5 && ex > -100 && ex < 100) d.exact |= 1 << k;
+  }
   return d;
 }
 

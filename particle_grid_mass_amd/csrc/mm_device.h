@@ -15,11 +15,24 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Grid passed by value to every kernel (origin/h in fp64; fp32 kernels round them).
+// Bit d of `exact` is set when h_d is a power of two: then (x - o) * (1/h)
+// equals the IEEE quotient (x - o) / h bit for bit, and the cheaper product is used.
 struct GridDev {
   int n0, n1, n2;
+  int exact;
   double o0, o1, o2;
   double h0, h1, h2;
+  double i0, i1, i2;  // 1 / h
 };
+
+// Grid coordinate u = (x - origin) / h along axis D.
+template <typename T, int D>
+__device__ __forceinline__ T grid_coord(T x, const GridDev& g) {
+  const T o = (T)(D == 0 ? g.o0 : D == 1 ? g.o1 : g.o2);
+  const T dx = x - o;
+  if ((g.exact >> D) & 1) return dx * (T)(D == 0 ? g.i0 : D == 1 ? g.i1 : g.i2);
+  return dx / (T)(D == 0 ? g.h0 : D == 1 ? g.h1 : g.h2);
+}
 
 template <typename T>
 __device__ __forceinline__ T dev_floor(T x);
@@ -33,15 +46,14 @@ __device__ __forceinline__ int wrap_node(int j, int n) {
   return r < 0 ? r + n : r;
 }
 
-// One axis of the support: returns the first support node (wrapped) and
-// writes the R+1 one-dimensional B-spline weights.
-//   u = (x - origin)/h, j = floor(u), xi = u - j.
+// One axis of the support from the grid coordinate u = (x - origin)/h:
+// returns the first support node (wrapped) and writes the R+1
+// one-dimensional B-spline weights. j = floor(u), xi = u - j.
 //   CIC: nodes j, j+1 with (1 - xi, xi).
 //   TSC: centre m = j (xi < 1/2) or j+1 (xi >= 1/2); delta = offset from m;
 //        nodes m-1, m, m+1 with (1/2 (1/2 - delta)^2, 3/4 - delta^2, 1/2 (1/2 + delta)^2).
 template <typename T, int R>
-__device__ __forceinline__ int axis_support(T x, T o, T h, int n, T* wt) {
-  T u = (x - o) / h;
+__device__ __forceinline__ int axis_support(T u, int n, T* wt) {
   T fl = dev_floor<T>(u);
   int j = (int)fl;
   T xi = u - fl;
@@ -68,9 +80,9 @@ __device__ __forceinline__ int axis_support(T x, T o, T h, int n, T* wt) {
 template <typename T, int R>
 __device__ __forceinline__ int particle_key(const T* p3, const GridDev& g) {
   T wt[3];
-  int fx = axis_support<T, R>(p3[0], (T)g.o0, (T)g.h0, g.n0, wt);
-  int fy = axis_support<T, R>(p3[1], (T)g.o1, (T)g.h1, g.n1, wt);
-  int fz = axis_support<T, R>(p3[2], (T)g.o2, (T)g.h2, g.n2, wt);
+  int fx = axis_support<T, R>(grid_coord<T, 0>(p3[0], g), g.n0, wt);
+  int fy = axis_support<T, R>(grid_coord<T, 1>(p3[1], g), g.n1, wt);
+  int fz = axis_support<T, R>(grid_coord<T, 2>(p3[2], g), g.n2, wt);
   return fx + g.n0 * (fy + g.n1 * fz);
 }
 
