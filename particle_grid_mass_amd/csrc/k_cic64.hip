@@ -21,9 +21,9 @@
 //    lane feeds (r and 4 + r) are one 16-byte read.
 //  * The permutation entries of the chunk after next and the particle data of
 //    the next chunk are in flight while the current chunk is contracted.
-//  * A finished group stages its four packed upper-triangle records in LDS and
-//    writes them with 16-byte stores (the records of consecutive bins are
-//    contiguous).
+//  * A finished group stages its packed upper-triangle records in LDS, two
+//    bins at a time, and writes them with 16-byte stores (the records of
+//    consecutive bins are contiguous). 9 KB of LDS per wave: 16 waves per CU.
 #include "mm_contract.h"
 
 namespace mmk {
@@ -32,14 +32,14 @@ namespace {
 
 constexpr int NB = 4;          // bins per wave group (= 4x4x4 blocks)
 constexpr int CH = 16;         // particles per bin per chunk
-constexpr int SW = 10;         // staged doubles per particle for W (8 used)
+constexpr int SW = 8;          // staged doubles per particle for W
 constexpr int NPAIR = 36;      // packed upper triangle of 8 x 8
 
 template <int NC>
 struct Cfg {
   static constexpr int ST = NC == 9 ? 10 : 2;                 // staged doubles per particle for t
   static constexpr int STAGE = 64 * (SW + ST);                 // doubles of particle staging
-  static constexpr int REC = NB * NPAIR * NC;                  // doubles of one group's records
+  static constexpr int REC = 2 * NPAIR * NC;                   // records of two bins (staged in halves)
   static constexpr int SMEM = STAGE > REC ? STAGE : REC;
 };
 
@@ -214,26 +214,34 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
 
   // D_blk[i][j] sits in lane (i << 4) | (blk << 2) | j. Stage the packed
   // records rec[bin][pair(a, b)][c] (a <= b, pair(a, b) = 8a - a(a-1)/2 + b - a)
-  // of the group's bins in LDS, then write them with 16-byte stores.
+  // two bins at a time in LDS and write them with 16-byte stores (the records
+  // of consecutive bins are contiguous).
   const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
-  double* sr = sm + db * NPAIR * NC;
   const int p00 = di * 8 - (di * (di - 1)) / 2 + (dj - di);
   const int p01 = di * 8 - (di * (di - 1)) / 2 + (4 + dj - di);
   const int a1 = 4 + di;
   const int p11 = a1 * 8 - (a1 * (a1 - 1)) / 2 + (dj - di);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (di <= dj) sr[p00 * NC + c] = acc.q[c][0];
-    sr[p01 * NC + c] = acc.q[c][1];
-    if (di <= dj) sr[p11 * NC + c] = acc.q[c][2];
-  }
-  __syncthreads();
   const int b0 = NB * grp;
   const int nvalid = nbins - b0 < NB ? nbins - b0 : NB;
-  const int n2 = nvalid * NPAIR * NC / 2;  // NPAIR is even, so whole 16-byte words
-  double2* dst = reinterpret_cast<double2*>(rec + (size_t)b0 * NPAIR * NC);
-  const double2* src = reinterpret_cast<const double2*>(sm);
-  for (int i = lane; i < n2; i += 64) dst[i] = src[i];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((db >> 1) == half) {
+      double* sr = sm + (db & 1) * NPAIR * NC;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (di <= dj) sr[p00 * NC + c] = acc.q[c][0];
+        sr[p01 * NC + c] = acc.q[c][1];
+        if (di <= dj) sr[p11 * NC + c] = acc.q[c][2];
+      }
+    }
+    __syncthreads();
+    const int nb = nvalid - 2 * half < 2 ? nvalid - 2 * half : 2;
+    const int n2 = nb > 0 ? nb * NPAIR * NC / 2 : 0;  // NPAIR is even: whole 16-byte words
+    double2* dst = reinterpret_cast<double2*>(rec + (size_t)(b0 + 2 * half) * NPAIR * NC);
+    const double2* src = reinterpret_cast<const double2*>(sm);
+    for (int i = lane; i < n2; i += 64) dst[i] = src[i];
+    __syncthreads();
+  }
 }
 
 hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
