@@ -10,11 +10,11 @@
 //
 // Pipeline (all on the caller's stream), 8-bit digits, npass = ceil(bits/8):
 //   k_keys_hist   key[p] = first support node of particle p, and per tile of
-//                 4096 particles the counts of the first digit
+//                 2048 particles the counts of the first digit
 //   per pass d:   k_hist (d > 0: per-tile counts of digit d in the order the
 //                 previous pass left), k_scan_cols (exclusive scan of each
 //                 digit's column over the tiles, plus the column totals),
-//                 k_scatter (stable in-tile ranks: each wave ranks its 1024
+//                 k_scatter (stable in-tile ranks: each wave ranks its 512
 //                 particles in index order with wave-private digit counters;
 //                 position = digit base + tile prefix + wave prefix + rank)
 //   k_bounds      bin_start[k] = first sorted position whose key is >= k
@@ -25,7 +25,7 @@ namespace mmk {
 namespace {
 
 constexpr int BT = 256;                // threads per block
-constexpr int BI = 16;                 // items per thread
+constexpr int BI = 8;                  // items per thread
 constexpr int TILE = BT * BI;          // particles per tile
 constexpr int NWV = BT / 64;           // waves per block
 constexpr int WITEMS = TILE / NWV;     // particles per wave in the scatter

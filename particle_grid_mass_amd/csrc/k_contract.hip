@@ -434,7 +434,10 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 // record entry are contiguous, and the threads of one entry cover it without
 // gaps. Each block covers part of one row of nodes (fixed y, z), so the row
 // decomposition is wave-uniform and the per-thread index arithmetic divides
-// only by compile-time constants.
+// only by compile-time constants. Rows are visited in z-blocks of ZB planes,
+// y-major and z-minor within a block, and each XCD takes a contiguous range of
+// blocks: the 4 (CIC) or 9 (TSC) bin rows a node row reads were read by the
+// XCD a few rows earlier and are still in its L2.
 template <typename T, int R, int NC>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
                                                 T* __restrict__ M, int blocks_per_row) {
@@ -443,10 +446,23 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
   constexpr int ROWT = NOFF * TPE;      // threads per node
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int row = blk / blocks_per_row;  // y + n1 * z
-  const int t = (blk - row * blocks_per_row) * 256 + threadIdx.x;
+  const int rv = blk / blocks_per_row;  // visit order of the row
+  const int t = (blk - rv * blocks_per_row) * 256 + threadIdx.x;
   if (t >= g.n0 * ROWT) return;
-  const int gy = row % g.n1, gz = row / g.n1;
+  constexpr int ZB = 4;
+  const int nfull = g.n2 / ZB;           // complete z-blocks
+  const int inb = g.n1 * ZB;             // rows per complete z-block
+  int gy, gz;
+  if (rv < nfull * inb) {
+    const int zb = rv / inb, rem = rv - zb * inb;
+    gy = rem / ZB;
+    gz = zb * ZB + (rem - gy * ZB);
+  } else {                               // last, thinner z-block
+    const int zl = g.n2 - nfull * ZB, rem = rv - nfull * inb;
+    gy = rem / zl;
+    gz = nfull * ZB + (rem - gy * zl);
+  }
+  const int row = gy + g.n1 * gz;
   const int gx = t / ROWT;
   const int rr = t - gx * ROWT;
   const int o = rr / TPE, c0 = (rr - o * TPE) * CPT;
