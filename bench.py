@@ -32,17 +32,28 @@ METRIC = "particles/s assembled (ECSIM 3x3 mass matrix, fp64) + % MFMA/HBM roofl
 PEAK_FP64_MFMA = 78.6e12
 PEAK_FP32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12
-PMC_FILE = os.path.join(ROOT, "profiles", "contract_pmc.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "particle_grid_mass_amd", "csrc", f) for f in
-                  ("k_contract.hip", "mm_device.h", "mm_contract.h")]
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+CSRC = os.path.join(ROOT, "particle_grid_mass_amd", "csrc")
+HEADERS = ("mm_device.h", "mm_contract.h", "mm_internal.h")
+# Source files that define each kernel the roofline may name.
+KERNEL_FILES = {
+    "k_cic64": ("k_cic64.hip",) + HEADERS,
+    "k_contract": ("k_contract.hip",) + HEADERS,
+    "k_gather": ("k_contract.hip",) + HEADERS,
+    "k_atomic_scatter": ("k_scatter.hip",) + HEADERS,
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_FILES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def contract_kernel(order: int, dtype: str) -> str:
+    return "k_cic64" if order == 1 and dtype == "f64" else "k_contract"
 
 
 def flops_per_particle(order: int, tensorial: bool) -> int:
@@ -78,17 +89,25 @@ def workload_name(case) -> str:
             f"({len(case.species)} species), {case.name}")
 
 
-def pmc_traffic(kernel_hash: str, config: int, launches_per_step: int):
-    """HBM bytes per contraction launch from the committed rocprofv3 counter runs,
-    or None when they were taken on a different kernel or workload."""
+def workload_key(args) -> str:
+    return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
+            + ("-shuffled" if args.shuffled else ""))
+
+
+def pmc_traffic(kernel: str, khash: str, wkey: str):
+    """Measured HBM bytes per launch of `kernel` on workload `wkey` from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the readings of
+    a plain copy kernel; None when the counters were taken on other source."""
     try:
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_hash") != kernel_hash or d.get("config") != config:
+    cal = d.get("calibration", {})
+    ent = d.get("kernels", {}).get(f"{kernel}:{wkey}")
+    if not ent or ent.get("source_hash") != khash or "fetch_factor" not in cal:
         return None
-    return d.get("traffic_bytes_per_launch")
+    return (ent["fetch_kib"] * cal["fetch_factor"] + ent["write_kib"] * cal["write_factor"]) * 1024.0
 
 
 def cpu_baseline(case, budget_s: float):
@@ -114,7 +133,7 @@ def cpu_baseline(case, budget_s: float):
                                prec32=case.dtype == "f32")
         total_t += time.perf_counter() - t0
         reps += 1
-        if total_t >= min(budget_s, 3.0) or reps >= 5:
+        if total_t >= budget_s or reps >= 100:
             break
     value = sample * reps / total_t
     desc = (f"species 0 of the workload, {'all' if sample == sp.np else 'first'} {sample:,} particles"
@@ -133,7 +152,7 @@ def main():
     ap.add_argument("--dtype", default="f64")
     ap.add_argument("--shuffled", action="store_true", help="config 3: randomly shuffled particle order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work at most")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
@@ -252,36 +271,46 @@ def main():
     np_total = case.np_total
     value = np_total / (ms_step * 1e-3)
 
-    # roofline of the dominant kernel
+    # roofline of the dominant kernel (the longest single launch of the step)
+    np_launch = np_total / len(spec)
     if args.algo == "mfma":
         dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
-        t_dom = phase_per_launch_ms[dom] * 1e-3
-    else:
+    elif args.algo == "mfma_atomic":
         dom = "contract"
-        t_dom = phase_ms["contract"] / launches * 1e-3
-    np_launch = np_total / len(spec)
-    khash = kernel_source_hash()
-    if dom == "contract":
-        flops = flops_per_particle(order, tensorial) * np_launch
-        peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
-        roof = {"kernel": "k_contract (per-bin MFMA contraction)", "bound": "mfma", "achieved": flops / t_dom / 1e12,
-                "peak": peak / 1e12, "unit": "TFLOP/s"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["algorithmic_flops_per_launch"] = flops
-        traffic = pmc_traffic(khash, args.config, 1)
-        roof["traffic"] = traffic
-        roof["algorithmic_bytes_per_launch"] = contract_bytes(order, tensorial, elem, int(np_launch), nbins)
     else:
-        byts = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
-        roof = {"kernel": "k_gather (stencil deposition of bin records)", "bound": "hbm",
-                "achieved": byts / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = None
-        roof["algorithmic_bytes_per_launch"] = byts
+        dom = "atomic"
+    t_dom = (phase_ms["contract"] if dom in ("contract", "atomic") else phase_ms["deposit"]) / launches * 1e-3
+    flops = flops_per_particle(order, tensorial) * np_launch
+    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins)
+    dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
+    if dom == "deposit":
+        kname = "k_gather"
+        roof = {"kernel": "k_gather (stencil deposition of the per-bin records)", "bound": "hbm",
+                "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        roof["algorithmic_bytes_per_launch"] = dbytes
+    else:
+        kname = contract_kernel(order, case.dtype) if dom == "contract" else "k_atomic_scatter"
+        if args.algo == "mfma_atomic":
+            kname = "k_contract"
+        peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
+        label = {"k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+                 "k_contract": "k_contract (per-bin MFMA contraction)",
+                 "k_atomic_scatter": "k_atomic_scatter (per-particle atomic scatter, comparison only)"}[kname]
+        roof = {"kernel": label, "bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s"}
+        roof["algorithmic_flops_per_launch"] = flops
+        roof["algorithmic_bytes_per_launch"] = cbytes
+        # the same launch against the HBM roof (the CIC ECSIM contraction sits near the ridge)
+        roof["hbm_achieved_GBps"] = cbytes / t_dom / 1e9
+        roof["hbm_frac"] = cbytes / t_dom / PEAK_HBM
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    khash = kernel_source_hash(kname)
+    traffic = pmc_traffic(kname, khash, workload_key(args))
+    roof["traffic"] = traffic
+    roof["traffic_note"] = ("rocprofv3 FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor per launch "
+                            "(profiles/pmc_traffic.json)" if traffic is not None else
+                            "no counter run on this kernel source and workload")
     roof["avg_launch_ms"] = t_dom * 1e3
-    if args.algo != "mfma":
-        roof["kernel"] = {"atomic": "k_atomic_scatter (comparison)", "mfma_atomic": "k_contract, atomic deposit"}.get(
-            args.algo, args.algo)
     roof["kernel_source_hash"] = khash
 
     # parity of this run's output against the oracle (and the CPU baseline timing)
