@@ -207,14 +207,34 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
   }
 #pragma unroll
   for (int r = 0; r < BI; ++r) {
+    // rank = number of this wave's earlier particles with the same digit.
+    // The leader of each digit's lanes adds their count to the wave's counter
+    // with an LDS fetch-and-add (a wave's LDS atomics complete in order, so
+    // the returned value is the count of earlier rounds) and shares it.
     const size_t idx = base + (size_t)r * 64 + lane;
-    const bool valid = idx < (size_t)np;
+    const bool valid = idx < (size_t)np;  // valid lanes are a prefix of the wave
     const int d = (int)((k[r] >> shift) & 255u);
-    const unsigned long long peers = match_digit(d, valid);
-    const int rank = __popcll(peers & lt);
-    const int cnt = wcnt[wave][d];
-    rk[r] = valid ? cnt + rank : -1;
-    if (valid && rank == 0) wcnt[wave][d] = cnt + __popcll(peers);
+    const int dprev = __shfl_up(d, 1);
+    const int end = __popcll(__ballot(valid));  // all lanes active here: the ballot sees every lane
+    int rank, leader, cnt;
+    if (__ballot(valid && lane > 0 && d < dprev) == 0) {
+      // digits never decrease across the wave (cell-sorted input): each digit
+      // is one run of lanes, ranked by position in the run
+      const unsigned long long heads = __ballot(valid && (lane == 0 || d != dprev));
+      leader = 63 - __clzll(heads & (lt | (1ull << lane)));
+      rank = lane - leader;
+      const unsigned long long after = lane == 63 ? 0ull : (heads >> (lane + 1));
+      cnt = after ? __ffsll((long long)after) : end - lane;
+    } else {
+      const unsigned long long peers = match_digit(d, valid);
+      rank = __popcll(peers & lt);
+      leader = __ffsll((long long)peers) - 1;
+      cnt = __popcll(peers);
+    }
+    int old = 0;
+    if (valid && rank == 0) old = atomicAdd(&wcnt[wave][d], cnt);
+    const int first = __shfl(old, leader < 0 ? 0 : leader);
+    rk[r] = valid ? first + rank : -1;
   }
   __syncthreads();
   {
