@@ -18,6 +18,11 @@
 //                 particles in index order with wave-private digit counters;
 //                 position = digit base + tile prefix + wave prefix + rank)
 //   k_bounds      bin_start[k] = first sorted position whose key is >= k
+//
+// Particles already stored in key order (e.g. cell by cell for CIC) are
+// detected on the device: k_keys_hist raises a flag at the first descent, and
+// while the flag is clear the digit passes return at once and k_bounds writes
+// the identity permutation. The result is the same unique stable order.
 #include "mm_internal.h"
 
 namespace mmk {
@@ -62,18 +67,25 @@ __device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int 
 }
 
 // Keys, and per tile of TILE particles the counts of the first digit. The
-// positions of KB items per thread are loaded before any is processed.
+// positions of KB items per thread are loaded before any is processed. A
+// descent (key below the previous particle's key) anywhere in the tile sets
+// *unsorted: inside a wave by a shuffle, across waves and items through the
+// first and last key of each wave's run of 64, and across tiles by
+// recomputing the key of the particle before the tile. One atomic per tile
+// at most, skipped when the flag is already set.
 template <typename T, int R>
 __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np,
                                                   uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
-                                                  int ntiles) {
+                                                  int ntiles, int32_t* __restrict__ unsorted) {
   constexpr int KB = 8;
   __shared__ int h[256];
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint32_t kfirst[BI][NWV], klast[BI][NWV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   h[tid] = 0;
   __syncthreads();
   const int tile = blockIdx.x;
   const size_t base = (size_t)tile * TILE;
+  bool desc = false;
   for (int i0 = 0; i0 < BI; i0 += KB) {
     T x[KB][3];
 #pragma unroll
@@ -90,16 +102,39 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict
       const uint32_t key = (uint32_t)particle_key<T, R>(x[i], g);
       if (valid) keys[idx] = key;
       count_digit_runs(h, (int)(key & 255u), valid, lane);
+      const uint32_t kprev = __shfl_up(key, 1);
+      desc |= valid && lane > 0 && key < kprev;
+      if (lane == 0) kfirst[i0 + i][wave] = key;
+      if (lane == 63) klast[i0 + i][wave] = key;
     }
   }
   __syncthreads();
+  if (tid < BI * NWV) {  // first particle of each wave's run of 64 against its predecessor
+    const int i = tid / NWV, wv = tid - i * NWV;
+    const size_t idx = base + (size_t)i * BT + 64 * wv;
+    if (idx < (size_t)np && idx > 0) {
+      uint32_t prev;
+      if (wv > 0)
+        prev = klast[i][wv - 1];
+      else if (i > 0)
+        prev = klast[i - 1][NWV - 1];
+      else
+        prev = (uint32_t)particle_key<T, R>(pos + 3 * (idx - 1), g);  // last particle of the previous tile
+      desc |= kfirst[i][wv] < prev;
+    }
+  }
+  if (__syncthreads_or(desc) && tid == 0 &&
+      __hip_atomic_load(unsorted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+    atomicOr(unsorted, 1);
   ghist[(size_t)tid * ntiles + tile] = h[tid];
 }
 
 // Per-tile counts of the digit at `shift` of keys in their current order.
 __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, int np, int shift,
-                                             int32_t* __restrict__ ghist, int ntiles) {
+                                             int32_t* __restrict__ ghist, int ntiles,
+                                             const int32_t* __restrict__ unsorted) {
   __shared__ int h[256];
+  if (*unsorted == 0) return;  // already in key order
   const int tid = threadIdx.x, lane = tid & 63;
   h[tid] = 0;
   const int tile = blockIdx.x;
@@ -123,8 +158,9 @@ __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, 
 // One block per digit column: exclusive scan over the tiles in place, column
 // total to totals[digit].
 __global__ __launch_bounds__(256) void k_scan_cols(int32_t* __restrict__ ghist, int ntiles,
-                                                   int32_t* __restrict__ totals) {
+                                                   int32_t* __restrict__ totals, const int32_t* __restrict__ unsorted) {
   __shared__ int wsum[4];
+  if (*unsorted == 0) return;  // already in key order
   const int col = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* c = ghist + (size_t)col * ntiles;
   int carry = 0;
@@ -168,8 +204,9 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
                                                 const int32_t* __restrict__ vals_in, int np, int shift,
                                                 const int32_t* __restrict__ ghist, const int32_t* __restrict__ totals,
                                                 int ntiles, uint32_t* __restrict__ keys_out,
-                                                int32_t* __restrict__ vals_out) {
+                                                int32_t* __restrict__ vals_out, const int32_t* __restrict__ unsorted) {
   __shared__ int wcnt[NWV][256];
+  if (*unsorted == 0) return;  // already in key order
   __shared__ int wpre[NWV][256];
   __shared__ int dsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -262,9 +299,16 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
 // bin_start[k] = lower bound of k in the sorted keys, for k in [0, nbins]:
 // thread i (0 <= i <= np) writes i for every k in (skeys[i-1], skeys[i]]
 // (with skeys[-1] = -1 and skeys[np] = nbins), so each entry is written once.
-__global__ void k_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start) {
+// Input already in key order (*unsorted == 0): the keys are `keys0` and
+// perm is the identity, written here.
+__global__ void k_bounds(const uint32_t* __restrict__ sorted_keys, const uint32_t* __restrict__ keys0, int np,
+                         int nbins, int32_t* __restrict__ bin_start, int32_t* __restrict__ perm,
+                         const int32_t* __restrict__ unsorted) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i > np) return;
+  const bool in_order = *unsorted == 0;
+  const uint32_t* skeys = in_order ? keys0 : sorted_keys;
+  if (in_order && i < np) perm[i] = i;
   const int lo = i == 0 ? -1 : (int)skeys[i - 1];
   int hi = i == np ? nbins : (int)skeys[i];
   hi = hi > nbins ? nbins : hi;
@@ -291,6 +335,7 @@ struct BinWs {
   int32_t* vtmp;
   int32_t* ghist;
   int32_t* totals;
+  int32_t* unsorted;  // set when some particle's key is below its predecessor's
   size_t bytes;
 };
 
@@ -310,6 +355,8 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
   off += align256((size_t)256 * (ntiles > 0 ? ntiles : 1) * 4);
   w.totals = (int32_t*)(b + off);
   off += align256((size_t)256 * 4);
+  w.unsorted = (int32_t*)(b + off);
+  off += 256;
   w.bytes = off;
   return w;
 }
@@ -318,11 +365,13 @@ size_t bin_workspace_bytes(int64_t np, int64_t nbins) { return bin_layout(nullpt
 
 template <typename T>
 static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, uint32_t* keys, int32_t* ghist,
-                         int ntiles, hipStream_t s) {
+                         int ntiles, int32_t* unsorted, hipStream_t s) {
   if (order == 1)
-    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles);
+    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles,
+                       unsorted);
   else
-    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles);
+    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles,
+                       unsorted);
   return hipGetLastError();
 }
 
@@ -335,30 +384,36 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
   BinWs w = bin_layout(ws, np, nbins);
   const int npass = digit_passes(nbins);
   const int ntiles = (np + TILE - 1) / TILE;
-  hipError_t e = f32 ? keys_t<float>(g, order, pos, np, w.keysA, w.ghist, ntiles, s)
-                     : keys_t<double>(g, order, pos, np, w.keysA, w.ghist, ntiles, s);
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, w.unsorted, 1, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = f32 ? keys_t<float>(g, order, pos, np, w.keysA, w.ghist, ntiles, w.unsorted, s)
+          : keys_t<double>(g, order, pos, np, w.keysA, w.ghist, ntiles, w.unsorted, s);
   if (e != hipSuccess) return e;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;
   const int32_t* vin = nullptr;
   for (int p = 0; p < npass; ++p) {
     if (p > 0) {
-      hipLaunchKernelGGL(k_hist, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, np, 8 * p, w.ghist, ntiles);
+      hipLaunchKernelGGL(k_hist, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, np, 8 * p, w.ghist, ntiles,
+                         (const int32_t*)w.unsorted);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_scan_cols, dim3(256), dim3(256), 0, s, w.ghist, ntiles, w.totals);
+    hipLaunchKernelGGL(k_scan_cols, dim3(256), dim3(256), 0, s, w.ghist, ntiles, w.totals,
+                       (const int32_t*)w.unsorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t* vout = ((npass - 1 - p) % 2 == 0) ? perm : w.vtmp;
     hipLaunchKernelGGL(k_scatter, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, vin, np, 8 * p,
-                       (const int32_t*)w.ghist, (const int32_t*)w.totals, ntiles, kout, vout);
+                       (const int32_t*)w.ghist, (const int32_t*)w.totals, ntiles, kout, vout,
+                       (const int32_t*)w.unsorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     vin = vout;
     uint32_t* t = kin;
     kin = kout;
     kout = t;
   }
-  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
-                     bin_start);
+  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin,
+                     (const uint32_t*)w.keysA, np, nbins, bin_start, perm, (const int32_t*)w.unsorted);
   return hipGetLastError();
 }
 
