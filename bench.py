@@ -38,9 +38,19 @@ HEADERS = ("mm_device.h", "mm_contract.h", "mm_internal.h")
 # Source files that define each kernel the roofline may name.
 KERNEL_FILES = {
     "k_cic64": ("k_cic64.hip",) + HEADERS,
+    "k_tsc64": ("k_tsc64.hip",) + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
     "k_atomic_scatter": ("k_scatter.hip",) + HEADERS,
+}
+
+
+KERNEL_LABELS = {
+    "k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+    "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+    "k_contract": "k_contract (per-bin MFMA contraction)",
+    "k_gather": "k_gather (stencil deposition of the per-bin records)",
+    "k_atomic_scatter": "k_atomic_scatter (per-particle atomic scatter, comparison only)",
 }
 
 
@@ -52,8 +62,12 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def contract_kernel(order: int, dtype: str) -> str:
-    return "k_cic64" if order == 1 and dtype == "f64" else "k_contract"
+def contract_kernel(order: int, dtype: str, tensorial: bool) -> str:
+    if dtype == "f64" and order == 1:
+        return "k_cic64"
+    if dtype == "f64" and tensorial:
+        return "k_tsc64"
+    return "k_contract"
 
 
 def flops_per_particle(order: int, tensorial: bool) -> int:
@@ -285,17 +299,15 @@ def main():
     dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
     if dom == "deposit":
         kname = "k_gather"
-        roof = {"kernel": "k_gather (stencil deposition of the per-bin records)", "bound": "hbm",
+        roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
                 "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
         roof["algorithmic_bytes_per_launch"] = dbytes
     else:
-        kname = contract_kernel(order, case.dtype) if dom == "contract" else "k_atomic_scatter"
+        kname = contract_kernel(order, case.dtype, tensorial) if dom == "contract" else "k_atomic_scatter"
         if args.algo == "mfma_atomic":
             kname = "k_contract"
         peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
-        label = {"k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
-                 "k_contract": "k_contract (per-bin MFMA contraction)",
-                 "k_atomic_scatter": "k_atomic_scatter (per-particle atomic scatter, comparison only)"}[kname]
+        label = KERNEL_LABELS[kname]
         roof = {"kernel": label, "bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s"}
         roof["algorithmic_flops_per_launch"] = flops

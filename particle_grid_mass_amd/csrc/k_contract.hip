@@ -20,7 +20,8 @@
 //      (block = batch), so no block is padded; the 4 block partials are summed
 //      across lanes once per bin. 16 particles per round.
 //    CIC fp32 - v_mfma_f32_4x4x1, 16 blocks, one particle per block.
-//    TSC      - 27 rows padded to 32, tiles (0,0), (0,1), (1,1) of
+//    TSC      - (scalar, fp32 and the atomic mode; fp64 ECSIM records: k_tsc64.hip)
+//      27 rows padded to 32, tiles (0,0), (0,1), (1,1) of
 //      v_mfma_{f64,f32}_16x16x4, 4 particles per batch.
 //  * the next chunk's particle index and data are fetched while the current
 //    chunk computes.
@@ -415,6 +416,8 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
   if (mode == MODE_RECORD && order == 1 && !f32)
     return launch_cic64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
+  if (mode == MODE_RECORD && order == 2 && !f32 && P.B)
+    return launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
   if (mode == MODE_RECORD)
     return f32 ? contract_t<float, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s)
                : contract_t<double, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s);

@@ -1,0 +1,279 @@
+// Second-order (TSC) fp64 per-bin contraction on v_mfma_f64_4x4x4_4b, phase 1
+// of the two-phase assembly.
+//
+// Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+// Particle-In-Cell Methods": particles with the same 27-node support form one
+// support group (Sec. 3.3; here one bin per first support node), whose local
+// matrix Mhat^c_ab = sum_p t_p^c W_pa W_pb (Sec. 3.1, Eq. 15) is accumulated
+// over batches of K_t particles (Sec. 3.2); blocks below the diagonal are
+// skipped by the symmetry Mhat_ab = Mhat_ba (Table 1 and its footnote).
+//
+// gfx950 mapping.
+//  * The 27 support rows are padded to 28 = 7 row blocks of 4. The 4x4x4_4b
+//    instruction computes one 4x4 block (I, J) of four bins at once (one bin
+//    per block, K_t = 4 particles of each bin); the 28 blocks with I <= J
+//    cover the upper triangle: 28 instructions per component per 16
+//    particles, against 27 16x16x4 instructions per 4 particles when the
+//    rows are padded to 32 (4.3x less matrix-core time per particle).
+//  * One single-wave workgroup per (group of four consecutive bins, row i of
+//    alpha): the wave keeps the 28 blocks of components 3i .. 3i+2 (84
+//    accumulators). The three waves of a group run on one XCD, so the
+//    particles all three read come from that XCD's L2 after the first.
+//  * Particle preparation runs one particle per lane: the 27 support weights
+//    W_a (Eq. 12) and the wave's three coefficients are staged in LDS, W
+//    interleaved so that the 7 row-block values a lane feeds are contiguous.
+//  * Particle data of the next chunk is in flight during the current rounds.
+//  * Two waves per SIMD (the accumulators live in VGPRs), so that one wave's
+//    preparation and record writes overlap the other's matrix instructions.
+//  * Records rec[bin][pair][comp] are staged in LDS one bin at a time; the
+//    three components a wave owns per pair are written as one 24-byte piece
+//    (the three waves of a group fill the 72 bytes of a pair in the XCD's L2).
+#include "mm_contract.h"
+
+namespace mmk {
+
+namespace {
+
+constexpr int NB = 4;       // bins per group (= 4x4x4 blocks)
+constexpr int CH = 16;      // particles per bin per chunk
+constexpr int NS = 3;       // support nodes per axis
+constexpr int N = 27;       // support nodes
+constexpr int NBLK = 7;     // row blocks of 4 (28 rows)
+constexpr int NBP = NBLK * (NBLK + 1) / 2;  // upper blocks
+constexpr int NPAIR = 378;  // packed upper triangle of 27 x 27
+constexpr int WROW = 8;     // staged doubles per (slot, r): W_{4I + r}, I = 0..6, and a zero
+constexpr int WSLOT = 4 * WROW;
+
+constexpr int NC = 9;       // components of the tensorial matrix
+constexpr int CPW = 3;      // components per wave (one row of alpha)
+constexpr int NQ = NC / CPW;  // waves per group of bins
+constexpr int ST = 4;       // staged doubles per particle for t (16-byte aligned)
+constexpr int SMEM = 64 * WSLOT + 64 * ST;
+static_assert(NPAIR * CPW <= 64 * WSLOT, "record staging fits the W region");
+
+// Bins 4g .. 4g+3. Prep lane l serves bin 4g + (l >> 4): start in perm and
+// count; maxn (the largest count of the group) is wave-uniform.
+struct Group {
+  int s, n;
+  int maxn;
+  int nchunks;
+};
+
+__device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int nbins, int np,
+                                            int lane) {
+  Group G;
+  const int bin = NB * g + (lane >> 4);
+  int s = 0, e = 0;
+  if (bin < nbins) {
+    s = bin_start[bin];
+    e = bin_start[bin + 1];
+    s = s < 0 ? 0 : (s > np ? np : s);
+    e = e < s ? s : (e > np ? np : e);
+  }
+  G.s = s;
+  G.n = e - s;
+  int m = __builtin_amdgcn_readlane(G.n, 0);
+  m = max(m, __builtin_amdgcn_readlane(G.n, 16));
+  m = max(m, __builtin_amdgcn_readlane(G.n, 32));
+  m = max(m, __builtin_amdgcn_readlane(G.n, 48));
+  G.maxn = m;
+  G.nchunks = m > 0 ? (m + CH - 1) / CH : 1;  // an empty group still writes zero records
+  return G;
+}
+
+__device__ __forceinline__ int chunk_perm(const int32_t* __restrict__ perm, const Group& G, int j, int lane) {
+  const int q = j * CH + (lane & 15);
+  return q < G.n ? perm[G.s + q] : -1;
+}
+
+struct Raw {
+  double x, y, z, w, bx, by, bz;
+  bool valid;
+};
+
+__device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
+                                        const double* __restrict__ Bf, int p, int np) {
+  Raw r{0, 0, 0, 0, 0, 0, 0, false};
+  if ((unsigned)p < (unsigned)np) {
+    r.valid = true;
+    r.x = pos[3 * (size_t)p];
+    r.y = pos[3 * (size_t)p + 1];
+    r.z = pos[3 * (size_t)p + 2];
+    r.w = w[p];
+    r.bx = Bf[3 * (size_t)p];
+    r.by = Bf[3 * (size_t)p + 1];
+    r.bz = Bf[3 * (size_t)p + 2];
+  }
+  return r;
+}
+
+// Row `row` of t = f alpha, alpha = (I + beta^2 B B^T - beta [B]x) / (1 + beta^2 |B|^2),
+// [B]x = [[0,-Bz,By],[Bz,0,-Bx],[-By,Bx,0]]; `row` is wave-uniform.
+__device__ __forceinline__ void response_row(double bx, double by, double bz, double beta, double f, int row,
+                                             double* t) {
+  const double b2 = beta * beta;
+  const double den = 1.0 + b2 * (bx * bx + by * by + bz * bz);
+  const double gq = f / den;
+  const double cx = beta * bx, cy = beta * by, cz = beta * bz;
+  if (row == 0) {
+    const double s = b2 * bx;
+    t[0] = gq * (1.0 + s * bx);
+    t[1] = gq * (s * by + cz);
+    t[2] = gq * (s * bz - cy);
+  } else if (row == 1) {
+    const double s = b2 * by;
+    t[0] = gq * (s * bx - cz);
+    t[1] = gq * (1.0 + s * by);
+    t[2] = gq * (s * bz + cx);
+  } else {
+    const double s = b2 * bz;
+    t[0] = gq * (s * bx + cy);
+    t[1] = gq * (s * by - cx);
+    t[2] = gq * (1.0 + s * bz);
+  }
+}
+
+// Support weights of the lane's particle into LDS slot `lane` (W_a at
+// (a & 3) * WROW + (a >> 2)) and its coefficients for this wave's components
+// (zeros for a lane without a particle).
+__device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, int row,
+                                      double* sW, double* sT, int lane) {
+  double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[3] = {0, 0, 0};
+  if (r.valid) {
+    axis_support<double, 2>(grid_coord<double, 0>(r.x, g), g.n0, wx);
+    axis_support<double, 2>(grid_coord<double, 1>(r.y, g), g.n1, wy);
+    axis_support<double, 2>(grid_coord<double, 2>(r.z, g), g.n2, wz);
+    response_row(r.bx, r.by, r.bz, beta, sigma * r.w, row, t);
+  }
+  double* sw = sW + lane * WSLOT;
+#pragma unroll
+  for (int az = 0; az < NS; ++az)
+#pragma unroll
+    for (int ay = 0; ay < NS; ++ay) {
+      const double wyz = wy[ay] * wz[az];
+#pragma unroll
+      for (int ax = 0; ax < NS; ++ax) {
+        const int a = ax + NS * (ay + NS * az);
+        sw[(a & 3) * WROW + (a >> 2)] = wx[ax] * wyz;
+      }
+    }
+  sw[3 * WROW + 6] = 0.0;  // row 27 (padding)
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) sw[r4 * WROW + 7] = 0.0;
+  double* st = sT + lane * ST;
+  *reinterpret_cast<double2*>(st) = double2{t[0], t[1]};
+  st[2] = t[2];
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
+    GridDev g, const double* __restrict__ pos, const double* __restrict__ w, const double* __restrict__ Bf,
+    const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
+    double sigma, double* __restrict__ rec) {
+  __shared__ __attribute__((aligned(16))) double smem[SMEM];
+  double* sW = smem;
+  double* sT = smem + 64 * WSLOT;
+  const int lane = threadIdx.x;
+  const int ngroups = (nbins + NB - 1) / NB;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);  // the NQ waves of a group share an XCD
+  const int grp = lid / NQ, row = lid - grp * NQ;     // row of alpha: components CPW*row ..
+  if (grp >= ngroups) return;
+  const Group G = load_group(bin_start, grp, nbins, np, lane);
+
+  // MFMA lane roles: particle k of the batch, block (= bin) mb, row/column mr.
+  const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
+
+  Raw raw = load_raw(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  int pnext = chunk_perm(perm, G, 1, lane);
+  double acc[CPW][NBP];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int k = 0; k < NBP; ++k) acc[c][k] = 0.0;
+
+  for (int j = 0; j < G.nchunks; ++j) {
+    stage(raw, g, beta, sigma, row, sW, sT, lane);
+    wave_sync();
+    raw = load_raw(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
+    pnext = chunk_perm(perm, G, j + 2, lane);
+
+    const int left = G.maxn - j * CH;
+    const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
+    for (int rd = 0; rd < nr; ++rd) {
+      const int slot = CH * mb + 4 * rd + mk;
+      const double* wrow = sW + slot * WSLOT + mr * WROW;
+      double wv[8];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const double2 v = *reinterpret_cast<const double2*>(wrow + i);
+        wv[i] = v.x;
+        wv[i + 1] = v.y;
+      }
+      const double* st = sT + slot * ST;
+      const double2 t01 = *reinterpret_cast<const double2*>(st);
+      const double tv[3] = {t01.x, t01.y, st[2]};
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        double a[NBLK];
+#pragma unroll
+        for (int I = 0; I < NBLK; ++I) a[I] = tv[c] * wv[I];
+        int k = 0;
+#pragma unroll
+        for (int I = 0; I < NBLK; ++I)
+#pragma unroll
+          for (int J = I; J < NBLK; ++J, ++k) acc[c][k] = mfma_f64_4x4x4(a[I], wv[J], acc[c][k]);
+      }
+    }
+    wave_sync();
+  }
+
+  // D_blk[i][j] of block (I, J) sits in lane (i << 4) | (blk << 2) | j: local
+  // entry (4I + i, 4J + j) of bin 4 grp + blk. Stage each bin's CPW * NPAIR
+  // record values (contiguous in rec) in LDS, then write them with 16-byte stores.
+  const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
+#pragma unroll 1
+  for (int b = 0; b < NB; ++b) {
+    const int bin = NB * grp + b;
+    if (bin >= nbins) break;  // wave-uniform
+    if (db == b) {
+      int k = 0;
+#pragma unroll
+      for (int I = 0; I < NBLK; ++I)
+#pragma unroll
+        for (int J = I; J < NBLK; ++J, ++k) {
+          const int a = 4 * I + di, bb = 4 * J + dj;
+          if (a < N && bb < N && (I < J || di <= dj)) {
+            const int pair = a * N - (a * (a - 1)) / 2 + (bb - a);
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) sW[pair * CPW + c] = acc[c][k];
+          }
+        }
+    }
+    wave_sync();
+    double* dst = rec + (size_t)bin * NPAIR * NC + CPW * row;
+    for (int i = lane; i < NPAIR * CPW; i += 64) {
+      const int pair = i / CPW;
+      dst[(size_t)pair * NC + (i - pair * CPW)] = sW[i];
+    }
+    wave_sync();
+  }
+}
+
+hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s) {
+  if (!P.B) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
+  const int nbins = g.n0 * g.n1 * g.n2;
+  const int ngroups = (nbins + NB - 1) / NB;  // NQ single-wave workgroups per group of four bins
+  hipLaunchKernelGGL(k_tsc64, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
+                     (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  return hipGetLastError();
+}
+
+}  // namespace mmk

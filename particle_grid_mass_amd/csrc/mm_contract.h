@@ -18,6 +18,11 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
 hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
 
+// Phase 1 for TSC fp64 ECSIM (tensorial) records: 4x4x4 blocks, one bin per block, one wave
+// per (group of four bins, row of alpha).
+hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s);
+
 // Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 
