@@ -13,8 +13,13 @@ per cell (2,097,152 particles), beta = 0.5, sigma = 1.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--kind K]
                     [--dtype f64|f32] [--shuffled] [--algo A] [--no-cpu-baseline]
 
-Prints one JSON line. ``--gpus`` above 1 is rejected: this build runs on a
-single GPU (see the design doc for how the path would shard).
+Timing: W warm-up steps; an untimed pass with events at every phase
+boundary (the per-phase breakdown, and which kernel dominates); then K timed
+steps between two events, with only the dominant kernel's launches bracketed
+by events (its average launch duration feeds the roofline).
+
+Prints one JSON line. ``--gpus`` above 1 is rejected: the path runs on a
+single GPU; a multi-GPU decomposition is not implemented.
 """
 from __future__ import annotations
 
@@ -176,7 +181,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but this build runs on exactly one "
-              f"GPU; the multi-GPU decomposition is described in DESIGN.md and not implemented.", file=sys.stderr)
+              f"GPU; a multi-GPU decomposition (spatial slabs with a halo sum of ghost stencil rows) is not "
+              f"implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -216,10 +222,16 @@ def main():
     stream = torch.cuda.current_stream(dev)
     phases = ("bin", "contract", "deposit")
 
-    def step(evs):
+    def step(evs, marks=(0, 1, 2, 3)):
+        """One step over every species; records evs[si][k] for k in marks at the
+        phase boundaries (0 before binning, 1 after binning, 2 after the
+        contraction, 3 after the deposit)."""
+        def mark(si, k):
+            if evs is not None and k in marks:
+                evs[si][k].record(stream)
+
         for si, s in enumerate(spec):
-            if evs is not None:
-                evs[si][0].record(stream)
+            mark(si, 0)
             if args.algo == "atomic":
                 if tensorial:
                     mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], None, None, s["beta"], case.sigma,
@@ -227,17 +239,14 @@ def main():
                 else:
                     mm.assemble_scalar(case.grid, order, s["pos"], s["w"], None, None, case.sigma, M=M,
                                        accumulate=si > 0, algo="atomic")
-                if evs is not None:
-                    for k in (1, 2, 3):
-                        evs[si][k].record(stream)
+                for k in (1, 2, 3):
+                    mark(si, k)
                 continue
             bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"])
-            if evs is not None:
-                evs[si][1].record(stream)
+            mark(si, 1)
             if args.algo == "mfma":
                 mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec)
-                if evs is not None:
-                    evs[si][2].record(stream)
+                mark(si, 2)
                 mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0)
             else:
                 if tensorial:
@@ -246,10 +255,8 @@ def main():
                 else:
                     mm.assemble_scalar(case.grid, order, s["pos"], s["w"], bs, perm, case.sigma, M=M,
                                        accumulate=si > 0, algo=args.algo)
-                if evs is not None:
-                    evs[si][2].record(stream)
-            if evs is not None:
-                evs[si][3].record(stream)
+                mark(si, 2)
+            mark(si, 3)
 
     for _ in range(args.warmup):
         step(None)
@@ -261,39 +268,55 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in spec] for _ in range(args.steps)]
+
+    def new_events(nsteps):
+        return [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in spec] for _ in range(nsteps)]
+
+    # Phase pass (untimed): events at every phase boundary give the breakdown
+    # and name the dominant kernel (the longest single launch of the step).
+    psteps = max(3, min(args.steps, 20))
+    pev = new_events(psteps)
+    for k in range(psteps):
+        step(pev[k])
+    torch.cuda.synchronize()
+    phases = ("bin", "contract", "deposit")
+    phase_ms = {p: 0.0 for p in phases}
+    for k in range(psteps):
+        for si in range(len(spec)):
+            for pi, p in enumerate(phases):
+                phase_ms[p] += pev[k][si][pi].elapsed_time(pev[k][si][pi + 1])
+    phase_per_launch_ms = {p: phase_ms[p] / (psteps * len(spec)) for p in phases}
+    if args.algo == "mfma":
+        dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
+    elif args.algo == "mfma_atomic":
+        dom = "contract"
+    else:  # one kernel per species: the per-particle atomic scatter, bracketed by marks 0 and 1
+        dom = "atomic"
+        phase_per_launch_ms = {"atomic_scatter": phase_per_launch_ms["bin"]}
+    bracket = {"contract": (1, 2), "deposit": (2, 3), "atomic": (0, 1)}[dom]
+
+    # Timed pass: whole-step time between t_start and t_end, and the dominant
+    # kernel's own launches bracketed by events on its stream (two per species
+    # and step, so the timing markers add as little as possible to the step).
+    ev = new_events(args.steps)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for k in range(args.steps):
-        step(ev[k])
+        step(ev[k], bracket)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    phase_ms = {p: 0.0 for p in phases}
-    for k in range(args.steps):
-        for si in range(len(spec)):
-            for pi, p in enumerate(phases):
-                phase_ms[p] += ev[k][si][pi].elapsed_time(ev[k][si][pi + 1])
     launches = args.steps * len(spec)
-    phase_per_launch_ms = {p: phase_ms[p] / launches for p in phases}
-    if args.algo == "atomic":  # one kernel per species: the per-particle atomic scatter
-        phase_per_launch_ms = {"atomic_scatter": phase_per_launch_ms["bin"]}
-        phase_ms = {"bin": 0.0, "contract": phase_ms["bin"], "deposit": 0.0}
+    dom_ms = sum(ev[k][si][bracket[0]].elapsed_time(ev[k][si][bracket[1]])
+                 for k in range(args.steps) for si in range(len(spec)))
     np_total = case.np_total
     value = np_total / (ms_step * 1e-3)
 
-    # roofline of the dominant kernel (the longest single launch of the step)
     np_launch = np_total / len(spec)
-    if args.algo == "mfma":
-        dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
-    elif args.algo == "mfma_atomic":
-        dom = "contract"
-    else:
-        dom = "atomic"
-    t_dom = (phase_ms["contract"] if dom in ("contract", "atomic") else phase_ms["deposit"]) / launches * 1e-3
+    t_dom = dom_ms / launches * 1e-3
     flops = flops_per_particle(order, tensorial) * np_launch
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins)
     dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
@@ -352,7 +375,8 @@ def main():
                    "step": "bin + contract + deposit per species" if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
         "phases_ms_per_launch": phase_per_launch_ms,
-        "assembly_only_particles_per_s": np_total / ((phase_ms["contract"] + phase_ms["deposit"]) / args.steps * 1e-3)
+        "phases_from": f"untimed pass of {psteps} steps with events at every phase boundary",
+        "assembly_only_particles_per_s": np_total / ((phase_ms["contract"] + phase_ms["deposit"]) / psteps * 1e-3)
         if args.algo != "atomic" else value,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -20,9 +20,13 @@
 //   k_bounds      bin_start[k] = first sorted position whose key is >= k
 //
 // Particles already stored in key order (e.g. cell by cell for CIC) are
-// detected on the device: k_keys_hist raises a flag at the first descent, and
-// while the flag is clear the digit passes return at once and k_bounds writes
-// the identity permutation. The result is the same unique stable order.
+// detected on the device: k_keys_hist records per tile whether a key is below
+// its predecessor's and, for a tile in order, already writes its part of the
+// identity permutation and of bin_start. The first k_scan_cols reduces the
+// tile records into one flag; while it is clear the digit passes and k_bounds
+// return at once. Every flag is written before it is read in the same call,
+// so the workspace needs no initialisation. The result is the same unique
+// stable order either way.
 #include "mm_internal.h"
 
 namespace mmk {
@@ -68,46 +72,56 @@ __device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int 
 
 // Keys, and per tile of TILE particles the counts of the first digit. The
 // positions of KB items per thread are loaded before any is processed. A
-// descent (key below the previous particle's key) anywhere in the tile sets
-// *unsorted: inside a wave by a shuffle, across waves and items through the
-// first and last key of each wave's run of 64, and across tiles by
-// recomputing the key of the particle before the tile. One atomic per tile
-// at most, skipped when the flag is already set.
+// descent (key below the previous particle's key) is found inside a wave by a
+// shuffle, across waves and items through the first and last key of each
+// wave's run of 64, and across tiles by recomputing the key of the particle
+// before the tile; tile_unsorted[tile] records it. A tile without a descent
+// writes perm[p] = p and bin_start[k] = p for k in (key[p-1], key[p]] (the
+// tail up to nbins from the last particle): the final values when the whole
+// input is in key order, and overwritten by the digit passes and k_bounds
+// otherwise.
 template <typename T, int R>
-__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np,
+__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np, int nbins,
                                                   uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
-                                                  int ntiles, int32_t* __restrict__ unsorted) {
+                                                  int ntiles, int32_t* __restrict__ tile_unsorted,
+                                                  int32_t* __restrict__ bin_start, int32_t* __restrict__ perm) {
+  static_assert(BI == 8, "one batch of KB = BI loads per thread");
   constexpr int KB = 8;
   __shared__ int h[256];
   __shared__ uint32_t kfirst[BI][NWV], klast[BI][NWV];
+  __shared__ int kbefore;  // key of the particle before the tile (-1 for the first tile)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   h[tid] = 0;
   __syncthreads();
   const int tile = blockIdx.x;
   const size_t base = (size_t)tile * TILE;
   bool desc = false;
-  for (int i0 = 0; i0 < BI; i0 += KB) {
+  uint32_t kv[BI];
+  {
     T x[KB][3];
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      size_t idx = base + (size_t)(i0 + i) * BT + tid;
+      size_t idx = base + (size_t)i * BT + tid;
       idx = idx < (size_t)np ? idx : (size_t)np - 1;  // clamped: loads are unconditional
 #pragma unroll
       for (int d = 0; d < 3; ++d) x[i][d] = pos[3 * idx + d];
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
-      const size_t idx = base + (size_t)(i0 + i) * BT + tid;
+      const size_t idx = base + (size_t)i * BT + tid;
       const bool valid = idx < (size_t)np;
       const uint32_t key = (uint32_t)particle_key<T, R>(x[i], g);
+      kv[i] = key;
       if (valid) keys[idx] = key;
       count_digit_runs(h, (int)(key & 255u), valid, lane);
       const uint32_t kprev = __shfl_up(key, 1);
       desc |= valid && lane > 0 && key < kprev;
-      if (lane == 0) kfirst[i0 + i][wave] = key;
-      if (lane == 63) klast[i0 + i][wave] = key;
+      if (lane == 0) kfirst[i][wave] = key;
+      if (lane == 63) klast[i][wave] = key;
     }
   }
+  if (tid == 0)
+    kbefore = base > 0 ? particle_key<T, R>(pos + 3 * (base - 1), g) : -1;  // last particle of the previous tile
   __syncthreads();
   if (tid < BI * NWV) {  // first particle of each wave's run of 64 against its predecessor
     const int i = tid / NWV, wv = tid - i * NWV;
@@ -119,14 +133,34 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict
       else if (i > 0)
         prev = klast[i - 1][NWV - 1];
       else
-        prev = (uint32_t)particle_key<T, R>(pos + 3 * (idx - 1), g);  // last particle of the previous tile
+        prev = (uint32_t)kbefore;
       desc |= kfirst[i][wv] < prev;
     }
   }
-  if (__syncthreads_or(desc) && tid == 0 &&
-      __hip_atomic_load(unsorted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
-    atomicOr(unsorted, 1);
+  const bool tile_desc = __syncthreads_or(desc);
+  if (tid == 0) tile_unsorted[tile] = tile_desc ? 1 : 0;
   ghist[(size_t)tid * ntiles + tile] = h[tid];
+  if (tile_desc) return;
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const size_t idx = base + (size_t)i * BT + tid;
+    const uint32_t up = __shfl_up(kv[i], 1);
+    if (idx >= (size_t)np) continue;
+    int lo;
+    if (lane > 0)
+      lo = (int)up;
+    else if (wave > 0)
+      lo = (int)klast[i][wave - 1];
+    else if (i > 0)
+      lo = (int)klast[i - 1][NWV - 1];
+    else
+      lo = kbefore;
+    perm[idx] = (int32_t)idx;
+    const int hi = (int)kv[i] < nbins ? (int)kv[i] : nbins;
+    for (int k = lo + 1; k <= hi; ++k) bin_start[k] = (int32_t)idx;
+    if (idx == (size_t)np - 1)
+      for (int k = hi + 1; k <= nbins; ++k) bin_start[k] = np;
+  }
 }
 
 // Per-tile counts of the digit at `shift` of keys in their current order.
@@ -156,11 +190,23 @@ __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, 
 }
 
 // One block per digit column: exclusive scan over the tiles in place, column
-// total to totals[digit].
+// total to totals[digit]. In the first pass (tile_unsorted != NULL) every
+// block reduces the per-tile descent records itself and block 0 stores the
+// result in *unsorted for the kernels after it.
 __global__ __launch_bounds__(256) void k_scan_cols(int32_t* __restrict__ ghist, int ntiles,
-                                                   int32_t* __restrict__ totals, const int32_t* __restrict__ unsorted) {
+                                                   int32_t* __restrict__ totals,
+                                                   const int32_t* __restrict__ tile_unsorted,
+                                                   int32_t* __restrict__ unsorted) {
   __shared__ int wsum[4];
-  if (*unsorted == 0) return;  // already in key order
+  if (tile_unsorted) {
+    bool any = false;
+    for (int t = threadIdx.x; t < ntiles; t += 256) any |= tile_unsorted[t] != 0;
+    any = __syncthreads_or(any);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *unsorted = any ? 1 : 0;
+    if (!any) return;  // already in key order
+  } else if (*unsorted == 0) {
+    return;
+  }
   const int col = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* c = ghist + (size_t)col * ntiles;
   int carry = 0;
@@ -299,16 +345,11 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
 // bin_start[k] = lower bound of k in the sorted keys, for k in [0, nbins]:
 // thread i (0 <= i <= np) writes i for every k in (skeys[i-1], skeys[i]]
 // (with skeys[-1] = -1 and skeys[np] = nbins), so each entry is written once.
-// Input already in key order (*unsorted == 0): the keys are `keys0` and
-// perm is the identity, written here.
-__global__ void k_bounds(const uint32_t* __restrict__ sorted_keys, const uint32_t* __restrict__ keys0, int np,
-                         int nbins, int32_t* __restrict__ bin_start, int32_t* __restrict__ perm,
+// Input already in key order: k_keys_hist has written bin_start and perm.
+__global__ void k_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start,
                          const int32_t* __restrict__ unsorted) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i > np) return;
-  const bool in_order = *unsorted == 0;
-  const uint32_t* skeys = in_order ? keys0 : sorted_keys;
-  if (in_order && i < np) perm[i] = i;
+  if (i > np || *unsorted == 0) return;
   const int lo = i == 0 ? -1 : (int)skeys[i - 1];
   int hi = i == np ? nbins : (int)skeys[i];
   hi = hi > nbins ? nbins : hi;
@@ -335,7 +376,8 @@ struct BinWs {
   int32_t* vtmp;
   int32_t* ghist;
   int32_t* totals;
-  int32_t* unsorted;  // set when some particle's key is below its predecessor's
+  int32_t* tile_unsorted;  // per tile: some key is below its predecessor's
+  int32_t* unsorted;       // the same over all tiles
   size_t bytes;
 };
 
@@ -355,6 +397,8 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
   off += align256((size_t)256 * (ntiles > 0 ? ntiles : 1) * 4);
   w.totals = (int32_t*)(b + off);
   off += align256((size_t)256 * 4);
+  w.tile_unsorted = (int32_t*)(b + off);
+  off += align256((ntiles > 0 ? ntiles : 1) * 4);
   w.unsorted = (int32_t*)(b + off);
   off += 256;
   w.bytes = off;
@@ -364,14 +408,14 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
 size_t bin_workspace_bytes(int64_t np, int64_t nbins) { return bin_layout(nullptr, np, nbins).bytes; }
 
 template <typename T>
-static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, uint32_t* keys, int32_t* ghist,
-                         int ntiles, int32_t* unsorted, hipStream_t s) {
+static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, int nbins, const BinWs& w, int ntiles,
+                         int32_t* bin_start, int32_t* perm, hipStream_t s) {
   if (order == 1)
-    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles,
-                       unsorted);
+    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, nbins, w.keysA,
+                       w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   else
-    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, keys, ghist, ntiles,
-                       unsorted);
+    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, nbins, w.keysA,
+                       w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   return hipGetLastError();
 }
 
@@ -384,11 +428,8 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
   BinWs w = bin_layout(ws, np, nbins);
   const int npass = digit_passes(nbins);
   const int ntiles = (np + TILE - 1) / TILE;
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, w.unsorted, 1, 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = f32 ? keys_t<float>(g, order, pos, np, w.keysA, w.ghist, ntiles, w.unsorted, s)
-          : keys_t<double>(g, order, pos, np, w.keysA, w.ghist, ntiles, w.unsorted, s);
+  hipError_t e = f32 ? keys_t<float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
+                     : keys_t<double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
   if (e != hipSuccess) return e;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;
@@ -400,7 +441,7 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_scan_cols, dim3(256), dim3(256), 0, s, w.ghist, ntiles, w.totals,
-                       (const int32_t*)w.unsorted);
+                       p == 0 ? (const int32_t*)w.tile_unsorted : nullptr, w.unsorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t* vout = ((npass - 1 - p) % 2 == 0) ? perm : w.vtmp;
     hipLaunchKernelGGL(k_scatter, dim3(ntiles), dim3(BT), 0, s, (const uint32_t*)kin, vin, np, 8 * p,
@@ -412,8 +453,8 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
     kin = kout;
     kout = t;
   }
-  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin,
-                     (const uint32_t*)w.keysA, np, nbins, bin_start, perm, (const int32_t*)w.unsorted);
+  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
+                     bin_start, (const int32_t*)w.unsorted);
   return hipGetLastError();
 }
 

@@ -60,6 +60,47 @@ def test_bin_parity(seed, order, n, npart, spread, srt, dtype):
     assert np.array_equal(perm.cpu().numpy(), perm_ref)
 
 
+def _one_descent(srt, keys, t):
+    """``srt`` (keys non-decreasing) with exactly one descent, between t-1 and
+    t: the first particle of the next bin after t-1's is moved to t-1."""
+    t = t % len(srt)
+    j = int(np.searchsorted(keys, keys[t - 1], side="right"))
+    assert j < len(srt), "t-1 must not be in the last bin"
+    out = np.concatenate([srt[:t - 1], srt[j:j + 1], srt[t - 1:j], srt[j + 1:]])
+    k = np.concatenate([keys[:t - 1], keys[j:j + 1], keys[t - 1:j], keys[j + 1:]])
+    assert np.count_nonzero(k[1:] < k[:-1]) == 1 and k[t] < k[t - 1]
+    return np.ascontiguousarray(out)
+
+
+# descent positions: wave (64), item row (256) and tile (2048, 4096) boundaries, inside a wave of the
+# ragged last tile (5000)
+DESCENT_AT = [None, 64, 256, 2048, 4096, 5000]
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("t", DESCENT_AT)
+def test_bin_key_ordered_input(order, t):
+    """Input already in key order (the device short cut), and the same input
+    with exactly one descent at a wave, item-row or tile boundary or in the
+    ragged last tile (the full radix path); three calls in a row so that state
+    left in a reused workspace would show."""
+    case = random_case(31 + order, order, (9, 8, 7), 6100, kind="scalar", spread=0.6,
+                       origin=(-1.5, 0.25, 3.0), h=(0.5, 0.75, 1.25))
+    g = case.grid
+    pos0 = case.species[0].pos + np.array([0.0, 0.0, 2 * g.h[2]])  # two empty z-planes of bins first
+    bs0, perm0 = oracle.bin_particles(order, g.n, g.origin, g.h, pos0)
+    srt = np.ascontiguousarray(pos0[perm0])  # keys non-decreasing
+    keys = np.searchsorted(bs0, np.arange(len(srt)), side="right") - 1
+    mixed = srt if t is None else _one_descent(srt, keys, t)
+    for arr in (srt, mixed, srt):
+        print(f"[case] key-ordered order={order} descent at {t}", flush=True)
+        bs_ref, perm_ref = oracle.bin_particles(order, g.n, g.origin, g.h, arr)
+        bs, perm = mm.bin_particles(g, order, to_dev(arr, torch.float64))
+        torch.cuda.synchronize()
+        assert np.array_equal(bs.cpu().numpy(), bs_ref)
+        assert np.array_equal(perm.cpu().numpy(), perm_ref)
+
+
 def test_bin_empty():
     g = Grid((5, 5, 5))
     bs, perm = mm.bin_particles(g, 1, torch.zeros((0, 3), dtype=torch.float64, device="cuda"))
