@@ -18,7 +18,8 @@
 //  * Particle preparation runs one particle per lane (16 per bin per chunk):
 //    the support weights W_a (Eq. 12) and the coefficients t^c = sigma w alpha^c
 //    are computed once and staged in LDS, W interleaved so that the two rows a
-//    lane feeds (r and 4 + r) are one 16-byte read.
+//    lane feeds (r and 4 + r) are one 16-byte read, and laid out so that
+//    staging stores and round loads meet no LDS bank conflict.
 //  * The permutation entries of the chunk after next and the particle data of
 //    the next chunk are in flight while the current chunk is contracted.
 //  * A finished group stages its packed upper-triangle records in LDS, two
@@ -35,10 +36,12 @@ constexpr int CH = 16;         // particles per bin per chunk
 constexpr int SW = 8;          // staged doubles per particle for W
 constexpr int NPAIR = 36;      // packed upper triangle of 8 x 8
 
+constexpr int WREG = 64 * SW + NB * SW;  // W region: SW per slot plus 64 bytes per bin (w_unit)
+
 template <int NC>
 struct Cfg {
   static constexpr int ST = NC == 9 ? 10 : 2;                 // staged doubles per particle for t
-  static constexpr int STAGE = 64 * (SW + ST);                 // doubles of particle staging
+  static constexpr int STAGE = WREG + 64 * ST + 8;             // doubles of particle staging (t_base)
   static constexpr int REC = 2 * NPAIR * NC;                   // records of two bins (staged in halves)
   static constexpr int SMEM = STAGE > REC ? STAGE : REC;
 };
@@ -107,6 +110,16 @@ __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const do
 // Weights and coefficients of the lane's particle into LDS slot `lane` (zeros
 // for a lane without a particle). W_a, a = ax + 2 ay + 4 az, is stored at
 // 2 (a & 3) + (a >> 2).
+// LDS layout of the staged particles, chosen so that neither the staging
+// stores (lane = slot) nor the operand loads of a round (lanes = 4 bins x 4
+// rows, each group of 16 lanes served together) meet two lanes on one bank.
+// W: slot s holds the 16-byte units (W_r, W_{4+r}), r = 0..3; each bin's 16
+// slots start 64 bytes further on, and unit r sits at r ^ ((s >> 2) & 3).
+__device__ __forceinline__ int w_unit(int s, int r) { return (s + ((s >> 4) & 3)) * (SW / 2) + (r ^ ((s >> 2) & 3)); }
+// t: ST doubles per slot after the W region, and 16 bytes more per bin.
+template <int NC>
+__device__ __forceinline__ int t_base(int s) { return WREG + s * Cfg<NC>::ST + ((s >> 4) & 3) * 2; }
+
 template <int NC>
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, double* sm,
                                       int lane) {
@@ -123,16 +136,16 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
     else
       t[0] = f;
   }
-  double* sw = sm + lane * SW;
+  double2* su = reinterpret_cast<double2*>(sm);
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
     const double wxy = wx[r4 & 1] * wy[r4 >> 1];
     double2 v;
     v.x = wxy * wz[0];
     v.y = wxy * wz[1];
-    *reinterpret_cast<double2*>(sw + 2 * r4) = v;
+    su[w_unit(lane, r4)] = v;
   }
-  double* st = sm + 64 * SW + lane * Cfg<NC>::ST;
+  double* st = sm + t_base<NC>(lane);
   if (NC == 9) {
 #pragma unroll
     for (int c = 0; c < 8; c += 2) *reinterpret_cast<double2*>(st + c) = double2{t[c], t[c + 1]};
@@ -168,6 +181,8 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
 
   // MFMA lane roles: particle k of the K_t batch, block (= bin) mb, row/column mr.
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
+  const int wl = w_unit(CH * mb + mk, 0);  // = (17 mb + mk) * 4; round rd adds 16 rd, unit mr ^ rd
+  const int tl = t_base<NC>(CH * mb + mk);
 
   Raw raw = load_raw<NC>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
@@ -185,9 +200,10 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
     const int left = G.maxn - j * CH;
     const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
     for (int rd = 0; rd < nr; ++rd) {
-      const int slot = CH * mb + 4 * rd + mk;
-      const double2 wv = *reinterpret_cast<const double2*>(sm + slot * SW + 2 * mr);
-      const double* st = sm + 64 * SW + slot * Cfg<NC>::ST;
+      // slot = 16 mb + 4 rd + mk: w_unit(slot, mr) and t_base(slot) with the
+      // lane's constant part taken out of the loop
+      const double2 wv = reinterpret_cast<const double2*>(sm)[wl + 16 * rd + (mr ^ rd)];
+      const double* st = sm + tl + 4 * Cfg<NC>::ST * rd;
       double tv[NC];
       if (NC == 9) {
 #pragma unroll

@@ -21,7 +21,7 @@
 //    particles all three read come from that XCD's L2 after the first.
 //  * Particle preparation runs one particle per lane: the 27 support weights
 //    W_a (Eq. 12) and the wave's three coefficients are staged in LDS, W
-//    interleaved so that the 7 row-block values a lane feeds are contiguous.
+//    laid out so that staging stores and round loads meet no LDS bank conflict.
 //  * Particle data of the next chunk is in flight during the current rounds.
 //  * Two waves per SIMD (the accumulators live in VGPRs), so that one wave's
 //    preparation and record writes overlap the other's matrix instructions.
@@ -41,14 +41,14 @@ constexpr int N = 27;       // support nodes
 constexpr int NBLK = 7;     // row blocks of 4 (28 rows)
 constexpr int NBP = NBLK * (NBLK + 1) / 2;  // upper blocks
 constexpr int NPAIR = 378;  // packed upper triangle of 27 x 27
-constexpr int WROW = 8;     // staged doubles per (slot, r): W_{4I + r}, I = 0..6, and a zero
-constexpr int WSLOT = 4 * WROW;
+constexpr int WSLOT = 32;   // staged doubles per particle: 16 units of 16 bytes (see w_unit)
 
 constexpr int NC = 9;       // components of the tensorial matrix
 constexpr int CPW = 3;      // components per wave (one row of alpha)
 constexpr int NQ = NC / CPW;  // waves per group of bins
 constexpr int ST = 4;       // staged doubles per particle for t (16-byte aligned)
-constexpr int SMEM = 64 * WSLOT + 64 * ST;
+constexpr int TREG = 64 * ST + 8;  // t region: ST per slot plus 16 bytes per bin (t_base)
+constexpr int SMEM = 64 * WSLOT + TREG;
 static_assert(NPAIR * CPW <= 64 * WSLOT, "record staging fits the W region");
 
 // Bins 4g .. 4g+3. Prep lane l serves bin 4g + (l >> 4): start in perm and
@@ -133,9 +133,19 @@ __device__ __forceinline__ void response_row(double bx, double by, double bz, do
   }
 }
 
-// Support weights of the lane's particle into LDS slot `lane` (W_a at
-// (a & 3) * WROW + (a >> 2)) and its coefficients for this wave's components
-// (zeros for a lane without a particle).
+// LDS layout, chosen so that neither the staging stores (lane = slot) nor
+// the operand loads of a round (lanes = 4 bins x 4 rows, each group of 16
+// lanes served together) meet two lanes on one bank.
+// W: slot s holds W_{4I + r} (I = 0..7, zero where 4I + r > 26) in logical
+// 16-byte unit u = 4r + I/2, half I & 1; the unit is stored at position
+// u ^ ((s >> 4) ^ (s & 15)).
+__device__ __forceinline__ int w_unit(int s, int u) { return s * (WSLOT / 2) + (u ^ (((s >> 4) & 3) ^ (s & 15))); }
+// t: ST doubles per slot, and 16 bytes more per bin so that the four bins of
+// a round start on different banks.
+__device__ __forceinline__ int t_base(int s) { return s * ST + ((s >> 4) & 3) * 2; }
+
+// Support weights and this wave's coefficients of the lane's particle into
+// slot `lane` (zeros for a lane without a particle).
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, int row,
                                       double* sW, double* sT, int lane) {
   double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[3] = {0, 0, 0};
@@ -145,22 +155,19 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
     axis_support<double, 2>(grid_coord<double, 2>(r.z, g), g.n2, wz);
     response_row(r.bx, r.by, r.bz, beta, sigma * r.w, row, t);
   }
-  double* sw = sW + lane * WSLOT;
+  double wyz[NS * NS];
 #pragma unroll
   for (int az = 0; az < NS; ++az)
 #pragma unroll
-    for (int ay = 0; ay < NS; ++ay) {
-      const double wyz = wy[ay] * wz[az];
+    for (int ay = 0; ay < NS; ++ay) wyz[ay + NS * az] = wy[ay] * wz[az];
+  // W_a = wx[a % 3] * wyz[a / 3], zero for the padding rows a >= 27
+  auto wsup = [&](int a) { return a < N ? wx[a % NS] * wyz[a / NS] : 0.0; };
+  double2* su = reinterpret_cast<double2*>(sW);
 #pragma unroll
-      for (int ax = 0; ax < NS; ++ax) {
-        const int a = ax + NS * (ay + NS * az);
-        sw[(a & 3) * WROW + (a >> 2)] = wx[ax] * wyz;
-      }
-    }
-  sw[3 * WROW + 6] = 0.0;  // row 27 (padding)
+  for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) sw[r4 * WROW + 7] = 0.0;
-  double* st = sT + lane * ST;
+    for (int h = 0; h < 4; ++h) su[w_unit(lane, 4 * r4 + h)] = double2{wsup(8 * h + r4), wsup(8 * h + 4 + r4)};
+  double* st = sT + t_base(lane);
   *reinterpret_cast<double2*>(st) = double2{t[0], t[1]};
   st[2] = t[2];
 }
@@ -189,6 +196,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // MFMA lane roles: particle k of the batch, block (= bin) mb, row/column mr.
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
+  // slot = 16 mb + 4 rd + mk in round rd: w_unit(slot, 4 mr + h) and
+  // t_base(slot) with the lane's constant part taken out of the loop
+  const int wl = (CH * mb + mk) * (WSLOT / 2), wx = mb ^ mk;
+  const int tl = t_base(CH * mb + mk);
 
   Raw raw = load_raw(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
@@ -207,16 +218,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int left = G.maxn - j * CH;
     const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
     for (int rd = 0; rd < nr; ++rd) {
-      const int slot = CH * mb + 4 * rd + mk;
-      const double* wrow = sW + slot * WSLOT + mr * WROW;
+      const double2* su = reinterpret_cast<const double2*>(sW) + wl + 64 * rd;
+      const int ux = wx ^ (4 * rd);
       double wv[8];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const double2 v = *reinterpret_cast<const double2*>(wrow + i);
-        wv[i] = v.x;
-        wv[i + 1] = v.y;
+      for (int h = 0; h < 4; ++h) {
+        const double2 v = su[(4 * mr + h) ^ ux];
+        wv[2 * h] = v.x;
+        wv[2 * h + 1] = v.y;
       }
-      const double* st = sT + slot * ST;
+      const double* st = sT + tl + 16 * rd;
       const double2 t01 = *reinterpret_cast<const double2*>(st);
       const double tv[3] = {t01.x, t01.y, st[2]};
 #pragma unroll
