@@ -10,7 +10,8 @@ and the compact stencil storage of Sec. 3.4. See the header of
 ``mm_oracle.c`` for every reading it takes where the page is silent.
 
 Arrays are numpy float64 (positions ``[np, 3]``, weights ``[np]``, magnetic
-field ``[np, 3]``); the output layout is ``[nnodes, noff, ncomp]`` with
+field ``[np, 3]`` per particle, or ``[nnodes, 3]`` on the grid for
+``interp_field``); the output layout is ``[nnodes, noff, ncomp]`` with
 ``ncomp`` = 1 (scalar) or 9 (3x3 tensorial, row-major).
 """
 from __future__ import annotations
@@ -55,9 +56,10 @@ def _load():
     lib.oracle_bin.argtypes = [I, I, P, P, P, I64, P, P, P]
     lib.oracle_bilinear.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, P, P, P]
     lib.oracle_rows.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I64, P, P]
+    lib.oracle_interp_field.argtypes = [I, I, P, P, P, I64, P, P, P]
     lib.oracle_max_threads.argtypes = []
     for f in (lib.oracle_alpha, lib.oracle_support, lib.oracle_assemble, lib.oracle_bin,
-              lib.oracle_bilinear, lib.oracle_rows, lib.oracle_max_threads):
+              lib.oracle_bilinear, lib.oracle_rows, lib.oracle_interp_field, lib.oracle_max_threads):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -161,4 +163,15 @@ def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32
     out = np.zeros((len(nodes), noff(order), ncomp))
     _check(_load().oracle_rows(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
                                float(beta), float(sigma), len(nodes), _ptr(nodes), _ptr(out)), "rows")
+    return out
+
+
+def interp_field(order, n, origin, h, pos, F, prec32=False) -> np.ndarray:
+    """Particle values ``[np, 3]`` of the nodal field ``F[nnodes, 3]``: sum_a W_pa F[g_a]."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos, F = _f64(pos), _f64(F)
+    npart = pos.reshape(-1, 3).shape[0]
+    out = np.zeros((npart, 3))
+    _check(_load().oracle_interp_field(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(F),
+                                       _ptr(out)), "interp_field")
     return out

@@ -454,3 +454,37 @@ int oracle_rows(int order, int prec32, const int32_t* n, const double* origin, c
   free(next);
   return OR_OK;
 }
+
+/*
+ * Particle values of a nodal vector field, gathered with the particle's own
+ * support weights (the same W_pa that enter Eq. 6):
+ *   out[p][i] = sum_a W_pa F[g_a][i],   i = 0..2
+ * F holds nnodes*3 values (node-major). This is how the magnetic field of the
+ * grid reaches each particle before its response tensor alpha_p is formed
+ * (Sec. 4.1 names loading the field values and precomputing alpha_p as the
+ * non-matrix work of the tensorial kernel); that the field lives on the same
+ * nodes as M and is gathered with the same weights is a reading, the plainest
+ * one the page supports.
+ */
+int oracle_interp_field(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+                        int64_t np, const double* pos, const double* F, double* out) {
+  or_grid g;
+  if (!fill_grid(&g, order, prec32, n, origin, h) || np < 0) return OR_ERR_ARG;
+  if (np > 0 && (!pos || !F || !out)) return OR_ERR_ARG;
+  const int NS = order + 1, nsup = NS * NS * NS;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < np; ++p) {
+    or_support s;
+    particle_support(&g, pos + 3 * p, &s);
+    double acc[3] = {0.0, 0.0, 0.0};
+    for (int a = 0; a < nsup; ++a) {
+      int ax = a % NS, ay = (a / NS) % NS, az = a / (NS * NS);
+      int64_t gx = (s.first[0] + ax) % n[0], gy = (s.first[1] + ay) % n[1], gz = (s.first[2] + az) % n[2];
+      int64_t node = gx + (int64_t)n[0] * (gy + (int64_t)n[1] * gz);
+      double W = (s.w1d[0][ax] * s.w1d[1][ay]) * s.w1d[2][az];
+      for (int i = 0; i < 3; ++i) acc[i] += W * F[node * 3 + i];
+    }
+    for (int i = 0; i < 3; ++i) out[3 * p + i] = acc[i];
+  }
+  return OR_OK;
+}

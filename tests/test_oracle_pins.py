@@ -321,3 +321,71 @@ def test_config_generators_shapes():
     assert len(c3.species) == 2 and c3.species[0].beta == -0.5
     assert abs(c3.species[1].beta - 0.5 / 1836) < 1e-18
     assert c3.np_total == 125 * 512
+
+
+# ---------------------------------------------------------------- grid field gathered at the particles
+def _field(seed, n):
+    return np.random.default_rng(seed).normal(size=(int(np.prod(n)), 3))
+
+
+@pytest.mark.parametrize("order,n", [(1, (3, 4, 5)), (1, (6, 5, 4)), (2, (5, 5, 5)), (2, (7, 6, 5))])
+def test_interp_field_dense(order, n):
+    """B_p = sum_a W_pa F[g_a] against the dense interpolation matrix (wrapped
+    distances, no first-support-node logic), with particles shifted by whole
+    periods."""
+    case = random_case(41 + order + n[0], order, n, 60, kind="scalar", origin=(-0.25, 0.5, 1.0), h=(0.5, 1.25, 2.0))
+    pos = case.species[0].pos.copy()
+    pos[::2, 1] += 3 * n[1] * case.grid.h[1]
+    pos[1::4, 0] -= 2 * n[0] * case.grid.h[0]
+    F = _field(5 + order, n)
+    got = oracle.interp_field(order, n, case.grid.origin, case.grid.h, pos, F)
+    ref = dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, pos) @ F
+    assert rel(got, ref) < 1e-14
+    # a swapped pair of field components or a node shifted by one fails it
+    assert rel(got, dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, pos) @ F[:, [1, 0, 2]]) > 1e-2
+    assert rel(got, dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, pos) @ np.roll(F, 1, axis=0)) > 1e-2
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_interp_field_constant_and_linear(order):
+    """Partition of unity: a constant field comes back unchanged. Linear
+    reproduction: both B-splines reproduce a + G x for particles whose support
+    does not cross the periodic boundary."""
+    n = (9, 8, 10)
+    origin, h = (1.0, -2.0, 0.5), (0.5, 0.25, 2.0)
+    rng = np.random.default_rng(11 + order)
+    u = 2.0 + rng.random((200, 3)) * (np.array(n) - 5.0)  # grid units, away from the wrap
+    pos = np.asarray(origin) + u * np.asarray(h)
+    c = np.array([0.3, -1.7, 2.5])
+    got = oracle.interp_field(order, n, origin, h, pos, np.tile(c, (int(np.prod(n)), 1)))
+    assert np.max(np.abs(got - c)) < 1e-14
+    k = np.arange(int(np.prod(n)))
+    xn = np.stack([origin[0] + h[0] * (k % n[0]), origin[1] + h[1] * ((k // n[0]) % n[1]),
+                   origin[2] + h[2] * (k // (n[0] * n[1]))], axis=1)
+    G = rng.normal(size=(3, 3))
+    got = oracle.interp_field(order, n, origin, h, pos, c + xn @ G.T)
+    assert np.max(np.abs(got - (c + pos @ G.T))) < 1e-12
+
+
+def test_interp_field_cic_on_node_exact():
+    """A CIC particle on a node takes that node's value exactly."""
+    n = (4, 5, 6)
+    F = _field(3, n)
+    pos = np.array([[2.0, 3.0, 1.0], [0.0, 0.0, 0.0]])
+    got = oracle.interp_field(1, n, (0, 0, 0), (1, 1, 1), pos, F)
+    assert np.array_equal(got[0], F[2 + 4 * (3 + 5 * 1)]) and np.array_equal(got[1], F[0])
+
+
+@pytest.mark.parametrize("order,n", [(1, (4, 5, 3)), (2, (6, 5, 7))])
+def test_grid_field_assembly_dense(order, n):
+    """Tensorial assembly with the field gathered from the grid: the oracle
+    (gather, then Eq. 6) against the dense form W^T diag(sigma w alpha(W F)) W."""
+    case = random_case(71 + order, order, n, 40, kind="ecsim", beta=0.6, sigma=0.9,
+                       origin=(-0.25, 0.5, 1.0), h=(0.5, 1.25, 2.0))
+    sp = case.species[0]
+    F = _field(9, n)
+    Bp = oracle.interp_field(order, n, case.grid.origin, case.grid.h, sp.pos, F)
+    M = oracle.assemble(order, n, case.grid.origin, case.grid.h, sp.pos, sp.w, Bp, sp.beta, case.sigma)
+    Wd = dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, sp.pos)
+    Md = dense_ref.dense_M(order, n, case.grid.origin, case.grid.h, sp.pos, sp.w, Wd @ F, sp.beta, case.sigma)
+    assert rel(M, dense_ref.dense_to_stencil(order, n, Md)) < 1e-14
