@@ -80,14 +80,16 @@ def flops_per_particle(order: int, tensorial: bool) -> int:
     return 2 * n * n * (9 if tensorial else 1)
 
 
-def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int) -> int:
+def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int, field_on_grid: bool = False) -> int:
     """Algorithmic HBM bytes of one contraction launch: each particle's
     position, weight (and field) and permutation entry read once, bin bounds
-    read once, one packed upper-triangle record written per bin."""
+    read once, one packed upper-triangle record written per bin; a field on
+    the grid nodes is read once instead of the per-particle field."""
     n = (order + 1) ** 3
-    per_particle = (3 + 1 + (3 if tensorial else 0)) * elem + 4
+    per_particle = (3 + 1 + (3 if tensorial and not field_on_grid else 0)) * elem + 4
     record = n * (n + 1) // 2 * (9 if tensorial else 1) * elem
-    return np_ * per_particle + (nbins + 1) * 4 + nbins * record
+    field = nbins * 3 * elem if tensorial and field_on_grid else 0
+    return np_ * per_particle + (nbins + 1) * 4 + nbins * record + field
 
 
 def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool) -> int:
@@ -100,17 +102,18 @@ def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate
     return nbins * n * (n + 1) // 2 * nc * elem + out * (2 if accumulate else 1)
 
 
-def workload_name(case) -> str:
+def workload_name(case, field_on_grid: bool = False) -> str:
     n = case.grid.n
     kind = "ECSIM 3x3" if case.kind == "ecsim" else "scalar"
     order = "CIC" if case.order == 1 else "TSC"
     return (f"{order} {kind} {case.dtype}, {n[0]}x{n[1]}x{n[2]} periodic cells, {case.np_total:,} particles "
-            f"({len(case.species)} species), {case.name}")
+            f"({len(case.species)} species)" + (", magnetic field on the grid nodes" if field_on_grid else "")
+            + f", {case.name}" + ("_gridB" if field_on_grid else ""))
 
 
 def workload_key(args) -> str:
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
-            + ("-shuffled" if args.shuffled else ""))
+            + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -129,18 +132,27 @@ def pmc_traffic(kernel: str, khash: str, wkey: str):
     return (ent["fetch_kib"] * cal["fetch_factor"] + ent["write_kib"] * cal["write_factor"]) * 1024.0
 
 
-def cpu_baseline(case, budget_s: float):
-    """The oracle as it stands, on the host cores, on a bounded sample."""
+def cpu_baseline(case, budget_s: float, Fgrid=None):
+    """The oracle as it stands, on the host cores, on a bounded sample. With a
+    field on the grid nodes the oracle gathers it at the particles first, and
+    that gather is timed with the assembly."""
     import numpy as np
     import oracle
     sp = case.species[0]
+
+    def field(k):
+        if case.kind != "ecsim":
+            return None
+        if Fgrid is None:
+            return sp.B[:k]
+        return oracle.interp_field(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:k], Fgrid,
+                                   prec32=case.dtype == "f32")
     # whole species if it fits the budget estimate, else a cell-sorted prefix (a slab of cells)
     sample = sp.np
     t0 = time.perf_counter()
     probe = min(sp.np, 200_000)
     oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:probe], sp.w[:probe],
-                    sp.B[:probe] if case.kind == "ecsim" else None, sp.beta, case.sigma,
-                    prec32=case.dtype == "f32")
+                    field(probe), sp.beta, case.sigma, prec32=case.dtype == "f32")
     rate_guess = probe / max(time.perf_counter() - t0, 1e-6)
     if sp.np / rate_guess > budget_s:
         sample = int(rate_guess * budget_s)
@@ -148,8 +160,7 @@ def cpu_baseline(case, budget_s: float):
     while True:
         t0 = time.perf_counter()
         Mref = oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:sample],
-                               sp.w[:sample], sp.B[:sample] if case.kind == "ecsim" else None, sp.beta, case.sigma,
-                               prec32=case.dtype == "f32")
+                               sp.w[:sample], field(sample), sp.beta, case.sigma, prec32=case.dtype == "f32")
         total_t += time.perf_counter() - t0
         reps += 1
         if total_t >= budget_s or reps >= 100:
@@ -173,6 +184,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
+    ap.add_argument("--field", default="particle", choices=("particle", "grid"),
+                    help="ECSIM magnetic field per particle (default) or on the grid nodes, gathered at each "
+                         "particle with its support weights")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -188,12 +202,17 @@ def main():
     import numpy as np
     import torch
     import particle_grid_mass_amd as mm
-    from workloads import make_config
+    from workloads import grid_field, make_config
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     case = make_config(args.config, kind=args.kind, dtype=args.dtype, shuffled=args.shuffled)
+    on_grid = args.field == "grid"
+    if on_grid and case.kind != "ecsim":
+        print("bench.py: --field grid needs an ECSIM workload", file=sys.stderr)
+        sys.exit(2)
+    Fgrid = grid_field(case.grid, 1000 + args.config, case.dtype) if on_grid else None
     tdt = torch.float64 if case.dtype == "f64" else torch.float32
     elem = 8 if case.dtype == "f64" else 4
     tensorial = case.kind == "ecsim"
@@ -207,16 +226,27 @@ def main():
 
     spec = []
     for sp in case.species:
-        spec.append(dict(pos=to_dev(sp.pos), w=to_dev(sp.w), B=to_dev(sp.B) if tensorial else None, beta=sp.beta,
+        spec.append(dict(pos=to_dev(sp.pos), w=to_dev(sp.w), B=to_dev(sp.B) if tensorial and not on_grid else None,
+                         beta=sp.beta,
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
     ncomp = 9 if tensorial else 1
     M = torch.empty(nbins * mm.noff(order) * ncomp, dtype=tdt, device=dev)
+    Fd = to_dev(Fgrid) if on_grid else None
     rec = None
     if args.algo == "mfma":
         s0 = spec[0]
         bs0, perm0 = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"])
-        rec = mm.contract_bins(case.grid, order, s0["pos"], s0["w"], s0["B"], bs0, perm0, s0["beta"], case.sigma)
+        rec = mm.contract_bins(case.grid, order, s0["pos"], s0["w"], s0["B"], bs0, perm0, s0["beta"], case.sigma,
+                               Bgrid=Fd)
+
+    def ecsim(s, bs, perm, si, algo):
+        if on_grid:
+            mm.assemble_ecsim_gridB(case.grid, order, s["pos"], s["w"], Fd, bs, perm, s["beta"], case.sigma, M=M,
+                                    accumulate=si > 0, algo=algo)
+        else:
+            mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, M=M,
+                              accumulate=si > 0, algo=algo)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -234,8 +264,7 @@ def main():
             mark(si, 0)
             if args.algo == "atomic":
                 if tensorial:
-                    mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], None, None, s["beta"], case.sigma,
-                                      M=M, accumulate=si > 0, algo="atomic")
+                    ecsim(s, None, None, si, "atomic")
                 else:
                     mm.assemble_scalar(case.grid, order, s["pos"], s["w"], None, None, case.sigma, M=M,
                                        accumulate=si > 0, algo="atomic")
@@ -245,13 +274,13 @@ def main():
             bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"])
             mark(si, 1)
             if args.algo == "mfma":
-                mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec)
+                mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec,
+                                 Bgrid=Fd)
                 mark(si, 2)
                 mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0)
             else:
                 if tensorial:
-                    mm.assemble_ecsim(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma,
-                                      M=M, accumulate=si > 0, algo=args.algo)
+                    ecsim(s, bs, perm, si, args.algo)
                 else:
                     mm.assemble_scalar(case.grid, order, s["pos"], s["w"], bs, perm, case.sigma, M=M,
                                        accumulate=si > 0, algo=args.algo)
@@ -318,7 +347,7 @@ def main():
     np_launch = np_total / len(spec)
     t_dom = dom_ms / launches * 1e-3
     flops = flops_per_particle(order, tensorial) * np_launch
-    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins)
+    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid)
     dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
     if dom == "deposit":
         kname = "k_gather"
@@ -352,7 +381,7 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu, Mref = cpu_baseline(case, args.cpu_budget)
+        cpu, Mref = cpu_baseline(case, args.cpu_budget, Fgrid)
         if Mref is not None and len(spec) == 1:
             got = M.double().cpu().numpy().reshape(Mref.shape)
             parity = float(np.linalg.norm(got - Mref) / np.linalg.norm(Mref))
@@ -370,8 +399,9 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_name(case), "config_id": args.config, "grid": list(case.grid.n),
-                   "order": order, "kind": case.kind, "np": np_total, "species": len(spec), "algo": args.algo,
+        "config": {"workload": workload_name(case, on_grid), "config_id": args.config, "grid": list(case.grid.n),
+                   "order": order, "kind": case.kind, "field": args.field if tensorial else None, "np": np_total,
+                   "species": len(spec), "algo": args.algo,
                    "step": "bin + contract + deposit per species" if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
         "phases_ms_per_launch": phase_per_launch_ms,

@@ -132,6 +132,24 @@ mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t
                             size_t* ws_bytes, mm_stream_t stream);
 
 /*
+ * mm_assemble_ecsim_gridB - as mm_assemble_ecsim, with the magnetic field on
+ * the grid nodes instead of per particle: each particle's field is gathered
+ * with its own support weights, B_p = sum_a W_pa Bgrid[g_a] (the weights of
+ * Sec. 2.3 Eq. 12), before alpha_p is formed. Sec. 4.1 names loading the field
+ * and forming alpha_p as the non-matrix work of the tensorial kernels; here it
+ * is fused into the particle preparation of the fp64 MFMA contraction, and
+ * the other algorithms and fp32 interpolate B_p into the workspace first.
+ *
+ *  Bgrid [nnodes][3]: field at every node (dtype dt), node = x + nx*(y + ny*z).
+ *  Other arguments as for mm_assemble_ecsim; the workspace size depends on
+ *  whether the field is gathered in the contraction (query with ws == NULL).
+ */
+mm_status mm_assemble_ecsim_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                  const void* w, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
+                                  double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                                  size_t* ws_bytes, mm_stream_t stream);
+
+/*
  * The two phases of mm_assemble_* with MM_ALGO_MFMA, for callers that time,
  * overlap or reuse them. Calling both is the same as one MFMA assembly call.
  *
@@ -141,17 +159,26 @@ mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t
  * for support rows a <= b (upper triangle, pair(a,b) = a*N - a(a-1)/2 + b - a,
  * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp).
  *  rec       device buffer of *rec_bytes bytes (query with rec == NULL),
- *            16-byte aligned (else MM_ERR_ARG).
+ *            16-byte aligned (else MM_ERR_ARG). The records start at rec.
  *  Other arguments as for mm_assemble_ecsim; bin_start/perm are required.
+ *
+ * mm_contract_bins_gridB - mm_contract_bins with the field on the grid
+ * (Bgrid [nnodes][3], as for mm_assemble_ecsim_gridB); the records are
+ * tensorial. For fp32 the query adds room after the records for the field
+ * interpolated to the particles.
  *
  * mm_deposit_records - the sparse stencil deposition of Sec. 3.4: every
  * M[g][o][comp] is set (accumulate == 0) or incremented by the sum, in a fixed
  * order, of the records of all bins whose support holds both g and g+o.
- *  tensorial  1 for the 3x3 records of mm_contract_bins with B != NULL, else 0.
+ *  tensorial  1 for the 3x3 records (mm_contract_bins with B != NULL, or
+ *             mm_contract_bins_gridB), else 0.
  */
 mm_status mm_contract_bins(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
                            const void* B, const int32_t* bin_start, const int32_t* perm, double beta, double sigma,
                            void* rec, size_t* rec_bytes, mm_stream_t stream);
+mm_status mm_contract_bins_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                 const void* w, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
+                                 double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream);
 mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
                              int accumulate, void* M, mm_stream_t stream);
 

@@ -3,7 +3,8 @@
 The computation lives in ``libmm.so`` (hand-written HIP kernels behind the C
 ABI of ``include/mm.h``); this package is its thin torch binding.
 """
-from .api import (MMError, assemble_ecsim, assemble_scalar, bin_particles, contract_bins,  # noqa: F401
-                  deposit_records, noff)
+from .api import (MMError, assemble_ecsim, assemble_ecsim_gridB, assemble_scalar, bin_particles,  # noqa: F401
+                  contract_bins, deposit_records, noff)
 
-__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "contract_bins", "deposit_records", "noff", "MMError"]
+__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "assemble_ecsim_gridB", "contract_bins",
+           "deposit_records", "noff", "MMError"]

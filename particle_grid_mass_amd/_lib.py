@@ -12,8 +12,8 @@ MM_F64, MM_F32 = 0, 1
 ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
 
 # Every symbol the public header include/mm.h declares.
-EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_contract_bins",
-            "mm_deposit_records", "mm_status_string", "mm_version")
+EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_assemble_ecsim_gridB",
+            "mm_contract_bins", "mm_contract_bins_gridB", "mm_deposit_records", "mm_status_string", "mm_version")
 
 
 class MMGrid(ctypes.Structure):
@@ -47,10 +47,12 @@ def load():
     lib.mm_bin_particles.argtypes = [G, I, I, I64, P, P, P, P, SZ, P]
     lib.mm_assemble_scalar.argtypes = [G, I, I, I64, P, P, P, P, D, I, I, P, P, SZ, P]
     lib.mm_assemble_ecsim.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, P, SZ, P]
+    lib.mm_assemble_ecsim_gridB.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, P, SZ, P]
     lib.mm_contract_bins.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, P, SZ, P]
+    lib.mm_contract_bins_gridB.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, P, SZ, P]
     lib.mm_deposit_records.argtypes = [G, I, I, I, P, I, P, P]
-    for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim, lib.mm_contract_bins,
-              lib.mm_deposit_records):
+    for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim, lib.mm_assemble_ecsim_gridB,
+              lib.mm_contract_bins, lib.mm_contract_bins_gridB, lib.mm_deposit_records):
         f.restype = ctypes.c_int
     lib.mm_status_string.argtypes = [ctypes.c_int]
     lib.mm_status_string.restype = ctypes.c_char_p

@@ -92,7 +92,7 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
     return bin_start, perm[:npart]
 
 
-def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo):
+def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo, Bgrid=None):
     lib = _lib.load()
     g = _grid_of(grid)
     dt = pos.dtype
@@ -102,6 +102,10 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
     _check_tensor(w, "w", dt)
     if B is not None:
         _check_tensor(B, "B", dt)
+    if Bgrid is not None:
+        _check_tensor(Bgrid, "Bgrid", dt)
+        if Bgrid.numel() != 3 * _nnodes(g):
+            raise ValueError(f"Bgrid has {Bgrid.numel()} elements, expected 3 * nnodes = {3 * _nnodes(g)}")
     npart = pos.numel() // 3
     if w.numel() != npart or (B is not None and B.numel() != 3 * npart):
         raise ValueError("pos, w and B disagree on the particle count")
@@ -123,7 +127,11 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
         raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * noff(order) * ncomp}")
     s = _stream(dev)
     a = _lib.ALGOS[algo]
-    if kind == "ecsim":
+    if kind == "ecsim" and Bgrid is not None:
+        fn, name = lib.mm_assemble_ecsim_gridB, "mm_assemble_ecsim_gridB"
+        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(Bgrid), _ptr(bin_start),
+                _ptr(perm), float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
+    elif kind == "ecsim":
         fn, name = lib.mm_assemble_ecsim, "mm_assemble_ecsim"
         head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
                 float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
@@ -148,29 +156,54 @@ def assemble_ecsim(grid, order: int, pos, w, B, bin_start=None, perm=None, beta:
     return _assemble("ecsim", grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo)
 
 
+def assemble_ecsim_gridB(grid, order: int, pos, w, Bgrid, bin_start=None, perm=None, beta: float = 0.0,
+                         sigma: float = 1.0, M: Optional[torch.Tensor] = None, accumulate: bool = False,
+                         algo: str = "mfma") -> torch.Tensor:
+    """3x3 tensorial ECSIM mass matrix with the field on the grid nodes
+    (``Bgrid [nnodes, 3]``), gathered at each particle with its support weights."""
+    if Bgrid is None:
+        raise ValueError("Bgrid is required")
+    return _assemble("ecsim", grid, order, pos, w, None, bin_start, perm, beta, sigma, M, accumulate, algo,
+                     Bgrid=Bgrid)
+
+
 def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.0, sigma: float = 1.0,
-                  rec: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Phase 1 of the matrix-core assembly: packed per-bin local matrices (uint8 buffer)."""
+                  rec: Optional[torch.Tensor] = None, Bgrid: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Phase 1 of the matrix-core assembly: packed per-bin local matrices (uint8
+    buffer). The field is per particle (``B``) or on the grid nodes (``Bgrid``
+    ``[nnodes, 3]``, gathered at each particle with its support weights)."""
     lib = _lib.load()
     g = _grid_of(grid)
     dt = pos.dtype
     for t, name in ((pos, "pos"), (w, "w")):
         _check_tensor(t, name, dt)
+    if B is not None and Bgrid is not None:
+        raise ValueError("give the field per particle (B) or on the grid (Bgrid), not both")
     if B is not None:
         _check_tensor(B, "B", dt)
+    if Bgrid is not None:
+        _check_tensor(Bgrid, "Bgrid", dt)
+        if Bgrid.numel() != 3 * _nnodes(g):
+            raise ValueError(f"Bgrid has {Bgrid.numel()} elements, expected 3 * nnodes = {3 * _nnodes(g)}")
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
     npart = pos.numel() // 3
     s = _stream(pos.device)
-    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
-            float(beta), float(sigma))
+    if Bgrid is not None:
+        fn, name = lib.mm_contract_bins_gridB, "mm_contract_bins_gridB"
+        field = Bgrid
+    else:
+        fn, name = lib.mm_contract_bins, "mm_contract_bins"
+        field = B
+    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
+            _ptr(perm), float(beta), float(sigma))
     nbytes = ctypes.c_size_t(0)
-    _call(lib.mm_contract_bins, "mm_contract_bins (size query)", *head, None, ctypes.byref(nbytes), s)
+    _call(fn, name + " (size query)", *head, None, ctypes.byref(nbytes), s)
     if rec is None:
         rec = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=pos.device)
     else:
         nbytes = ctypes.c_size_t(rec.numel() * rec.element_size())
-    _call(lib.mm_contract_bins, "mm_contract_bins", *head, _ptr(rec), ctypes.byref(nbytes), s)
+    _call(fn, name, *head, _ptr(rec), ctypes.byref(nbytes), s)
     return rec
 
 

@@ -42,8 +42,10 @@ template <int NC>
 struct Cfg {
   static constexpr int ST = NC == 9 ? 10 : 2;                 // staged doubles per particle for t
   static constexpr int STAGE = WREG + 64 * ST + 8;             // doubles of particle staging (t_base)
+  static constexpr int FIELD = NB * 8 * 3;                     // grid field at the group's support nodes
   static constexpr int REC = 2 * NPAIR * NC;                   // records of two bins (staged in halves)
   static constexpr int SMEM = STAGE > REC ? STAGE : REC;
+  static constexpr int SMEM_GB = STAGE + FIELD > REC ? STAGE + FIELD : REC;  // field on the grid
 };
 
 // A group is bins 4g .. 4g+3. Prep lane l serves bin 4g + (l >> 4): `s` and
@@ -88,7 +90,8 @@ struct Raw {
   bool valid;
 };
 
-template <int NC>
+// GB: the field is on the grid (gathered in stage), not per particle.
+template <int NC, bool GB>
 __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
                                         const double* __restrict__ Bf, int p, int np) {
   Raw r{0, 0, 0, 0, 0, 0, 0, false};
@@ -98,7 +101,7 @@ __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const do
     r.y = pos[3 * (size_t)p + 1];
     r.z = pos[3 * (size_t)p + 2];
     r.w = w[p];
-    if (NC == 9) {
+    if (NC == 9 && !GB) {
       r.bx = Bf[3 * (size_t)p];
       r.by = Bf[3 * (size_t)p + 1];
       r.bz = Bf[3 * (size_t)p + 2];
@@ -107,9 +110,6 @@ __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const do
   return r;
 }
 
-// Weights and coefficients of the lane's particle into LDS slot `lane` (zeros
-// for a lane without a particle). W_a, a = ax + 2 ay + 4 az, is stored at
-// 2 (a & 3) + (a >> 2).
 // LDS layout of the staged particles, chosen so that neither the staging
 // stores (lane = slot) nor the operand loads of a round (lanes = 4 bins x 4
 // rows, each group of 16 lanes served together) meet two lanes on one bank.
@@ -120,9 +120,13 @@ __device__ __forceinline__ int w_unit(int s, int r) { return (s + ((s >> 4) & 3)
 template <int NC>
 __device__ __forceinline__ int t_base(int s) { return WREG + s * Cfg<NC>::ST + ((s >> 4) & 3) * 2; }
 
-template <int NC>
+// Weights and coefficients of the lane's particle into LDS slot `lane` (zeros
+// for a lane without a particle). With GB the field at the particle is
+// gathered from sB, the grid field at the 8 support nodes of each bin of the
+// group (node a = ax + 2 ay + 4 az, 3 components), with the particle's weights.
+template <int NC, bool GB>
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, double* sm,
-                                      int lane) {
+                                      const double* sB, int lane) {
   double wx[2] = {0, 0}, wy[2] = {0, 0}, wz[2] = {0, 0}, t[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) t[c] = 0.0;
@@ -131,8 +135,20 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
     axis_support<double, 1>(grid_coord<double, 1>(r.y, g), g.n1, wy);
     axis_support<double, 1>(grid_coord<double, 2>(r.z, g), g.n2, wz);
     const double f = sigma * r.w;
+    double bx = r.bx, by = r.by, bz = r.bz;
+    if (NC == 9 && GB) {
+      const double* fb = sB + (lane >> 4) * 24;
+      bx = by = bz = 0.0;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const double W = (wx[a & 1] * wy[(a >> 1) & 1]) * wz[a >> 2];
+        bx += W * fb[3 * a];
+        by += W * fb[3 * a + 1];
+        bz += W * fb[3 * a + 2];
+      }
+    }
     if (NC == 9)
-      response<double>(r.bx, r.by, r.bz, beta, f, t);
+      response<double>(bx, by, bz, beta, f, t);
     else
       t[0] = f;
   }
@@ -166,35 +182,56 @@ struct Acc {
 
 }  // namespace
 
-template <int NC>
+template <int NC, bool GB>
 __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restrict__ pos,
                                               const double* __restrict__ w, const double* __restrict__ Bf,
                                               const int32_t* __restrict__ bin_start,
                                               const int32_t* __restrict__ perm, int np, int nbins, double beta,
                                               double sigma, double* __restrict__ rec) {
-  __shared__ __attribute__((aligned(16))) double sm[Cfg<NC>::SMEM];
+  __shared__ __attribute__((aligned(16))) double sm[GB ? Cfg<NC>::SMEM_GB : Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
   const int grp = blockIdx.x;
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, grp, nbins, np, lane);
+  double* sB = sm + Cfg<NC>::STAGE;
+  if (GB && lane < NB * 8) {
+    // Bf is the grid field [nnodes][3]: node a of bin 4 grp + (lane >> 3) is
+    // the bin's own node (its first support node) shifted by (ax, ay, az).
+    const int bin = NB * grp + (lane >> 3), a = lane & 7;
+    double f0 = 0.0, f1 = 0.0, f2 = 0.0;
+    if (bin < nbins) {
+      const int kx = bin % g.n0, ky = (bin / g.n0) % g.n1, kz = bin / (g.n0 * g.n1);
+      const int x = kx + (a & 1) < g.n0 ? kx + (a & 1) : 0;
+      const int y = ky + ((a >> 1) & 1) < g.n1 ? ky + ((a >> 1) & 1) : 0;
+      const int z = kz + (a >> 2) < g.n2 ? kz + (a >> 2) : 0;
+      const double* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
+      f0 = f[0];
+      f1 = f[1];
+      f2 = f[2];
+    }
+    sB[3 * lane] = f0;
+    sB[3 * lane + 1] = f1;
+    sB[3 * lane + 2] = f2;
+  }
+  if (GB) __syncthreads();
 
   // MFMA lane roles: particle k of the K_t batch, block (= bin) mb, row/column mr.
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
   const int wl = w_unit(CH * mb + mk, 0);  // = (17 mb + mk) * 4; round rd adds 16 rd, unit mr ^ rd
   const int tl = t_base<NC>(CH * mb + mk);
 
-  Raw raw = load_raw<NC>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  Raw raw = load_raw<NC, GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
   Acc<NC> acc;
   acc.zero();
 
   for (int j = 0; j < G.nchunks; ++j) {
-    stage<NC>(raw, g, beta, sigma, sm, lane);
+    stage<NC, GB>(raw, g, beta, sigma, sm, sB, lane);
     __syncthreads();
     // In flight during this chunk's rounds: the next chunk's particle data and
     // the permutation entries of the chunk after it.
-    raw = load_raw<NC>(pos, w, Bf, pnext, np);
+    raw = load_raw<NC, GB>(pos, w, Bf, pnext, np);
     const int p2 = chunk_perm(perm, G, j + 2, lane);
 
     const int left = G.maxn - j * CH;
@@ -264,12 +301,15 @@ hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin
                         double beta, double sigma, double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // one single-wave workgroup per group of four bins
-  if (P.B)
-    hipLaunchKernelGGL(k_cic64<9>, dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos, (const double*)P.w,
-                       (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  if (P.Bgrid)
+    hipLaunchKernelGGL((k_cic64<9, true>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
+                       (const double*)P.w, (const double*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  else if (P.B)
+    hipLaunchKernelGGL((k_cic64<9, false>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
+                       (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
   else
-    hipLaunchKernelGGL(k_cic64<1>, dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos, (const double*)P.w,
-                       (const double*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<1, false>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
+                       (const double*)P.w, (const double*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
   return hipGetLastError();
 }
 

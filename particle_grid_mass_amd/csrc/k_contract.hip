@@ -416,13 +416,18 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
   if (mode == MODE_RECORD && order == 1 && !f32)
     return launch_cic64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
-  if (mode == MODE_RECORD && order == 2 && !f32 && P.B)
+  if (mode == MODE_RECORD && order == 2 && !f32 && (P.B || P.Bgrid))
     return launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
+  if (P.Bgrid) return hipErrorInvalidValue;  // the other kernels take a per-particle field (interp first)
   if (mode == MODE_RECORD)
     return f32 ? contract_t<float, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s)
                : contract_t<double, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s);
   return f32 ? contract_t<float, MODE_ATOMIC>(g, order, P, bin_start, perm, beta, sigma, out, s)
              : contract_t<double, MODE_ATOMIC>(g, order, P, bin_start, perm, beta, sigma, out, s);
+}
+
+bool contract_gathers_field(int order, bool f32, int mode) {
+  return mode == MODE_RECORD && !f32 && (order == 1 || order == 2);  // k_cic64, k_tsc64
 }
 
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {

@@ -1,0 +1,72 @@
+// The grid's magnetic field at each particle, gathered with the particle's own
+// support weights: B_p = sum_a W_pa B[g_a] over the N support nodes (Eq. 12
+// weights of Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for
+// Implicit Particle-In-Cell Methods", Sec. 2.3). Sec. 4.1 of that page names
+// loading the field and forming alpha_p as the preparation work of the
+// tensorial assembly. The fp64 matrix-core contractions gather the field
+// themselves; this kernel serves the other paths, which then read B_p as a
+// per-particle field.
+//
+// One thread per particle; the N nodes of one particle are gathered through
+// the cache (neighbouring particles share them).
+#include "mm_internal.h"
+
+namespace mmk {
+
+template <typename T, int R>
+__global__ __launch_bounds__(256) void k_interp_field(GridDev g, const T* __restrict__ pos, int np,
+                                                      const T* __restrict__ F, T* __restrict__ out) {
+  constexpr int NS = R + 1;
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= np) return;
+  T wx[3], wy[3], wz[3];
+  const int fx = axis_support<T, R>(grid_coord<T, 0>(pos[3 * (size_t)p], g), g.n0, wx);
+  const int fy = axis_support<T, R>(grid_coord<T, 1>(pos[3 * (size_t)p + 1], g), g.n1, wy);
+  const int fz = axis_support<T, R>(grid_coord<T, 2>(pos[3 * (size_t)p + 2], g), g.n2, wz);
+  T b[3] = {T(0), T(0), T(0)};
+#pragma unroll
+  for (int az = 0; az < NS; ++az) {
+    const int z = fz + az < g.n2 ? fz + az : fz + az - g.n2;
+#pragma unroll
+    for (int ay = 0; ay < NS; ++ay) {
+      const int y = fy + ay < g.n1 ? fy + ay : fy + ay - g.n1;
+      const size_t row = (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z);
+#pragma unroll
+      for (int ax = 0; ax < NS; ++ax) {
+        const int x = fx + ax < g.n0 ? fx + ax : fx + ax - g.n0;
+        const T W = (wx[ax] * wy[ay]) * wz[az];
+        const T* f = F + 3 * (row + x);
+        b[0] += W * f[0];
+        b[1] += W * f[1];
+        b[2] += W * f[2];
+      }
+    }
+  }
+  out[3 * (size_t)p] = b[0];
+  out[3 * (size_t)p + 1] = b[1];
+  out[3 * (size_t)p + 2] = b[2];
+}
+
+hipError_t launch_interp_field(const GridDev& g, int order, bool f32, const void* pos, int np, const void* F,
+                               void* out, hipStream_t s) {
+  if (np <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((np + 255) / 256)), block(256);
+  if (f32) {
+    if (order == 1)
+      hipLaunchKernelGGL((k_interp_field<float, 1>), grid, block, 0, s, g, (const float*)pos, np, (const float*)F,
+                         (float*)out);
+    else
+      hipLaunchKernelGGL((k_interp_field<float, 2>), grid, block, 0, s, g, (const float*)pos, np, (const float*)F,
+                         (float*)out);
+  } else {
+    if (order == 1)
+      hipLaunchKernelGGL((k_interp_field<double, 1>), grid, block, 0, s, g, (const double*)pos, np,
+                         (const double*)F, (double*)out);
+    else
+      hipLaunchKernelGGL((k_interp_field<double, 2>), grid, block, 0, s, g, (const double*)pos, np,
+                         (const double*)F, (double*)out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mmk

@@ -49,6 +49,7 @@ constexpr int NQ = NC / CPW;  // waves per group of bins
 constexpr int ST = 4;       // staged doubles per particle for t (16-byte aligned)
 constexpr int TREG = 64 * ST + 8;  // t region: ST per slot plus 16 bytes per bin (t_base)
 constexpr int SMEM = 64 * WSLOT + TREG;
+constexpr int FIELD = NB * N * 3;  // grid field at the group's support nodes (field on the grid), after SMEM
 static_assert(NPAIR * CPW <= 64 * WSLOT, "record staging fits the W region");
 
 // Bins 4g .. 4g+3. Prep lane l serves bin 4g + (l >> 4): start in perm and
@@ -91,6 +92,8 @@ struct Raw {
   bool valid;
 };
 
+// GB: the field is on the grid (gathered in stage), not per particle.
+template <bool GB>
 __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
                                         const double* __restrict__ Bf, int p, int np) {
   Raw r{0, 0, 0, 0, 0, 0, 0, false};
@@ -100,9 +103,11 @@ __device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const do
     r.y = pos[3 * (size_t)p + 1];
     r.z = pos[3 * (size_t)p + 2];
     r.w = w[p];
-    r.bx = Bf[3 * (size_t)p];
-    r.by = Bf[3 * (size_t)p + 1];
-    r.bz = Bf[3 * (size_t)p + 2];
+    if (!GB) {
+      r.bx = Bf[3 * (size_t)p];
+      r.by = Bf[3 * (size_t)p + 1];
+      r.bz = Bf[3 * (size_t)p + 2];
+    }
   }
   return r;
 }
@@ -145,15 +150,30 @@ __device__ __forceinline__ int w_unit(int s, int u) { return s * (WSLOT / 2) + (
 __device__ __forceinline__ int t_base(int s) { return s * ST + ((s >> 4) & 3) * 2; }
 
 // Support weights and this wave's coefficients of the lane's particle into
-// slot `lane` (zeros for a lane without a particle).
+// slot `lane` (zeros for a lane without a particle). With GB the field at the
+// particle is gathered from sF, the grid field at the 27 support nodes of each
+// bin of the group (node a = ax + 3 ay + 9 az, 3 components).
+template <bool GB>
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, int row,
-                                      double* sW, double* sT, int lane) {
+                                      double* sW, double* sT, const double* sF, int lane) {
   double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[3] = {0, 0, 0};
   if (r.valid) {
     axis_support<double, 2>(grid_coord<double, 0>(r.x, g), g.n0, wx);
     axis_support<double, 2>(grid_coord<double, 1>(r.y, g), g.n1, wy);
     axis_support<double, 2>(grid_coord<double, 2>(r.z, g), g.n2, wz);
-    response_row(r.bx, r.by, r.bz, beta, sigma * r.w, row, t);
+    double bx = r.bx, by = r.by, bz = r.bz;
+    if (GB) {
+      const double* fb = sF + (lane >> 4) * (3 * N);
+      bx = by = bz = 0.0;
+#pragma unroll
+      for (int a = 0; a < N; ++a) {
+        const double W = (wx[a % NS] * wy[(a / NS) % NS]) * wz[a / (NS * NS)];
+        bx += W * fb[3 * a];
+        by += W * fb[3 * a + 1];
+        bz += W * fb[3 * a + 2];
+      }
+    }
+    response_row(bx, by, bz, beta, sigma * r.w, row, t);
   }
   double wyz[NS * NS];
 #pragma unroll
@@ -180,11 +200,12 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
+template <bool GB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
     GridDev g, const double* __restrict__ pos, const double* __restrict__ w, const double* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
     double sigma, double* __restrict__ rec) {
-  __shared__ __attribute__((aligned(16))) double smem[SMEM];
+  __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
   double* sW = smem;
   double* sT = smem + 64 * WSLOT;
   const int lane = threadIdx.x;
@@ -193,6 +214,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int grp = lid / NQ, row = lid - grp * NQ;     // row of alpha: components CPW*row ..
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, grp, nbins, np, lane);
+  double* sF = smem + 64 * WSLOT + TREG;
+  if (GB) {
+    // Bf is the grid field [nnodes][3]: node a of bin 4 grp + b is the bin's
+    // own node (its first support node) shifted by (ax, ay, az).
+    for (int i = lane; i < NB * N; i += 64) {
+      const int bin = NB * grp + i / N, a = i % N;
+      double f0 = 0.0, f1 = 0.0, f2 = 0.0;
+      if (bin < nbins) {
+        const int kx = bin % g.n0, ky = (bin / g.n0) % g.n1, kz = bin / (g.n0 * g.n1);
+        int x = kx + a % NS, y = ky + (a / NS) % NS, z = kz + a / (NS * NS);
+        x = x < g.n0 ? x : x - g.n0;
+        y = y < g.n1 ? y : y - g.n1;
+        z = z < g.n2 ? z : z - g.n2;
+        const double* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
+        f0 = f[0];
+        f1 = f[1];
+        f2 = f[2];
+      }
+      sF[3 * i] = f0;
+      sF[3 * i + 1] = f1;
+      sF[3 * i + 2] = f2;
+    }
+    wave_sync();
+  }
 
   // MFMA lane roles: particle k of the batch, block (= bin) mb, row/column mr.
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
@@ -201,7 +246,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int wl = (CH * mb + mk) * (WSLOT / 2), wx = mb ^ mk;
   const int tl = t_base(CH * mb + mk);
 
-  Raw raw = load_raw(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  Raw raw = load_raw<GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
   double acc[CPW][NBP];
 #pragma unroll
@@ -210,9 +255,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int k = 0; k < NBP; ++k) acc[c][k] = 0.0;
 
   for (int j = 0; j < G.nchunks; ++j) {
-    stage(raw, g, beta, sigma, row, sW, sT, lane);
+    stage<GB>(raw, g, beta, sigma, row, sW, sT, sF, lane);
     wave_sync();
-    raw = load_raw(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
+    raw = load_raw<GB>(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
     pnext = chunk_perm(perm, G, j + 2, lane);
 
     const int left = G.maxn - j * CH;
@@ -279,11 +324,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s) {
-  if (!P.B) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
+  if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // NQ single-wave workgroups per group of four bins
-  hipLaunchKernelGGL(k_tsc64, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
-                     (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  if (P.Bgrid)
+    hipLaunchKernelGGL(k_tsc64<true>, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
+                       (const double*)P.w, (const double*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  else
+    hipLaunchKernelGGL(k_tsc64<false>, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
+                       (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
   return hipGetLastError();
 }
 

@@ -54,11 +54,14 @@ GridDev to_dev(const mm_grid* g) {
 
 mm_status hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
 
-// Shared argument checks of the two assembly entry points.
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Shared argument checks of the assembly entry points. The tensorial field is
+// per particle (B) or on the grid nodes (Bgrid, gathered at each particle).
 mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
-                          const void* B, bool tensorial, const int32_t* bin_start, const int32_t* perm, double beta,
-                          double sigma, mm_algo algo, void* M, void* ws, size_t* ws_bytes, mm_stream_t stream,
-                          int accumulate) {
+                          const void* B, const void* Bgrid, bool tensorial, const int32_t* bin_start,
+                          const int32_t* perm, double beta, double sigma, mm_algo algo, void* M, void* ws,
+                          size_t* ws_bytes, mm_stream_t stream, int accumulate) {
   if (!ws_bytes) return MM_ERR_NULL;
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
@@ -71,14 +74,19 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (!M) return MM_ERR_NULL;
   const bool mfma = algo != MM_ALGO_ATOMIC;
   if (np > 0) {
-    if (!pos || !w || (tensorial && !B)) return MM_ERR_NULL;
+    if (!pos || !w || (tensorial && !B && !Bgrid)) return MM_ERR_NULL;
     if (mfma && (!bin_start || !perm)) return MM_ERR_NULL;
   }
   const bool f32 = dt == MM_F32;
+  const size_t elem = f32 ? 4 : 8;
   // The two-phase deposit keeps one packed record per bin; the atomic
-  // deposits need no workspace.
+  // deposits need no workspace. A grid field that the chosen kernel does not
+  // gather itself is first interpolated to the particles, after the records.
   const bool records = algo == MM_ALGO_MFMA && np > 0;
-  const size_t need = records ? record_bytes(order, f32, tensorial, nnodes) : 0;
+  const size_t rec_need = records ? align256(record_bytes(order, f32, tensorial, nnodes)) : 0;
+  const bool interp = Bgrid && np > 0 &&
+                      !(records && contract_gathers_field(order, f32, MODE_RECORD));
+  const size_t need = rec_need + (interp ? (size_t)np * 3 * elem : 0);
   if (!ws) {
     *ws_bytes = need;
     return MM_OK;
@@ -92,6 +100,16 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   GridDev g = to_dev(grid);
   hipError_t e = hipSuccess;
   Particles P{pos, w, tensorial ? B : nullptr, (int)np};
+  if (Bgrid && np > 0) {
+    if (interp) {
+      void* bp = (char*)ws + rec_need;
+      e = launch_interp_field(g, order, f32, pos, (int)np, Bgrid, bp, s);
+      if (e != hipSuccess) return hip_status(e);
+      P.B = bp;
+    } else {
+      P.Bgrid = Bgrid;
+    }
+  }
   if (records) {
     e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
     if (e == hipSuccess) e = launch_gather(g, order, f32, tensorial, ws, accumulate, M, s);
@@ -104,6 +122,47 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   else
     e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_ATOMIC, M, s);
   return hip_status(e);
+}
+
+// mm_contract_bins with the field per particle (B) or on the grid (Bgrid).
+mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
+                          const void* B, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
+                          double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream) {
+  if (!rec_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
+  if (Bgrid && np > 0 && !pos) return MM_ERR_NULL;
+  const bool f32 = dt == MM_F32;
+  const bool tensorial = B != nullptr || Bgrid != nullptr;
+  const size_t rec_need = record_bytes(order, f32, tensorial, nnodes);
+  const bool interp = Bgrid && np > 0 && !contract_gathers_field(order, f32, MODE_RECORD);
+  const size_t need = interp ? align256(rec_need) + (size_t)np * 3 * (f32 ? 4 : 8) : rec_need;
+  if (!rec) {
+    *rec_bytes = need;
+    return MM_OK;
+  }
+  if (*rec_bytes < need) return MM_ERR_WORKSPACE;
+  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
+  GridDev g = to_dev(grid);
+  hipStream_t s = (hipStream_t)stream;
+  Particles P{pos, w, B, (int)np};
+  if (Bgrid) {
+    if (interp) {
+      void* bp = (char*)rec + align256(rec_need);
+      hipError_t e = launch_interp_field(g, order, f32, pos, (int)np, Bgrid, bp, s);
+      if (e != hipSuccess) return hip_status(e);
+      P.B = bp;
+    } else {
+      P.Bgrid = Bgrid;
+    }
+  }
+  return hip_status(launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, s));
 }
 
 }  // namespace
@@ -135,41 +194,39 @@ mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_
                              const void* w, const int32_t* bin_start, const int32_t* perm, double sigma,
                              int accumulate, mm_algo algo, void* M, void* ws, size_t* ws_bytes,
                              mm_stream_t stream) {
-  return assemble_common(grid, order, dt, np, pos, w, nullptr, false, bin_start, perm, 0.0, sigma, algo, M, ws,
-                         ws_bytes, stream, accumulate);
+  return assemble_common(grid, order, dt, np, pos, w, nullptr, nullptr, false, bin_start, perm, 0.0, sigma, algo, M,
+                         ws, ws_bytes, stream, accumulate);
 }
 
 mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
                             const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
                             double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
                             size_t* ws_bytes, mm_stream_t stream) {
-  return assemble_common(grid, order, dt, np, pos, w, B, true, bin_start, perm, beta, sigma, algo, M, ws, ws_bytes,
-                         stream, accumulate);
+  return assemble_common(grid, order, dt, np, pos, w, B, nullptr, true, bin_start, perm, beta, sigma, algo, M, ws,
+                         ws_bytes, stream, accumulate);
+}
+
+mm_status mm_assemble_ecsim_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                  const void* w, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
+                                  double beta, double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                                  size_t* ws_bytes, mm_stream_t stream) {
+  return assemble_common(grid, order, dt, np, pos, w, nullptr, Bgrid, true, bin_start, perm, beta, sigma, algo, M,
+                         ws, ws_bytes, stream, accumulate);
 }
 
 mm_status mm_contract_bins(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
                            const void* B, const int32_t* bin_start, const int32_t* perm, double beta, double sigma,
                            void* rec, size_t* rec_bytes, mm_stream_t stream) {
-  if (!rec_bytes) return MM_ERR_NULL;
-  int64_t nnodes = 0;
-  mm_status st = check_grid(grid, order, &nnodes);
-  if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
-  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
-  if (np < 0) return MM_ERR_ARG;
-  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
-  if (!bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
-  const bool f32 = dt == MM_F32;
-  const size_t need = record_bytes(order, f32, B != nullptr, nnodes);
-  if (!rec) {
-    *rec_bytes = need;
-    return MM_OK;
-  }
-  if (*rec_bytes < need) return MM_ERR_WORKSPACE;
-  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
-  Particles P{pos, w, B, (int)np};
-  return hip_status(
-      launch_contract(to_dev(grid), order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, (hipStream_t)stream));
+  return contract_common(grid, order, dt, np, pos, w, B, nullptr, bin_start, perm, beta, sigma, rec, rec_bytes,
+                         stream);
+}
+
+mm_status mm_contract_bins_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                 const void* w, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
+                                 double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream) {
+  if (!Bgrid) return MM_ERR_NULL;
+  return contract_common(grid, order, dt, np, pos, w, nullptr, Bgrid, bin_start, perm, beta, sigma, rec, rec_bytes,
+                         stream);
 }
 
 mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,

@@ -23,6 +23,11 @@ hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
 
+// Whether launch_contract gathers a grid field itself (Particles::Bgrid) for
+// this order, precision and mode; otherwise the field must first be
+// interpolated to the particles (launch_interp_field) and passed as B.
+bool contract_gathers_field(int order, bool f32, int mode);
+
 // Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 

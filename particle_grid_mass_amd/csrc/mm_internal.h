@@ -13,9 +13,14 @@ namespace mmk {
 struct Particles {
   const void* pos;  // [np][3]
   const void* w;    // [np]
-  const void* B;    // [np][3] or NULL (scalar)
+  const void* B;    // [np][3] or NULL (scalar, or the field is on the grid)
   int np;
+  const void* Bgrid = nullptr;  // [nnodes][3]: field on the grid nodes, gathered at each particle
 };
+
+// out[p] = sum_a W_pa F[g_a]: the nodal field F [nnodes][3] at every particle.
+hipError_t launch_interp_field(const GridDev& g, int order, bool f32, const void* pos, int np, const void* F,
+                               void* out, hipStream_t s);
 
 // M <- 0 (a fill kernel, so the stream stays capturable).
 hipError_t launch_fill_zero(void* M, size_t count, bool f32, hipStream_t s);

@@ -1,9 +1,10 @@
 """Seeded synthetic particle workloads shared by the oracle tests, the GPU
 tests and the benchmark.
 
-This module only draws inputs (grid, positions, weights, magnetic field,
-species constants). It holds none of the assembly arithmetic, so the oracle
-and the GPU path can both consume it without sharing any of the method.
+This module only draws inputs (grid, positions, weights, magnetic field per
+particle or on the grid nodes, species constants). It holds none of the
+assembly arithmetic, so the oracle and the GPU path can both consume it
+without sharing any of the method.
 
 The workloads follow the isolation setup of Pennati & Markidis, "Mass Matrix
 Assembly on Tensor Cores for Implicit Particle-In-Cell Methods" (Sec. 4.1):
@@ -12,7 +13,7 @@ particles stored cell by cell. The named configurations extend it to two
 species, shuffled order and a clustered density.
 """
 from .gen import (Grid, Species, Case, CONFIGS, make_config, uniform_species, random_case,
-                  clustered_counts, species_from_counts)
+                  clustered_counts, species_from_counts, grid_field)
 
 __all__ = ["Grid", "Species", "Case", "CONFIGS", "make_config", "uniform_species", "random_case",
-           "clustered_counts", "species_from_counts"]
+           "clustered_counts", "species_from_counts", "grid_field"]

@@ -213,3 +213,11 @@ def random_case(seed: int, order: int, n: Tuple[int, int, int], npart: int, kind
     B = rb.standard_normal((npart, 3)) if kind == "ecsim" else None
     sp = _cast(Species(pos, w, B, beta, "random"), dtype)
     return Case(f"random_s{seed}_o{order}_{kind}", g, order, kind, [sp], sigma=sigma, dtype=dtype, seed=seed)
+
+
+def grid_field(grid: Grid, seed: int, dtype: str = "f64") -> np.ndarray:
+    """Magnetic field on the grid nodes, ``[nnodes, 3]``: N(0, 1) per node and
+    component (the per-particle field of the configurations, moved to the
+    nodes), node index x + nx*(y + ny*z). Drawn from its own seeded stream."""
+    (rng,) = _streams(7000 + seed, 1)
+    return _round(rng.standard_normal((grid.ncells, 3)), dtype)
