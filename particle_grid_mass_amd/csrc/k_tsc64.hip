@@ -46,9 +46,7 @@ constexpr int WSLOT = 32;   // staged doubles per particle: 16 units of 16 bytes
 constexpr int NC = 9;       // components of the tensorial matrix
 constexpr int CPW = 3;      // components per wave (one row of alpha)
 constexpr int NQ = NC / CPW;  // waves per group of bins
-constexpr int ST = 4;       // staged doubles per particle for t (16-byte aligned)
-constexpr int TREG = 64 * ST + 8;  // t region: ST per slot plus 16 bytes per bin (t_base)
-constexpr int SMEM = 64 * WSLOT + TREG;
+constexpr int SMEM = 64 * WSLOT;
 constexpr int FIELD = NB * N * 3;  // grid field at the group's support nodes (field on the grid), after SMEM
 static_assert(NPAIR * CPW <= 64 * WSLOT, "record staging fits the W region");
 
@@ -141,13 +139,20 @@ __device__ __forceinline__ void response_row(double bx, double by, double bz, do
 // LDS layout, chosen so that neither the staging stores (lane = slot) nor
 // the operand loads of a round (lanes = 4 bins x 4 rows, each group of 16
 // lanes served together) meet two lanes on one bank.
-// W: slot s holds W_{4I + r} (I = 0..7, zero where 4I + r > 26) in logical
+// W: slot s holds W_{4I + r} (I = 0..6, zero where 4I + r > 26) in logical
 // 16-byte unit u = 4r + I/2, half I & 1; the unit is stored at position
-// u ^ ((s >> 4) ^ (s & 15)).
+// u ^ ((s >> 4) ^ (s & 15)). The half I = 7 of row r < 3 (never a matrix
+// operand) holds the coefficient t_r of this wave's row of alpha.
 __device__ __forceinline__ int w_unit(int s, int u) { return s * (WSLOT / 2) + (u ^ (((s >> 4) & 3) ^ (s & 15))); }
-// t: ST doubles per slot, and 16 bytes more per bin so that the four bins of
-// a round start on different banks.
-__device__ __forceinline__ int t_base(int s) { return s * ST + ((s >> 4) & 3) * 2; }
+
+// Value of v in lane C of each group of four lanes (DPP quad_perm broadcast).
+template <int C>
+__device__ __forceinline__ double quad_bcast(double v) {
+  constexpr int ctrl = C | (C << 2) | (C << 4) | (C << 6);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), ctrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), ctrl, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
 
 // Support weights and this wave's coefficients of the lane's particle into
 // slot `lane` (zeros for a lane without a particle). With GB the field at the
@@ -155,7 +160,7 @@ __device__ __forceinline__ int t_base(int s) { return s * ST + ((s >> 4) & 3) * 
 // bin of the group (node a = ax + 3 ay + 9 az, 3 components).
 template <bool GB>
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, int row,
-                                      double* sW, double* sT, const double* sF, int lane) {
+                                      double* sW, const double* sF, int lane) {
   double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[3] = {0, 0, 0};
   if (r.valid) {
     axis_support<double, 2>(grid_coord<double, 0>(r.x, g), g.n0, wx);
@@ -186,10 +191,8 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) su[w_unit(lane, 4 * r4 + h)] = double2{wsup(8 * h + r4), wsup(8 * h + 4 + r4)};
-  double* st = sT + t_base(lane);
-  *reinterpret_cast<double2*>(st) = double2{t[0], t[1]};
-  st[2] = t[2];
+    for (int h = 0; h < 4; ++h)
+      su[w_unit(lane, 4 * r4 + h)] = double2{wsup(8 * h + r4), h < 3 ? wsup(8 * h + 4 + r4) : (r4 < 3 ? t[r4] : 0.0)};
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -207,14 +210,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     double sigma, double* __restrict__ rec) {
   __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
   double* sW = smem;
-  double* sT = smem + 64 * WSLOT;
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);  // the NQ waves of a group share an XCD
   const int grp = lid / NQ, row = lid - grp * NQ;     // row of alpha: components CPW*row ..
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, grp, nbins, np, lane);
-  double* sF = smem + 64 * WSLOT + TREG;
+  double* sF = smem + SMEM;
   if (GB) {
     // Bf is the grid field [nnodes][3]: node a of bin 4 grp + b is the bin's
     // own node (its first support node) shifted by (ax, ay, az).
@@ -241,10 +243,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // MFMA lane roles: particle k of the batch, block (= bin) mb, row/column mr.
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
-  // slot = 16 mb + 4 rd + mk in round rd: w_unit(slot, 4 mr + h) and
-  // t_base(slot) with the lane's constant part taken out of the loop
+  // slot = 16 mb + 4 rd + mk in round rd: w_unit(slot, 4 mr + h) with the
+  // lane's constant part taken out of the loop
   const int wl = (CH * mb + mk) * (WSLOT / 2), wx = mb ^ mk;
-  const int tl = t_base(CH * mb + mk);
 
   Raw raw = load_raw<GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int k = 0; k < NBP; ++k) acc[c][k] = 0.0;
 
   for (int j = 0; j < G.nchunks; ++j) {
-    stage<GB>(raw, g, beta, sigma, row, sW, sT, sF, lane);
+    stage<GB>(raw, g, beta, sigma, row, sW, sF, lane);
     wave_sync();
     raw = load_raw<GB>(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
     pnext = chunk_perm(perm, G, j + 2, lane);
@@ -272,9 +273,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         wv[2 * h] = v.x;
         wv[2 * h + 1] = v.y;
       }
-      const double* st = sT + tl + 16 * rd;
-      const double2 t01 = *reinterpret_cast<const double2*>(st);
-      const double tv[3] = {t01.x, t01.y, st[2]};
+      // wv[7] of the slot's lane r holds t_r
+      const double tv[3] = {quad_bcast<0>(wv[7]), quad_bcast<1>(wv[7]), quad_bcast<2>(wv[7])};
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
         double a[NBLK];
