@@ -348,7 +348,9 @@ def main():
     t_dom = dom_ms / launches * 1e-3
     flops = flops_per_particle(order, tensorial) * np_launch
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid)
-    dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False)
+    # average over the species' launches: the first overwrites M, the others
+    # accumulate into it (read and write)
+    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0) for si in range(len(spec))) / len(spec)
     if dom == "deposit":
         kname = "k_gather"
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",

@@ -175,3 +175,68 @@ def interp_field(order, n, origin, h, pos, F, prec32=False) -> np.ndarray:
     _check(_load().oracle_interp_field(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(F),
                                        _ptr(out)), "interp_field")
     return out
+
+
+# ---------------------------------------------------------------- canonical half and the stencil product
+def canonical_offsets(order: int) -> np.ndarray:
+    """Full offset indices of the canonical half: the displacements o with
+    (dz, dy, dx) >= 0 lexicographically, i.e. full index >= the centre's.
+    Sec. 3.4 stores (3^3+1)/2 = 14 (CIC) or (5^3+1)/2 = 63 (TSC) canonical
+    offsets, one of each pair o, -o since M[g][o] = M[g+o][-o]; which half is
+    not stated, and this one is the reading taken. Canonical index
+    k = full index - centre."""
+    nof = noff(order)
+    return np.arange((nof - 1) // 2, nof)
+
+
+def canonical_half(order: int, M: np.ndarray) -> np.ndarray:
+    """``Mc[g][k] = M[g][centre + k]`` for the full stencil ``M [nnodes, noff, ncomp]``."""
+    return np.ascontiguousarray(M[:, canonical_offsets(order), :])
+
+
+def _offset_vectors(order: int):
+    NO = 2 * order + 1
+    o = np.arange(NO ** 3)
+    return o % NO - order, (o // NO) % NO - order, o // (NO * NO) - order
+
+
+def _neighbour(n, dx, dy, dz):
+    """Node index g + (dx, dy, dz) for every node g (periodic)."""
+    nx, ny, nz = (int(v) for v in n)
+    g = np.arange(nx * ny * nz)
+    gx, gy, gz = g % nx, (g // nx) % ny, g // (nx * ny)
+    return ((gx + dx) % nx) + nx * (((gy + dy) % ny) + ny * ((gz + dz) % nz))
+
+
+def full_from_canonical(order: int, n, Mc: np.ndarray) -> np.ndarray:
+    """Rebuild the full stencil from the canonical half with M[g][-o] = M[g-o][o]."""
+    nof = noff(order)
+    c = (nof - 1) // 2
+    nn = Mc.shape[0]
+    M = np.empty((nn, nof, Mc.shape[2]))
+    M[:, c:, :] = Mc
+    ox, oy, oz = _offset_vectors(order)
+    for k in range(1, nof - c):
+        o = c + k
+        src = _neighbour(n, -ox[o], -oy[o], -oz[o])  # g - o
+        M[:, c - k, :] = Mc[src, k, :]
+    return M
+
+
+def stencil_matvec(order: int, n, M: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """The product of the assembled matrix with a grid vector, as the mass
+    matrix acts on the grid electric field in the implicit field equation
+    (Sec. 2.1), read off the stencil storage: y[g] = sum_o M[g][o] x[g+o],
+    with M[g][o] a 3x3 block
+    (row i, column j) acting on the 3-vector x[g+o] in the tensorial case and
+    a scalar otherwise. x, y are ``[nnodes, 3]`` (tensorial) or ``[nnodes]``."""
+    ox, oy, oz = _offset_vectors(order)
+    tens = M.shape[2] == 9
+    y = np.zeros_like(np.asarray(x, dtype=np.float64))
+    for o in range(noff(order)):
+        xo = x[_neighbour(n, ox[o], oy[o], oz[o])]
+        if tens:
+            y += np.einsum("gij,gj->gi", M[:, o, :].reshape(-1, 3, 3), xo)
+        else:
+            y += M[:, o, 0] * xo
+    return y

@@ -389,3 +389,47 @@ def test_grid_field_assembly_dense(order, n):
     Wd = dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, sp.pos)
     Md = dense_ref.dense_M(order, n, case.grid.origin, case.grid.h, sp.pos, sp.w, Wd @ F, sp.beta, case.sigma)
     assert rel(M, dense_ref.dense_to_stencil(order, n, Md)) < 1e-14
+
+
+# ---------------------------------------------------------------- canonical half and stencil product
+@pytest.mark.parametrize("order,n", [(1, (3, 4, 5)), (2, (5, 6, 7))])
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+def test_stencil_matvec_dense(order, n, kind):
+    """y = M x read off the stencil storage equals the dense product built by
+    brute force (tests/dense_ref.py), for scalar and 3x3 blocks."""
+    case = random_case(81 + order, order, n, 50, kind=kind, beta=0.6, sigma=1.1,
+                       origin=(-0.25, 0.5, 1.0), h=(0.5, 1.25, 2.0))
+    sp = case.species[0]
+    M = run_oracle(case)
+    Md = dense_ref.dense_M(order, n, case.grid.origin, case.grid.h, sp.pos, sp.w,
+                           sp.B if kind == "ecsim" else None, sp.beta, case.sigma)
+    nn = case.grid.ncells
+    rng = np.random.default_rng(5)
+    if kind == "ecsim":
+        x = rng.normal(size=(nn, 3))
+        # dense [3 nn, 3 nn] operator with block (g, g') = M^{ij}_{g g'}
+        D = Md.reshape(3, 3, nn, nn).transpose(2, 0, 3, 1).reshape(3 * nn, 3 * nn)
+        ref = (D @ x.reshape(-1)).reshape(nn, 3)
+    else:
+        x = rng.normal(size=nn)
+        ref = Md[0] @ x
+    got = oracle.stencil_matvec(order, n, M, x)
+    assert rel(got, ref) < 1e-14
+    # the (i, j) blocks transposed give another product
+    if kind == "ecsim":
+        Mt = M.reshape(nn, -1, 3, 3).transpose(0, 1, 3, 2).reshape(M.shape)
+        assert rel(oracle.stencil_matvec(order, n, Mt, x), ref) > 1e-3
+
+
+@pytest.mark.parametrize("order,n", [(1, (4, 5, 3)), (2, (6, 5, 7))])
+def test_canonical_half_roundtrip(order, n):
+    """The canonical half holds (noff + 1) / 2 offsets (14 or 63) and, with the
+    spatial symmetry M[g][-o] = M[g-o][o], gives back the full stencil bitwise."""
+    case = random_case(91 + order, order, n, 300, kind="ecsim", beta=0.5)
+    M = run_oracle(case)
+    Mc = oracle.canonical_half(order, M)
+    assert Mc.shape[1] == {1: 14, 2: 63}[order]
+    assert np.array_equal(oracle.full_from_canonical(order, n, Mc), M)
+    # a canonical half from the wrong side of the centre does not round-trip
+    bad = np.ascontiguousarray(M[:, :Mc.shape[1], :])
+    assert not np.allclose(oracle.full_from_canonical(order, n, bad), M)
