@@ -92,11 +92,15 @@ def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int,
     return np_ * per_particle + (nbins + 1) * 4 + nbins * record + field
 
 
-def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool) -> int:
+def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool,
+                  canonical: bool = False) -> int:
     """Algorithmic HBM bytes of one deposition launch: every record read once,
-    every stencil entry written once (read too when accumulating)."""
+    every stencil entry written once (read too when accumulating); the
+    canonical half stores (noff + 1) / 2 offsets."""
     n = (order + 1) ** 3
     noff = (2 * order + 1) ** 3
+    if canonical:
+        noff = (noff + 1) // 2
     nc = 9 if tensorial else 1
     out = nbins * noff * nc * elem
     return nbins * n * (n + 1) // 2 * nc * elem + out * (2 if accumulate else 1)
@@ -113,7 +117,8 @@ def workload_name(case, field_on_grid: bool = False) -> str:
 
 def workload_key(args) -> str:
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
-            + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else ""))
+            + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
+            + ("-canonical" if args.canonical else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -184,6 +189,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
+    ap.add_argument("--canonical", action="store_true",
+                    help="deposit into the canonical half of the stencil (14 / 63 offsets) instead of the full one")
+    ap.add_argument("--matvec", action="store_true",
+                    help="also time the stencil matrix-vector product y = M x on the assembled matrix")
     ap.add_argument("--field", default="particle", choices=("particle", "grid"),
                     help="ECSIM magnetic field per particle (default) or on the grid nodes, gathered at each "
                          "particle with its support weights")
@@ -208,6 +217,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     case = make_config(args.config, kind=args.kind, dtype=args.dtype, shuffled=args.shuffled)
+    if args.canonical and args.algo != "mfma":
+        print("bench.py: --canonical deposits the records of the matrix-core path (--algo mfma)", file=sys.stderr)
+        sys.exit(2)
     on_grid = args.field == "grid"
     if on_grid and case.kind != "ecsim":
         print("bench.py: --field grid needs an ECSIM workload", file=sys.stderr)
@@ -231,7 +243,8 @@ def main():
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
     ncomp = 9 if tensorial else 1
-    M = torch.empty(nbins * mm.noff(order) * ncomp, dtype=tdt, device=dev)
+    nof = mm.noff_canonical(order) if args.canonical else mm.noff(order)
+    M = torch.empty(nbins * nof * ncomp, dtype=tdt, device=dev)
     Fd = to_dev(Fgrid) if on_grid else None
     rec = None
     if args.algo == "mfma":
@@ -277,7 +290,7 @@ def main():
                 mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec,
                                  Bgrid=Fd)
                 mark(si, 2)
-                mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0)
+                mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0, canonical=args.canonical)
             else:
                 if tensorial:
                     ecsim(s, bs, perm, si, args.algo)
@@ -350,7 +363,8 @@ def main():
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid)
     # average over the species' launches: the first overwrites M, the others
     # accumulate into it (read and write)
-    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0) for si in range(len(spec))) / len(spec)
+    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical)
+                 for si in range(len(spec))) / len(spec)
     if dom == "deposit":
         kname = "k_gather"
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
@@ -379,14 +393,40 @@ def main():
     roof["avg_launch_ms"] = t_dom * 1e3
     roof["kernel_source_hash"] = khash
 
+    # the assembled matrix applied to a grid vector (the field-equation product),
+    # timed on its own after the assembly, from the stencil just assembled
+    matvec = None
+    if args.matvec:
+        nv = 3 if tensorial else 1
+        x = torch.randn(nbins * nv, dtype=tdt, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            mm.stencil_matvec(case.grid, order, M, x, tensorial, canonical=args.canonical, y=y)
+        reps = 20
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in mev:
+            a.record(stream)
+            mm.stencil_matvec(case.grid, order, M, x, tensorial, canonical=args.canonical, y=y)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t_mv = sum(a.elapsed_time(b) for a, b in mev) / reps * 1e-3
+        mv_bytes = (M.numel() + 2 * x.numel()) * elem  # stencil and x read once, y written once
+        matvec = {"kernel": "k_stencil_matvec", "stencil": "canonical half" if args.canonical else "full",
+                  "avg_launch_ms": t_mv * 1e3, "algorithmic_bytes": mv_bytes,
+                  "achieved_GBps": mv_bytes / t_mv / 1e9, "hbm_frac": mv_bytes / t_mv / PEAK_HBM}
+
     # parity of this run's output against the oracle (and the CPU baseline timing)
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
         cpu, Mref = cpu_baseline(case, args.cpu_budget, Fgrid)
         if Mref is not None and len(spec) == 1:
-            got = M.double().cpu().numpy().reshape(Mref.shape)
-            parity = float(np.linalg.norm(got - Mref) / np.linalg.norm(Mref))
+            got = M.double().cpu().numpy().reshape(nbins, nof, ncomp)
+            if args.canonical:
+                import oracle
+                Mref = oracle.canonical_half(order, Mref)
+            parity = float(np.linalg.norm(got - Mref.reshape(got.shape)) / np.linalg.norm(Mref))
 
     line = {
         "metric": METRIC,
@@ -403,7 +443,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(case, on_grid), "config_id": args.config, "grid": list(case.grid.n),
                    "order": order, "kind": case.kind, "field": args.field if tensorial else None, "np": np_total,
-                   "species": len(spec), "algo": args.algo,
+                   "species": len(spec), "algo": args.algo, "stencil": "canonical half" if args.canonical else "full",
                    "step": "bin + contract + deposit per species" if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
         "phases_ms_per_launch": phase_per_launch_ms,
@@ -411,6 +451,7 @@ def main():
         "assembly_only_particles_per_s": np_total / ((phase_ms["contract"] + phase_ms["deposit"]) / psteps * 1e-3)
         if args.algo != "atomic" else value,
         "roofline": roof,
+        "stencil_matvec": matvec,
         "cpu_baseline": cpu,
         "parity_rel_fro_vs_oracle": parity,
     }

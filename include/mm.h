@@ -182,6 +182,34 @@ mm_status mm_contract_bins_gridB(const mm_grid* grid, int order, mm_dtype dt, in
 mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
                              int accumulate, void* M, mm_stream_t stream);
 
+/*
+ * mm_deposit_records_canonical - mm_deposit_records into the canonical half of
+ * the stencil (Sec. 3.4: (3^3+1)/2 = 14 offsets for CIC, (5^3+1)/2 = 63 for
+ * TSC): only the displacements o >= 0 in (dz, dy, dx) lexicographic order are
+ * stored, at Mc[g][k][comp] with k = o - centre (o the full offset index of
+ * mm_assemble_*, centre = 13 or 62). The other half follows from the spatial
+ * symmetry M[g][-o] = M[g-o][o] (component by component; not a transpose of
+ * the 3x3 block). Each entry equals the full deposit's bit for bit.
+ *  Mc  [nnodes][14 or 63][ncomp] (dtype dt); other arguments as for
+ *      mm_deposit_records.
+ */
+mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
+                                       int accumulate, void* Mc, mm_stream_t stream);
+
+/*
+ * mm_stencil_matvec - the assembled matrix applied to a grid vector, as it
+ * acts on the electric field in the implicit field equation (Sec. 2.1):
+ *   y[g] = sum_o M[g][o] x[g+o]
+ * with M[g][o] the 3x3 block (row i = comp / 3, column j = comp % 3) acting on
+ * the 3-vector x[g+o] (tensorial != 0), or a scalar (tensorial == 0).
+ *  canonical  0: M is the full stencil [nnodes][noff][ncomp]; 1: M is the
+ *             canonical half of mm_deposit_records_canonical.
+ *  x, y       [nnodes][3] (tensorial) or [nnodes], dtype dt; y is
+ *             overwritten; x and y must not overlap (x == y is MM_ERR_ARG).
+ */
+mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical, const void* M,
+                            const void* x, void* y, mm_stream_t stream);
+
 /* Static description of a status code. */
 const char* mm_status_string(mm_status s);
 

@@ -207,17 +207,54 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     return rec
 
 
+def noff_canonical(order: int) -> int:
+    """Offsets kept in the canonical half of the stencil: 14 (CIC) or 63 (TSC)."""
+    return (noff(order) + 1) // 2
+
+
 def deposit_records(grid, order: int, rec: torch.Tensor, M: torch.Tensor, tensorial: bool,
-                    accumulate: bool = False) -> torch.Tensor:
-    """Phase 2: stencil deposition of the packed records into ``M``."""
+                    accumulate: bool = False, canonical: bool = False) -> torch.Tensor:
+    """Phase 2: stencil deposition of the packed records into ``M`` (the full
+    stencil, or its canonical half ``[nnodes, 14 | 63, ncomp]``)."""
     lib = _lib.load()
     g = _grid_of(grid)
     _check_tensor(M, "M", None)
     if M.dtype not in _DT:
         raise TypeError(f"unsupported dtype {M.dtype}")
     ncomp = 9 if tensorial else 1
-    if M.numel() != _nnodes(g) * noff(order) * ncomp:
+    nof = noff_canonical(order) if canonical else noff(order)
+    if M.numel() != _nnodes(g) * nof * ncomp:
         raise ValueError("M has the wrong number of elements")
-    _call(lib.mm_deposit_records, "mm_deposit_records", ctypes.byref(g), int(order), _DT[M.dtype], int(bool(tensorial)),
-          _ptr(rec), int(bool(accumulate)), _ptr(M), _stream(M.device))
+    fn, name = ((lib.mm_deposit_records_canonical, "mm_deposit_records_canonical") if canonical
+                else (lib.mm_deposit_records, "mm_deposit_records"))
+    _call(fn, name, ctypes.byref(g), int(order), _DT[M.dtype], int(bool(tensorial)), _ptr(rec),
+          int(bool(accumulate)), _ptr(M), _stream(M.device))
     return M
+
+
+def stencil_matvec(grid, order: int, M: torch.Tensor, x: torch.Tensor, tensorial: bool, canonical: bool = False,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``y[g] = sum_o M[g][o] x[g+o]`` from the full stencil or its canonical
+    half; x, y are ``[nnodes, 3]`` (tensorial) or ``[nnodes]``."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    dt = M.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor(M, "M", dt)
+    _check_tensor(x, "x", dt)
+    nn = _nnodes(g)
+    nv = 3 if tensorial else 1
+    nof = noff_canonical(order) if canonical else noff(order)
+    if M.numel() != nn * nof * (9 if tensorial else 1):
+        raise ValueError("M has the wrong number of elements")
+    if x.numel() != nn * nv:
+        raise ValueError(f"x has {x.numel()} elements, expected {nn * nv}")
+    if y is None:
+        y = torch.empty_like(x)
+    _check_tensor(y, "y", dt)
+    if y.numel() != nn * nv or y.data_ptr() == x.data_ptr():
+        raise ValueError("y must have x's size and not be x")
+    _call(lib.mm_stencil_matvec, "mm_stencil_matvec", ctypes.byref(g), int(order), _DT[dt], int(bool(tensorial)),
+          int(bool(canonical)), _ptr(M), _ptr(x), _ptr(y), _stream(M.device))
+    return y

@@ -446,13 +446,17 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 // y-major and z-minor within a block, and each XCD takes a contiguous range of
 // blocks: the 4 (CIC) or 9 (TSC) bin rows a node row reads were read by the
 // XCD a few rows earlier and are still in its L2.
-template <typename T, int R, int NC>
+// CANON: only the canonical half of the offsets, o >= centre (Sec. 3.4),
+// stored at o - centre.
+template <typename T, int R, int NC, bool CANON>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
                                                 T* __restrict__ M, int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
   constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
-  constexpr int ROWT = NOFF * TPE;      // threads per node
+  constexpr int O0 = CANON ? (NOFF - 1) / 2 : 0;  // first offset stored
+  constexpr int NOUT = NOFF - O0;                  // offsets stored per node
+  constexpr int ROWT = NOUT * TPE;                 // threads per node
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the row
   const int t = (blk - rv * blocks_per_row) * 256 + threadIdx.x;
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
   const int row = gy + g.n1 * gz;
   const int gx = t / ROWT;
   const int rr = t - gx * ROWT;
-  const int o = rr / TPE, c0 = (rr - o * TPE) * CPT;
+  const int o = O0 + rr / TPE, c0 = (rr - (o - O0) * TPE) * CPT;
   const int ox = o % NO - R, oy = (o / NO) % NO - R, oz = o / (NO * NO) - R;
   const int dlin = ox + NS * (oy + NS * oz);  // b - a in support-linear numbering
   // bin coordinates g - a per axis (wrapped)
@@ -513,37 +517,45 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
       }
     }
   }
-  T* dst = M + ((size_t)row * g.n0 + gx) * (NOFF * NC) + o * NC + c0;
+  T* dst = M + ((size_t)row * g.n0 + gx) * (NOUT * NC) + (o - O0) * NC + c0;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) dst[j] = accumulate ? dst[j] + sum[j] : sum[j];
 }
 
-template <typename T, int R, int NC>
+template <typename T, int R, int NC, bool CANON>
 static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
-  const size_t row_len = (size_t)g.n0 * Geo<R>::NOFF * (NC == 9 ? 3 : 1);  // threads per row of nodes
+  constexpr int NOUT = CANON ? (Geo<R>::NOFF + 1) / 2 : Geo<R>::NOFF;
+  const size_t row_len = (size_t)g.n0 * NOUT * (NC == 9 ? 3 : 1);  // threads per row of nodes
   if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gather<T, R, NC>), dim3((unsigned)blocks), dim3(256), 0, s, g, (const T*)rec, accumulate,
+  hipLaunchKernelGGL((k_gather<T, R, NC, CANON>), dim3((unsigned)blocks), dim3(256), 0, s, g, (const T*)rec, accumulate,
                      (T*)M, bpr);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
-                         void* M, hipStream_t s) {
+template <bool CANON>
+static hipError_t gather_dispatch(const GridDev& g, int order, bool f32, bool tensorial, const void* rec,
+                                  int accumulate, void* M, hipStream_t s) {
   if (f32) {
     if (order == 1)
-      return tensorial ? gather_launch<float, 1, 9>(g, rec, accumulate, M, s)
-                       : gather_launch<float, 1, 1>(g, rec, accumulate, M, s);
-    return tensorial ? gather_launch<float, 2, 9>(g, rec, accumulate, M, s)
-                     : gather_launch<float, 2, 1>(g, rec, accumulate, M, s);
+      return tensorial ? gather_launch<float, 1, 9, CANON>(g, rec, accumulate, M, s)
+                       : gather_launch<float, 1, 1, CANON>(g, rec, accumulate, M, s);
+    return tensorial ? gather_launch<float, 2, 9, CANON>(g, rec, accumulate, M, s)
+                     : gather_launch<float, 2, 1, CANON>(g, rec, accumulate, M, s);
   }
   if (order == 1)
-    return tensorial ? gather_launch<double, 1, 9>(g, rec, accumulate, M, s)
-                     : gather_launch<double, 1, 1>(g, rec, accumulate, M, s);
-  return tensorial ? gather_launch<double, 2, 9>(g, rec, accumulate, M, s)
-                   : gather_launch<double, 2, 1>(g, rec, accumulate, M, s);
+    return tensorial ? gather_launch<double, 1, 9, CANON>(g, rec, accumulate, M, s)
+                     : gather_launch<double, 1, 1, CANON>(g, rec, accumulate, M, s);
+  return tensorial ? gather_launch<double, 2, 9, CANON>(g, rec, accumulate, M, s)
+                   : gather_launch<double, 2, 1, CANON>(g, rec, accumulate, M, s);
+}
+
+hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
+                         void* M, hipStream_t s, bool canonical) {
+  return canonical ? gather_dispatch<true>(g, order, f32, tensorial, rec, accumulate, M, s)
+                   : gather_dispatch<false>(g, order, f32, tensorial, rec, accumulate, M, s);
 }
 
 }  // namespace mmk

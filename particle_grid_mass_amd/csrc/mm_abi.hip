@@ -240,6 +240,29 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
                                   (hipStream_t)stream));
 }
 
+mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
+                                       int accumulate, void* Mc, mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!rec || !Mc) return MM_ERR_NULL;
+  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, Mc,
+                                  (hipStream_t)stream, true));
+}
+
+mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical, const void* M,
+                            const void* x, void* y, mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!M || !x || !y) return MM_ERR_NULL;
+  if (x == y) return MM_ERR_ARG;
+  return hip_status(launch_stencil_matvec(to_dev(grid), order, dt == MM_F32, tensorial != 0, canonical != 0, M, x, y,
+                                          (hipStream_t)stream));
+}
+
 const char* mm_status_string(mm_status s) {
   switch (s) {
     case MM_OK: return "ok";

@@ -32,7 +32,13 @@ bool contract_gathers_field(int order, bool f32, int mode);
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 
 // Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o.
+// canonical: only o >= centre, stored at M[g][o - centre][c].
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
-                         void* M, hipStream_t s);
+                         void* M, hipStream_t s, bool canonical = false);
+
+// y[g] = sum_o M[g][o] x[g+o] (3x3 blocks on 3-vectors, or scalars), from the
+// full stencil or from its canonical half (M[g][-o] = M[g-o][o]).
+hipError_t launch_stencil_matvec(const GridDev& g, int order, bool f32, bool tensorial, bool canonical, const void* M,
+                                 const void* x, void* y, hipStream_t s);
 
 }  // namespace mmk

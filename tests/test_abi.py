@@ -118,3 +118,48 @@ def test_assemble_validation():
 def test_scalar_tsc_grid_bounds():
     assert _scalar(_lib.make_grid((5, 5, 5)), order=2) == _lib.MM_OK
     assert _scalar(_lib.make_grid((4, 5, 5)), order=2) == _lib.MM_ERR_ARG
+
+
+def _gridB(grid, order=1, dt=_lib.MM_F64, np_=10, Bgrid=FAKE, algo=0, bs=FAKE, perm=FAKE):
+    lib = _lib.load()
+    nb = ctypes.c_size_t(0)
+    st = lib.mm_assemble_ecsim_gridB(ctypes.byref(grid), order, dt, np_, FAKE, FAKE, Bgrid, bs, perm, 0.5, 1.0, 0, algo,
+                                     FAKE, None, ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def test_grid_field_validation_and_workspace():
+    """Workspace query of the grid-field assembly: records only where the fp64
+    contraction gathers the field itself, records plus the interpolated field
+    (np * 3 values) for fp32, the field alone for the atomic algorithms."""
+    st, nb64 = _gridB(G8, np_=1000)
+    assert st == _lib.MM_OK
+    st, nb_plain = _ecsim(G8, np_=1000)
+    assert nb64 == ((nb_plain + 255) & ~255)
+    st, nb32 = _gridB(G8, dt=_lib.MM_F32, np_=1000)
+    assert st == _lib.MM_OK and nb32 >= 1000 * 3 * 4
+    st, nb_at = _gridB(G8, np_=1000, algo=1, bs=None, perm=None)
+    assert st == _lib.MM_OK and nb_at == 1000 * 3 * 8
+    assert _gridB(G8, Bgrid=None)[0] == _lib.MM_ERR_NULL
+    assert _gridB(G8, order=3)[0] == _lib.MM_ERR_ARG
+    lib = _lib.load()
+    nb = ctypes.c_size_t(0)
+    assert lib.mm_contract_bins_gridB(ctypes.byref(G8), 1, _lib.MM_F64, 10, FAKE, FAKE, None, FAKE, FAKE, 0.5, 1.0,
+                                      None, ctypes.byref(nb), None) == _lib.MM_ERR_NULL
+
+
+def test_stencil_matvec_and_canonical_validation():
+    lib = _lib.load()
+    mv = lambda g, order=1, dt=_lib.MM_F64, M=FAKE, x=FAKE, y=ctypes.c_void_p(0x2000): lib.mm_stencil_matvec(
+        ctypes.byref(g) if g is not None else None, order, dt, 1, 0, M, x, y, None)
+    assert mv(None) == _lib.MM_ERR_NULL
+    assert mv(G8, order=4) == _lib.MM_ERR_ARG
+    assert mv(G8, dt=3) == _lib.MM_ERR_ARG
+    assert mv(G8, M=None) == _lib.MM_ERR_NULL
+    assert mv(G8, y=None) == _lib.MM_ERR_NULL
+    assert mv(G8, y=FAKE) == _lib.MM_ERR_ARG  # x == y
+    dep = lambda g, rec=FAKE, M=FAKE: lib.mm_deposit_records_canonical(ctypes.byref(g), 2, _lib.MM_F64, 1, rec, 0, M,
+                                                                       None)
+    assert dep(G8, rec=None) == _lib.MM_ERR_NULL
+    assert dep(G8, M=None) == _lib.MM_ERR_NULL
+    assert dep(_lib.make_grid((4, 8, 8))) == _lib.MM_ERR_ARG  # n < 2R+1 for TSC

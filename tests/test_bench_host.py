@@ -24,3 +24,12 @@ def test_every_kernel_hashable():
         assert k in bench.KERNEL_LABELS
         h = bench.kernel_source_hash(k)
         assert len(h) == 16 and int(h, 16) >= 0
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_deposit_bytes_canonical_half(order):
+    full = bench.deposit_bytes(order, True, 8, 1000, False)
+    half = bench.deposit_bytes(order, True, 8, 1000, False, canonical=True)
+    n = (order + 1) ** 3
+    rec = 1000 * n * (n + 1) // 2 * 9 * 8
+    assert (half - rec) * (2 * order + 1) ** 3 == (full - rec) * ((2 * order + 1) ** 3 + 1) // 2
