@@ -316,11 +316,12 @@ def main():
 
     # Phase pass (untimed): events at every phase boundary give the breakdown
     # and name the dominant kernel (the longest single launch of the step).
-    psteps = max(3, min(args.steps, 20))
+    psteps = max(1, min(args.steps, 20))
     pev = new_events(psteps)
     for k in range(psteps):
         step(pev[k])
     torch.cuda.synchronize()
+    print(f"[bench] phase pass done ({psteps} steps)", file=sys.stderr, flush=True)
     phases = ("bin", "contract", "deposit")
     phase_ms = {p: 0.0 for p in phases}
     for k in range(psteps):
