@@ -57,9 +57,11 @@ def _load():
     lib.oracle_bilinear.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, P, P, P]
     lib.oracle_rows.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I64, P, P]
     lib.oracle_interp_field.argtypes = [I, I, P, P, P, I64, P, P, P]
+    lib.oracle_moments.argtypes = [I, I, P, P, P, I64, P, I, P, I, P]
     lib.oracle_max_threads.argtypes = []
     for f in (lib.oracle_alpha, lib.oracle_support, lib.oracle_assemble, lib.oracle_bin,
-              lib.oracle_bilinear, lib.oracle_rows, lib.oracle_interp_field, lib.oracle_max_threads):
+              lib.oracle_bilinear, lib.oracle_rows, lib.oracle_interp_field, lib.oracle_moments,
+              lib.oracle_max_threads):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -164,6 +166,22 @@ def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32
     _check(_load().oracle_rows(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
                                float(beta), float(sigma), len(nodes), _ptr(nodes), _ptr(out)), "rows")
     return out
+
+
+def moments(order, n, origin, h, pos, Q, m=None, accumulate=False, prec32=False) -> np.ndarray:
+    """Deposit of per-particle quantities ``Q [np, nq]``: ``m[g][k] = sum_p W_pg Q_p[k]``, ``[nnodes, nq]``."""
+    n_, o_, h_ = _grid_args(n, origin, h)
+    pos, Q = _f64(pos), _f64(Q)
+    npart = pos.reshape(-1, 3).shape[0]
+    nq = Q.reshape(npart, -1).shape[1] if npart else Q.shape[-1]
+    nnodes = int(np.prod(n_.astype(np.int64)))
+    if m is None:
+        m = np.zeros((nnodes, nq))
+        accumulate = False
+    assert m.shape == (nnodes, nq) and m.dtype == np.float64 and m.flags.c_contiguous
+    _check(_load().oracle_moments(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), int(nq),
+                                  _ptr(Q), int(bool(accumulate)), _ptr(m)), "moments")
+    return m
 
 
 def interp_field(order, n, origin, h, pos, F, prec32=False) -> np.ndarray:

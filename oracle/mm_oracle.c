@@ -488,3 +488,34 @@ int oracle_interp_field(int order, int prec32, const int32_t* n, const double* o
   }
   return OR_OK;
 }
+
+/*
+ * Particle-to-grid deposition of per-particle quantities with the same
+ * weights, m[g][k] = sum_p W_pg Q_p[k] for k < nq: charge and current (four
+ * quantities per particle in 3D) or the ten of the implicit moment method,
+ * the other scatters the page's Sec. 6 (Conclusion) names for the same
+ * contraction, one operand holding the quantities and the other the weights.
+ * Q holds np*nq values (particle-major), m holds nnodes*nq and is zeroed
+ * first unless accumulate != 0. Serial, particle by particle.
+ */
+int oracle_moments(int order, int prec32, const int32_t* n, const double* origin, const double* h, int64_t np,
+                   const double* pos, int nq, const double* Q, int accumulate, double* m) {
+  or_grid g;
+  if (!fill_grid(&g, order, prec32, n, origin, h) || !m || np < 0 || nq < 1) return OR_ERR_ARG;
+  if (np > 0 && (!pos || !Q)) return OR_ERR_ARG;
+  const int NS = order + 1, nsup = NS * NS * NS;
+  const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];
+  if (!accumulate) memset(m, 0, (size_t)nnodes * nq * sizeof(double));
+  for (int64_t p = 0; p < np; ++p) {
+    or_support s;
+    particle_support(&g, pos + 3 * p, &s);
+    for (int a = 0; a < nsup; ++a) {
+      int ax = a % NS, ay = (a / NS) % NS, az = a / (NS * NS);
+      int64_t gx = (s.first[0] + ax) % n[0], gy = (s.first[1] + ay) % n[1], gz = (s.first[2] + az) % n[2];
+      int64_t node = gx + (int64_t)n[0] * (gy + (int64_t)n[1] * gz);
+      double W = (s.w1d[0][ax] * s.w1d[1][ay]) * s.w1d[2][az];
+      for (int k = 0; k < nq; ++k) m[node * nq + k] += W * Q[p * nq + k];
+    }
+  }
+  return OR_OK;
+}

@@ -433,3 +433,36 @@ def test_canonical_half_roundtrip(order, n):
     # a canonical half from the wrong side of the centre does not round-trip
     bad = np.ascontiguousarray(M[:, :Mc.shape[1], :])
     assert not np.allclose(oracle.full_from_canonical(order, n, bad), M)
+
+
+# ---------------------------------------------------------------- moment deposition
+@pytest.mark.parametrize("order,n", [(1, (3, 4, 5)), (2, (5, 6, 7))])
+@pytest.mark.parametrize("nq", [1, 4, 10])
+def test_moments_dense(order, n, nq):
+    """m = W^T Q against the dense interpolation matrix (wrapped distances),
+    particles shifted by whole periods; a swapped pair of quantities or nodes
+    shifted by one fail it."""
+    case = random_case(111 + order + nq, order, n, 70, kind="scalar", origin=(-0.25, 0.5, 1.0), h=(0.5, 1.25, 2.0))
+    pos = case.species[0].pos.copy()
+    pos[::3, 2] += 2 * n[2] * case.grid.h[2]
+    Q = np.random.default_rng(nq).normal(size=(len(pos), nq))
+    got = oracle.moments(order, n, case.grid.origin, case.grid.h, pos, Q)
+    W = dense_ref.dense_W(order, n, case.grid.origin, case.grid.h, pos)
+    assert rel(got, W.T @ Q) < 1e-14
+    if nq > 1:
+        assert rel(got, W.T @ Q[:, ::-1]) > 1e-2
+    assert rel(got, np.roll(W.T @ Q, 1, axis=0)) > 1e-2
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_moments_charge_conservation_and_node(order):
+    """Partition of unity: the deposited total of each quantity is the particle
+    total; a CIC particle on a node puts its quantities on that node exactly."""
+    case = random_case(121 + order, order, (6, 5, 7), 500, kind="scalar")
+    Q = np.random.default_rng(2).uniform(0.5, 1.5, size=(500, 4))
+    m = oracle.moments(order, case.grid.n, case.grid.origin, case.grid.h, case.species[0].pos, Q)
+    assert np.max(np.abs(m.sum(axis=0) - Q.sum(axis=0))) < 1e-12 * Q.sum()
+    if order == 1:
+        q = np.array([[1.5, -2.0, 0.25, 3.0]])
+        m1 = oracle.moments(1, (4, 5, 6), (0, 0, 0), (1, 1, 1), np.array([[2.0, 3.0, 1.0]]), q)
+        assert np.array_equal(m1[2 + 4 * (3 + 5 * 1)], q[0]) and np.count_nonzero(m1) == 4
