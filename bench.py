@@ -193,6 +193,9 @@ def main():
                     help="deposit into the canonical half of the stencil (14 / 63 offsets) instead of the full one")
     ap.add_argument("--matvec", action="store_true",
                     help="also time the stencil matrix-vector product y = M x on the assembled matrix")
+    ap.add_argument("--moments", type=int, default=0,
+                    help="also time the deposition of this many quantities per particle (e.g. 4: charge and "
+                         "current) on the first species")
     ap.add_argument("--field", default="particle", choices=("particle", "grid"),
                     help="ECSIM magnetic field per particle (default) or on the grid nodes, gathered at each "
                          "particle with its support weights")
@@ -417,6 +420,34 @@ def main():
                   "avg_launch_ms": t_mv * 1e3, "algorithmic_bytes": mv_bytes,
                   "achieved_GBps": mv_bytes / t_mv / 1e9, "hbm_frac": mv_bytes / t_mv / PEAK_HBM}
 
+    # moment deposition (charge and current, or nq quantities per particle) on
+    # species 0, timed on its own with the binning of the same particles
+    moments = None
+    if args.moments:
+        nq = args.moments
+        s0 = spec[0]
+        npm = s0["pos"].shape[0]
+        Qm = torch.randn(npm, nq, dtype=tdt, device=dev)
+        bs_m, perm_m = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"])
+        mo = mm.deposit_moments(case.grid, order, s0["pos"], Qm, bs_m, perm_m)
+        for _ in range(3):
+            mm.deposit_moments(case.grid, order, s0["pos"], Qm, bs_m, perm_m, m=mo)
+        reps = 20
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in mev:
+            a.record(stream)
+            mm.deposit_moments(case.grid, order, s0["pos"], Qm, bs_m, perm_m, m=mo)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t_m = sum(a.elapsed_time(b) for a, b in mev) / reps * 1e-3
+        nsup = (order + 1) ** 3
+        rec_b = nbins * nsup * nq * 8
+        m_bytes = npm * (3 * elem + nq * elem + 4) + (nbins + 1) * 4 + 2 * rec_b + nbins * nq * elem
+        moments = {"kernels": "k_moments + k_gather_moments", "nq": nq, "avg_call_ms": t_m * 1e3,
+                   "particles_per_s": npm / t_m, "algorithmic_bytes": m_bytes,
+                   "achieved_GBps": m_bytes / t_m / 1e9, "hbm_frac": m_bytes / t_m / PEAK_HBM}
+
     # parity of this run's output against the oracle (and the CPU baseline timing)
     cpu = None
     parity = None
@@ -453,6 +484,7 @@ def main():
         if args.algo != "atomic" else value,
         "roofline": roof,
         "stencil_matvec": matvec,
+        "moments": moments,
         "cpu_baseline": cpu,
         "parity_rel_fro_vs_oracle": parity,
     }

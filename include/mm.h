@@ -197,6 +197,25 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
                                        int accumulate, void* Mc, mm_stream_t stream);
 
 /*
+ * mm_deposit_moments - deposition of per-particle quantities with the same
+ * support weights: m[g][k] = sum_p W_pg Q_p[k], k < nq (1 <= nq <= 16), e.g.
+ * charge and current (nq = 4) or the ten quantities of the implicit moment
+ * method. Sec. 6 of the page names these scatters as further uses of the
+ * same contraction, one operand holding the quantities and the other the
+ * weights; here it runs per bin on the matrix cores with fp64 accumulation
+ * (for both dtypes) and a fixed-order gather per node.
+ *  pos [np][3], Q [np][nq] (dtype dt); bin_start, perm from mm_bin_particles
+ *      (same grid, order, dtype and positions).
+ *  m [nnodes][nq] (dtype dt): overwritten (accumulate == 0) or added to.
+ *  ws: device workspace of *ws_bytes bytes, 16-byte aligned (query with
+ *      ws == NULL): nnodes * (order + 1)^3 * nq * 8 bytes of per-bin records.
+ *  nq outside [1, 16] is MM_ERR_ARG.
+ */
+mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* Q,
+                             int nq, const int32_t* bin_start, const int32_t* perm, int accumulate, void* m, void* ws,
+                             size_t* ws_bytes, mm_stream_t stream);
+
+/*
  * mm_stencil_matvec - the assembled matrix applied to a grid vector, as it
  * acts on the electric field in the implicit field equation (Sec. 2.1):
  *   y[g] = sum_o M[g][o] x[g+o]

@@ -258,3 +258,38 @@ def stencil_matvec(grid, order: int, M: torch.Tensor, x: torch.Tensor, tensorial
     _call(lib.mm_stencil_matvec, "mm_stencil_matvec", ctypes.byref(g), int(order), _DT[dt], int(bool(tensorial)),
           int(bool(canonical)), _ptr(M), _ptr(x), _ptr(y), _stream(M.device))
     return y
+
+
+def deposit_moments(grid, order: int, pos: torch.Tensor, Q: torch.Tensor, bin_start: torch.Tensor,
+                    perm: torch.Tensor, m: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+    """``m[g][k] = sum_p W_pg Q_p[k]`` for per-particle quantities ``Q [np, nq]``
+    (nq <= 16), e.g. charge and current; returns ``m [nnodes, nq]``."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    dt = pos.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check_tensor(pos, "pos", dt)
+    _check_tensor(Q, "Q", dt)
+    npart = pos.numel() // 3
+    if npart == 0:
+        nq = Q.shape[-1] if Q.dim() > 1 else 1
+    else:
+        if Q.numel() % npart:
+            raise ValueError("Q must hold nq values per particle")
+        nq = Q.numel() // npart
+    _check_tensor(bin_start, "bin_start", torch.int32)
+    _check_tensor(perm, "perm", torch.int32)
+    nn = _nnodes(g)
+    if m is None:
+        m = torch.empty((nn, nq), dtype=dt, device=pos.device)
+        accumulate = False
+    _check_tensor(m, "m", dt)
+    if m.numel() != nn * nq:
+        raise ValueError(f"m has {m.numel()} elements, expected {nn * nq}")
+    s = _stream(pos.device)
+    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(Q), int(nq), _ptr(bin_start), _ptr(perm),
+            int(bool(accumulate)), _ptr(m))
+    ws, nbytes = _workspace(lib.mm_deposit_moments, "mm_deposit_moments", head, pos.device, s)
+    _call(lib.mm_deposit_moments, "mm_deposit_moments", *head, _ptr(ws), ctypes.byref(nbytes), s)
+    return m

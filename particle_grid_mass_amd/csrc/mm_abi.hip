@@ -251,6 +251,36 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
                                   (hipStream_t)stream, true));
 }
 
+mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* Q,
+                             int nq, const int32_t* bin_start, const int32_t* perm, int accumulate, void* m, void* ws,
+                             size_t* ws_bytes, mm_stream_t stream) {
+  if (!ws_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (nq < 1 || nq > 16) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!m) return MM_ERR_NULL;
+  if (np > 0 && (!pos || !Q || !bin_start || !perm)) return MM_ERR_NULL;
+  const bool f32 = dt == MM_F32;
+  const size_t need = np > 0 ? moment_record_bytes(order, nq, nnodes) : 0;
+  if (!ws) {
+    *ws_bytes = need;
+    return MM_OK;
+  }
+  if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+  if (need > 0 && ((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (np == 0) {
+    if (accumulate) return MM_OK;
+    return hip_status(launch_fill_zero(m, (size_t)nnodes * nq, f32, s));
+  }
+  return hip_status(launch_moments(to_dev(grid), order, f32, pos, Q, nq, bin_start, perm, (int)np, accumulate, m, ws,
+                                   s));
+}
+
 mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical, const void* M,
                             const void* x, void* y, mm_stream_t stream) {
   int64_t nnodes = 0;

@@ -36,6 +36,13 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
                          void* M, hipStream_t s, bool canonical = false);
 
+// Moment deposition m[g][k] = sum_p W_pg Q_p[k], k < nq <= 16, through
+// per-bin fp64 records rec (moment_record_bytes) and a fixed-order gather.
+size_t moment_record_bytes(int order, int nq, int64_t nbins);
+hipError_t launch_moments(const GridDev& g, int order, bool f32, const void* pos, const void* Q, int nq,
+                          const int32_t* bin_start, const int32_t* perm, int np, int accumulate, void* m, void* rec,
+                          hipStream_t s);
+
 // y[g] = sum_o M[g][o] x[g+o] (3x3 blocks on 3-vectors, or scalars), from the
 // full stencil or from its canonical half (M[g][-o] = M[g-o][o]).
 hipError_t launch_stencil_matvec(const GridDev& g, int order, bool f32, bool tensorial, bool canonical, const void* M,
