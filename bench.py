@@ -80,15 +80,19 @@ def flops_per_particle(order: int, tensorial: bool) -> int:
     return 2 * n * n * (9 if tensorial else 1)
 
 
-def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int, field_on_grid: bool = False) -> int:
+def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int, field_on_grid: bool = False,
+                   pelem: int = 0) -> int:
     """Algorithmic HBM bytes of one contraction launch: each particle's
     position, weight (and field) and permutation entry read once, bin bounds
     read once, one packed upper-triangle record written per bin; a field on
-    the grid nodes is read once instead of the per-particle field."""
+    the grid nodes is read once instead of the per-particle field. pelem: bytes
+    of a stored position or field value when it differs from elem (the mixed
+    layout's fp32 positions)."""
+    pelem = pelem or elem
     n = (order + 1) ** 3
-    per_particle = (3 + 1 + (3 if tensorial and not field_on_grid else 0)) * elem + 4
+    per_particle = (3 + (3 if tensorial and not field_on_grid else 0)) * pelem + elem + 4
     record = n * (n + 1) // 2 * (9 if tensorial else 1) * elem
-    field = nbins * 3 * elem if tensorial and field_on_grid else 0
+    field = nbins * 3 * pelem if tensorial and field_on_grid else 0
     return np_ * per_particle + (nbins + 1) * 4 + nbins * record + field
 
 
@@ -106,13 +110,14 @@ def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate
     return nbins * n * (n + 1) // 2 * nc * elem + out * (2 if accumulate else 1)
 
 
-def workload_name(case, field_on_grid: bool = False) -> str:
+def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
     n = case.grid.n
     kind = "ECSIM 3x3" if case.kind == "ecsim" else "scalar"
     order = "CIC" if case.order == 1 else "TSC"
-    return (f"{order} {kind} {case.dtype}, {n[0]}x{n[1]}x{n[2]} periodic cells, {case.np_total:,} particles "
+    dt = "f64 on fp32 positions and fields" if mix else case.dtype
+    return (f"{order} {kind} {dt}, {n[0]}x{n[1]}x{n[2]} periodic cells, {case.np_total:,} particles "
             f"({len(case.species)} species)" + (", magnetic field on the grid nodes" if field_on_grid else "")
-            + f", {case.name}" + ("_gridB" if field_on_grid else ""))
+            + f", {case.name}" + ("_gridB" if field_on_grid else "") + ("_mix" if mix else ""))
 
 
 def workload_key(args) -> str:
@@ -184,7 +189,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--kind", default=None, help="scalar|ecsim where the config offers both (config 4)")
-    ap.add_argument("--dtype", default="f64")
+    ap.add_argument("--dtype", default="f64", choices=("f64", "f32", "mix"),
+                    help="f64, f32, or mix: fp32 positions and fields with fp64 weights, matrix and arithmetic")
     ap.add_argument("--shuffled", action="store_true", help="config 3: randomly shuffled particle order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
@@ -219,7 +225,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    case = make_config(args.config, kind=args.kind, dtype=args.dtype, shuffled=args.shuffled)
+    mix = args.dtype == "mix"
+    case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled)
+    if mix:  # the stored fp32 positions and fields, seen by the oracle as the same values in fp64
+        for sp in case.species:
+            sp.pos = sp.pos.astype(np.float32).astype(np.float64)
+            if sp.B is not None:
+                sp.B = sp.B.astype(np.float32).astype(np.float64)
     if args.canonical and args.algo != "mfma":
         print("bench.py: --canonical deposits the records of the matrix-core path (--algo mfma)", file=sys.stderr)
         sys.exit(2)
@@ -228,8 +240,12 @@ def main():
         print("bench.py: --field grid needs an ECSIM workload", file=sys.stderr)
         sys.exit(2)
     Fgrid = grid_field(case.grid, 1000 + args.config, case.dtype) if on_grid else None
+    if mix and on_grid:
+        Fgrid = Fgrid.astype(np.float32).astype(np.float64)
     tdt = torch.float64 if case.dtype == "f64" else torch.float32
     elem = 8 if case.dtype == "f64" else 4
+    pdt = torch.float32 if mix else tdt  # stored positions and fields
+    pelem = 4 if mix else elem
     tensorial = case.kind == "ecsim"
     order = case.order
     nbins = case.grid.ncells
@@ -239,20 +255,23 @@ def main():
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=tdt)
 
+    def to_devp(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=pdt)
+
     spec = []
     for sp in case.species:
-        spec.append(dict(pos=to_dev(sp.pos), w=to_dev(sp.w), B=to_dev(sp.B) if tensorial and not on_grid else None,
+        spec.append(dict(pos=to_devp(sp.pos), w=to_dev(sp.w), B=to_devp(sp.B) if tensorial and not on_grid else None,
                          beta=sp.beta,
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
     ncomp = 9 if tensorial else 1
     nof = mm.noff_canonical(order) if args.canonical else mm.noff(order)
     M = torch.empty(nbins * nof * ncomp, dtype=tdt, device=dev)
-    Fd = to_dev(Fgrid) if on_grid else None
+    Fd = to_devp(Fgrid) if on_grid else None
     rec = None
     if args.algo == "mfma":
         s0 = spec[0]
-        bs0, perm0 = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"])
+        bs0, perm0 = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"], mixed=mix)
         rec = mm.contract_bins(case.grid, order, s0["pos"], s0["w"], s0["B"], bs0, perm0, s0["beta"], case.sigma,
                                Bgrid=Fd)
 
@@ -287,7 +306,7 @@ def main():
                 for k in (1, 2, 3):
                     mark(si, k)
                 continue
-            bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"])
+            bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"], mixed=mix)
             mark(si, 1)
             if args.algo == "mfma":
                 mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec,
@@ -364,7 +383,7 @@ def main():
     np_launch = np_total / len(spec)
     t_dom = dom_ms / launches * 1e-3
     flops = flops_per_particle(order, tensorial) * np_launch
-    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid)
+    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem)
     # average over the species' launches: the first overwrites M, the others
     # accumulate into it (read and write)
     dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical)
@@ -428,7 +447,7 @@ def main():
         s0 = spec[0]
         npm = s0["pos"].shape[0]
         Qm = torch.randn(npm, nq, dtype=tdt, device=dev)
-        bs_m, perm_m = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"])
+        bs_m, perm_m = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"], mixed=mix)
         mo = mm.deposit_moments(case.grid, order, s0["pos"], Qm, bs_m, perm_m)
         for _ in range(3):
             mm.deposit_moments(case.grid, order, s0["pos"], Qm, bs_m, perm_m, m=mo)
@@ -443,7 +462,7 @@ def main():
         t_m = sum(a.elapsed_time(b) for a, b in mev) / reps * 1e-3
         nsup = (order + 1) ** 3
         rec_b = nbins * nsup * nq * 8
-        m_bytes = npm * (3 * elem + nq * elem + 4) + (nbins + 1) * 4 + 2 * rec_b + nbins * nq * elem
+        m_bytes = npm * (3 * pelem + nq * elem + 4) + (nbins + 1) * 4 + 2 * rec_b + nbins * nq * elem
         moments = {"kernels": "k_moments + k_gather_moments", "nq": nq, "avg_call_ms": t_m * 1e3,
                    "particles_per_s": npm / t_m, "algorithmic_bytes": m_bytes,
                    "achieved_GBps": m_bytes / t_m / 1e9, "hbm_frac": m_bytes / t_m / PEAK_HBM}
@@ -473,8 +492,10 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_name(case, on_grid), "config_id": args.config, "grid": list(case.grid.n),
-                   "order": order, "kind": case.kind, "field": args.field if tensorial else None, "np": np_total,
+        "config": {"workload": workload_name(case, on_grid, mix), "config_id": args.config, "grid": list(case.grid.n),
+                   "order": order, "kind": case.kind, "field": args.field if tensorial else None,
+                   "storage": "fp32 positions and fields, fp64 weights and matrix" if mix else case.dtype,
+                   "np": np_total,
                    "species": len(spec), "algo": args.algo, "stencil": "canonical half" if args.canonical else "full",
                    "step": "bin + contract + deposit per species" if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},

@@ -28,7 +28,13 @@
  *           The full stencil is stored (both g->g' and g'->g).
  *  dtype:   MM_F64: pos, w, B and M are double. MM_F32: all four are float,
  *           the cell decision, weights and matrix-core accumulation run in
- *           fp32 (sigma and beta are rounded to fp32).
+ *           fp32 (sigma and beta are rounded to fp32). MM_MIX: the
+ *           production layout of Sec. 5 ("Exactness and precision"):
+ *           positions and fields (pos, B, Bgrid) are float, weights w,
+ *           quantities Q, vectors x, y and the outputs M, m are double, and
+ *           every step runs in fp64 on the fp32 values read exactly into fp64
+ *           (the cell decision too). MM_ALGO_ATOMIC does not take MM_MIX
+ *           (MM_ERR_UNSUPPORTED).
  *  Memory:  every array argument is a device pointer (hipMalloc or an
  *           allocator on top of it, e.g. torch) on the current device,
  *           owned by the caller. The library allocates nothing and keeps no
@@ -62,7 +68,7 @@ typedef enum {
   MM_ERR_HIP = 5          /* a HIP launch or runtime call failed */
 } mm_status;
 
-typedef enum { MM_F64 = 0, MM_F32 = 1 } mm_dtype;
+typedef enum { MM_F64 = 0, MM_F32 = 1, MM_MIX = 2 } mm_dtype;
 
 /* Assembly algorithm. */
 typedef enum {

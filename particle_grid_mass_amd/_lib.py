@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmm.so")
 
 MM_OK, MM_ERR_NULL, MM_ERR_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP = range(6)
-MM_F64, MM_F32 = 0, 1
+MM_F64, MM_F32, MM_MIX = 0, 1, 2
 ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
 
 # Every symbol the public header include/mm.h declares.

@@ -18,6 +18,20 @@ from ._lib import MMError
 _DT = {torch.float64: _lib.MM_F64, torch.float32: _lib.MM_F32}
 
 
+def _modes(pos: torch.Tensor, other: torch.Tensor):
+    """(mm dtype code, field dtype, output dtype) from the position dtype and the
+    dtype of the weights / quantities: equal dtypes are MM_F64 or MM_F32;
+    float32 positions with float64 weights are the mixed production layout
+    MM_MIX (positions and fields fp32; weights, quantities and outputs fp64)."""
+    if pos.dtype not in _DT or other.dtype not in _DT:
+        raise TypeError(f"unsupported dtypes {pos.dtype}, {other.dtype}")
+    if pos.dtype == other.dtype:
+        return _DT[pos.dtype], pos.dtype, pos.dtype
+    if pos.dtype == torch.float32 and other.dtype == torch.float64:
+        return _lib.MM_MIX, torch.float32, torch.float64
+    raise TypeError("float64 positions with float32 weights are not a supported layout")
+
+
 def _grid_of(grid) -> _lib.MMGrid:
     if isinstance(grid, _lib.MMGrid):
         return grid
@@ -69,13 +83,18 @@ def noff(order: int) -> int:
 
 
 def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch.Tensor] = None,
-                  perm: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stable counting sort by first support node -> ``(bin_start[nbins+1], perm[np])`` (int32)."""
+                  perm: Optional[torch.Tensor] = None, mixed: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable counting sort by first support node -> ``(bin_start[nbins+1], perm[np])`` (int32).
+    ``mixed``: float32 positions binned in fp64 arithmetic, as the mixed layout
+    (fp32 positions, fp64 weights) assembles them; otherwise float32 positions
+    are binned in fp32."""
     lib = _lib.load()
     g = _grid_of(grid)
     dt = pos.dtype
     if dt not in _DT:
         raise TypeError(f"unsupported dtype {dt}")
+    if mixed and dt != torch.float32:
+        raise TypeError("mixed binning takes float32 positions")
     _check_tensor(pos, "pos", dt)
     npart = pos.numel() // 3
     dev = pos.device
@@ -86,7 +105,8 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
     s = _stream(dev)
-    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(bin_start), _ptr(perm))
+    head = (ctypes.byref(g), int(order), _lib.MM_MIX if mixed else _DT[dt], npart, _ptr(pos), _ptr(bin_start),
+            _ptr(perm))
     ws, nbytes = _workspace(lib.mm_bin_particles, "mm_bin_particles", head, dev, s)
     _call(lib.mm_bin_particles, "mm_bin_particles", *head, _ptr(ws), ctypes.byref(nbytes), s)
     return bin_start, perm[:npart]
@@ -95,15 +115,13 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
 def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, accumulate, algo, Bgrid=None):
     lib = _lib.load()
     g = _grid_of(grid)
-    dt = pos.dtype
-    if dt not in _DT:
-        raise TypeError(f"unsupported dtype {dt}")
-    _check_tensor(pos, "pos", dt)
+    code, fdt, dt = _modes(pos, w)
+    _check_tensor(pos, "pos", fdt)
     _check_tensor(w, "w", dt)
     if B is not None:
-        _check_tensor(B, "B", dt)
+        _check_tensor(B, "B", fdt)
     if Bgrid is not None:
-        _check_tensor(Bgrid, "Bgrid", dt)
+        _check_tensor(Bgrid, "Bgrid", fdt)
         if Bgrid.numel() != 3 * _nnodes(g):
             raise ValueError(f"Bgrid has {Bgrid.numel()} elements, expected 3 * nnodes = {3 * _nnodes(g)}")
     npart = pos.numel() // 3
@@ -129,15 +147,15 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
     a = _lib.ALGOS[algo]
     if kind == "ecsim" and Bgrid is not None:
         fn, name = lib.mm_assemble_ecsim_gridB, "mm_assemble_ecsim_gridB"
-        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(Bgrid), _ptr(bin_start),
+        head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(Bgrid), _ptr(bin_start),
                 _ptr(perm), float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
     elif kind == "ecsim":
         fn, name = lib.mm_assemble_ecsim, "mm_assemble_ecsim"
-        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
+        head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
                 float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
     else:
         fn, name = lib.mm_assemble_scalar, "mm_assemble_scalar"
-        head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(bin_start), _ptr(perm),
+        head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(bin_start), _ptr(perm),
                 float(sigma), int(bool(accumulate)), a, _ptr(M))
     ws, nbytes = _workspace(fn, name, head, dev, s)
     _call(fn, name, *head, _ptr(ws), ctypes.byref(nbytes), s)
@@ -174,15 +192,15 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     ``[nnodes, 3]``, gathered at each particle with its support weights)."""
     lib = _lib.load()
     g = _grid_of(grid)
-    dt = pos.dtype
-    for t, name in ((pos, "pos"), (w, "w")):
-        _check_tensor(t, name, dt)
+    code, fdt, dt = _modes(pos, w)
+    _check_tensor(pos, "pos", fdt)
+    _check_tensor(w, "w", dt)
     if B is not None and Bgrid is not None:
         raise ValueError("give the field per particle (B) or on the grid (Bgrid), not both")
     if B is not None:
-        _check_tensor(B, "B", dt)
+        _check_tensor(B, "B", fdt)
     if Bgrid is not None:
-        _check_tensor(Bgrid, "Bgrid", dt)
+        _check_tensor(Bgrid, "Bgrid", fdt)
         if Bgrid.numel() != 3 * _nnodes(g):
             raise ValueError(f"Bgrid has {Bgrid.numel()} elements, expected 3 * nnodes = {3 * _nnodes(g)}")
     _check_tensor(bin_start, "bin_start", torch.int32)
@@ -195,7 +213,7 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     else:
         fn, name = lib.mm_contract_bins, "mm_contract_bins"
         field = B
-    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
+    head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
             _ptr(perm), float(beta), float(sigma))
     nbytes = ctypes.c_size_t(0)
     _call(fn, name + " (size query)", *head, None, ctypes.byref(nbytes), s)
@@ -266,10 +284,8 @@ def deposit_moments(grid, order: int, pos: torch.Tensor, Q: torch.Tensor, bin_st
     (nq <= 16), e.g. charge and current; returns ``m [nnodes, nq]``."""
     lib = _lib.load()
     g = _grid_of(grid)
-    dt = pos.dtype
-    if dt not in _DT:
-        raise TypeError(f"unsupported dtype {dt}")
-    _check_tensor(pos, "pos", dt)
+    code, fdt, dt = _modes(pos, Q)
+    _check_tensor(pos, "pos", fdt)
     _check_tensor(Q, "Q", dt)
     npart = pos.numel() // 3
     if npart == 0:
@@ -288,7 +304,7 @@ def deposit_moments(grid, order: int, pos: torch.Tensor, Q: torch.Tensor, bin_st
     if m.numel() != nn * nq:
         raise ValueError(f"m has {m.numel()} elements, expected {nn * nq}")
     s = _stream(pos.device)
-    head = (ctypes.byref(g), int(order), _DT[dt], npart, _ptr(pos), _ptr(Q), int(nq), _ptr(bin_start), _ptr(perm),
+    head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(Q), int(nq), _ptr(bin_start), _ptr(perm),
             int(bool(accumulate)), _ptr(m))
     ws, nbytes = _workspace(lib.mm_deposit_moments, "mm_deposit_moments", head, pos.device, s)
     _call(lib.mm_deposit_moments, "mm_deposit_moments", *head, _ptr(ws), ctypes.byref(nbytes), s)

@@ -80,8 +80,9 @@ __device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int 
 // tail up to nbins from the last particle): the final values when the whole
 // input is in key order, and overwritten by the digit passes and k_bounds
 // otherwise.
-template <typename T, int R>
-__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict__ pos, int np, int nbins,
+// T: arithmetic of the key; PT: type of the stored positions (T, or fp32 read into fp64).
+template <typename T, int R, typename PT>
+__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restrict__ pos, int np, int nbins,
                                                   uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
                                                   int ntiles, int32_t* __restrict__ tile_unsorted,
                                                   int32_t* __restrict__ bin_start, int32_t* __restrict__ perm) {
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict
       size_t idx = base + (size_t)i * BT + tid;
       idx = idx < (size_t)np ? idx : (size_t)np - 1;  // clamped: loads are unconditional
 #pragma unroll
-      for (int d = 0; d < 3; ++d) x[i][d] = pos[3 * idx + d];
+      for (int d = 0; d < 3; ++d) x[i][d] = (T)pos[3 * idx + d];
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -120,8 +121,14 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const T* __restrict
       if (lane == 63) klast[i][wave] = key;
     }
   }
-  if (tid == 0)
-    kbefore = base > 0 ? particle_key<T, R>(pos + 3 * (base - 1), g) : -1;  // last particle of the previous tile
+  if (tid == 0) {  // key of the last particle of the previous tile
+    int kb = -1;
+    if (base > 0) {
+      const T xb[3] = {(T)pos[3 * (base - 1)], (T)pos[3 * (base - 1) + 1], (T)pos[3 * (base - 1) + 2]};
+      kb = particle_key<T, R>(xb, g);
+    }
+    kbefore = kb;
+  }
   __syncthreads();
   if (tid < BI * NWV) {  // first particle of each wave's run of 64 against its predecessor
     const int i = tid / NWV, wv = tid - i * NWV;
@@ -407,20 +414,20 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
 
 size_t bin_workspace_bytes(int64_t np, int64_t nbins) { return bin_layout(nullptr, np, nbins).bytes; }
 
-template <typename T>
+template <typename T, typename PT>
 static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, int nbins, const BinWs& w, int ntiles,
                          int32_t* bin_start, int32_t* perm, hipStream_t s) {
   if (order == 1)
-    hipLaunchKernelGGL((k_keys_hist<T, 1>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, nbins, w.keysA,
+    hipLaunchKernelGGL((k_keys_hist<T, 1, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, np, nbins, w.keysA,
                        w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   else
-    hipLaunchKernelGGL((k_keys_hist<T, 2>), dim3(ntiles), dim3(BT), 0, s, g, (const T*)pos, np, nbins, w.keysA,
+    hipLaunchKernelGGL((k_keys_hist<T, 2, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, np, nbins, w.keysA,
                        w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   return hipGetLastError();
 }
 
 hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, int np, int nbins, int32_t* bin_start,
-                      int32_t* perm, void* ws, hipStream_t s) {
+                      int32_t* perm, void* ws, hipStream_t s, bool pos32) {
   if (np == 0) {
     hipLaunchKernelGGL(k_fill_i32, dim3((nbins + 1 + 255) / 256), dim3(256), 0, s, bin_start, nbins + 1, 0);
     return hipGetLastError();
@@ -428,8 +435,9 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
   BinWs w = bin_layout(ws, np, nbins);
   const int npass = digit_passes(nbins);
   const int ntiles = (np + TILE - 1) / TILE;
-  hipError_t e = f32 ? keys_t<float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
-                     : keys_t<double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
+  hipError_t e = f32     ? keys_t<float, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
+                 : pos32 ? keys_t<double, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
+                         : keys_t<double, double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
   if (e != hipSuccess) return e;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;

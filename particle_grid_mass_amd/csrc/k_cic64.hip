@@ -91,9 +91,10 @@ struct Raw {
 };
 
 // GB: the field is on the grid (gathered in stage), not per particle.
-template <int NC, bool GB>
-__device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
-                                        const double* __restrict__ Bf, int p, int np) {
+// PT: type of the stored positions and field (fp64, or fp32 read into fp64).
+template <typename PT, int NC, bool GB>
+__device__ __forceinline__ Raw load_raw(const PT* __restrict__ pos, const double* __restrict__ w,
+                                        const PT* __restrict__ Bf, int p, int np) {
   Raw r{0, 0, 0, 0, 0, 0, 0, false};
   if ((unsigned)p < (unsigned)np) {
     r.valid = true;
@@ -182,9 +183,9 @@ struct Acc {
 
 }  // namespace
 
-template <int NC, bool GB>
-__global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restrict__ pos,
-                                              const double* __restrict__ w, const double* __restrict__ Bf,
+template <typename PT, int NC, bool GB>
+__global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ pos,
+                                              const double* __restrict__ w, const PT* __restrict__ Bf,
                                               const int32_t* __restrict__ bin_start,
                                               const int32_t* __restrict__ perm, int np, int nbins, double beta,
                                               double sigma, double* __restrict__ rec) {
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
       const int x = kx + (a & 1) < g.n0 ? kx + (a & 1) : 0;
       const int y = ky + ((a >> 1) & 1) < g.n1 ? ky + ((a >> 1) & 1) : 0;
       const int z = kz + (a >> 2) < g.n2 ? kz + (a >> 2) : 0;
-      const double* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
+      const PT* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
       f0 = f[0];
       f1 = f[1];
       f2 = f[2];
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
   const int wl = w_unit(CH * mb + mk, 0);  // = (17 mb + mk) * 4; round rd adds 16 rd, unit mr ^ rd
   const int tl = t_base<NC>(CH * mb + mk);
 
-  Raw raw = load_raw<NC, GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  Raw raw = load_raw<PT, NC, GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
   Acc<NC> acc;
   acc.zero();
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
     __syncthreads();
     // In flight during this chunk's rounds: the next chunk's particle data and
     // the permutation entries of the chunk after it.
-    raw = load_raw<NC, GB>(pos, w, Bf, pnext, np);
+    raw = load_raw<PT, NC, GB>(pos, w, Bf, pnext, np);
     const int p2 = chunk_perm(perm, G, j + 2, lane);
 
     const int left = G.maxn - j * CH;
@@ -297,20 +298,27 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const double* __restric
   }
 }
 
-hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, double* rec, hipStream_t s) {
+template <typename PT>
+static hipError_t cic64_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                          double beta, double sigma, double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // one single-wave workgroup per group of four bins
   if (P.Bgrid)
-    hipLaunchKernelGGL((k_cic64<9, true>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
-                       (const double*)P.w, (const double*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 9, true>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos, (const double*)P.w,
+                       (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
   else if (P.B)
-    hipLaunchKernelGGL((k_cic64<9, false>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
-                       (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 9, false>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
   else
-    hipLaunchKernelGGL((k_cic64<1, false>), dim3(ngroups), dim3(64), 0, s, g, (const double*)P.pos,
-                       (const double*)P.w, (const double*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 1, false>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
   return hipGetLastError();
+}
+
+hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s) {
+  return P.pos32 ? cic64_t<float>(g, P, bin_start, perm, beta, sigma, rec, s)
+                 : cic64_t<double>(g, P, bin_start, perm, beta, sigma, rec, s);
 }
 
 }  // namespace mmk

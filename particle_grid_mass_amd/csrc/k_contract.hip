@@ -100,9 +100,10 @@ struct Raw {
   bool valid;
 };
 
-template <typename T, int NC>
-__device__ __forceinline__ Raw<T> load_raw(const T* __restrict__ pos, const T* __restrict__ w,
-                                           const T* __restrict__ Bf, int p, int np) {
+// PT: type of the stored positions and field (T, or fp32 read into fp64).
+template <typename T, typename PT, int NC>
+__device__ __forceinline__ Raw<T> load_raw(const PT* __restrict__ pos, const T* __restrict__ w,
+                                           const PT* __restrict__ Bf, int p, int np) {
   Raw<T> r;
   r.valid = (unsigned)p < (unsigned)np;
   r.x = r.y = r.z = r.w = r.bx = r.by = r.bz = T(0);
@@ -327,9 +328,9 @@ struct AccSel<T, 2, NC> {
 // ---------------------------------------------------------------- kernel
 constexpr int CT_WAVES = 4;  // waves per block; each wave works alone
 
-template <typename T, int R, int NC, int MODE>
-__global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const T* __restrict__ pos,
-                                                            const T* __restrict__ w, const T* __restrict__ Bf,
+template <typename T, typename PT, int R, int NC, int MODE>
+__global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const PT* __restrict__ pos,
+                                                            const T* __restrict__ w, const PT* __restrict__ Bf,
                                                             const int32_t* __restrict__ bin_start,
                                                             const int32_t* __restrict__ perm, int np, int nbins,
                                                             T beta, T sigma, T* __restrict__ out) {
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const T* 
   s = s < 0 ? 0 : s;
   e = e > np ? np : e;
   int c0 = s;
-  Raw<T> cur = load_raw<T, NC>(pos, w, Bf, c0 + lane < e ? perm[c0 + lane] : -1, np);
+  Raw<T> cur = load_raw<T, PT, NC>(pos, w, Bf, c0 + lane < e ? perm[c0 + lane] : -1, np);
 
   while (true) {
     // Next chunk: the rest of this bin, else the wave's next bin.
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const T* 
     const int pnext = (more && nc0 + lane < ne) ? perm[nc0 + lane] : -1;
 
     stage_particle<T, R, NC>(cur, g, beta, sigma, sW, sT, lane);
-    Raw<T> nxt = load_raw<T, NC>(pos, w, Bf, pnext, np);
+    Raw<T> nxt = load_raw<T, PT, NC>(pos, w, Bf, pnext, np);
     const int cnt = e - c0 < 64 ? (e - c0 > 0 ? e - c0 : 0) : 64;
     acc.accumulate(sW, sT, cnt, lane);
 
@@ -395,8 +396,14 @@ static hipError_t contract_launch(const GridDev& g, const Particles& P, const in
   int blocks = (nbins + CT_WAVES - 1) / CT_WAVES;
   int cap = 256 * waves_per_cu / CT_WAVES;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((k_contract<T, R, NC, MODE>), dim3(blocks), dim3(64 * CT_WAVES), 0, s, g, (const T*)P.pos,
-                     (const T*)P.w, (const T*)P.B, bin_start, perm, P.np, nbins, (T)beta, (T)sigma, (T*)out);
+  if (P.pos32)  // fp32 positions and field into fp64 arithmetic
+    hipLaunchKernelGGL((k_contract<T, float, R, NC, MODE>), dim3(blocks), dim3(64 * CT_WAVES), 0, s, g,
+                       (const float*)P.pos, (const T*)P.w, (const float*)P.B, bin_start, perm, P.np, nbins, (T)beta,
+                       (T)sigma, (T*)out);
+  else
+    hipLaunchKernelGGL((k_contract<T, T, R, NC, MODE>), dim3(blocks), dim3(64 * CT_WAVES), 0, s, g,
+                       (const T*)P.pos, (const T*)P.w, (const T*)P.B, bin_start, perm, P.np, nbins, (T)beta,
+                       (T)sigma, (T*)out);
   return hipGetLastError();
 }
 

@@ -13,16 +13,17 @@
 
 namespace mmk {
 
-template <typename T, int R>
-__global__ __launch_bounds__(256) void k_interp_field(GridDev g, const T* __restrict__ pos, int np,
-                                                      const T* __restrict__ F, T* __restrict__ out) {
+// T: arithmetic and output; PT: stored positions and field (T, or fp32 into fp64).
+template <typename T, int R, typename PT>
+__global__ __launch_bounds__(256) void k_interp_field(GridDev g, const PT* __restrict__ pos, int np,
+                                                      const PT* __restrict__ F, T* __restrict__ out) {
   constexpr int NS = R + 1;
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= np) return;
   T wx[3], wy[3], wz[3];
-  const int fx = axis_support<T, R>(grid_coord<T, 0>(pos[3 * (size_t)p], g), g.n0, wx);
-  const int fy = axis_support<T, R>(grid_coord<T, 1>(pos[3 * (size_t)p + 1], g), g.n1, wy);
-  const int fz = axis_support<T, R>(grid_coord<T, 2>(pos[3 * (size_t)p + 2], g), g.n2, wz);
+  const int fx = axis_support<T, R>(grid_coord<T, 0>((T)pos[3 * (size_t)p], g), g.n0, wx);
+  const int fy = axis_support<T, R>(grid_coord<T, 1>((T)pos[3 * (size_t)p + 1], g), g.n1, wy);
+  const int fz = axis_support<T, R>(grid_coord<T, 2>((T)pos[3 * (size_t)p + 2], g), g.n2, wz);
   T b[3] = {T(0), T(0), T(0)};
 #pragma unroll
   for (int az = 0; az < NS; ++az) {
@@ -35,10 +36,10 @@ __global__ __launch_bounds__(256) void k_interp_field(GridDev g, const T* __rest
       for (int ax = 0; ax < NS; ++ax) {
         const int x = fx + ax < g.n0 ? fx + ax : fx + ax - g.n0;
         const T W = (wx[ax] * wy[ay]) * wz[az];
-        const T* f = F + 3 * (row + x);
-        b[0] += W * f[0];
-        b[1] += W * f[1];
-        b[2] += W * f[2];
+        const PT* f = F + 3 * (row + x);
+        b[0] += W * (T)f[0];
+        b[1] += W * (T)f[1];
+        b[2] += W * (T)f[2];
       }
     }
   }
@@ -47,26 +48,23 @@ __global__ __launch_bounds__(256) void k_interp_field(GridDev g, const T* __rest
   out[3 * (size_t)p + 2] = b[2];
 }
 
-hipError_t launch_interp_field(const GridDev& g, int order, bool f32, const void* pos, int np, const void* F,
-                               void* out, hipStream_t s) {
-  if (np <= 0) return hipSuccess;
+template <typename T, typename PT>
+static hipError_t interp_t(const GridDev& g, int order, const void* pos, int np, const void* F, void* out,
+                           hipStream_t s) {
   const dim3 grid((unsigned)((np + 255) / 256)), block(256);
-  if (f32) {
-    if (order == 1)
-      hipLaunchKernelGGL((k_interp_field<float, 1>), grid, block, 0, s, g, (const float*)pos, np, (const float*)F,
-                         (float*)out);
-    else
-      hipLaunchKernelGGL((k_interp_field<float, 2>), grid, block, 0, s, g, (const float*)pos, np, (const float*)F,
-                         (float*)out);
-  } else {
-    if (order == 1)
-      hipLaunchKernelGGL((k_interp_field<double, 1>), grid, block, 0, s, g, (const double*)pos, np,
-                         (const double*)F, (double*)out);
-    else
-      hipLaunchKernelGGL((k_interp_field<double, 2>), grid, block, 0, s, g, (const double*)pos, np,
-                         (const double*)F, (double*)out);
-  }
+  if (order == 1)
+    hipLaunchKernelGGL((k_interp_field<T, 1, PT>), grid, block, 0, s, g, (const PT*)pos, np, (const PT*)F, (T*)out);
+  else
+    hipLaunchKernelGGL((k_interp_field<T, 2, PT>), grid, block, 0, s, g, (const PT*)pos, np, (const PT*)F, (T*)out);
   return hipGetLastError();
+}
+
+hipError_t launch_interp_field(const GridDev& g, int order, bool f32, const void* pos, int np, const void* F,
+                               void* out, hipStream_t s, bool pos32) {
+  if (np <= 0) return hipSuccess;
+  if (f32) return interp_t<float, float>(g, order, pos, np, F, out, s);
+  return pos32 ? interp_t<double, float>(g, order, pos, np, F, out, s)
+               : interp_t<double, double>(g, order, pos, np, F, out, s);
 }
 
 }  // namespace mmk

@@ -41,8 +41,9 @@ __device__ __forceinline__ int q_base(int s) {
 
 }  // namespace
 
-template <typename T, int R, int KB>
-__global__ __launch_bounds__(64) void k_moments(GridDev g, const T* __restrict__ pos, const T* __restrict__ Q, int nq,
+// T: arithmetic of the weights and type of Q; PT: stored positions (T, or fp32 into fp64).
+template <typename T, int R, int KB, typename PT>
+__global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict__ pos, const T* __restrict__ Q, int nq,
                                                 const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm,
                                                 int np, int nbins, double* __restrict__ rec) {
   constexpr int NS = MGeo<R>::NS, N = MGeo<R>::N, NR = MGeo<R>::NR, NRB = NR / 4;
@@ -82,9 +83,9 @@ __global__ __launch_bounds__(64) void k_moments(GridDev g, const T* __restrict__
     T wx[3] = {T(0), T(0), T(0)}, wy[3] = {T(0), T(0), T(0)}, wz[3] = {T(0), T(0), T(0)};
     const bool valid = (unsigned)p < (unsigned)np;
     if (valid) {
-      axis_support<T, R>(grid_coord<T, 0>(pos[3 * (size_t)p], g), g.n0, wx);
-      axis_support<T, R>(grid_coord<T, 1>(pos[3 * (size_t)p + 1], g), g.n1, wy);
-      axis_support<T, R>(grid_coord<T, 2>(pos[3 * (size_t)p + 2], g), g.n2, wz);
+      axis_support<T, R>(grid_coord<T, 0>((T)pos[3 * (size_t)p], g), g.n0, wx);
+      axis_support<T, R>(grid_coord<T, 1>((T)pos[3 * (size_t)p + 1], g), g.n1, wy);
+      axis_support<T, R>(grid_coord<T, 2>((T)pos[3 * (size_t)p + 2], g), g.n2, wz);
     }
     double* sw = sm + w_base<R>(lane);
 #pragma unroll
@@ -157,19 +158,19 @@ size_t moment_record_bytes(int order, int nq, int64_t nbins) {
   return (size_t)nbins * n * nq * sizeof(double);
 }
 
-template <typename T, int R>
+template <typename T, int R, typename PT>
 static hipError_t moments_t(const GridDev& g, const void* pos, const void* Q, int nq, const int32_t* bin_start,
                             const int32_t* perm, int np, int accumulate, void* m, double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
-  const int ngroups = (nbins + NB - 1) / NB;
+  const dim3 grid((unsigned)((nbins + NB - 1) / NB)), block(64);
   const int kb = (nq + 3) / 4;
-  const T* P = (const T*)pos;
+  const PT* P = (const PT*)pos;
   const T* Qt = (const T*)Q;
   switch (kb) {
-    case 1: hipLaunchKernelGGL((k_moments<T, R, 1>), dim3(ngroups), dim3(64), 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
-    case 2: hipLaunchKernelGGL((k_moments<T, R, 2>), dim3(ngroups), dim3(64), 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
-    case 3: hipLaunchKernelGGL((k_moments<T, R, 3>), dim3(ngroups), dim3(64), 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
-    case 4: hipLaunchKernelGGL((k_moments<T, R, 4>), dim3(ngroups), dim3(64), 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
+    case 1: hipLaunchKernelGGL((k_moments<T, R, 1, PT>), grid, block, 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
+    case 2: hipLaunchKernelGGL((k_moments<T, R, 2, PT>), grid, block, 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
+    case 3: hipLaunchKernelGGL((k_moments<T, R, 3, PT>), grid, block, 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
+    case 4: hipLaunchKernelGGL((k_moments<T, R, 4, PT>), grid, block, 0, s, g, P, Qt, nq, bin_start, perm, np, nbins, rec); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -184,12 +185,16 @@ static hipError_t moments_t(const GridDev& g, const void* pos, const void* Q, in
 
 hipError_t launch_moments(const GridDev& g, int order, bool f32, const void* pos, const void* Q, int nq,
                           const int32_t* bin_start, const int32_t* perm, int np, int accumulate, void* m, void* rec,
-                          hipStream_t s) {
+                          hipStream_t s, bool pos32) {
+  double* r = (double*)rec;
   if (f32)
-    return order == 1 ? moments_t<float, 1>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, (double*)rec, s)
-                      : moments_t<float, 2>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, (double*)rec, s);
-  return order == 1 ? moments_t<double, 1>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, (double*)rec, s)
-                    : moments_t<double, 2>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, (double*)rec, s);
+    return order == 1 ? moments_t<float, 1, float>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s)
+                      : moments_t<float, 2, float>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s);
+  if (pos32)
+    return order == 1 ? moments_t<double, 1, float>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s)
+                      : moments_t<double, 2, float>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s);
+  return order == 1 ? moments_t<double, 1, double>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s)
+                    : moments_t<double, 2, double>(g, pos, Q, nq, bin_start, perm, np, accumulate, m, r, s);
 }
 
 }  // namespace mmk

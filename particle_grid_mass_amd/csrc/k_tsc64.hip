@@ -90,10 +90,11 @@ struct Raw {
   bool valid;
 };
 
-// GB: the field is on the grid (gathered in stage), not per particle.
-template <bool GB>
-__device__ __forceinline__ Raw load_raw(const double* __restrict__ pos, const double* __restrict__ w,
-                                        const double* __restrict__ Bf, int p, int np) {
+// GB: the field is on the grid (gathered in stage), not per particle. PT: type
+// of the stored positions and field (fp64, or fp32 read into fp64).
+template <typename PT, bool GB>
+__device__ __forceinline__ Raw load_raw(const PT* __restrict__ pos, const double* __restrict__ w,
+                                        const PT* __restrict__ Bf, int p, int np) {
   Raw r{0, 0, 0, 0, 0, 0, 0, false};
   if ((unsigned)p < (unsigned)np) {
     r.valid = true;
@@ -203,9 +204,9 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
-template <bool GB>
+template <typename PT, bool GB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
-    GridDev g, const double* __restrict__ pos, const double* __restrict__ w, const double* __restrict__ Bf,
+    GridDev g, const PT* __restrict__ pos, const double* __restrict__ w, const PT* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
     double sigma, double* __restrict__ rec) {
   __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         x = x < g.n0 ? x : x - g.n0;
         y = y < g.n1 ? y : y - g.n1;
         z = z < g.n2 ? z : z - g.n2;
-        const double* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
+        const PT* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
         f0 = f[0];
         f1 = f[1];
         f2 = f[2];
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // lane's constant part taken out of the loop
   const int wl = (CH * mb + mk) * (WSLOT / 2), wx = mb ^ mk;
 
-  Raw raw = load_raw<GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  Raw raw = load_raw<PT, GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
   int pnext = chunk_perm(perm, G, 1, lane);
   double acc[CPW][NBP];
 #pragma unroll
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   for (int j = 0; j < G.nchunks; ++j) {
     stage<GB>(raw, g, beta, sigma, row, sW, sF, lane);
     wave_sync();
-    raw = load_raw<GB>(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
+    raw = load_raw<PT, GB>(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
     pnext = chunk_perm(perm, G, j + 2, lane);
 
     const int left = G.maxn - j * CH;
@@ -322,18 +323,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, double* rec, hipStream_t s) {
-  if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
+template <typename PT>
+static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                          double beta, double sigma, double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // NQ single-wave workgroups per group of four bins
   if (P.Bgrid)
-    hipLaunchKernelGGL(k_tsc64<true>, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
-                       (const double*)P.w, (const double*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_tsc64<PT, true>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
   else
-    hipLaunchKernelGGL(k_tsc64<false>, dim3(ngroups * NQ), dim3(64), 0, s, g, (const double*)P.pos,
-                       (const double*)P.w, (const double*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_tsc64<PT, false>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
   return hipGetLastError();
+}
+
+hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, double* rec, hipStream_t s) {
+  if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
+  return P.pos32 ? tsc64_t<float>(g, P, bin_start, perm, beta, sigma, rec, s)
+                 : tsc64_t<double>(g, P, bin_start, perm, beta, sigma, rec, s);
 }
 
 }  // namespace mmk

@@ -54,6 +54,8 @@ GridDev to_dev(const mm_grid* g) {
 
 mm_status hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
 
+bool dtype_ok(mm_dtype dt) { return dt == MM_F64 || dt == MM_F32 || dt == MM_MIX; }
+
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Shared argument checks of the assembly entry points. The tensorial field is
@@ -66,8 +68,9 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC) return MM_ERR_ARG;
+  if (algo == MM_ALGO_ATOMIC && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -86,6 +89,8 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   const size_t rec_need = records ? align256(record_bytes(order, f32, tensorial, nnodes)) : 0;
   const bool interp = Bgrid && np > 0 &&
                       !(records && contract_gathers_field(order, f32, MODE_RECORD));
+  // fp32 positions with an fp64 interpolated field: not a combination the kernels take
+  if (interp && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
   const size_t need = rec_need + (interp ? (size_t)np * 3 * elem : 0);
   if (!ws) {
     *ws_bytes = need;
@@ -100,10 +105,11 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   GridDev g = to_dev(grid);
   hipError_t e = hipSuccess;
   Particles P{pos, w, tensorial ? B : nullptr, (int)np};
+  P.pos32 = dt == MM_MIX;
   if (Bgrid && np > 0) {
     if (interp) {
       void* bp = (char*)ws + rec_need;
-      e = launch_interp_field(g, order, f32, pos, (int)np, Bgrid, bp, s);
+      e = launch_interp_field(g, order, f32, pos, (int)np, Bgrid, bp, s, P.pos32);
       if (e != hipSuccess) return hip_status(e);
       P.B = bp;
     } else {
@@ -132,7 +138,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -152,6 +158,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   GridDev g = to_dev(grid);
   hipStream_t s = (hipStream_t)stream;
   Particles P{pos, w, B, (int)np};
+  P.pos32 = dt == MM_MIX;
   if (Bgrid) {
     if (interp) {
       void* bp = (char*)rec + align256(rec_need);
@@ -175,7 +182,7 @@ mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t 
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
   if (!bin_start) return MM_ERR_NULL;
@@ -187,7 +194,7 @@ mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t 
   }
   if (*ws_bytes < need) return MM_ERR_WORKSPACE;
   return hip_status(launch_bin(to_dev(grid), order, dt == MM_F32, pos, (int)np, (int)nnodes, bin_start, perm, ws,
-                               (hipStream_t)stream));
+                               (hipStream_t)stream, dt == MM_MIX));
 }
 
 mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
@@ -234,7 +241,7 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!rec || !M) return MM_ERR_NULL;
   return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, M,
                                   (hipStream_t)stream));
@@ -245,7 +252,7 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!rec || !Mc) return MM_ERR_NULL;
   return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, Mc,
                                   (hipStream_t)stream, true));
@@ -258,7 +265,7 @@ mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (nq < 1 || nq > 16) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -278,7 +285,7 @@ mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_
     return hip_status(launch_fill_zero(m, (size_t)nnodes * nq, f32, s));
   }
   return hip_status(launch_moments(to_dev(grid), order, f32, pos, Q, nq, bin_start, perm, (int)np, accumulate, m, ws,
-                                   s));
+                                   s, dt == MM_MIX));
 }
 
 mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical, const void* M,
@@ -286,7 +293,7 @@ mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int ten
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (dt != MM_F64 && dt != MM_F32) return MM_ERR_ARG;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!M || !x || !y) return MM_ERR_NULL;
   if (x == y) return MM_ERR_ARG;
   return hip_status(launch_stencil_matvec(to_dev(grid), order, dt == MM_F32, tensorial != 0, canonical != 0, M, x, y,

@@ -41,7 +41,7 @@ hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, 
 size_t moment_record_bytes(int order, int nq, int64_t nbins);
 hipError_t launch_moments(const GridDev& g, int order, bool f32, const void* pos, const void* Q, int nq,
                           const int32_t* bin_start, const int32_t* perm, int np, int accumulate, void* m, void* rec,
-                          hipStream_t s);
+                          hipStream_t s, bool pos32 = false);
 
 // y[g] = sum_o M[g][o] x[g+o] (3x3 blocks on 3-vectors, or scalars), from the
 // full stencil or from its canonical half (M[g][-o] = M[g-o][o]).

@@ -16,11 +16,13 @@ struct Particles {
   const void* B;    // [np][3] or NULL (scalar, or the field is on the grid)
   int np;
   const void* Bgrid = nullptr;  // [nnodes][3]: field on the grid nodes, gathered at each particle
+  bool pos32 = false;           // fp64 arithmetic on fp32 positions and fields (w and outputs fp64)
 };
 
 // out[p] = sum_a W_pa F[g_a]: the nodal field F [nnodes][3] at every particle.
+// pos32: fp32 positions and field, fp64 arithmetic and output (f32 must be false).
 hipError_t launch_interp_field(const GridDev& g, int order, bool f32, const void* pos, int np, const void* F,
-                               void* out, hipStream_t s);
+                               void* out, hipStream_t s, bool pos32 = false);
 
 // M <- 0 (a fill kernel, so the stream stays capturable).
 hipError_t launch_fill_zero(void* M, size_t count, bool f32, hipStream_t s);
@@ -31,7 +33,8 @@ hipError_t launch_atomic_scatter(const GridDev& g, int order, bool f32, const Pa
 
 // Binning: stable LSD radix sort of first-support-node keys.
 size_t bin_workspace_bytes(int64_t np, int64_t nbins);
+// pos32 (with f32 false): fp32 positions, keys found in fp64 arithmetic.
 hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, int np, int nbins, int32_t* bin_start,
-                      int32_t* perm, void* ws, hipStream_t s);
+                      int32_t* perm, void* ws, hipStream_t s, bool pos32 = false);
 
 }  // namespace mmk
