@@ -85,6 +85,12 @@ def _check(rc, what):
         raise ValueError(f"oracle {what} failed with code {rc}")
 
 
+def noff_grid(order: int, n) -> int:
+    """Stencil offsets per node: (2R+1)^3, or (2R+1)^2 on a 2D grid (n[2] == 1)."""
+    NO = 2 * order + 1
+    return NO * NO * (1 if int(n[2]) == 1 else NO)
+
+
 def noff(order: int) -> int:
     return (2 * order + 1) ** 3
 
@@ -120,7 +126,7 @@ def assemble(order, n, origin, h, pos, w, B=None, beta=0.0, sigma=1.0, M=None, a
     npart = 0 if pos is None else pos.reshape(-1, 3).shape[0]
     ncomp = 1 if B is None else 9
     nnodes = int(np.prod(n_.astype(np.int64)))
-    shape = (nnodes, noff(order), ncomp)
+    shape = (nnodes, noff_grid(order, n_), ncomp)
     if M is None:
         M = np.zeros(shape)
         accumulate = False
@@ -162,7 +168,7 @@ def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32
     nodes = np.ascontiguousarray(nodes, dtype=np.int64)
     npart = pos.reshape(-1, 3).shape[0]
     ncomp = 1 if B is None else 9
-    out = np.zeros((len(nodes), noff(order), ncomp))
+    out = np.zeros((len(nodes), noff_grid(order, n_), ncomp))
     _check(_load().oracle_rows(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
                                float(beta), float(sigma), len(nodes), _ptr(nodes), _ptr(out)), "rows")
     return out

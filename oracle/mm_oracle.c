@@ -23,7 +23,10 @@
  *    (1 + beta^2 |B|^2), [B]x u = B x u (the page cites it as Eq. 5 but the
  *    formula itself did not survive extraction).
  *  - Grid nodes sit at origin + k*h; the domain is periodic with n cells per
- *    dimension and as many nodes.
+ *    dimension and as many nodes. n[2] == 1 is the 2D problem (Sec. 5 reports
+ *    2D runs): the z coordinate is ignored, the support is (R+1)^2 nodes in
+ *    the x-y plane and the stencil (2R+1)^2 offsets, offset = (dx+R) +
+ *    (2R+1)*(dy+R).
  *  - Output layout M[node][offset][comp]: node = x + nx*(y + ny*z);
  *    offset = (dx+R) + (2R+1)*((dy+R) + (2R+1)*(dz+R)) for the node-pair
  *    displacement d = g' - g in [-R, R]^3; comp = 3*i + j (ncomp = 9) or 0.
@@ -65,7 +68,7 @@ typedef struct {
 static int grid_ok(const or_grid* g) {
   if (g->order != 1 && g->order != 2) return 0;
   for (int d = 0; d < 3; ++d) {
-    if (g->n[d] < 2 * g->order + 1) return 0;
+    if (g->n[d] < 2 * g->order + 1 && !(d == 2 && g->n[2] == 1)) return 0;
     if (!(g->h[d] > 0.0) || !isfinite(g->h[d]) || !isfinite(g->origin[d])) return 0;
   }
   return 1;
@@ -92,8 +95,24 @@ static void cell_and_fraction(const or_grid* g, int d, double x, int64_t* j, dou
 }
 
 /* Support rule and 1D B-spline weights (Sec. 2.3). */
+/* 2D (n[2] == 1): one node plane, no extent in z. */
+static int is2d(const or_grid* g) { return g->n[2] == 1; }
+/* support nodes per particle and stencil offsets per node */
+static int nsup_of(const or_grid* g) { return (g->order + 1) * (g->order + 1) * (is2d(g) ? 1 : g->order + 1); }
+static int noff_of(const or_grid* g) {
+  const int NO = 2 * g->order + 1;
+  return NO * NO * (is2d(g) ? 1 : NO);
+}
+
 static void particle_support(const or_grid* g, const double* x, or_support* s) {
   for (int d = 0; d < 3; ++d) {
+    if (d == 2 && is2d(g)) {
+      s->first[2] = 0;
+      s->w1d[2][0] = 1.0;
+      s->w1d[2][1] = 0.0;
+      s->w1d[2][2] = 0.0;
+      continue;
+    }
     int64_t j;
     double xi;
     cell_and_fraction(g, d, x[d], &j, &xi);
@@ -166,8 +185,8 @@ int oracle_support(int order, int prec32, const int32_t* n, const double* origin
 /* Add one particle's contribution (Eq. 6) into M. */
 static void scatter_particle(const or_grid* g, const double* x, double w, const double* B, double beta,
                              double sigma, double* M) {
-  const int R = g->order, NS = R + 1, NO = 2 * R + 1;
-  const int noff = NO * NO * NO;
+  const int R = g->order, NS = R + 1, NO = 2 * R + 1, RZ = is2d(g) ? 0 : R;
+  const int noff = noff_of(g);
   const int ncomp = B ? 9 : 1;
   or_support s;
   particle_support(g, x, &s);
@@ -181,7 +200,7 @@ static void scatter_particle(const or_grid* g, const double* x, double w, const 
     t[0] = sigma * w;
   }
 
-  int nsup = NS * NS * NS;
+  int nsup = nsup_of(g);
   int64_t node[27];
   double W[27];
   int ax[27], ay[27], az[27];
@@ -198,7 +217,7 @@ static void scatter_particle(const or_grid* g, const double* x, double w, const 
   for (int a = 0; a < nsup; ++a) {
     for (int b = 0; b < nsup; ++b) {
       double ww = W[a] * W[b];
-      int o = (ax[b] - ax[a] + R) + NO * ((ay[b] - ay[a] + R) + NO * (az[b] - az[a] + R));
+      int o = (ax[b] - ax[a] + R) + NO * ((ay[b] - ay[a] + R) + NO * (az[b] - az[a] + RZ));
       double* dst = M + ((size_t)node[a] * noff + o) * ncomp;
       for (int c = 0; c < ncomp; ++c) dst[c] += t[c] * ww;
     }
@@ -230,10 +249,10 @@ int oracle_assemble(int order, int prec32, const int32_t* n, const double* origi
   or_grid g;
   if (!fill_grid(&g, order, prec32, n, origin, h) || !M || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
-  const int R = order, NO = 2 * R + 1;
+  const int R = order;
   const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];
   const int ncomp = B ? 9 : 1;
-  const size_t nel = (size_t)nnodes * NO * NO * NO * ncomp;
+  const size_t nel = (size_t)nnodes * noff_of(&g) * ncomp;
   if (!accumulate) memset(M, 0, nel * sizeof(double));
   if (np == 0) return OR_OK;
 
@@ -348,7 +367,7 @@ int oracle_bilinear(int order, int prec32, const int32_t* n, const double* origi
   or_grid g;
   if (!fill_grid(&g, order, prec32, n, origin, h) || !u || !v || !out || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
-  const int R = order, NS = R + 1, nsup = NS * NS * NS;
+  const int NS = order + 1, nsup = nsup_of(&g);
   const int nv = B ? 3 : 1;
   double total = 0.0;
 #pragma omp parallel for reduction(+ : total) schedule(static)
@@ -393,7 +412,7 @@ int oracle_rows(int order, int prec32, const int32_t* n, const double* origin, c
   if (!fill_grid(&g, order, prec32, n, origin, h) || !rows || np < 0 || nsel < 0) return OR_ERR_ARG;
   if (nsel > 0 && !sel) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
-  const int R = order, NS = R + 1, NO = 2 * R + 1, nsup = NS * NS * NS, noff = NO * NO * NO;
+  const int R = order, NS = R + 1, NO = 2 * R + 1, nsup = nsup_of(&g), noff = noff_of(&g), RZ = is2d(&g) ? 0 : R;
   const int ncomp = B ? 9 : 1;
   const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];
   memset(rows, 0, (size_t)nsel * noff * ncomp * sizeof(double));
@@ -442,7 +461,7 @@ int oracle_rows(int order, int prec32, const int32_t* n, const double* origin, c
         int ax = a % NS, ay = (a / NS) % NS, az = a / (NS * NS);
         for (int b = 0; b < nsup; ++b) {
           int bx = b % NS, by = (b / NS) % NS, bz = b / (NS * NS);
-          int o = (bx - ax + R) + NO * ((by - ay + R) + NO * (bz - az + R));
+          int o = (bx - ax + R) + NO * ((by - ay + R) + NO * (bz - az + RZ));
           double ww = W[a] * W[b];
           double* dst = rows + ((size_t)slot * noff + o) * ncomp;
           for (int c = 0; c < ncomp; ++c) dst[c] += t[c] * ww;
@@ -471,7 +490,7 @@ int oracle_interp_field(int order, int prec32, const int32_t* n, const double* o
   or_grid g;
   if (!fill_grid(&g, order, prec32, n, origin, h) || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !F || !out)) return OR_ERR_ARG;
-  const int NS = order + 1, nsup = NS * NS * NS;
+  const int NS = order + 1, nsup = nsup_of(&g);
 #pragma omp parallel for schedule(static)
   for (int64_t p = 0; p < np; ++p) {
     or_support s;
@@ -503,7 +522,7 @@ int oracle_moments(int order, int prec32, const int32_t* n, const double* origin
   or_grid g;
   if (!fill_grid(&g, order, prec32, n, origin, h) || !m || np < 0 || nq < 1) return OR_ERR_ARG;
   if (np > 0 && (!pos || !Q)) return OR_ERR_ARG;
-  const int NS = order + 1, nsup = NS * NS * NS;
+  const int NS = order + 1, nsup = nsup_of(&g);
   const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];
   if (!accumulate) memset(m, 0, (size_t)nnodes * nq * sizeof(double));
   for (int64_t p = 0; p < np; ++p) {

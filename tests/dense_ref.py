@@ -26,6 +26,9 @@ def dense_W(order, n, origin, h, pos):
     pos = np.asarray(pos, dtype=np.float64).reshape(-1, 3)
     Wd = []
     for d in range(3):
+        if d == 2 and n[2] == 1:  # 2D: one node plane, weight 1
+            Wd.append(np.ones((pos.shape[0], 1)))
+            continue
         u = (pos[:, d] - origin[d]) / h[d]
         nodes = np.arange(n[d], dtype=np.float64)
         t = u[:, None] - nodes[None, :]
@@ -58,13 +61,14 @@ def dense_to_stencil(order, n, Md):
     nx, ny, nz = n
     ncomp = Md.shape[0]
     nn = nx * ny * nz
-    out = np.zeros((nn, NO ** 3, ncomp))
+    RZ = 0 if nz == 1 else R  # 2D grids: no z offsets
+    out = np.zeros((nn, NO * NO * (2 * RZ + 1), ncomp))
     g = np.arange(nn)
     gx, gy, gz = g % nx, (g // nx) % ny, g // (nx * ny)
-    for oz in range(-R, R + 1):
+    for oz in range(-RZ, RZ + 1):
         for oy in range(-R, R + 1):
             for ox in range(-R, R + 1):
-                o = (ox + R) + NO * ((oy + R) + NO * (oz + R))
+                o = (ox + R) + NO * ((oy + R) + NO * (oz + RZ))
                 g2 = ((gx + ox) % nx) + nx * (((gy + oy) % ny) + ny * ((gz + oz) % nz))
                 out[:, o, :] = Md[:, g, g2].T
     return out
@@ -83,7 +87,7 @@ def stencil_bilinear(order, n, M, u, v):
     for oz in range(-R, R + 1):
         for oy in range(-R, R + 1):
             for ox in range(-R, R + 1):
-                o = (ox + R) + NO * ((oy + R) + NO * (oz + R))
+                o = (ox + R) + NO * ((oy + R) + NO * (oz + RZ))
                 g2 = ((gx + ox) % nx) + nx * (((gy + oy) % ny) + ny * ((gz + oz) % nz))
                 if ncomp == 1:
                     total += float(np.sum(u * M[:, o, 0] * v[g2]))

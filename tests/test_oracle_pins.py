@@ -466,3 +466,42 @@ def test_moments_charge_conservation_and_node(order):
         q = np.array([[1.5, -2.0, 0.25, 3.0]])
         m1 = oracle.moments(1, (4, 5, 6), (0, 0, 0), (1, 1, 1), np.array([[2.0, 3.0, 1.0]]), q)
         assert np.array_equal(m1[2 + 4 * (3 + 5 * 1)], q[0]) and np.count_nonzero(m1) == 4
+
+
+# ---------------------------------------------------------------- 2D (n[2] == 1)
+@pytest.mark.parametrize("order,n", [(1, (3, 4, 1)), (1, (5, 4, 1)), (2, (5, 6, 1)), (2, (7, 5, 1))])
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+def test_dense_bruteforce_2d(order, n, kind):
+    """The 2D problem (z ignored, (R+1)^2 support, (2R+1)^2 offsets) against
+    the dense brute force with one node plane; the 2D stencil has 9 or 25
+    offsets and is symmetric, M[g][o] = M[g+o][-o]."""
+    case = random_case(181 + order + n[0], order, n, 60, kind=kind, beta=0.6, sigma=1.2,
+                       origin=(-0.25, 0.5, 1.0), h=(0.5, 1.25, 2.0))
+    sp = case.species[0]
+    pos = sp.pos.copy()
+    pos[::2, 2] += 17.3  # z is ignored
+    M = oracle.assemble(order, n, case.grid.origin, case.grid.h, pos, sp.w, sp.B if kind == "ecsim" else None,
+                        sp.beta, case.sigma)
+    assert M.shape[1] == (2 * order + 1) ** 2
+    Md = dense_ref.dense_M(order, n, case.grid.origin, case.grid.h, pos, sp.w, sp.B if kind == "ecsim" else None,
+                           sp.beta, case.sigma)
+    assert rel(M, dense_ref.dense_to_stencil(order, n, Md)) < 1e-14
+    NO = 2 * order + 1
+    g = np.arange(case.grid.ncells)
+    gx, gy = g % n[0], g // n[0]
+    for o in range(NO * NO):
+        ox, oy = o % NO - order, o // NO - order
+        g2 = (gx + ox) % n[0] + n[0] * ((gy + oy) % n[1])
+        assert np.array_equal(M[g, o], M[g2, (NO * NO - 1) - o])
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_binning_2d_keys(order):
+    """2D keys ignore z: a particle's bin is its first support node in the plane."""
+    case = random_case(191 + order, order, (6, 7, 1), 500, kind="scalar")
+    pos = case.species[0].pos.copy()
+    pos[:, 2] = np.random.default_rng(1).normal(size=500) * 100
+    bs, perm = oracle.bin_particles(order, case.grid.n, case.grid.origin, case.grid.h, pos)
+    assert bs[-1] == 500 and len(bs) == 43
+    bs0, perm0 = oracle.bin_particles(order, case.grid.n, case.grid.origin, case.grid.h, case.species[0].pos)
+    assert np.array_equal(bs, bs0) and np.array_equal(perm, perm0)
