@@ -46,6 +46,8 @@ KERNEL_FILES = {
     "k_tsc64": ("k_tsc64.hip",) + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
+    "k_mass2d": ("k_mass2d.hip",) + HEADERS,
+    "k_gather2d": ("k_mass2d.hip",) + HEADERS,
     "k_atomic_scatter": ("k_scatter.hip",) + HEADERS,
 }
 
@@ -55,6 +57,8 @@ KERNEL_LABELS = {
     "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
     "k_contract": "k_contract (per-bin MFMA contraction)",
     "k_gather": "k_gather (stencil deposition of the per-bin records)",
+    "k_mass2d": "k_mass2d (2D per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+    "k_gather2d": "k_gather2d (2D stencil deposition of the per-bin records)",
     "k_atomic_scatter": "k_atomic_scatter (per-particle atomic scatter, comparison only)",
 }
 
@@ -75,39 +79,42 @@ def contract_kernel(order: int, dtype: str, tensorial: bool) -> str:
     return "k_contract"
 
 
-def flops_per_particle(order: int, tensorial: bool) -> int:
-    n = (order + 1) ** 3
+def flops_per_particle(order: int, tensorial: bool, dims: int = 3) -> int:
+    n = (order + 1) ** dims
     return 2 * n * n * (9 if tensorial else 1)
 
 
 def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int, field_on_grid: bool = False,
-                   pelem: int = 0) -> int:
+                   pelem: int = 0, dims: int = 3, rec_elem: int = 0) -> int:
     """Algorithmic HBM bytes of one contraction launch: each particle's
     position, weight (and field) and permutation entry read once, bin bounds
     read once, one packed upper-triangle record written per bin; a field on
     the grid nodes is read once instead of the per-particle field. pelem: bytes
     of a stored position or field value when it differs from elem (the mixed
-    layout's fp32 positions)."""
+    layout's fp32 positions); rec_elem: bytes of a record value (fp64 records
+    of the 2D problem)."""
     pelem = pelem or elem
-    n = (order + 1) ** 3
+    rec_elem = rec_elem or elem
+    n = (order + 1) ** dims
     per_particle = (3 + (3 if tensorial and not field_on_grid else 0)) * pelem + elem + 4
-    record = n * (n + 1) // 2 * (9 if tensorial else 1) * elem
+    record = n * (n + 1) // 2 * (9 if tensorial else 1) * rec_elem
     field = nbins * 3 * pelem if tensorial and field_on_grid else 0
     return np_ * per_particle + (nbins + 1) * 4 + nbins * record + field
 
 
 def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool,
-                  canonical: bool = False) -> int:
+                  canonical: bool = False, dims: int = 3, rec_elem: int = 0) -> int:
     """Algorithmic HBM bytes of one deposition launch: every record read once,
     every stencil entry written once (read too when accumulating); the
     canonical half stores (noff + 1) / 2 offsets."""
-    n = (order + 1) ** 3
-    noff = (2 * order + 1) ** 3
+    rec_elem = rec_elem or elem
+    n = (order + 1) ** dims
+    noff = (2 * order + 1) ** dims
     if canonical:
         noff = (noff + 1) // 2
     nc = 9 if tensorial else 1
     out = nbins * noff * nc * elem
-    return nbins * n * (n + 1) // 2 * nc * elem + out * (2 if accumulate else 1)
+    return nbins * n * (n + 1) // 2 * nc * rec_elem + out * (2 if accumulate else 1)
 
 
 def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
@@ -123,7 +130,7 @@ def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
 def workload_key(args) -> str:
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
-            + ("-canonical" if args.canonical else ""))
+            + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -202,6 +209,9 @@ def main():
     ap.add_argument("--moments", type=int, default=0,
                     help="also time the deposition of this many quantities per particle (e.g. 4: charge and "
                          "current) on the first species")
+    ap.add_argument("--dims", type=int, default=3, choices=(2, 3),
+                    help="2: the config's order and kind on an n x n grid with one node plane, 64 per cell")
+    ap.add_argument("--n2d", type=int, default=256, help="grid edge of the 2D workload")
     ap.add_argument("--field", default="particle", choices=("particle", "grid"),
                     help="ECSIM magnetic field per particle (default) or on the grid nodes, gathered at each "
                          "particle with its support weights")
@@ -220,13 +230,18 @@ def main():
     import numpy as np
     import torch
     import particle_grid_mass_amd as mm
-    from workloads import grid_field, make_config
+    from workloads import grid_field, make_2d, make_config
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     mix = args.dtype == "mix"
-    case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled)
+    if args.dims == 2:  # the config's order and kind on a 2D grid (one node plane)
+        order2, kind2 = {1: (1, "scalar"), 2: (1, "ecsim"), 3: (1, "ecsim"), 4: (2, args.kind or "scalar"),
+                         5: (2, "ecsim")}[args.config]
+        case = make_2d(args.n2d, 64, order2, kind2, dtype="f64" if mix else args.dtype, seed=2000 + args.config)
+    else:
+        case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled)
     if mix:  # the stored fp32 positions and fields, seen by the oracle as the same values in fp64
         for sp in case.species:
             sp.pos = sp.pos.astype(np.float32).astype(np.float64)
@@ -265,7 +280,7 @@ def main():
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
     ncomp = 9 if tensorial else 1
-    nof = mm.noff_canonical(order) if args.canonical else mm.noff(order)
+    nof = mm.noff_canonical(order) if args.canonical else mm.noff_grid(order, case.grid)
     M = torch.empty(nbins * nof * ncomp, dtype=tdt, device=dev)
     Fd = to_devp(Fgrid) if on_grid else None
     rec = None
@@ -382,19 +397,23 @@ def main():
 
     np_launch = np_total / len(spec)
     t_dom = dom_ms / launches * 1e-3
-    flops = flops_per_particle(order, tensorial) * np_launch
-    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem)
+    flops = flops_per_particle(order, tensorial, args.dims) * np_launch
+    cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem, args.dims,
+                            8 if args.dims == 2 else 0)
     # average over the species' launches: the first overwrites M, the others
     # accumulate into it (read and write)
-    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical)
+    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
+                               dims=args.dims, rec_elem=8 if args.dims == 2 else 0)
                  for si in range(len(spec))) / len(spec)
     if dom == "deposit":
-        kname = "k_gather"
+        kname = "k_gather2d" if args.dims == 2 else "k_gather"
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
                 "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
         roof["algorithmic_bytes_per_launch"] = dbytes
     else:
         kname = contract_kernel(order, case.dtype, tensorial) if dom == "contract" else "k_atomic_scatter"
+        if args.dims == 2 and dom == "contract":
+            kname = "k_mass2d"
         if args.algo == "mfma_atomic":
             kname = "k_contract"
         peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA

@@ -26,6 +26,14 @@
  *           [-R,R]^3 (27 offsets for CIC, 125 for TSC). comp = 3*i + j
  *           (tensorial, 9 per entry, row i of alpha) or a single scalar.
  *           The full stencil is stored (both g->g' and g'->g).
+ *  2D:      a grid with n[2] == 1 is the 2D problem (Sec. 5 reports 2D runs):
+ *           z is ignored, the support is the (R+1)^2 nodes of the plane and
+ *           the stencil has (2R+1)^2 offsets, offset = (dx+R) + (2R+1)(dy+R).
+ *           It runs on the matrix-core path (MM_ALGO_MFMA) in MM_F64 or
+ *           MM_MIX, through mm_bin_particles, mm_assemble_scalar,
+ *           mm_assemble_ecsim, mm_contract_bins and mm_deposit_records (the
+ *           records are fp64); every other combination is
+ *           MM_ERR_UNSUPPORTED.
  *  dtype:   MM_F64: pos, w, B and M are double. MM_F32: all four are float,
  *           the cell decision, weights and matrix-core accumulation run in
  *           fp32 (sigma and beta are rounded to fp32). MM_MIX: the

@@ -78,6 +78,13 @@ def _workspace(fn, what, args_before_ws, device, stream):
     return ws, nbytes
 
 
+def noff_grid(order: int, grid) -> int:
+    """Stencil offsets per node on this grid: (2R+1)^3, or (2R+1)^2 on a 2D grid (n[2] == 1)."""
+    g = _grid_of(grid)
+    NO = 2 * order + 1
+    return NO * NO * (1 if g.n[2] == 1 else NO)
+
+
 def noff(order: int) -> int:
     return (2 * order + 1) ** 3
 
@@ -135,14 +142,15 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
         _check_tensor(bin_start, "bin_start", torch.int32)
         _check_tensor(perm, "perm", torch.int32)
     ncomp = 9 if kind == "ecsim" else 1
-    shape = (_nnodes(g), noff(order), ncomp) if ncomp == 9 else (_nnodes(g), noff(order))
+    nof = noff_grid(order, g)
+    shape = (_nnodes(g), nof, ncomp) if ncomp == 9 else (_nnodes(g), nof)
     dev = pos.device
     if M is None:
         M = torch.empty(shape, dtype=dt, device=dev)
         accumulate = False
     _check_tensor(M, "M", dt)
-    if M.numel() != _nnodes(g) * noff(order) * ncomp:
-        raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * noff(order) * ncomp}")
+    if M.numel() != _nnodes(g) * nof * ncomp:
+        raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * nof * ncomp}")
     s = _stream(dev)
     a = _lib.ALGOS[algo]
     if kind == "ecsim" and Bgrid is not None:
@@ -240,7 +248,7 @@ def deposit_records(grid, order: int, rec: torch.Tensor, M: torch.Tensor, tensor
     if M.dtype not in _DT:
         raise TypeError(f"unsupported dtype {M.dtype}")
     ncomp = 9 if tensorial else 1
-    nof = noff_canonical(order) if canonical else noff(order)
+    nof = noff_canonical(order) if canonical else noff_grid(order, g)
     if M.numel() != _nnodes(g) * nof * ncomp:
         raise ValueError("M has the wrong number of elements")
     fn, name = ((lib.mm_deposit_records_canonical, "mm_deposit_records_canonical") if canonical

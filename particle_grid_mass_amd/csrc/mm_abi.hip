@@ -18,7 +18,7 @@ mm_status check_grid(const mm_grid* g, int order, int64_t* nnodes) {
   if (order != 1 && order != 2) return MM_ERR_ARG;
   int64_t nn = 1;
   for (int d = 0; d < 3; ++d) {
-    if (g->n[d] < 2 * order + 1) return MM_ERR_ARG;
+    if (g->n[d] < 2 * order + 1 && !(d == 2 && g->n[2] == 1)) return MM_ERR_ARG;  // n[2] == 1: the 2D problem
     if (!(g->h[d] > 0.0) || !is_finite_d(g->h[d]) || !is_finite_d(g->origin[d])) return MM_ERR_ARG;
     nn *= g->n[d];
   }
@@ -56,6 +56,8 @@ mm_status hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP
 
 bool dtype_ok(mm_dtype dt) { return dt == MM_F64 || dt == MM_F32 || dt == MM_MIX; }
 
+bool is2d(const mm_grid* g) { return g->n[2] == 1; }
+
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Shared argument checks of the assembly entry points. The tensorial field is
@@ -71,6 +73,8 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC) return MM_ERR_ARG;
   if (algo == MM_ALGO_ATOMIC && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
+  // 2D: the matrix-core path in fp64 (or the mixed layout), field per particle
+  if (is2d(grid) && (algo != MM_ALGO_MFMA || dt == MM_F32 || Bgrid)) return MM_ERR_UNSUPPORTED;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -86,7 +90,9 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   // deposits need no workspace. A grid field that the chosen kernel does not
   // gather itself is first interpolated to the particles, after the records.
   const bool records = algo == MM_ALGO_MFMA && np > 0;
-  const size_t rec_need = records ? align256(record_bytes(order, f32, tensorial, nnodes)) : 0;
+  const size_t rec_need =
+      records ? align256(is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, nnodes))
+              : 0;
   const bool interp = Bgrid && np > 0 &&
                       !(records && contract_gathers_field(order, f32, MODE_RECORD));
   // fp32 positions with an fp64 interpolated field: not a combination the kernels take
@@ -99,7 +105,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (*ws_bytes < need) return MM_ERR_WORKSPACE;
   if (need > 0 && ((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
 
-  const int noff = order == 1 ? 27 : 125;
+  const int noff = is2d(grid) ? (order == 1 ? 9 : 25) : (order == 1 ? 27 : 125);
   const size_t count = (size_t)nnodes * noff * (tensorial ? 9 : 1);
   hipStream_t s = (hipStream_t)stream;
   GridDev g = to_dev(grid);
@@ -115,6 +121,11 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     } else {
       P.Bgrid = Bgrid;
     }
+  }
+  if (records && is2d(grid)) {
+    e = launch_contract_2d(g, order, P, bin_start, perm, beta, sigma, ws, s);
+    if (e == hipSuccess) e = launch_gather_2d(g, order, tensorial, ws, accumulate, M, s);
+    return hip_status(e);
   }
   if (records) {
     e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
@@ -146,7 +157,8 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (Bgrid && np > 0 && !pos) return MM_ERR_NULL;
   const bool f32 = dt == MM_F32;
   const bool tensorial = B != nullptr || Bgrid != nullptr;
-  const size_t rec_need = record_bytes(order, f32, tensorial, nnodes);
+  if (is2d(grid) && (f32 || Bgrid)) return MM_ERR_UNSUPPORTED;
+  const size_t rec_need = is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, nnodes);
   const bool interp = Bgrid && np > 0 && !contract_gathers_field(order, f32, MODE_RECORD);
   const size_t need = interp ? align256(rec_need) + (size_t)np * 3 * (f32 ? 4 : 8) : rec_need;
   if (!rec) {
@@ -169,6 +181,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
       P.Bgrid = Bgrid;
     }
   }
+  if (is2d(grid)) return hip_status(launch_contract_2d(g, order, P, bin_start, perm, beta, sigma, rec, s));
   return hip_status(launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, s));
 }
 
@@ -243,6 +256,10 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!rec || !M) return MM_ERR_NULL;
+  if (is2d(grid)) {
+    if (dt == MM_F32) return MM_ERR_UNSUPPORTED;
+    return hip_status(launch_gather_2d(to_dev(grid), order, tensorial != 0, rec, accumulate, M, (hipStream_t)stream));
+  }
   return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, M,
                                   (hipStream_t)stream));
 }
@@ -254,6 +271,7 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!rec || !Mc) return MM_ERR_NULL;
+  if (is2d(grid)) return MM_ERR_UNSUPPORTED;
   return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, Mc,
                                   (hipStream_t)stream, true));
 }
@@ -267,6 +285,7 @@ mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (nq < 1 || nq > 16) return MM_ERR_ARG;
+  if (is2d(grid)) return MM_ERR_UNSUPPORTED;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
   if (!m) return MM_ERR_NULL;
@@ -295,6 +314,7 @@ mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int ten
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!M || !x || !y) return MM_ERR_NULL;
+  if (is2d(grid)) return MM_ERR_UNSUPPORTED;
   if (x == y) return MM_ERR_ARG;
   return hip_status(launch_stencil_matvec(to_dev(grid), order, dt == MM_F32, tensorial != 0, canonical != 0, M, x, y,
                                           (hipStream_t)stream));

@@ -36,6 +36,15 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
                          void* M, hipStream_t s, bool canonical = false);
 
+// The 2D problem (n2 == 1): per-bin fp64 records rec[bin][pair][comp] of the
+// (R+1)^2 support, and their fixed-order sum into M [nnodes][(2R+1)^2][comp]
+// (fp64 output).
+size_t record_bytes_2d(int order, bool tensorial, int64_t nbins);
+hipError_t launch_contract_2d(const GridDev& g, int order, const Particles& P, const int32_t* bin_start,
+                              const int32_t* perm, double beta, double sigma, void* rec, hipStream_t s);
+hipError_t launch_gather_2d(const GridDev& g, int order, bool tensorial, const void* rec, int accumulate, void* M,
+                            hipStream_t s);
+
 // Moment deposition m[g][k] = sum_p W_pg Q_p[k], k < nq <= 16, through
 // per-bin fp64 records rec (moment_record_bytes) and a fixed-order gather.
 size_t moment_record_bytes(int order, int nq, int64_t nbins);

@@ -77,12 +77,13 @@ __device__ __forceinline__ int axis_support(T u, int n, T* wt) {
 }
 
 // First support node of a particle as a linear node index (the bin key).
+// On a 2D grid (n2 == 1) z is ignored and the key is the node in the plane.
 template <typename T, int R>
 __device__ __forceinline__ int particle_key(const T* p3, const GridDev& g) {
   T wt[3];
   int fx = axis_support<T, R>(grid_coord<T, 0>(p3[0], g), g.n0, wt);
   int fy = axis_support<T, R>(grid_coord<T, 1>(p3[1], g), g.n1, wt);
-  int fz = axis_support<T, R>(grid_coord<T, 2>(p3[2], g), g.n2, wt);
+  int fz = g.n2 == 1 ? 0 : axis_support<T, R>(grid_coord<T, 2>(p3[2], g), g.n2, wt);
   return fx + g.n0 * (fy + g.n1 * fz);
 }
 

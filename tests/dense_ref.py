@@ -83,8 +83,9 @@ def stencil_bilinear(order, n, M, u, v):
     g = np.arange(nn)
     gx, gy, gz = g % nx, (g // nx) % ny, g // (nx * ny)
     ncomp = M.shape[2]
+    RZ = 0 if nz == 1 else R  # 2D grids: no z offsets
     total = 0.0
-    for oz in range(-R, R + 1):
+    for oz in range(-RZ, RZ + 1):
         for oy in range(-R, R + 1):
             for ox in range(-R, R + 1):
                 o = (ox + R) + NO * ((oy + R) + NO * (oz + RZ))

@@ -13,7 +13,7 @@ particles stored cell by cell. The named configurations extend it to two
 species, shuffled order and a clustered density.
 """
 from .gen import (Grid, Species, Case, CONFIGS, make_config, uniform_species, random_case,
-                  clustered_counts, species_from_counts, grid_field)
+                  clustered_counts, species_from_counts, grid_field, make_2d)
 
 __all__ = ["Grid", "Species", "Case", "CONFIGS", "make_config", "uniform_species", "random_case",
-           "clustered_counts", "species_from_counts", "grid_field"]
+           "clustered_counts", "species_from_counts", "grid_field", "make_2d"]

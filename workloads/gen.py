@@ -221,3 +221,15 @@ def grid_field(grid: Grid, seed: int, dtype: str = "f64") -> np.ndarray:
     nodes), node index x + nx*(y + ny*z). Drawn from its own seeded stream."""
     (rng,) = _streams(7000 + seed, 1)
     return _round(rng.standard_normal((grid.ncells, 3)), dtype)
+
+
+def make_2d(n: int = 256, ppc: int = 64, order: int = 1, kind: str = "ecsim", dtype: str = "f64",
+            seed: int = 2002) -> Case:
+    """The 2D problem (one node plane): an n x n periodic grid with ``ppc``
+    particles per cell, cell-major, z of every particle inside the single
+    plane (ignored by the assembly); beta = 0.5, sigma = 1."""
+    g = Grid((n, n, 1))
+    sp = uniform_species(g, ppc, seed, with_B=kind == "ecsim", beta=0.5, name="electrons")
+    name = f"2d_{'cic' if order == 1 else 'tsc'}_{kind}_{n}sq_{ppc}ppc"
+    return Case(name, g, order, kind, [_cast(sp, dtype)], dtype=dtype, seed=seed,
+                note=f"2D {('CIC' if order == 1 else 'TSC')} {kind}, {n}x{n} cells, {ppc} ppc")
