@@ -353,14 +353,18 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
 // thread i (0 <= i <= np) writes i for every k in (skeys[i-1], skeys[i]]
 // (with skeys[-1] = -1 and skeys[np] = nbins), so each entry is written once.
 // Input already in key order: k_keys_hist has written bin_start and perm.
+// Grid-stride over i = 0..np with a capped grid, so that the launch is cheap
+// when the input was already in key order.
 __global__ void k_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start,
                          const int32_t* __restrict__ unsorted) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i > np || *unsorted == 0) return;
-  const int lo = i == 0 ? -1 : (int)skeys[i - 1];
-  int hi = i == np ? nbins : (int)skeys[i];
-  hi = hi > nbins ? nbins : hi;
-  for (int k = lo + 1; k <= hi; ++k) bin_start[k] = i;
+  if (*unsorted == 0) return;
+  const int stride = gridDim.x * blockDim.x;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= np; i += stride) {
+    const int lo = i == 0 ? -1 : (int)skeys[i - 1];
+    int hi = i == np ? nbins : (int)skeys[i];
+    hi = hi > nbins ? nbins : hi;
+    for (int k = lo + 1; k <= hi; ++k) bin_start[k] = i;
+  }
 }
 
 __global__ void k_fill_i32(int32_t* p, int n, int v) {
@@ -461,7 +465,9 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
     kin = kout;
     kout = t;
   }
-  hipLaunchKernelGGL(k_bounds, dim3((np + 1 + 255) / 256), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
+  const size_t nbb = ((size_t)np + 256) / 256;  // blocks for np + 1 threads
+  const int bblocks = nbb < 2048 ? (int)nbb : 2048;
+  hipLaunchKernelGGL(k_bounds, dim3(bblocks), dim3(256), 0, s, (const uint32_t*)kin, np, nbins,
                      bin_start, (const int32_t*)w.unsorted);
   return hipGetLastError();
 }
