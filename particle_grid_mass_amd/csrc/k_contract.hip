@@ -466,8 +466,10 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
   constexpr int ROWT = NOUT * TPE;                 // threads per node
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the row
-  const int t = (blk - rv * blocks_per_row) * 256 + threadIdx.x;
-  if (t >= g.n0 * ROWT) return;
+  const int t0 = (blk - rv * blocks_per_row) * 256;
+  const int t = t0 + threadIdx.x;
+  const bool active = t < g.n0 * ROWT;
+  if (R != 1 && !active) return;  // (order 1 keeps every thread for the block's barrier)
   constexpr int ZB = 4;
   const int nfull = g.n2 / ZB;           // complete z-blocks
   const int inb = g.n1 * ZB;             // rows per complete z-block
@@ -503,6 +505,7 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
   T sum[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) sum[j] = T(0);
+  if (active) {
 #pragma unroll
   for (int az = 0; az < NS; ++az) {
     if (az + oz < 0 || az + oz > R) continue;
@@ -524,9 +527,38 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
       }
     }
   }
-  T* dst = M + ((size_t)row * g.n0 + gx) * (NOUT * NC) + (o - O0) * NC + c0;
+  }
+  if (R == 1) {
+    // The block's outputs are contiguous (thread t holds values CPT t ..
+    // CPT t + CPT - 1 of its row): stage them in LDS and store 16 bytes per
+    // lane. 10% faster at 64^3 cells; at order 2 the plain stores were faster.
+    __shared__ __attribute__((aligned(16))) T so[256 * CPT];
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) dst[j] = accumulate ? dst[j] + sum[j] : sum[j];
+    for (int j = 0; j < CPT; ++j) so[threadIdx.x * CPT + j] = sum[j];
+    __syncthreads();
+    const int nval = (g.n0 * ROWT - t0 < 256 ? g.n0 * ROWT - t0 : 256) * CPT;
+    T* base = M + (size_t)row * g.n0 * (NOUT * NC) + (size_t)t0 * CPT;
+    if (sizeof(T) == 8 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
+      const int npair = nval / 2;
+      for (int i = threadIdx.x; i < npair; i += 256) {
+        double2 v = reinterpret_cast<const double2*>(so)[i];
+        double2* d = reinterpret_cast<double2*>(base) + i;
+        if (accumulate) {
+          const double2 old = *d;
+          v.x += old.x;
+          v.y += old.y;
+        }
+        *d = v;
+      }
+      if ((nval & 1) && threadIdx.x == 0) base[nval - 1] = accumulate ? base[nval - 1] + so[nval - 1] : so[nval - 1];
+    } else {
+      for (int i = threadIdx.x; i < nval; i += 256) base[i] = accumulate ? base[i] + so[i] : so[i];
+    }
+  } else {
+    T* dst = M + ((size_t)row * g.n0 + gx) * (NOUT * NC) + (o - O0) * NC + c0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) dst[j] = accumulate ? dst[j] + sum[j] : sum[j];
+  }
 }
 
 template <typename T, int R, int NC, bool CANON>
