@@ -243,6 +243,22 @@ mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_
 mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical, const void* M,
                             const void* x, void* y, mm_stream_t stream);
 
+/*
+ * mm_probe_mfma_f64 - measurement aid, not part of the assembly: the on-box
+ * throughput of v_mfma_f64_4x4x4_4b, the instruction of the fp64
+ * contractions (the measured peak reported beside MI355X's published
+ * 78.6 TFLOP/s fp64 matrix peak).
+ *  nblocks  workgroups of 256 threads (1 .. 2^20); 4 per CU or more fill the chip
+ *  iters    iterations (>= 1); every wave issues 16 * iters independent
+ *           instructions of 512 flop each, so the work is
+ *           nblocks * 4 * 16 * iters * 512 flop
+ *  out      device buffer of nblocks * 256 doubles, owned by the caller;
+ *           receives per-thread sums (so the work is not optimised away)
+ * Enqueued on `stream`; time it with events. NULL out -> MM_ERR_NULL, counts
+ * out of range -> MM_ERR_ARG.
+ */
+mm_status mm_probe_mfma_f64(int nblocks, int iters, double* out, mm_stream_t stream);
+
 /* Static description of a status code. */
 const char* mm_status_string(mm_status s);
 

@@ -5,7 +5,8 @@ ABI of ``include/mm.h``); this package is its thin torch binding.
 """
 from .api import (MMError, assemble_ecsim, assemble_ecsim_gridB, assemble_scalar, bin_particles,  # noqa: F401
                   contract_bins, deposit_moments, deposit_records, noff, noff_canonical, noff_grid,
-                  stencil_matvec)
+                  probe_mfma_f64, stencil_matvec)
 
 __all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "assemble_ecsim_gridB", "contract_bins",
-           "deposit_records", "deposit_moments", "stencil_matvec", "noff", "noff_canonical", "noff_grid", "MMError"]
+           "deposit_records", "deposit_moments", "stencil_matvec", "probe_mfma_f64", "noff", "noff_canonical",
+           "noff_grid", "MMError"]

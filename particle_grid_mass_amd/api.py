@@ -317,3 +317,20 @@ def deposit_moments(grid, order: int, pos: torch.Tensor, Q: torch.Tensor, bin_st
     ws, nbytes = _workspace(lib.mm_deposit_moments, "mm_deposit_moments", head, pos.device, s)
     _call(lib.mm_deposit_moments, "mm_deposit_moments", *head, _ptr(ws), ctypes.byref(nbytes), s)
     return m
+
+
+def probe_mfma_f64(nblocks: int, iters: int, out: Optional[torch.Tensor] = None,
+                   device: Optional[torch.device] = None) -> torch.Tensor:
+    """Measurement aid: enqueue the fp64 matrix-instruction throughput probe
+    (``nblocks`` x 256 threads, ``16 * iters`` v_mfma_f64_4x4x4_4b per wave,
+    512 flop each) and return its per-thread output buffer. Time it with
+    events on the current stream."""
+    lib = _lib.load()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(int(nblocks) * 256, dtype=torch.float64, device=dev)
+    _check_tensor(out, "out", torch.float64)
+    if out.numel() < int(nblocks) * 256:
+        raise ValueError("out holds fewer than nblocks * 256 doubles")
+    _call(lib.mm_probe_mfma_f64, "mm_probe_mfma_f64", int(nblocks), int(iters), _ptr(out), _stream(out.device))
+    return out

@@ -320,6 +320,12 @@ mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int ten
                                           (hipStream_t)stream));
 }
 
+mm_status mm_probe_mfma_f64(int nblocks, int iters, double* out, mm_stream_t stream) {
+  if (!out) return MM_ERR_NULL;
+  if (nblocks <= 0 || nblocks > (1 << 20) || iters <= 0) return MM_ERR_ARG;
+  return hip_status(launch_probe_mfma_f64(nblocks, iters, out, (hipStream_t)stream));
+}
+
 const char* mm_status_string(mm_status s) {
   switch (s) {
     case MM_OK: return "ok";

@@ -28,6 +28,10 @@ hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin
 // interpolated to the particles (launch_interp_field) and passed as B.
 bool contract_gathers_field(int order, bool f32, int mode);
 
+// Throughput probe of v_mfma_f64_4x4x4_4b (k_probe.hip): nblocks x 256 threads,
+// 16 * iters instructions per wave; out holds nblocks * 256 doubles.
+hipError_t launch_probe_mfma_f64(int nblocks, int iters, double* out, hipStream_t s);
+
 // Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 

@@ -163,3 +163,12 @@ def test_stencil_matvec_and_canonical_validation():
     assert dep(G8, rec=None) == _lib.MM_ERR_NULL
     assert dep(G8, M=None) == _lib.MM_ERR_NULL
     assert dep(_lib.make_grid((4, 8, 8))) == _lib.MM_ERR_ARG  # n < 2R+1 for TSC
+
+
+def test_probe_validation():
+    """The throughput probe rejects a NULL buffer and counts out of range on the host."""
+    lib = _lib.load()
+    assert lib.mm_probe_mfma_f64(4, 10, None, None) == _lib.MM_ERR_NULL
+    assert lib.mm_probe_mfma_f64(0, 10, FAKE, None) == _lib.MM_ERR_ARG
+    assert lib.mm_probe_mfma_f64(4, 0, FAKE, None) == _lib.MM_ERR_ARG
+    assert lib.mm_probe_mfma_f64((1 << 20) + 1, 10, FAKE, None) == _lib.MM_ERR_ARG
