@@ -12,8 +12,8 @@ a 3D periodic box, one species, a fixed number of particles per cell and
 particles stored cell by cell. The named configurations extend it to two
 species, shuffled order and a clustered density.
 """
-from .gen import (Grid, Species, Case, CONFIGS, make_config, uniform_species, random_case,
+from .gen import (Grid, Species, Case, WORKLOAD_NOTES, make_config, uniform_species, random_case,
                   clustered_counts, species_from_counts, grid_field, make_2d)
 
-__all__ = ["Grid", "Species", "Case", "CONFIGS", "make_config", "uniform_species", "random_case",
+__all__ = ["Grid", "Species", "Case", "WORKLOAD_NOTES", "make_config", "uniform_species", "random_case",
            "clustered_counts", "species_from_counts", "grid_field", "make_2d"]

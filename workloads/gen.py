@@ -132,7 +132,7 @@ def clustered_counts(n: int, mean: float, seed: int, sigma_cells: float = 16.0, 
 
 
 # Named configurations (sizes, orders and constants of the five workloads).
-CONFIGS = {
+WORKLOAD_NOTES = {
     1: "CIC scalar fp64, 8^3 cells, 64 ppc uniform (32,768 particles)",
     2: "CIC ECSIM fp64, 32^3 cells, 64 ppc uniform (2,097,152 particles), beta=0.5",
     3: "CIC ECSIM fp64, 64^3 cells, 125 ppc, two species (electrons beta=-0.5, ions beta=+1/3672), "
@@ -153,12 +153,12 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
     if cid == 1:
         g = Grid((8, 8, 8) if scale is None else (scale,) * 3)
         sp = uniform_species(g, 64, seed, with_B=False, beta=0.0)
-        return Case("c1_cic_scalar", g, 1, "scalar", [sp], dtype="f64", seed=seed, note=CONFIGS[1])
+        return Case("c1_cic_scalar", g, 1, "scalar", [sp], dtype="f64", seed=seed, note=WORKLOAD_NOTES[1])
     if cid == 2:
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
         sp = uniform_species(g, 64, seed, with_B=True, beta=0.5)
         sp = Species(sp.pos, sp.w, sp.B, 0.5, "electrons")
-        return Case("c2_cic_ecsim", g, 1, "ecsim", [_cast(sp, dtype)], dtype=dtype, seed=seed, note=CONFIGS[2])
+        return Case("c2_cic_ecsim", g, 1, "ecsim", [_cast(sp, dtype)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[2])
     if cid == 3:
         g = Grid((64, 64, 64) if scale is None else (scale,) * 3)
         ppc = 125
@@ -173,12 +173,12 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
                 sel = sel[rperm.permutation(sel.shape[0])]
             species.append(_cast(Species(allp.pos[sel], allp.w[sel], allp.B[sel], beta, name), dtype))
         return Case("c3_cic_ecsim_2sp" + ("_shuffled" if shuffled else "_sorted"), g, 1, "ecsim", species,
-                    dtype=dtype, seed=seed, note=CONFIGS[3])
+                    dtype=dtype, seed=seed, note=WORKLOAD_NOTES[3])
     if cid == 4:
         kind = kind or "ecsim"
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
         sp = uniform_species(g, 64, seed, with_B=(kind == "ecsim"), beta=0.5)
-        return Case(f"c4_tsc_{kind}", g, 2, kind, [_cast(sp, dtype)], dtype=dtype, seed=seed, note=CONFIGS[4])
+        return Case(f"c4_tsc_{kind}", g, 2, kind, [_cast(sp, dtype)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[4])
     if cid == 5:
         n = 128 if scale is None else scale
         g = Grid((n, n, n))
@@ -186,7 +186,7 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
         rp, rw, rb = _streams(seed, 3)
         sp = species_from_counts(g, counts, rp, rw, rb, True, 0.5, "electrons")
         return Case(f"c5_tsc_ecsim_clustered_{dtype}", g, 2, "ecsim", [_cast(sp, dtype)], dtype=dtype, seed=seed,
-                    note=CONFIGS[5])
+                    note=WORKLOAD_NOTES[5])
     raise ValueError(f"unknown config {cid}")
 
 
