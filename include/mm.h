@@ -174,6 +174,11 @@ mm_status mm_assemble_ecsim_gridB(const mm_grid* grid, int order, mm_dtype dt, i
  * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp).
  *  rec       device buffer of *rec_bytes bytes (query with rec == NULL),
  *            16-byte aligned (else MM_ERR_ARG). The records start at rec.
+ *            For order 2 tensorial fp64 (and MM_MIX) the query also counts
+ *            room after the records where the contraction orders the bins
+ *            of each window of 256 by particle count (groups of bins with
+ *            similar counts waste fewer matrix instructions); the records
+ *            are the same.
  *  Other arguments as for mm_assemble_ecsim; bin_start/perm are required.
  *
  * mm_contract_bins_gridB - mm_contract_bins with the field on the grid

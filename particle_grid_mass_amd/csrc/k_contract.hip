@@ -439,7 +439,10 @@ bool contract_gathers_field(int order, bool f32, int mode) {
 
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
   const int npair = order == 1 ? Geo<1>::NPAIR : Geo<2>::NPAIR;
-  return (size_t)nbins * npair * (tensorial ? 9 : 1) * (f32 ? 4 : 8);
+  const size_t recb = (size_t)nbins * npair * (tensorial ? 9 : 1) * (f32 ? 4 : 8);
+  if (order == 2 && !f32 && tensorial)  // k_tsc64 keeps its bin order after the records
+    return (recb + 255) / 256 * 256 + tsc64_order_bytes(nbins);
+  return recb;
 }
 
 // ---------------------------------------------------------------- phase 2

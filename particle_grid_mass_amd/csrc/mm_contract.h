@@ -22,6 +22,8 @@ hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin
 // per (group of four bins, row of alpha).
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
+// Bytes k_tsc64 uses after its records (rounded up to 256) for the bin order.
+size_t tsc64_order_bytes(int64_t nbins);
 
 // Whether launch_contract gathers a grid field itself (Particles::Bgrid) for
 // this order, precision and mode; otherwise the field must first be
