@@ -28,9 +28,10 @@
 //
 // Output of a bin (MODE):
 //  MODE_RECORD - the upper triangle (a <= b) of the local matrix is written as
-//    one compact record rec[bin][pair(a,b)][comp]; a second kernel (k_gather)
-//    sums records into the stencil matrix (deterministic, every output entry
-//    written once, no atomics);
+//    one compact record rec[bin][pair(a,b)][comp], assembled in the wave's LDS
+//    region and stored with coalesced 8-byte stores; a second kernel
+//    (k_gather) sums records into the stencil matrix (deterministic, every
+//    output entry written once, no atomics);
 //  MODE_ATOMIC - every local entry is added into the stencil matrix with a
 //    hardware atomic ((a,b) and (b,a) for off-diagonal tiles).
 #include "mm_contract.h"
@@ -46,6 +47,12 @@ struct Geo {
   static constexpr int NOFF = NO * NO * NO;
 };
 
+// Row stride (elements) of the staged weights sW[a][lane]. The rounds read 16
+// rows at one column: a stride of 64 would put those 16 reads on one LDS bank;
+// 68 spreads them (fp32: 4 i + k covers all 64 banks for 16 rows x 4 columns),
+// and the staging stores (one column per lane) stay conflict-free.
+constexpr int SWS = 68;
+
 // Position of the pair (a, b), a <= b, in the packed upper triangle.
 template <int N>
 __device__ __forceinline__ int pair_index(int a, int b) {
@@ -60,12 +67,15 @@ __device__ __forceinline__ size_t support_node(int fx, int fy, int fz, int ax, i
   return (size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * (size_t)z);
 }
 
-// Bin output for local entry (a, b) of component c (value v).
+// Bin output for local entry (a, b) of component c (value v). Records are
+// assembled in the wave's LDS region `lds` ([pair][comp], the layout of one
+// bin's record) and leave with coalesced stores (store_record).
 template <typename T, int R, int NC, int MODE>
 struct Sink {
   T* out;
   int bin, fx, fy, fz;
   GridDev g;
+  T* lds;
   __device__ __forceinline__ void atomic_entry(int a, int b, int c, T v) const {
     constexpr int NS = Geo<R>::NS, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF;
     int ax = a % NS, ay = (a / NS) % NS, az = a / (NS * NS);
@@ -77,7 +87,7 @@ struct Sink {
   // Diagonal-tile entry: stored once as (a,b) with a <= b (record) or added as is (atomic).
   __device__ __forceinline__ void diag_tile(int a, int b, int c, T v) const {
     if (MODE == MODE_RECORD) {
-      if (a <= b) out[((size_t)bin * Geo<R>::NPAIR + pair_index<Geo<R>::N>(a, b)) * NC + c] = v;
+      if (a <= b) lds[pair_index<Geo<R>::N>(a, b) * NC + c] = v;
     } else {
       atomic_entry(a, b, c, v);
     }
@@ -85,11 +95,23 @@ struct Sink {
   // Off-diagonal-tile entry with a < b: stands for both (a,b) and (b,a).
   __device__ __forceinline__ void off_tile(int a, int b, int c, T v) const {
     if (MODE == MODE_RECORD) {
-      out[((size_t)bin * Geo<R>::NPAIR + pair_index<Geo<R>::N>(a, b)) * NC + c] = v;
+      lds[pair_index<Geo<R>::N>(a, b) * NC + c] = v;
     } else {
       atomic_entry(a, b, c, v);
       atomic_entry(b, a, c, v);
     }
+  }
+  // The bin's record, complete in LDS, to rec[bin] in 8-byte units (every
+  // record length is a multiple of 8 bytes and the records start 256-byte
+  // aligned). The wave is alone on its LDS region, and its LDS accesses are
+  // performed in program order, so no barrier is needed.
+  __device__ __forceinline__ void store_record(int lane) const {
+    constexpr int LEN = Geo<R>::NPAIR * NC;
+    static_assert((LEN * sizeof(T)) % 8 == 0, "record of whole 8-byte units");
+    constexpr int N8 = LEN * (int)sizeof(T) / 8;
+    const uint2* src = reinterpret_cast<const uint2*>(lds);
+    uint2* dst = reinterpret_cast<uint2*>(out + (size_t)bin * LEN);
+    for (int i = lane; i < N8; i += 64) dst[i] = src[i];
   }
 };
 
@@ -121,7 +143,7 @@ __device__ __forceinline__ Raw<T> load_raw(const PT* __restrict__ pos, const T* 
   return r;
 }
 
-// One particle per lane: weights W[a] (a = ax + NS*(ay + NS*az)) into sW[a][lane],
+// One particle per lane: weights W[a] (a = ax + NS*(ay + NS*az)) into sW[a * SWS + lane],
 // coefficients t^c into sT[c][lane]; zeros for an empty lane.
 template <typename T, int R, int NC>
 __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g, T beta, T sigma, T* sW, T* sT,
@@ -145,7 +167,7 @@ __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g
 #pragma unroll
     for (int ay = 0; ay < NS; ++ay)
 #pragma unroll
-      for (int ax = 0; ax < NS; ++ax) sW[(ax + NS * (ay + NS * az)) * 64 + lane] = (wx[ax] * wy[ay]) * wz[az];
+      for (int ax = 0; ax < NS; ++ax) sW[(ax + NS * (ay + NS * az)) * SWS + lane] = (wx[ax] * wy[ay]) * wz[az];
 #pragma unroll
   for (int c = 0; c < NC; ++c) sT[c * 64 + lane] = t[c];
   static_assert(N == NS * NS * NS, "support size");
@@ -165,7 +187,7 @@ struct AccCicF64 {
     const int slot = (lane >> 2) & 3, r4 = lane & 3, kq = lane >> 4;
     for (int r0 = 0; r0 < cnt; r0 += 16) {
       const int pl = r0 + 4 * slot + kq;
-      const double wlo = sW[r4 * 64 + pl], whi = sW[(4 + r4) * 64 + pl];
+      const double wlo = sW[r4 * SWS + pl], whi = sW[(4 + r4) * SWS + pl];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const double tc = sT[c * 64 + pl];
@@ -212,7 +234,7 @@ struct AccCicF32 {
     const int blk = lane >> 2, r4 = lane & 3;
     for (int r0 = 0; r0 < cnt; r0 += 16) {
       const int pl = r0 + blk;
-      const float wlo = sW[r4 * 64 + pl], whi = sW[(4 + r4) * 64 + pl];
+      const float wlo = sW[r4 * SWS + pl], whi = sW[(4 + r4) * SWS + pl];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const float tc = sT[c * 64 + pl];
@@ -282,8 +304,8 @@ struct AccTsc {
     const bool hi_ok = 16 + i16 < 27;
     for (int b0 = 0; b0 < cnt; b0 += 4) {
       const int pl = b0 + kq;
-      const T w0 = sW[i16 * 64 + pl];
-      const T w1 = hi_ok ? sW[(16 + i16) * 64 + pl] : T(0);
+      const T w0 = sW[i16 * SWS + pl];
+      const T w1 = hi_ok ? sW[(16 + i16) * SWS + pl] : T(0);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const T tc = sT[c * 64 + pl];
@@ -328,17 +350,29 @@ struct AccSel<T, 2, NC> {
 // ---------------------------------------------------------------- kernel
 constexpr int CT_WAVES = 4;  // waves per block; each wave works alone
 
+// Waves per SIMD the register allocation must allow: two for the fp32
+// tensorial record kernels, whose 108 fp32 accumulators otherwise leave one.
+template <typename T, int NC, int MODE>
+constexpr int contract_wpe() {
+  return sizeof(T) == 4 && NC == 9 && MODE == MODE_RECORD ? 2 : 1;
+}
+
 template <typename T, typename PT, int R, int NC, int MODE>
-__global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const PT* __restrict__ pos,
+__global__ __launch_bounds__(64 * CT_WAVES) __attribute__((amdgpu_waves_per_eu(contract_wpe<T, NC, MODE>())))
+void k_contract(GridDev g, const PT* __restrict__ pos,
                                                             const T* __restrict__ w, const PT* __restrict__ Bf,
                                                             const int32_t* __restrict__ bin_start,
                                                             const int32_t* __restrict__ perm, int np, int nbins,
                                                             T beta, T sigma, T* __restrict__ out) {
   constexpr int N = Geo<R>::N;
-  __shared__ T smem[CT_WAVES][(N + NC) * 64];
+  // per wave: the staged weights and coefficients, or one bin's record
+  constexpr int STG = N * SWS + NC * 64;
+  constexpr int REC = MODE == MODE_RECORD ? Geo<R>::NPAIR * NC : 0;
+  constexpr int WSZ = ((STG > REC ? STG : REC) + 3) & ~3;
+  __shared__ __attribute__((aligned(16))) T smem[CT_WAVES][WSZ];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   T* sW = smem[wv];
-  T* sT = smem[wv] + N * 64;
+  T* sT = smem[wv] + N * SWS;
   const int nwaves = gridDim.x * CT_WAVES;
   int b = blockIdx.x * CT_WAVES + wv;
   if (b >= nbins) return;
@@ -375,8 +409,9 @@ __global__ __launch_bounds__(64 * CT_WAVES) void k_contract(GridDev g, const PT*
 
     if (c0 + 64 >= e) {  // bin complete
       const int fx = b % g.n0, fy = (b / g.n0) % g.n1, fz = b / (g.n0 * g.n1);
-      Sink<T, R, NC, MODE> sk{out, b, fx, fy, fz, g};
+      Sink<T, R, NC, MODE> sk{out, b, fx, fy, fz, g, smem[wv]};
       if (MODE == MODE_RECORD || e > s) acc.template finish<MODE>(sk, lane);
+      if (MODE == MODE_RECORD) sk.store_record(lane);
       acc.zero();
     }
     if (!more) break;
@@ -415,7 +450,8 @@ static hipError_t contract_t(const GridDev& g, int order, const Particles& P, co
   if (order == 1)
     return ten ? contract_launch<T, 1, 9, MODE>(g, P, bin_start, perm, beta, sigma, out, 16, s)
                : contract_launch<T, 1, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 32, s);
-  return ten ? contract_launch<T, 2, 9, MODE>(g, P, bin_start, perm, beta, sigma, out, 4, s)
+  return ten ? contract_launch<T, 2, 9, MODE>(g, P, bin_start, perm, beta, sigma, out,
+                                               4 * contract_wpe<T, 9, MODE>(), s)
              : contract_launch<T, 2, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 16, s);
 }
 
