@@ -482,6 +482,11 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 }
 
 // ---------------------------------------------------------------- phase 2
+// Thread order of the gather: rows of offsets for the scalar order-2 matrix
+// (10% faster there); node-major elsewhere (for the 3x3 blocks the offset rows
+// were no faster, and order 1 stores its contiguous outputs through LDS).
+constexpr bool gather_offset_rows(int R, int NC) { return R == 2 && NC == 1; }
+
 // M[g][o][c] = sum over the bins k = g - a whose support holds both g and
 // g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
 // One thread per (node, offset, group of CPT components): the CPT values of a
@@ -503,11 +508,12 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
   constexpr int O0 = CANON ? (NOFF - 1) / 2 : 0;  // first offset stored
   constexpr int NOUT = NOFF - O0;                  // offsets stored per node
   constexpr int ROWT = NOUT * TPE;                 // threads per node
+  constexpr bool ROWS_OF_OFFSETS = gather_offset_rows(R, NC);
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the row
   const int t0 = (blk - rv * blocks_per_row) * 256;
   const int t = t0 + threadIdx.x;
-  const bool active = t < g.n0 * ROWT;
+  const bool active = t < g.n0 * (ROWS_OF_OFFSETS ? (NO * NO - O0 / NO) * NO * TPE : ROWT);
   if (R != 1 && !active) return;  // (order 1 keeps every thread for the block's barrier)
   constexpr int ZB = 4;
   const int nfull = g.n2 / ZB;           // complete z-blocks
@@ -523,9 +529,29 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
     gz = nfull * ZB + (rem - gy * zl);
   }
   const int row = gy + g.n1 * gz;
-  const int gx = t / ROWT;
-  const int rr = t - gx * ROWT;
-  const int o = O0 + rr / TPE, c0 = (rr - (o - O0) * TPE) * CPT;
+  int gx, o, c0;
+  if (!ROWS_OF_OFFSETS) {  // (node, offset, component group), offset-minor: contiguous outputs
+    gx = t / ROWT;
+    const int rr = t - gx * ROWT;
+    o = O0 + rr / TPE;
+    c0 = (rr - (o - O0) * TPE) * CPT;
+  } else {
+    // (oy, oz), then node, then (ox, component group): a wave shares the y and
+    // z parts of its offsets, so the y and z loops below run the same terms on
+    // every lane and only the three x terms depend on the lane (in node-major
+    // order a wave spans about 21 offsets and runs nearly all 27 terms with
+    // few lanes each). Offsets below O0 (canonical half) are idle threads.
+    constexpr int OYZ0 = O0 / NO;
+    const int per = g.n0 * NO * TPE;  // threads per (oy, oz)
+    const int oyz = OYZ0 + t / per;
+    const int rem = t - (oyz - OYZ0) * per;
+    gx = rem / (NO * TPE);
+    const int r2 = rem - gx * (NO * TPE);
+    const int oxi = r2 / TPE;
+    o = oxi + NO * oyz;
+    c0 = (r2 - oxi * TPE) * CPT;
+    if (o < O0) return;
+  }
   const int ox = o % NO - R, oy = (o / NO) % NO - R, oz = o / (NO * NO) - R;
   const int dlin = ox + NS * (oy + NS * oz);  // b - a in support-linear numbering
   // bin coordinates g - a per axis (wrapped)
@@ -603,7 +629,12 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
 template <typename T, int R, int NC, bool CANON>
 static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
   constexpr int NOUT = CANON ? (Geo<R>::NOFF + 1) / 2 : Geo<R>::NOFF;
-  const size_t row_len = (size_t)g.n0 * NOUT * (NC == 9 ? 3 : 1);  // threads per row of nodes
+  constexpr int NO = Geo<R>::NO;
+  // threads per row of nodes (with rows of offsets: whole (oy, oz) rows)
+  const size_t row_len =
+      (size_t)g.n0 *
+      (gather_offset_rows(R, NC) ? (NO * NO - (NOUT == Geo<R>::NOFF ? 0 : (Geo<R>::NOFF - 1) / 2 / NO)) * NO : NOUT) *
+      (NC == 9 ? 3 : 1);
   if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
