@@ -103,10 +103,11 @@ def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int,
 
 
 def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool,
-                  canonical: bool = False, dims: int = 3, rec_elem: int = 0) -> int:
-    """Algorithmic HBM bytes of one deposition launch: every record read once,
-    every stencil entry written once (read too when accumulating); the
-    canonical half stores (noff + 1) / 2 offsets."""
+                  canonical: bool = False, dims: int = 3, rec_elem: int = 0, nrec: int = 1) -> int:
+    """Algorithmic HBM bytes of one deposition launch: every record of the
+    nrec record sets (one per species) read once, every stencil entry written
+    once (read too when accumulating); the canonical half stores
+    (noff + 1) / 2 offsets."""
     rec_elem = rec_elem or elem
     n = (order + 1) ** dims
     noff = (2 * order + 1) ** dims
@@ -114,7 +115,7 @@ def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate
         noff = (noff + 1) // 2
     nc = 9 if tensorial else 1
     out = nbins * noff * nc * elem
-    return nbins * n * (n + 1) // 2 * nc * rec_elem + out * (2 if accumulate else 1)
+    return nrec * nbins * n * (n + 1) // 2 * nc * rec_elem + out * (2 if accumulate else 1)
 
 
 def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
@@ -129,6 +130,7 @@ def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
 
 def workload_key(args) -> str:
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
+            + ("-perspecies" if args.deposit_per_species else "")
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
             + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else ""))
 
@@ -235,6 +237,9 @@ def main():
                     help="f64, f32, or mix: fp32 positions and fields with fp64 weights, matrix and arithmetic")
     ap.add_argument("--shuffled", action="store_true", help="config 3: randomly shuffled particle order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deposit-per-species", action="store_true",
+                    help="several species: deposit each species' records on its own (accumulating into M) "
+                         "instead of one deposition of all species' records")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
     ap.add_argument("--canonical", action="store_true",
@@ -322,12 +327,17 @@ def main():
     nof = mm.noff_canonical(order) if args.canonical else mm.noff_grid(order, case.grid)
     M = torch.empty(nbins * nof * ncomp, dtype=tdt, device=dev)
     Fd = to_devp(Fgrid) if on_grid else None
-    rec = None
+    # Several species on the matrix-core path: each species is contracted into
+    # a record set of its own and one deposition adds all sets into M (the
+    # species' matrices enter one field operator); --deposit-per-species
+    # deposits each species' records on its own instead.
+    multi = args.algo == "mfma" and len(spec) > 1 and args.dims == 3 and not args.deposit_per_species
+    recs = []
     if args.algo == "mfma":
-        s0 = spec[0]
-        bs0, perm0 = mm.bin_particles(case.grid, order, s0["pos"], s0["bs"], s0["perm"], mixed=mix)
-        rec = mm.contract_bins(case.grid, order, s0["pos"], s0["w"], s0["B"], bs0, perm0, s0["beta"], case.sigma,
-                               Bgrid=Fd)
+        for s_ in (spec if multi else spec[:1]):
+            bs_, perm_ = mm.bin_particles(case.grid, order, s_["pos"], s_["bs"], s_["perm"], mixed=mix)
+            recs.append(mm.contract_bins(case.grid, order, s_["pos"], s_["w"], s_["B"], bs_, perm_, s_["beta"],
+                                         case.sigma, Bgrid=Fd))
 
     def ecsim(s, bs, perm, si, algo):
         if on_grid:
@@ -363,10 +373,15 @@ def main():
             bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"], mixed=mix)
             mark(si, 1)
             if args.algo == "mfma":
+                rec = recs[si] if multi else recs[0]
                 mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec,
                                  Bgrid=Fd)
                 mark(si, 2)
-                mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0, canonical=args.canonical)
+                if not multi:
+                    mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0,
+                                       canonical=args.canonical)
+                elif si == len(spec) - 1:  # one deposition of every species' records
+                    mm.deposit_records(case.grid, order, recs, M, tensorial, canonical=args.canonical)
             else:
                 if tensorial:
                     ecsim(s, bs, perm, si, args.algo)
@@ -404,7 +419,8 @@ def main():
         for si in range(len(spec)):
             for pi, p in enumerate(phases):
                 phase_ms[p] += pev[k][si][pi].elapsed_time(pev[k][si][pi + 1])
-    phase_per_launch_ms = {p: phase_ms[p] / (psteps * len(spec)) for p in phases}
+    nlaunch = {"bin": len(spec), "contract": len(spec), "deposit": 1 if multi else len(spec)}
+    phase_per_launch_ms = {p: phase_ms[p] / (psteps * nlaunch[p]) for p in phases}
     if args.algo == "mfma":
         dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
     elif args.algo == "mfma_atomic":
@@ -428,9 +444,12 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    launches = args.steps * len(spec)
+    # species whose launches the bracket holds (one deposition per step when
+    # the species' records are deposited together)
+    dom_species = [len(spec) - 1] if (multi and dom == "deposit") else list(range(len(spec)))
+    launches = args.steps * len(dom_species)
     dom_ms = sum(ev[k][si][bracket[0]].elapsed_time(ev[k][si][bracket[1]])
-                 for k in range(args.steps) for si in range(len(spec)))
+                 for k in range(args.steps) for si in dom_species)
     np_total = case.np_total
     value = np_total / (ms_step * 1e-3)
 
@@ -460,11 +479,16 @@ def main():
     flops = flops_per_particle(order, tensorial, args.dims) * np_launch
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem, args.dims,
                             8 if args.dims == 2 else 0)
-    # average over the species' launches: the first overwrites M, the others
-    # accumulate into it (read and write)
-    dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
-                               dims=args.dims, rec_elem=8 if args.dims == 2 else 0)
-                 for si in range(len(spec))) / len(spec)
+    # one deposition of every species' record sets, or the average over the
+    # species' launches: the first overwrites M, the others accumulate into it
+    # (read and write)
+    if multi:
+        dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False, canonical=args.canonical,
+                               nrec=len(spec))
+    else:
+        dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
+                                   dims=args.dims, rec_elem=8 if args.dims == 2 else 0)
+                     for si in range(len(spec))) / len(spec)
     if dom == "deposit":
         kname = "k_gather2d" if args.dims == 2 else "k_gather"
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
@@ -598,7 +622,8 @@ def main():
                    "storage": "fp32 positions and fields, fp64 weights and matrix" if mix else case.dtype,
                    "np": np_total,
                    "species": len(spec), "algo": args.algo, "stencil": "canonical half" if args.canonical else "full",
-                   "step": "bin + contract + deposit per species" if args.algo == "mfma" else
+                   "step": ("bin + contract per species, one deposit of all species' records" if multi else
+                            "bin + contract + deposit per species") if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
         "phases_ms_per_launch": phase_per_launch_ms,
         "phases_from": f"untimed pass of {psteps} steps with events at every phase boundary",

@@ -171,7 +171,8 @@ mm_status mm_assemble_ecsim_gridB(const mm_grid* grid, int order, mm_dtype dt, i
  * in Sec. 3.2, one per support group of Sec. 3.3):
  *   rec[bin][pair(a,b)][comp] = sigma * sum_{p in bin} t_p^comp W_pa W_pb,
  * for support rows a <= b (upper triangle, pair(a,b) = a*N - a(a-1)/2 + b - a,
- * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp).
+ * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp);
+ * with np == 0 a tensorial call still passes a non-NULL B (it is not read).
  *  rec       device buffer of *rec_bytes bytes (query with rec == NULL),
  *            16-byte aligned (else MM_ERR_ARG). The records start at rec.
  *            For order 2 tensorial fp64 (and MM_MIX) the query also counts
@@ -214,6 +215,28 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
  */
 mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
                                        int accumulate, void* Mc, mm_stream_t stream);
+
+/*
+ * mm_deposit_records_multi - one deposition of several record sets, for the
+ * sum over species of the field equation (Sec. 2.1: the mass matrices of all
+ * species enter one operator). Each species is contracted into a record set
+ * of its own (mm_contract_bins, same grid, order, dtype and kind); one pass
+ * over M then adds, for every M[g][o][comp], the records of all bins whose
+ * support holds both g and g+o, each term summed over the sets in their
+ * order. The result equals depositing the sets one after the other
+ * (accumulating) up to rounding, with one write of M instead of nrec, and
+ * no re-read of M between species.
+ *  canonical  0: the full stencil (as mm_deposit_records); 1: the canonical
+ *             half (as mm_deposit_records_canonical).
+ *  nrec       number of sets, 1 .. MM_MAX_RECORD_SETS (else MM_ERR_ARG).
+ *  recs       host array of nrec device pointers (each as rec of
+ *             mm_deposit_records; NULL entries give MM_ERR_NULL). The host
+ *             array is read during the call only.
+ *  2D grids: MM_ERR_UNSUPPORTED.
+ */
+#define MM_MAX_RECORD_SETS 4
+mm_status mm_deposit_records_multi(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical,
+                                   int nrec, const void* const* recs, int accumulate, void* M, mm_stream_t stream);
 
 /*
  * mm_deposit_moments - deposition of per-particle quantities with the same

@@ -221,6 +221,12 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     else:
         fn, name = lib.mm_contract_bins, "mm_contract_bins"
         field = B
+    if field is not None and field.numel() == 0:
+        # no particles: an empty tensor has no device address, but a NULL
+        # field would select the scalar records; the library does not read
+        # the field when np == 0, so a one-element stand-in marks the call
+        # as tensorial
+        field = torch.empty(1, dtype=field.dtype, device=field.device)
     head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
             _ptr(perm), float(beta), float(sigma))
     nbytes = ctypes.c_size_t(0)
@@ -238,11 +244,15 @@ def noff_canonical(order: int) -> int:
     return (noff(order) + 1) // 2
 
 
-def deposit_records(grid, order: int, rec: torch.Tensor, M: torch.Tensor, tensorial: bool,
+def deposit_records(grid, order: int, rec, M: torch.Tensor, tensorial: bool,
                     accumulate: bool = False, canonical: bool = False) -> torch.Tensor:
     """Phase 2: stencil deposition of the packed records into ``M`` (the full
-    stencil, or its canonical half ``[nnodes, 14 | 63, ncomp]``)."""
+    stencil, or its canonical half ``[nnodes, 14 | 63, ncomp]``). ``rec`` is
+    one record buffer, or a list of up to four (one per species), summed in
+    one pass over ``M`` (``mm_deposit_records_multi``)."""
     lib = _lib.load()
+    if isinstance(rec, (list, tuple)):
+        return _deposit_multi(lib, grid, order, list(rec), M, tensorial, accumulate, canonical)
     g = _grid_of(grid)
     _check_tensor(M, "M", None)
     if M.dtype not in _DT:
@@ -255,6 +265,27 @@ def deposit_records(grid, order: int, rec: torch.Tensor, M: torch.Tensor, tensor
                 else (lib.mm_deposit_records, "mm_deposit_records"))
     _call(fn, name, ctypes.byref(g), int(order), _DT[M.dtype], int(bool(tensorial)), _ptr(rec),
           int(bool(accumulate)), _ptr(M), _stream(M.device))
+    return M
+
+
+def _deposit_multi(lib, grid, order, recs, M, tensorial, accumulate, canonical):
+    g = _grid_of(grid)
+    _check_tensor(M, "M", None)
+    if M.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {M.dtype}")
+    if not 1 <= len(recs) <= _lib.MM_MAX_RECORD_SETS:
+        raise ValueError(f"1 to {_lib.MM_MAX_RECORD_SETS} record sets, got {len(recs)}")
+    ncomp = 9 if tensorial else 1
+    nof = noff_canonical(order) if canonical else noff_grid(order, g)
+    if M.numel() != _nnodes(g) * nof * ncomp:
+        raise ValueError("M has the wrong number of elements")
+    for r in recs:
+        if not r.is_cuda or r.device != M.device:
+            raise ValueError("record sets must be device tensors on M's device")
+    arr = (ctypes.c_void_p * len(recs))(*[r.data_ptr() for r in recs])
+    _call(lib.mm_deposit_records_multi, "mm_deposit_records_multi", ctypes.byref(g), int(order), _DT[M.dtype],
+          int(bool(tensorial)), int(bool(canonical)), len(recs), arr, int(bool(accumulate)), _ptr(M),
+          _stream(M.device))
     return M
 
 

@@ -489,6 +489,9 @@ constexpr bool gather_offset_rows(int R, int NC) { return R == 2 && NC == 1; }
 
 // M[g][o][c] = sum over the bins k = g - a whose support holds both g and
 // g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
+// With several record sets (one per species, NR > 1) each term is the sum of
+// the sets' entries in set order, so the species' matrices are added in one
+// pass over M.
 // One thread per (node, offset, group of CPT components): the CPT values of a
 // record entry are contiguous, and the threads of one entry cover it without
 // gaps. Each block covers part of one row of nodes (fixed y, z), so the row
@@ -499,9 +502,9 @@ constexpr bool gather_offset_rows(int R, int NC) { return R == 2 && NC == 1; }
 // XCD a few rows earlier and are still in its L2.
 // CANON: only the canonical half of the offsets, o >= centre (Sec. 3.4),
 // stored at o - centre.
-template <typename T, int R, int NC, bool CANON>
-__global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__ rec, int accumulate,
-                                                T* __restrict__ M, int blocks_per_row) {
+template <typename T, int R, int NC, bool CANON, int NR>
+__global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int accumulate, T* __restrict__ M,
+                                                int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
   constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
@@ -586,9 +589,15 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
         const int lo = a < b ? a : b, hi = a < b ? b : a;
         const int pi = lo * (2 * N - lo - 1) / 2 + hi;
         const unsigned k = (unsigned)(kx[ax] + kyz[az][ay]);
-        const T* src = rec + ((size_t)k * NPAIR + pi) * NC + c0;
+        const size_t off = ((size_t)k * NPAIR + pi) * NC + c0;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) sum[j] += src[j];
+        for (int q = 0; q < NR; ++q) {
+          if (q == 0 || q < recs.n) {  // (wave-uniform)
+            const T* src = recs.r[q] + off;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) sum[j] += src[j];
+          }
+        }
       }
     }
   }
@@ -627,7 +636,8 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, const T* __restrict__
 }
 
 template <typename T, int R, int NC, bool CANON>
-static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulate, void* M, hipStream_t s) {
+static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
+                                hipStream_t s) {
   constexpr int NOUT = CANON ? (Geo<R>::NOFF + 1) / 2 : Geo<R>::NOFF;
   constexpr int NO = Geo<R>::NO;
   // threads per row of nodes (with rows of offsets: whole (oy, oz) rows)
@@ -639,32 +649,41 @@ static hipError_t gather_launch(const GridDev& g, const void* rec, int accumulat
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gather<T, R, NC, CANON>), dim3((unsigned)blocks), dim3(256), 0, s, g, (const T*)rec, accumulate,
-                     (T*)M, bpr);
+  if (nrec < 1 || nrec > MAX_REC) return hipErrorInvalidValue;
+  RecSet<T> rs{};
+  for (int q = 0; q < nrec; ++q) rs.r[q] = (const T*)rec[q];
+  rs.n = nrec;
+  if (nrec == 1)
+    hipLaunchKernelGGL((k_gather<T, R, NC, CANON, 1>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs, accumulate,
+                       (T*)M, bpr);
+  else
+    hipLaunchKernelGGL((k_gather<T, R, NC, CANON, MAX_REC>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs,
+                       accumulate, (T*)M, bpr);
   return hipGetLastError();
 }
 
 template <bool CANON>
-static hipError_t gather_dispatch(const GridDev& g, int order, bool f32, bool tensorial, const void* rec,
-                                  int accumulate, void* M, hipStream_t s) {
+static hipError_t gather_dispatch(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec,
+                                  int nrec, int accumulate, void* M, hipStream_t s) {
   if (f32) {
     if (order == 1)
-      return tensorial ? gather_launch<float, 1, 9, CANON>(g, rec, accumulate, M, s)
-                       : gather_launch<float, 1, 1, CANON>(g, rec, accumulate, M, s);
-    return tensorial ? gather_launch<float, 2, 9, CANON>(g, rec, accumulate, M, s)
-                     : gather_launch<float, 2, 1, CANON>(g, rec, accumulate, M, s);
+      return tensorial ? gather_launch<float, 1, 9, CANON>(g, rec, nrec, accumulate, M, s)
+                       : gather_launch<float, 1, 1, CANON>(g, rec, nrec, accumulate, M, s);
+    return tensorial ? gather_launch<float, 2, 9, CANON>(g, rec, nrec, accumulate, M, s)
+                     : gather_launch<float, 2, 1, CANON>(g, rec, nrec, accumulate, M, s);
   }
   if (order == 1)
-    return tensorial ? gather_launch<double, 1, 9, CANON>(g, rec, accumulate, M, s)
-                     : gather_launch<double, 1, 1, CANON>(g, rec, accumulate, M, s);
-  return tensorial ? gather_launch<double, 2, 9, CANON>(g, rec, accumulate, M, s)
-                   : gather_launch<double, 2, 1, CANON>(g, rec, accumulate, M, s);
+    return tensorial ? gather_launch<double, 1, 9, CANON>(g, rec, nrec, accumulate, M, s)
+                     : gather_launch<double, 1, 1, CANON>(g, rec, nrec, accumulate, M, s);
+  return tensorial ? gather_launch<double, 2, 9, CANON>(g, rec, nrec, accumulate, M, s)
+                   : gather_launch<double, 2, 1, CANON>(g, rec, nrec, accumulate, M, s);
 }
 
-hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
+hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
+                         int accumulate,
                          void* M, hipStream_t s, bool canonical) {
-  return canonical ? gather_dispatch<true>(g, order, f32, tensorial, rec, accumulate, M, s)
-                   : gather_dispatch<false>(g, order, f32, tensorial, rec, accumulate, M, s);
+  return canonical ? gather_dispatch<true>(g, order, f32, tensorial, rec, nrec, accumulate, M, s)
+                   : gather_dispatch<false>(g, order, f32, tensorial, rec, nrec, accumulate, M, s);
 }
 
 }  // namespace mmk

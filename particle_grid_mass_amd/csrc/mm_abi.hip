@@ -5,6 +5,8 @@
 #include "../../include/mm.h"
 #include "mm_contract.h"
 
+static_assert(MM_MAX_RECORD_SETS == mmk::MAX_REC, "record set limit of the ABI and the gather");
+
 using namespace mmk;
 
 namespace {
@@ -129,7 +131,10 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   }
   if (records) {
     e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
-    if (e == hipSuccess) e = launch_gather(g, order, f32, tensorial, ws, accumulate, M, s);
+    if (e == hipSuccess) {
+      const void* recs[1] = {ws};
+      e = launch_gather(g, order, f32, tensorial, recs, 1, accumulate, M, s);
+    }
     return hip_status(e);
   }
   if (!accumulate) e = launch_fill_zero(M, count, f32, s);
@@ -260,7 +265,8 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
     if (dt == MM_F32) return MM_ERR_UNSUPPORTED;
     return hip_status(launch_gather_2d(to_dev(grid), order, tensorial != 0, rec, accumulate, M, (hipStream_t)stream));
   }
-  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, M,
+  const void* recs[1] = {rec};
+  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, recs, 1, accumulate, M,
                                   (hipStream_t)stream));
 }
 
@@ -272,8 +278,24 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (!rec || !Mc) return MM_ERR_NULL;
   if (is2d(grid)) return MM_ERR_UNSUPPORTED;
-  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, rec, accumulate, Mc,
+  const void* recs[1] = {rec};
+  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, recs, 1, accumulate, Mc,
                                   (hipStream_t)stream, true));
+}
+
+mm_status mm_deposit_records_multi(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical,
+                                   int nrec, const void* const* recs, int accumulate, void* M, mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (nrec < 1 || nrec > MM_MAX_RECORD_SETS) return MM_ERR_ARG;
+  if (!recs || !M) return MM_ERR_NULL;
+  for (int q = 0; q < nrec; ++q)
+    if (!recs[q]) return MM_ERR_NULL;
+  if (is2d(grid)) return MM_ERR_UNSUPPORTED;
+  return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, recs, nrec, accumulate, M,
+                                  (hipStream_t)stream, canonical != 0));
 }
 
 mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* Q,

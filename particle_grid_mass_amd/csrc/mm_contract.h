@@ -37,10 +37,17 @@ hipError_t launch_probe_mfma_f64(int nblocks, int iters, double* out, hipStream_
 // Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
 size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
 
-// Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o.
+// Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o,
+// over nrec (1 .. MAX_REC) record sets rec[0..nrec-1] (one per species).
 // canonical: only o >= centre, stored at M[g][o - centre][c].
-hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* rec, int accumulate,
-                         void* M, hipStream_t s, bool canonical = false);
+constexpr int MAX_REC = 4;
+template <typename T>
+struct RecSet {
+  const T* r[MAX_REC];
+  int n;
+};
+hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
+                         int accumulate, void* M, hipStream_t s, bool canonical = false);
 
 // The 2D problem (n2 == 1): per-bin fp64 records rec[bin][pair][comp] of the
 // (R+1)^2 support, and their fixed-order sum into M [nnodes][(2R+1)^2][comp]

@@ -172,3 +172,29 @@ def test_probe_validation():
     assert lib.mm_probe_mfma_f64(0, 10, FAKE, None) == _lib.MM_ERR_ARG
     assert lib.mm_probe_mfma_f64(4, 0, FAKE, None) == _lib.MM_ERR_ARG
     assert lib.mm_probe_mfma_f64((1 << 20) + 1, 10, FAKE, None) == _lib.MM_ERR_ARG
+
+
+def test_deposit_records_multi_validation():
+    """The several-species deposition rejects a set count outside 1..4, a NULL
+    array, NULL entries and 2D grids on the host."""
+    lib = _lib.load()
+    P = ctypes.c_void_p
+
+    def dep(g, nrec=2, recs="ok", M=FAKE, order=1, dt=_lib.MM_F64):
+        arr = (P * 4)(FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000))
+        if recs == "null_entry":
+            arr[1] = None
+        a = None if recs is None else arr
+        return lib.mm_deposit_records_multi(ctypes.byref(g) if g is not None else None, order, dt, 1, 0, nrec, a, 0,
+                                            M, None)
+
+    assert _lib.MM_MAX_RECORD_SETS == 4
+    assert dep(None) == _lib.MM_ERR_NULL
+    assert dep(G8, nrec=0) == _lib.MM_ERR_ARG
+    assert dep(G8, nrec=5) == _lib.MM_ERR_ARG
+    assert dep(G8, recs=None) == _lib.MM_ERR_NULL
+    assert dep(G8, recs="null_entry") == _lib.MM_ERR_NULL
+    assert dep(G8, M=None) == _lib.MM_ERR_NULL
+    assert dep(G8, order=3) == _lib.MM_ERR_ARG
+    assert dep(G8, dt=7) == _lib.MM_ERR_ARG
+    assert dep(_lib.make_grid((8, 8, 1))) == _lib.MM_ERR_UNSUPPORTED

@@ -1,0 +1,111 @@
+"""GPU parity of the several-species deposition (mm_deposit_records_multi):
+every species contracted into a record set of its own, one pass over M for
+all of them (the mass matrices of all species enter the one field operator,
+Sec. 2.1), through the C ABI, against the oracle of all species."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import particle_grid_mass_amd as mm
+from tests.gpu_util import TOL, TDT, oracle_assemble, rel_fro, require_gpu, to_dev
+from workloads import make_config, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def species_case(seed, order, n, counts, kind, dtype):
+    """One grid, len(counts) species with their own particles, weights, fields and beta."""
+    sp = []
+    for k, npart in enumerate(counts):
+        c = random_case(seed + 17 * k, order, n, npart, kind=kind, dtype=dtype, beta=0.6 - 0.45 * k,
+                        sigma=1.2, origin=(0.25, -2.0, 1.0), h=(0.5, 1.0, 0.75), spread=1.0 if k != 1 else 0.5)
+        sp += c.species
+    return dataclasses.replace(c, species=sp, name=f"species{len(counts)}")
+
+
+def record_sets(case):
+    dt = TDT[case.dtype]
+    tens = case.kind == "ecsim"
+    recs = []
+    for sp in case.species:
+        pos, w = to_dev(sp.pos, dt), to_dev(sp.w, dt)
+        B = to_dev(sp.B, dt) if tens else None
+        bs, perm = mm.bin_particles(case.grid, case.order, pos)
+        recs.append(mm.contract_bins(case.grid, case.order, pos, w, B, bs, perm, sp.beta, case.sigma))
+    return recs
+
+
+def new_M(case, canonical, fill=None):
+    nc = 9 if case.kind == "ecsim" else 1
+    nof = mm.noff_canonical(case.order) if canonical else mm.noff(case.order)
+    M = torch.empty(case.grid.ncells * nof * nc, dtype=TDT[case.dtype], device="cuda")
+    if fill is not None:
+        M.copy_(torch.from_numpy(fill.reshape(-1)).to(M.dtype))
+    return M, (case.grid.ncells, nof, nc)
+
+
+CASES = [(201, 1, (5, 6, 7), (3000, 1200)), (202, 2, (7, 6, 5), (2500, 900, 40)),
+         (203, 2, (9, 8, 7), (20000, 7000, 3, 500)), (204, 1, (6, 5, 5), (0, 800))]
+
+
+@pytest.mark.parametrize("canonical", [False, True])
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+@pytest.mark.parametrize("seed,order,n,counts", CASES)
+def test_deposit_multi(seed, order, n, counts, kind, dtype, canonical):
+    case = species_case(seed, order, n, counts, kind, dtype)
+    print(f"[case] multi order={order} n={n} counts={counts} {kind} {dtype} canonical={canonical}", flush=True)
+    tens = kind == "ecsim"
+    recs = record_sets(case)
+    M, shape = new_M(case, canonical)
+    mm.deposit_records(case.grid, order, recs, M, tens, canonical=canonical)
+    # the same sets deposited one after the other (accumulating)
+    Ms, _ = new_M(case, canonical)
+    for k, r in enumerate(recs):
+        mm.deposit_records(case.grid, order, r, Ms, tens, accumulate=k > 0, canonical=canonical)
+    # one set through the several-set entry is the single-set deposit, bit for bit
+    M1, _ = new_M(case, canonical)
+    mm.deposit_records(case.grid, order, recs[:1], M1, tens, canonical=canonical)
+    Ms1, _ = new_M(case, canonical)
+    mm.deposit_records(case.grid, order, recs[0], Ms1, tens, canonical=canonical)
+    torch.cuda.synchronize()
+    ref = oracle_assemble(case).reshape(case.grid.ncells, mm.noff(order), -1)
+    if canonical:
+        ref = oracle.canonical_half(order, ref)
+    got = M.view(shape).double().cpu().numpy()
+    assert rel_fro(got, ref) <= TOL[dtype]
+    assert rel_fro(got, Ms.view(shape).double().cpu().numpy()) <= TOL[dtype]
+    assert torch.equal(M1, Ms1)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_deposit_multi_accumulate(order):
+    case = species_case(300 + order, order, (7, 7, 6), (4000, 2500), "ecsim", "f64")
+    recs = record_sets(case)
+    rng = np.random.default_rng(7)
+    nc, nof = 9, mm.noff(order)
+    base = rng.standard_normal((case.grid.ncells, nof, nc))
+    M, shape = new_M(case, False, fill=base)
+    mm.deposit_records(case.grid, order, recs, M, True, accumulate=True)
+    torch.cuda.synchronize()
+    ref = base + oracle_assemble(case).reshape(shape)
+    assert rel_fro(M.view(shape).cpu().numpy(), ref) <= 1e-12
+
+
+def test_config3_multi():
+    """Both species of the 64^3, 125-particle-per-cell workload in one deposition."""
+    case = make_config(3)
+    print("[case] c3 multi", flush=True)
+    recs = record_sets(case)
+    M, shape = new_M(case, False)
+    mm.deposit_records(case.grid, 1, recs, M, True)
+    torch.cuda.synchronize()
+    assert rel_fro(M.view(shape).cpu().numpy(), oracle_assemble(case).reshape(shape)) <= 1e-12
