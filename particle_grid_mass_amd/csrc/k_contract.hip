@@ -502,15 +502,31 @@ constexpr bool gather_offset_rows(int R, int NC) { return R == 2 && NC == 1; }
 // XCD a few rows earlier and are still in its L2.
 // CANON: only the canonical half of the offsets, o >= centre (Sec. 3.4),
 // stored at o - centre.
+// Full stencil at order 2 (SYM): the threads run the canonical half too and
+// each stores its sum twice, at M[g][o] and at the mirrored entry
+// M[g + d(o)][-o], equal by the spatial symmetry M_gg' = M_g'g. Each record
+// entry is then read once: run over all offsets, the two reads of a pair
+// (for o and for -o) fall far apart and the second missed the L2, so the
+// order-2 deposit fetched 2.2 times its records.
+template <int R, bool CANON>
+struct GatherShape {
+  static constexpr int NOFF = Geo<R>::NOFF;
+  static constexpr bool SYM = R == 2 && !CANON;
+  static constexpr int O0 = (CANON || SYM) ? (NOFF - 1) / 2 : 0;  // first offset computed
+  static constexpr int NIT = NOFF - O0;                            // offsets computed per node
+  static constexpr int NOUT = CANON ? NIT : NOFF;                  // offsets stored per node
+  static constexpr int SO0 = CANON ? O0 : 0;                       // offset o is stored at o - SO0
+};
+
 template <typename T, int R, int NC, bool CANON, int NR>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int accumulate, T* __restrict__ M,
                                                 int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
   constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
-  constexpr int O0 = CANON ? (NOFF - 1) / 2 : 0;  // first offset stored
-  constexpr int NOUT = NOFF - O0;                  // offsets stored per node
-  constexpr int ROWT = NOUT * TPE;                 // threads per node
+  typedef GatherShape<R, CANON> GS;
+  constexpr int O0 = GS::O0, NOUT = GS::NOUT, SO0 = GS::SO0;
+  constexpr int ROWT = GS::NIT * TPE;              // threads per node
   constexpr bool ROWS_OF_OFFSETS = gather_offset_rows(R, NC);
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the row
@@ -543,7 +559,8 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
     // z parts of its offsets, so the y and z loops below run the same terms on
     // every lane and only the three x terms depend on the lane (in node-major
     // order a wave spans about 21 offsets and runs nearly all 27 terms with
-    // few lanes each). Offsets below O0 (canonical half) are idle threads.
+    // few lanes each). Offsets below O0 (the half that is not computed) are
+    // idle threads.
     constexpr int OYZ0 = O0 / NO;
     const int per = g.n0 * NO * TPE;  // threads per (oy, oz)
     const int oyz = OYZ0 + t / per;
@@ -629,22 +646,30 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
       for (int i = threadIdx.x; i < nval; i += 256) base[i] = accumulate ? base[i] + so[i] : so[i];
     }
   } else {
-    T* dst = M + ((size_t)row * g.n0 + gx) * (NOUT * NC) + (o - O0) * NC + c0;
+    T* dst = M + ((size_t)row * g.n0 + gx) * (NOUT * NC) + (o - SO0) * NC + c0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) dst[j] = accumulate ? dst[j] + sum[j] : sum[j];
+    if (GS::SYM && o != O0) {  // the mirrored entry (O0 is the centre offset here)
+      int mx = gx + ox, my = gy + oy, mz = gz + oz;
+      mx = mx < 0 ? mx + g.n0 : (mx >= g.n0 ? mx - g.n0 : mx);
+      my = my < 0 ? my + g.n1 : (my >= g.n1 ? my - g.n1 : my);
+      mz = mz < 0 ? mz + g.n2 : (mz >= g.n2 ? mz - g.n2 : mz);
+      T* mdst = M + ((size_t)mx + (size_t)g.n0 * ((size_t)my + (size_t)g.n1 * mz)) * (NOUT * NC) +
+                (NOFF - 1 - o) * NC + c0;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) mdst[j] = accumulate ? mdst[j] + sum[j] : sum[j];
+    }
   }
 }
 
 template <typename T, int R, int NC, bool CANON>
 static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
                                 hipStream_t s) {
-  constexpr int NOUT = CANON ? (Geo<R>::NOFF + 1) / 2 : Geo<R>::NOFF;
+  typedef GatherShape<R, CANON> GS;
   constexpr int NO = Geo<R>::NO;
   // threads per row of nodes (with rows of offsets: whole (oy, oz) rows)
   const size_t row_len =
-      (size_t)g.n0 *
-      (gather_offset_rows(R, NC) ? (NO * NO - (NOUT == Geo<R>::NOFF ? 0 : (Geo<R>::NOFF - 1) / 2 / NO)) * NO : NOUT) *
-      (NC == 9 ? 3 : 1);
+      (size_t)g.n0 * (gather_offset_rows(R, NC) ? (NO * NO - GS::O0 / NO) * NO : GS::NIT) * (NC == 9 ? 3 : 1);
   if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
