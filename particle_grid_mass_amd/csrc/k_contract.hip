@@ -502,16 +502,19 @@ constexpr bool gather_offset_rows(int R, int NC) { return R == 2 && NC == 1; }
 // XCD a few rows earlier and are still in its L2.
 // CANON: only the canonical half of the offsets, o >= centre (Sec. 3.4),
 // stored at o - centre.
-// Full stencil at order 2 (SYM): the threads run the canonical half too and
-// each stores its sum twice, at M[g][o] and at the mirrored entry
-// M[g + d(o)][-o], equal by the spatial symmetry M_gg' = M_g'g. Each record
-// entry is then read once: run over all offsets, the two reads of a pair
-// (for o and for -o) fall far apart and the second missed the L2, so the
-// order-2 deposit fetched 2.2 times its records.
-template <int R, bool CANON>
+// Full stencil (SYM): the threads run the canonical half too and each stores
+// its sum twice, at M[g][o] and at the mirrored entry M[g + d(o)][-o], equal
+// by the spatial symmetry M_gg' = M_g'g. Each record entry is then read
+// once: run over all offsets, the two reads of a pair (for o and for -o)
+// fall far apart and the second missed the L2 (the order-2 deposit fetched
+// 2.2 times its records, the order-1 deposit of two species on 64^3 cells
+// 1.7 times). At order 1 with one record set the node-major order with its
+// contiguous outputs staged through LDS stays ahead (37.4 against 36.4 us on
+// 32^3 cells), so there the mirrored form serves several sets only.
+template <int R, bool CANON, int NR>
 struct GatherShape {
   static constexpr int NOFF = Geo<R>::NOFF;
-  static constexpr bool SYM = R == 2 && !CANON;
+  static constexpr bool SYM = !CANON && (R == 2 || NR > 1);
   static constexpr int O0 = (CANON || SYM) ? (NOFF - 1) / 2 : 0;  // first offset computed
   static constexpr int NIT = NOFF - O0;                            // offsets computed per node
   static constexpr int NOUT = CANON ? NIT : NOFF;                  // offsets stored per node
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
   constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
-  typedef GatherShape<R, CANON> GS;
+  typedef GatherShape<R, CANON, NR> GS;
   constexpr int O0 = GS::O0, NOUT = GS::NOUT, SO0 = GS::SO0;
   constexpr int ROWT = GS::NIT * TPE;              // threads per node
   constexpr bool ROWS_OF_OFFSETS = gather_offset_rows(R, NC);
@@ -533,7 +536,10 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
   const int t0 = (blk - rv * blocks_per_row) * 256;
   const int t = t0 + threadIdx.x;
   const bool active = t < g.n0 * (ROWS_OF_OFFSETS ? (NO * NO - O0 / NO) * NO * TPE : ROWT);
-  if (R != 1 && !active) return;  // (order 1 keeps every thread for the block's barrier)
+  // order 1 without the mirrored form stages its contiguous outputs through
+  // LDS (every thread stays for the block's barrier); the others store directly
+  constexpr bool STAGED = R == 1 && !GS::SYM;
+  if (!STAGED && !active) return;
   constexpr int ZB = 4;
   const int nfull = g.n2 / ZB;           // complete z-blocks
   const int inb = g.n1 * ZB;             // rows per complete z-block
@@ -619,10 +625,10 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
     }
   }
   }
-  if (R == 1) {
+  if (STAGED) {
     // The block's outputs are contiguous (thread t holds values CPT t ..
     // CPT t + CPT - 1 of its row): stage them in LDS and store 16 bytes per
-    // lane. 10% faster at 64^3 cells; at order 2 the plain stores were faster.
+    // lane. 10% faster at 64^3 cells.
     __shared__ __attribute__((aligned(16))) T so[256 * CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) so[threadIdx.x * CPT + j] = sum[j];
@@ -662,10 +668,9 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
   }
 }
 
-template <typename T, int R, int NC, bool CANON>
-static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
-                                hipStream_t s) {
-  typedef GatherShape<R, CANON> GS;
+template <typename T, int R, int NC, bool CANON, int NR>
+static hipError_t gather_go(const GridDev& g, const RecSet<T>& rs, int accumulate, void* M, hipStream_t s) {
+  typedef GatherShape<R, CANON, NR> GS;
   constexpr int NO = Geo<R>::NO;
   // threads per row of nodes (with rows of offsets: whole (oy, oz) rows)
   const size_t row_len =
@@ -674,17 +679,20 @@ static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nr
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gather<T, R, NC, CANON, NR>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs, accumulate,
+                     (T*)M, bpr);
+  return hipGetLastError();
+}
+
+template <typename T, int R, int NC, bool CANON>
+static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
+                                hipStream_t s) {
   if (nrec < 1 || nrec > MAX_REC) return hipErrorInvalidValue;
   RecSet<T> rs{};
   for (int q = 0; q < nrec; ++q) rs.r[q] = (const T*)rec[q];
   rs.n = nrec;
-  if (nrec == 1)
-    hipLaunchKernelGGL((k_gather<T, R, NC, CANON, 1>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs, accumulate,
-                       (T*)M, bpr);
-  else
-    hipLaunchKernelGGL((k_gather<T, R, NC, CANON, MAX_REC>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs,
-                       accumulate, (T*)M, bpr);
-  return hipGetLastError();
+  return nrec == 1 ? gather_go<T, R, NC, CANON, 1>(g, rs, accumulate, M, s)
+                   : gather_go<T, R, NC, CANON, MAX_REC>(g, rs, accumulate, M, s);
 }
 
 template <bool CANON>
