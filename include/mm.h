@@ -231,7 +231,8 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
  *  nrec       number of sets, 1 .. MM_MAX_RECORD_SETS (else MM_ERR_ARG).
  *  recs       host array of nrec device pointers (each as rec of
  *             mm_deposit_records; NULL entries give MM_ERR_NULL). The host
- *             array is read during the call only.
+ *             array is read during the call only. M must not overlap any
+ *             record set (the sets are read while M is written).
  *  2D grids: MM_ERR_UNSUPPORTED.
  */
 #define MM_MAX_RECORD_SETS 4
