@@ -33,3 +33,18 @@ def test_deposit_bytes_canonical_half(order):
     n = (order + 1) ** 3
     rec = 1000 * n * (n + 1) // 2 * 9 * 8
     assert (half - rec) * (2 * order + 1) ** 3 == (full - rec) * ((2 * order + 1) ** 3 + 1) // 2
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_deposit_bytes_several_sets(order):
+    """One deposition of k record sets reads k sets and writes M once: k - 1
+    sets more than one single-set deposit, and less than k single-set deposits
+    into one M (the later ones also read M)."""
+    n = (order + 1) ** 3
+    rec = 1000 * n * (n + 1) // 2 * 9 * 8
+    one = bench.deposit_bytes(order, True, 8, 1000, False)
+    for k in (2, 3, 4):
+        multi = bench.deposit_bytes(order, True, 8, 1000, False, nrec=k)
+        assert multi == one + (k - 1) * rec
+        seq = one + (k - 1) * bench.deposit_bytes(order, True, 8, 1000, True)
+        assert multi < seq
