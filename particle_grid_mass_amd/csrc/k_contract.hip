@@ -359,11 +359,9 @@ constexpr int contract_wpe() {
 
 template <typename T, typename PT, int R, int NC, int MODE>
 __global__ __launch_bounds__(64 * CT_WAVES) __attribute__((amdgpu_waves_per_eu(contract_wpe<T, NC, MODE>())))
-void k_contract(GridDev g, const PT* __restrict__ pos,
-                                                            const T* __restrict__ w, const PT* __restrict__ Bf,
-                                                            const int32_t* __restrict__ bin_start,
-                                                            const int32_t* __restrict__ perm, int np, int nbins,
-                                                            T beta, T sigma, T* __restrict__ out) {
+void k_contract(GridDev g, const PT* __restrict__ pos, const T* __restrict__ w, const PT* __restrict__ Bf,
+                const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, T beta,
+                T sigma, T* __restrict__ out) {
   constexpr int N = Geo<R>::N;
   // per wave: the staged weights and coefficients, or one bin's record
   constexpr int STG = N * SWS + NC * 64;
