@@ -53,6 +53,21 @@ struct Geo {
 // and the staging stores (one column per lane) stay conflict-free.
 constexpr int SWS = 68;
 
+// The fp64 scalar order-2 kernel stages the 3 + 3 + 3 one-dimensional
+// weights of each particle (sW[3 d + k][lane], axis d) instead of the 27
+// products, and forms W_a = (wx wy) wz in the rounds: 9 instead of 27 staged
+// rows per wave, so that the registers rather than the LDS bound the waves
+// per SIMD (5 instead of 2; contraction 12% faster on 32^3 cells x 64). In
+// fp32 the LDS did not bound them, and the extra products cost 5%.
+template <typename T, int R, int NC>
+constexpr bool stage_1d() {
+  return R == 2 && NC == 1 && sizeof(T) == 8;
+}
+template <typename T, int R, int NC>
+constexpr int staged_rows() {
+  return stage_1d<T, R, NC>() ? 9 : Geo<R>::N;
+}
+
 // Position of the pair (a, b), a <= b, in the packed upper triangle.
 template <int N>
 __device__ __forceinline__ int pair_index(int a, int b) {
@@ -143,7 +158,8 @@ __device__ __forceinline__ Raw<T> load_raw(const PT* __restrict__ pos, const T* 
   return r;
 }
 
-// One particle per lane: weights W[a] (a = ax + NS*(ay + NS*az)) into sW[a * SWS + lane],
+// One particle per lane: weights W[a] (a = ax + NS*(ay + NS*az)) into sW[a * SWS + lane]
+// (or the one-dimensional weights, stage_1d),
 // coefficients t^c into sT[c][lane]; zeros for an empty lane.
 template <typename T, int R, int NC>
 __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g, T beta, T sigma, T* sW, T* sT,
@@ -162,12 +178,21 @@ __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g
     else
       t[0] = f;
   }
+  if (stage_1d<T, R, NC>()) {
 #pragma unroll
-  for (int az = 0; az < NS; ++az)
+    for (int k = 0; k < NS; ++k) {
+      sW[k * SWS + lane] = wx[k];
+      sW[(NS + k) * SWS + lane] = wy[k];
+      sW[(2 * NS + k) * SWS + lane] = wz[k];
+    }
+  } else {
 #pragma unroll
-    for (int ay = 0; ay < NS; ++ay)
+    for (int az = 0; az < NS; ++az)
 #pragma unroll
-      for (int ax = 0; ax < NS; ++ax) sW[(ax + NS * (ay + NS * az)) * SWS + lane] = (wx[ax] * wy[ay]) * wz[az];
+      for (int ay = 0; ay < NS; ++ay)
+#pragma unroll
+        for (int ax = 0; ax < NS; ++ax) sW[(ax + NS * (ay + NS * az)) * SWS + lane] = (wx[ax] * wy[ay]) * wz[az];
+  }
 #pragma unroll
   for (int c = 0; c < NC; ++c) sT[c * 64 + lane] = t[c];
   static_assert(N == NS * NS * NS, "support size");
@@ -302,10 +327,22 @@ struct AccTsc {
   __device__ __forceinline__ void accumulate(const T* sW, const T* sT, int cnt, int lane) {
     const int i16 = lane & 15, kq = lane >> 4;
     const bool hi_ok = 16 + i16 < 27;
+    // one-dimensional staging (scalar): rows of the x, y, z weights of
+    // support rows i16 and 16 + i16
+    constexpr bool S1 = stage_1d<T, 2, NC>();
+    const int a1 = hi_ok ? 16 + i16 : 0;
+    const int x0 = (i16 % 3) * SWS, y0 = (3 + (i16 / 3) % 3) * SWS, z0 = (6 + i16 / 9) * SWS;
+    const int x1 = (a1 % 3) * SWS, y1 = (3 + (a1 / 3) % 3) * SWS, z1 = (6 + a1 / 9) * SWS;
     for (int b0 = 0; b0 < cnt; b0 += 4) {
       const int pl = b0 + kq;
-      const T w0 = sW[i16 * SWS + pl];
-      const T w1 = hi_ok ? sW[(16 + i16) * SWS + pl] : T(0);
+      T w0, w1;
+      if (S1) {
+        w0 = (sW[x0 + pl] * sW[y0 + pl]) * sW[z0 + pl];
+        w1 = hi_ok ? (sW[x1 + pl] * sW[y1 + pl]) * sW[z1 + pl] : T(0);
+      } else {
+        w0 = sW[i16 * SWS + pl];
+        w1 = hi_ok ? sW[(16 + i16) * SWS + pl] : T(0);
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const T tc = sT[c * 64 + pl];
@@ -364,13 +401,13 @@ void k_contract(GridDev g, const PT* __restrict__ pos, const T* __restrict__ w, 
                 T sigma, T* __restrict__ out) {
   constexpr int N = Geo<R>::N;
   // per wave: the staged weights and coefficients, or one bin's record
-  constexpr int STG = N * SWS + NC * 64;
+  constexpr int STG = staged_rows<T, R, NC>() * SWS + NC * 64;
   constexpr int REC = MODE == MODE_RECORD ? Geo<R>::NPAIR * NC : 0;
   constexpr int WSZ = ((STG > REC ? STG : REC) + 3) & ~3;
   __shared__ __attribute__((aligned(16))) T smem[CT_WAVES][WSZ];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   T* sW = smem[wv];
-  T* sT = smem[wv] + N * SWS;
+  T* sT = smem[wv] + staged_rows<T, R, NC>() * SWS;
   const int nwaves = gridDim.x * CT_WAVES;
   int b = blockIdx.x * CT_WAVES + wv;
   if (b >= nbins) return;
@@ -450,7 +487,8 @@ static hipError_t contract_t(const GridDev& g, int order, const Particles& P, co
                : contract_launch<T, 1, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 32, s);
   return ten ? contract_launch<T, 2, 9, MODE>(g, P, bin_start, perm, beta, sigma, out,
                                                4 * contract_wpe<T, 9, MODE>(), s)
-             : contract_launch<T, 2, 1, MODE>(g, P, bin_start, perm, beta, sigma, out, 16, s);
+             : contract_launch<T, 2, 1, MODE>(g, P, bin_start, perm, beta, sigma, out,
+                                              stage_1d<T, 2, 1>() ? 20 : 16, s);
 }
 
 hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
