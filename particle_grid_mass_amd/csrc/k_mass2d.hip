@@ -140,17 +140,23 @@ __global__ __launch_bounds__(64) void k_mass2d(GridDev g, const PT* __restrict__
 }
 
 // M[g][o][c] (=|+=) sum over the support nodes a with a + o in the support of
-// rec[bin g - a][pair(a, a + o)][c], in a fixed order. One thread per (node, offset).
+// rec[bin g - a][pair(a, a + o)][c], in a fixed order. One thread per (node,
+// offset o >= centre), which stores its sum at M[g][o] and at the mirrored
+// entry M[g + d(o)][-o] (equal by the spatial symmetry), so that each record
+// entry is read once (one thread per offset read each pair twice: the TSC
+// deposit on 256^2 cells took 134 instead of 112 us, CIC 38.4 instead of 36.9).
 template <typename T, int R, int NC>
 __global__ __launch_bounds__(256) void k_gather2d(GridDev g, const double* __restrict__ rec, int accumulate,
                                                   T* __restrict__ M) {
   using G = G2<R>;
   constexpr int NS = G::NS, N = G::N, NO = G::NO, NOFF = G::NOFF;
+  constexpr int O0 = (NOFF - 1) / 2;            // first offset computed: the centre
+  constexpr int NIT = NOFF - O0;                // offsets computed per node
   const size_t nn = (size_t)g.n0 * g.n1;
   const size_t t = (size_t)xcd_remap(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x;
-  if (t >= nn * NOFF) return;
-  const size_t node = t / NOFF;
-  const int o = (int)(t - node * NOFF);
+  if (t >= nn * NIT) return;
+  const size_t node = t / NIT;
+  const int o = O0 + (int)(t - node * NIT);
   const int gx = (int)(node % g.n0), gy = (int)(node / g.n0);
   const int ox = o % NO - R, oy = o / NO - R;
   double sum[NC];
@@ -172,9 +178,17 @@ __global__ __launch_bounds__(256) void k_gather2d(GridDev g, const double* __res
       for (int c = 0; c < NC; ++c) sum[c] += src[c];
     }
   }
-  T* dst = M + t * NC;
+  T* dst = M + (node * NOFF + o) * NC;
 #pragma unroll
   for (int c = 0; c < NC; ++c) dst[c] = accumulate ? (T)((double)dst[c] + sum[c]) : (T)sum[c];
+  if (o != O0) {
+    int mx = gx + ox, my = gy + oy;
+    mx = mx < 0 ? mx + g.n0 : (mx >= g.n0 ? mx - g.n0 : mx);
+    my = my < 0 ? my + g.n1 : (my >= g.n1 ? my - g.n1 : my);
+    T* mdst = M + (((size_t)mx + (size_t)g.n0 * my) * NOFF + (NOFF - 1 - o)) * NC;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) mdst[c] = accumulate ? (T)((double)mdst[c] + sum[c]) : (T)sum[c];
+  }
 }
 
 size_t record_bytes_2d(int order, bool tensorial, int64_t nbins) {
@@ -208,7 +222,8 @@ hipError_t launch_contract_2d(const GridDev& g, int order, const Particles& P, c
 
 hipError_t launch_gather_2d(const GridDev& g, int order, bool tensorial, const void* rec, int accumulate, void* M,
                             hipStream_t s) {
-  const size_t nt = (size_t)g.n0 * g.n1 * (order == 1 ? 9 : 25);
+  const int noff = order == 1 ? 9 : 25;
+  const size_t nt = (size_t)g.n0 * g.n1 * ((noff + 1) / 2);  // threads: nodes x offsets from the centre on
   const size_t blocks = (nt + 255) / 256;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(256);
