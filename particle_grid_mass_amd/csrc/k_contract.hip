@@ -518,11 +518,11 @@ size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
 }
 
 // ---------------------------------------------------------------- phase 2
-// Thread order of the gather: rows of offsets at order 2 (with the mirrored
-// stores, the deposit is 10% faster for the scalar matrix and 9% (fp64) to
-// 21% (fp32) for 3x3 blocks than in node-major order); node-major at order 1,
-// whose contiguous outputs are staged through LDS.
-constexpr bool gather_offset_rows(int R) { return R == 2; }
+// Thread order of the gather (GatherShape::ROWS): rows of offsets at order 2
+// (with the mirrored stores, the deposit is 10% faster for the scalar matrix
+// and 9% (fp64) to 21% (fp32) for 3x3 blocks than in node-major order) and for
+// the mirrored single-set deposit at order 1; node-major otherwise, where
+// order 1 stages its contiguous outputs through LDS.
 
 // M[g][o][c] = sum over the bins k = g - a whose support holds both g and
 // g + o of rec[k][pair(a, a+o)][c]; the terms are added in a fixed order.
@@ -545,29 +545,31 @@ constexpr bool gather_offset_rows(int R) { return R == 2; }
 // once: run over all offsets, the two reads of a pair (for o and for -o)
 // fall far apart and the second missed the L2 (the order-2 deposit fetched
 // 2.2 times its records, the order-1 deposit of two species on 64^3 cells
-// 1.7 times). At order 1 with one record set the node-major order with its
-// contiguous outputs staged through LDS stays ahead (37.4 against 36.4 us on
-// 32^3 cells), so there the mirrored form serves several sets only.
-template <int R, bool CANON, int NR>
+// 1.7 times). At order 1 with one record set (MIR1) it is taken only on
+// small planes, in rows of offsets: 34 against 36.5 us on 32^3 cells, while
+// on 64^3 cells the node-major order with its contiguous outputs staged
+// through LDS stays ahead (387 against 469 us).
+template <int R, bool CANON, int NR, bool MIR1 = false>
 struct GatherShape {
   static constexpr int NOFF = Geo<R>::NOFF;
-  static constexpr bool SYM = !CANON && (R == 2 || NR > 1);
+  static constexpr bool SYM = !CANON && (R == 2 || NR > 1 || MIR1);
+  static constexpr bool ROWS = R == 2 || (MIR1 && R == 1 && NR == 1 && !CANON);  // rows of offsets
   static constexpr int O0 = (CANON || SYM) ? (NOFF - 1) / 2 : 0;  // first offset computed
   static constexpr int NIT = NOFF - O0;                            // offsets computed per node
   static constexpr int NOUT = CANON ? NIT : NOFF;                  // offsets stored per node
   static constexpr int SO0 = CANON ? O0 : 0;                       // offset o is stored at o - SO0
 };
 
-template <typename T, int R, int NC, bool CANON, int NR>
+template <typename T, int R, int NC, bool CANON, int NR, bool MIR1>
 __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int accumulate, T* __restrict__ M,
                                                 int blocks_per_row) {
   constexpr int NS = Geo<R>::NS, N = Geo<R>::N, NO = Geo<R>::NO, NOFF = Geo<R>::NOFF, NPAIR = Geo<R>::NPAIR;
   constexpr int CPT = NC == 9 ? 3 : 1;  // components per thread
   constexpr int TPE = NC / CPT;         // threads per (node, offset)
-  typedef GatherShape<R, CANON, NR> GS;
+  typedef GatherShape<R, CANON, NR, MIR1> GS;
   constexpr int O0 = GS::O0, NOUT = GS::NOUT, SO0 = GS::SO0;
   constexpr int ROWT = GS::NIT * TPE;              // threads per node
-  constexpr bool ROWS_OF_OFFSETS = gather_offset_rows(R);
+  constexpr bool ROWS_OF_OFFSETS = GS::ROWS;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the row
   const int t0 = (blk - rv * blocks_per_row) * 256;
@@ -705,19 +707,19 @@ __global__ __launch_bounds__(256) void k_gather(GridDev g, RecSet<T> recs, int a
   }
 }
 
-template <typename T, int R, int NC, bool CANON, int NR>
+template <typename T, int R, int NC, bool CANON, int NR, bool MIR1 = false>
 static hipError_t gather_go(const GridDev& g, const RecSet<T>& rs, int accumulate, void* M, hipStream_t s) {
-  typedef GatherShape<R, CANON, NR> GS;
+  typedef GatherShape<R, CANON, NR, MIR1> GS;
   constexpr int NO = Geo<R>::NO;
   // threads per row of nodes (with rows of offsets: whole (oy, oz) rows)
   const size_t row_len =
-      (size_t)g.n0 * (gather_offset_rows(R) ? (NO * NO - GS::O0 / NO) * NO : GS::NIT) * (NC == 9 ? 3 : 1);
+      (size_t)g.n0 * (GS::ROWS ? (NO * NO - GS::O0 / NO) * NO : GS::NIT) * (NC == 9 ? 3 : 1);
   if (row_len > 0x7fffff00ULL) return hipErrorInvalidValue;
   const int bpr = (int)((row_len + 255) / 256);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gather<T, R, NC, CANON, NR>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs, accumulate,
-                     (T*)M, bpr);
+  hipLaunchKernelGGL((k_gather<T, R, NC, CANON, NR, MIR1>), dim3((unsigned)blocks), dim3(256), 0, s, g, rs,
+                     accumulate, (T*)M, bpr);
   return hipGetLastError();
 }
 
@@ -728,8 +730,12 @@ static hipError_t gather_launch(const GridDev& g, const void* const* rec, int nr
   RecSet<T> rs{};
   for (int q = 0; q < nrec; ++q) rs.r[q] = (const T*)rec[q];
   rs.n = nrec;
-  return nrec == 1 ? gather_go<T, R, NC, CANON, 1>(g, rs, accumulate, M, s)
-                   : gather_go<T, R, NC, CANON, MAX_REC>(g, rs, accumulate, M, s);
+  if (nrec > 1) return gather_go<T, R, NC, CANON, MAX_REC>(g, rs, accumulate, M, s);
+  // one set at order 1 (full stencil): the mirrored form on planes of at most 32 x 32 nodes
+  if constexpr (R == 1 && !CANON) {
+    if ((int64_t)g.n0 * g.n1 <= 1024) return gather_go<T, R, NC, CANON, 1, true>(g, rs, accumulate, M, s);
+  }
+  return gather_go<T, R, NC, CANON, 1>(g, rs, accumulate, M, s);
 }
 
 template <bool CANON>
