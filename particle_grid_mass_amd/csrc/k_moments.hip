@@ -29,25 +29,59 @@ struct MGeo {
   static constexpr int NS = R + 1;
   static constexpr int N = NS * NS * NS;   // support nodes
   static constexpr int NR = (N + 3) / 4 * 4;  // rows padded to blocks of 4
+  // staged weights per particle: the 27 products at order 1 would be 8, the
+  // 3 x 3 one-dimensional weights at order 2 (products formed in the rounds)
+  static constexpr int WS = R == 2 ? 9 : NR;
 };
 
-// LDS slots: W row-major per slot with 32 bytes more per bin, then Q.
+// LDS slots: W per slot with 32 bytes more per bin, then Q.
 template <int R>
-__device__ __forceinline__ int w_base(int s) { return s * MGeo<R>::NR + (s >> 4) * 4; }
+__device__ __forceinline__ int w_base(int s) { return s * MGeo<R>::WS + (s >> 4) * 4; }
 template <int R, int KB>
 __device__ __forceinline__ int q_base(int s) {
-  return 64 * MGeo<R>::NR + NB * 4 + s * (4 * KB) + (s >> 4) * 4;
+  return 64 * MGeo<R>::WS + NB * 4 + s * (4 * KB) + (s >> 4) * 4;
+}
+
+// Data of the particle a lane prepares: position and quantities.
+template <typename T, int KB>
+struct MRaw {
+  T x, y, z;
+  T q[4 * KB];
+  bool valid;
+};
+
+template <typename T, int KB, typename PT>
+__device__ __forceinline__ MRaw<T, KB> load_mraw(const PT* __restrict__ pos, const T* __restrict__ Q, int nq, int p,
+                                                 int np) {
+  MRaw<T, KB> r;
+  r.valid = (unsigned)p < (unsigned)np;
+  r.x = r.y = r.z = T(0);
+#pragma unroll
+  for (int k = 0; k < 4 * KB; ++k) r.q[k] = T(0);
+  if (r.valid) {
+    r.x = (T)pos[3 * (size_t)p];
+    r.y = (T)pos[3 * (size_t)p + 1];
+    r.z = (T)pos[3 * (size_t)p + 2];
+#pragma unroll
+    for (int k = 0; k < 4 * KB; ++k)
+      if (k < nq) r.q[k] = Q[(size_t)p * nq + k];
+  }
+  return r;
 }
 
 }  // namespace
 
 // T: arithmetic of the weights and type of Q; PT: stored positions (T, or fp32 into fp64).
+// The particle data of the next chunk, and the permutation entries of the
+// chunk after it, are in flight while the current chunk is contracted.
 template <typename T, int R, int KB, typename PT>
 __global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict__ pos, const T* __restrict__ Q, int nq,
                                                 const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm,
                                                 int np, int nbins, double* __restrict__ rec) {
   constexpr int NS = MGeo<R>::NS, N = MGeo<R>::N, NR = MGeo<R>::NR, NRB = NR / 4;
-  constexpr int SMEM = 64 * NR + NB * 4 + 64 * 4 * KB + NB * 4;
+  constexpr int STAGE = 64 * MGeo<R>::WS + NB * 4 + 64 * 4 * KB + NB * 4;
+  constexpr int RECS = NB * N * 4 * KB;  // the group's records, staged after the rounds
+  constexpr int SMEM = STAGE > RECS ? STAGE : RECS;
   __shared__ __attribute__((aligned(16))) double sm[SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
@@ -70,31 +104,56 @@ __global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict_
   const int nchunks = (maxn + CH - 1) / CH;
 
   const int mk = lane >> 4, mb = (lane >> 2) & 3, mr = lane & 3;
+  // order 2: this lane's support rows a = 4 I + mr as indices of their x, y, z weights
+  int ix[NRB], iy[NRB], iz[NRB];
+#pragma unroll
+  for (int I = 0; I < NRB; ++I) {
+    const int a = 4 * I + mr;
+    ix[I] = a % NS;
+    iy[I] = NS + (a / NS) % NS;
+    iz[I] = 2 * NS + a / (NS * NS);
+  }
   double acc[NRB][KB];
 #pragma unroll
   for (int I = 0; I < NRB; ++I)
 #pragma unroll
     for (int J = 0; J < KB; ++J) acc[I][J] = 0.0;
 
+  auto chunk_perm = [&](int j) {
+    const int qi = j * CH + (lane & 15);
+    return qi < n_l ? perm[s0 + qi] : -1;
+  };
+  MRaw<T, KB> raw = load_mraw<T, KB, PT>(pos, Q, nq, chunk_perm(0), np);
+  int pnext = chunk_perm(1);
   for (int j = 0; j < nchunks; ++j) {
     // stage: one particle per lane (zeros for an empty lane)
-    const int qi = j * CH + (lane & 15);
-    const int p = qi < n_l ? perm[s0 + qi] : -1;
-    T wx[3] = {T(0), T(0), T(0)}, wy[3] = {T(0), T(0), T(0)}, wz[3] = {T(0), T(0), T(0)};
-    const bool valid = (unsigned)p < (unsigned)np;
-    if (valid) {
-      axis_support<T, R>(grid_coord<T, 0>((T)pos[3 * (size_t)p], g), g.n0, wx);
-      axis_support<T, R>(grid_coord<T, 1>((T)pos[3 * (size_t)p + 1], g), g.n1, wy);
-      axis_support<T, R>(grid_coord<T, 2>((T)pos[3 * (size_t)p + 2], g), g.n2, wz);
+    {
+      T wx[3] = {T(0), T(0), T(0)}, wy[3] = {T(0), T(0), T(0)}, wz[3] = {T(0), T(0), T(0)};
+      if (raw.valid) {
+        axis_support<T, R>(grid_coord<T, 0>(raw.x, g), g.n0, wx);
+        axis_support<T, R>(grid_coord<T, 1>(raw.y, g), g.n1, wy);
+        axis_support<T, R>(grid_coord<T, 2>(raw.z, g), g.n2, wz);
+      }
+      double* sw = sm + w_base<R>(lane);
+      if (R == 2) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          sw[k] = (double)wx[k];
+          sw[NS + k] = (double)wy[k];
+          sw[2 * NS + k] = (double)wz[k];
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+          sw[a] = a < N ? (double)((wx[a % NS] * wy[(a / NS) % NS]) * wz[a / (NS * NS)]) : 0.0;
+      }
+      double* sq = sm + q_base<R, KB>(lane);
+#pragma unroll
+      for (int k = 0; k < 4 * KB; ++k) sq[k] = (double)raw.q[k];
     }
-    double* sw = sm + w_base<R>(lane);
-#pragma unroll
-    for (int a = 0; a < NR; ++a)
-      sw[a] = a < N ? (double)((wx[a % NS] * wy[(a / NS) % NS]) * wz[a / (NS * NS)]) : 0.0;
-    double* sq = sm + q_base<R, KB>(lane);
-#pragma unroll
-    for (int k = 0; k < 4 * KB; ++k) sq[k] = valid && k < nq ? (double)Q[(size_t)p * nq + k] : 0.0;
     __syncthreads();
+    raw = load_mraw<T, KB, PT>(pos, Q, nq, pnext, np);  // next chunk, in flight during the rounds
+    pnext = chunk_perm(j + 2);
 
     const int left = maxn - j * CH;
     const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
@@ -107,25 +166,34 @@ __global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict_
       for (int J = 0; J < KB; ++J) qb[J] = qv[4 * J + mr];
 #pragma unroll
       for (int I = 0; I < NRB; ++I) {
-        const double a = wv[4 * I + mr];
+        double a;
+        if (R == 2)  // W_a = (wx wy) wz in the weights' own type, as staged at order 1
+          a = 4 * I + mr < N ? (double)(((T)wv[ix[I]] * (T)wv[iy[I]]) * (T)wv[iz[I]]) : 0.0;
+        else
+          a = wv[4 * I + mr];
 #pragma unroll
         for (int J = 0; J < KB; ++J) acc[I][J] = mfma_f64_4x4x4(a, qb[J], acc[I][J]);
       }
     }
     __syncthreads();
   }
-  // D_blk[i][j] at lane (i << 4) | (blk << 2) | j: node row 4I + i, quantity 4J + j of bin 4 grp + blk
+  // D_blk[i][j] at lane (i << 4) | (blk << 2) | j: node row 4I + i, quantity 4J + j of bin 4 grp + blk.
+  // The group's records rec[bin][a][k] are contiguous: stage them in LDS and
+  // store them with consecutive lanes on consecutive values.
   const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
-  const int bin = NB * grp + db;
-  if (bin < nbins) {
+  const int b0 = NB * grp;
+  const int nvalid = nbins - b0 < NB ? nbins - b0 : NB;
 #pragma unroll
-    for (int I = 0; I < NRB; ++I)
+  for (int I = 0; I < NRB; ++I)
 #pragma unroll
-      for (int J = 0; J < KB; ++J) {
-        const int a = 4 * I + di, k = 4 * J + dj;
-        if (a < N && k < nq) rec[((size_t)bin * N + a) * nq + k] = acc[I][J];
-      }
-  }
+    for (int J = 0; J < KB; ++J) {
+      const int a = 4 * I + di, k = 4 * J + dj;
+      if (a < N && k < nq && db < nvalid) sm[(db * N + a) * nq + k] = acc[I][J];
+    }
+  __syncthreads();
+  const int nval = nvalid * N * nq;
+  double* dst = rec + (size_t)b0 * N * nq;
+  for (int i = lane; i < nval; i += 64) dst[i] = sm[i];
 }
 
 // m[g][k] (=|+=) sum over the support offsets a of rec[bin g - a][a][k], in a
