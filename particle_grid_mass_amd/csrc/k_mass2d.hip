@@ -73,20 +73,44 @@ __global__ __launch_bounds__(64) void k_mass2d(GridDev g, const PT* __restrict__
 #pragma unroll
     for (int k = 0; k < NBP; ++k) acc[c][k] = 0.0;
 
+  // The particle data of the next chunk, and the permutation entries of the
+  // chunk after it, are in flight while the current chunk is contracted.
+  struct Raw2 {
+    double x, y, w, bx, by, bz;
+    bool valid;
+  };
+  auto chunk_perm = [&](int j) {
+    const int qi = j * CH + (lane & 15);
+    return qi < n_l ? perm[s0 + qi] : -1;
+  };
+  auto load_raw2 = [&](int p) {
+    Raw2 r{0, 0, 0, 0, 0, 0, false};
+    if ((unsigned)p < (unsigned)np) {
+      r.valid = true;
+      r.x = (double)pos[3 * (size_t)p];
+      r.y = (double)pos[3 * (size_t)p + 1];
+      r.w = w[p];
+      if (NC == 9) {
+        r.bx = (double)Bf[3 * (size_t)p];
+        r.by = (double)Bf[3 * (size_t)p + 1];
+        r.bz = (double)Bf[3 * (size_t)p + 2];
+      }
+    }
+    return r;
+  };
+  Raw2 raw = load_raw2(chunk_perm(0));
+  int pnext = chunk_perm(1);
   for (int j = 0; j < nchunks; ++j) {
     // stage one particle per lane: W_a (a = ax + NS ay) and t^c = sigma w alpha^c
-    const int qi = j * CH + (lane & 15);
-    const int p = qi < n_l ? perm[s0 + qi] : -1;
     double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, t[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) t[c] = 0.0;
-    if ((unsigned)p < (unsigned)np) {
-      axis_support<double, R>(grid_coord<double, 0>((double)pos[3 * (size_t)p], g), g.n0, wx);
-      axis_support<double, R>(grid_coord<double, 1>((double)pos[3 * (size_t)p + 1], g), g.n1, wy);
-      const double f = sigma * w[p];
+    if (raw.valid) {
+      axis_support<double, R>(grid_coord<double, 0>(raw.x, g), g.n0, wx);
+      axis_support<double, R>(grid_coord<double, 1>(raw.y, g), g.n1, wy);
+      const double f = sigma * raw.w;
       if (NC == 9)
-        response<double>((double)Bf[3 * (size_t)p], (double)Bf[3 * (size_t)p + 1], (double)Bf[3 * (size_t)p + 2],
-                         beta, f, t);
+        response<double>(raw.bx, raw.by, raw.bz, beta, f, t);
       else
         t[0] = f;
     }
@@ -97,6 +121,8 @@ __global__ __launch_bounds__(64) void k_mass2d(GridDev g, const PT* __restrict__
 #pragma unroll
     for (int c = 0; c < NC; ++c) st[c] = t[c];
     __syncthreads();
+    raw = load_raw2(pnext);  // next chunk, in flight during the rounds
+    pnext = chunk_perm(j + 2);
 
     const int left = maxn - j * CH;
     const int nr = left >= CH ? CH / 4 : (left + 3) / 4;
