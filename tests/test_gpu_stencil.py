@@ -78,7 +78,8 @@ def test_stencil_matvec(seed, order, n, npart, kind, dtype):
 
 
 def test_canonical_two_species_and_matvec_config3():
-    """Two species accumulated into the canonical half at full size, and the
+    """Two species with the two-species configuration's makeup (125 particles
+    per cell, sorted, on 4^3 cells) accumulated into the canonical half, and the
     product from the canonical half against the oracle's from the full M."""
     case = make_config(3, scale=4)
     print(f"[case] canonical two species np={case.np_total}", flush=True)
