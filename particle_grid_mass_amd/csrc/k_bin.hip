@@ -262,6 +262,9 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
   if (*unsorted == 0) return;  // already in key order
   __shared__ int wpre[NWV][256];
   __shared__ int dsum[4];
+  __shared__ int doff[256];          // global position minus tile-local position, per digit
+  __shared__ uint32_t sk[TILE];      // the tile's keys and values in digit order
+  __shared__ int32_t sv[TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
 
@@ -327,23 +330,74 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
     rk[r] = valid ? first + rank : -1;
   }
   __syncthreads();
+  // Tile-local position of (wave, digit tid): the tile's count of smaller
+  // digits plus the counts of digit tid in earlier waves. Where the tile's
+  // digits form short runs (fewer than 16 particles per digit on average, as
+  // for shuffled input), the particles are placed in LDS in that order and
+  // written out by consecutive threads, so that each digit's run is one
+  // contiguous stretch of stores. Longer runs are already contiguous enough
+  // in the direct stores, and the LDS pass would only add to them.
+  const size_t t0 = (size_t)tile * TILE;
+  const int nvalid = (size_t)np - t0 < (size_t)TILE ? (int)((size_t)np - t0) : TILE;
+  bool staged;
   {
-    int run = dbase;
+    int cnt_d = 0;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) {
-      wpre[w][tid] = run;
-      run += wcnt[w][tid];
+      wpre[w][tid] = cnt_d;
+      cnt_d += wcnt[w][tid];
+    }
+    int inc = cnt_d;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    if (lane == 63) dsum[wave] = inc;  // every thread read dsum for dbase before the barrier above
+    const int ndigits = __syncthreads_count(cnt_d > 0);
+    staged = ndigits * 16 > nvalid;
+    int lbase = inc - cnt_d;
+    for (int w = 0; w < wave; ++w) lbase += dsum[w];
+    doff[tid] = dbase - lbase;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) wpre[w][tid] += lbase;
+  }
+  __syncthreads();
+  if (!staged) {
+#pragma unroll
+    for (int r = 0; r < BI; ++r) {
+      if (rk[r] >= 0) {
+        const int d = (int)((k[r] >> shift) & 255u);
+        const int dst = doff[d] + wpre[wave][d] + rk[r];
+        if ((unsigned)dst < (unsigned)np) {  // always true for consistent inputs; guards the writes
+          keys_out[dst] = k[r];
+          vals_out[dst] = v[r];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < BI; ++r) {
+    if (rk[r] >= 0) {
+      const int d = (int)((k[r] >> shift) & 255u);
+      const int lp = wpre[wave][d] + rk[r];
+      if ((unsigned)lp < (unsigned)TILE) {  // always true for consistent inputs; guards the LDS
+        sk[lp] = k[r];
+        sv[lp] = v[r];
+      }
     }
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < BI; ++r) {
-    if (rk[r] >= 0) {
-      const int d = (int)((k[r] >> shift) & 255u);
-      const int dst = wpre[wave][d] + rk[r];
+    const int i = r * BT + tid;
+    if (i < nvalid) {
+      const uint32_t kk = sk[i];
+      const int dst = doff[(kk >> shift) & 255u] + i;
       if ((unsigned)dst < (unsigned)np) {  // always true for consistent inputs; guards the writes
-        keys_out[dst] = k[r];
-        vals_out[dst] = v[r];
+        keys_out[dst] = kk;
+        vals_out[dst] = sv[i];
       }
     }
   }
