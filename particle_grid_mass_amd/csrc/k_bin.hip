@@ -339,28 +339,31 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
   // in the direct stores, and the LDS pass would only add to them.
   const size_t t0 = (size_t)tile * TILE;
   const int nvalid = (size_t)np - t0 < (size_t)TILE ? (int)((size_t)np - t0) : TILE;
-  bool staged;
-  {
-    int cnt_d = 0;
+  int cnt_d = 0;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      wpre[w][tid] = cnt_d;
-      cnt_d += wcnt[w][tid];
-    }
+  for (int w = 0; w < NWV; ++w) cnt_d += wcnt[w][tid];
+  const bool staged = __syncthreads_count(cnt_d > 0) * 16 > nvalid;  // block-uniform
+  // wpre[w][d]: output position (direct stores) or tile-local position
+  // (staged) of wave w's first particle with digit d
+  int run = dbase;
+  if (staged) {
     int inc = cnt_d;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(inc, off);
       if (lane >= off) inc += y;
     }
-    if (lane == 63) dsum[wave] = inc;  // every thread read dsum for dbase before the barrier above
-    const int ndigits = __syncthreads_count(cnt_d > 0);
-    staged = ndigits * 16 > nvalid;
+    if (lane == 63) dsum[wave] = inc;  // every thread read dsum for dbase before the barriers above
+    __syncthreads();
     int lbase = inc - cnt_d;
     for (int w = 0; w < wave; ++w) lbase += dsum[w];
     doff[tid] = dbase - lbase;
+    run = lbase;
+  }
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) wpre[w][tid] += lbase;
+  for (int w = 0; w < NWV; ++w) {
+    wpre[w][tid] = run;
+    run += wcnt[w][tid];
   }
   __syncthreads();
   if (!staged) {
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
     for (int r = 0; r < BI; ++r) {
       if (rk[r] >= 0) {
         const int d = (int)((k[r] >> shift) & 255u);
-        const int dst = doff[d] + wpre[wave][d] + rk[r];
+        const int dst = wpre[wave][d] + rk[r];
         if ((unsigned)dst < (unsigned)np) {  // always true for consistent inputs; guards the writes
           keys_out[dst] = k[r];
           vals_out[dst] = v[r];
