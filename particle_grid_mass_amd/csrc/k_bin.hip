@@ -411,16 +411,32 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
 // (with skeys[-1] = -1 and skeys[np] = nbins), so each entry is written once.
 // Input already in key order: k_keys_hist has written bin_start and perm.
 // Grid-stride over i = 0..np with a capped grid, so that the launch is cheap
-// when the input was already in key order.
+// when the input was already in key order; the keys of UB strides are loaded
+// before any is used, so that UB loads per thread are in flight at once.
 __global__ void k_bounds(const uint32_t* __restrict__ skeys, int np, int nbins, int32_t* __restrict__ bin_start,
                          const int32_t* __restrict__ unsorted) {
   if (*unsorted == 0) return;
+  constexpr int UB = 4;
   const int stride = gridDim.x * blockDim.x;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= np; i += stride) {
-    const int lo = i == 0 ? -1 : (int)skeys[i - 1];
-    int hi = i == np ? nbins : (int)skeys[i];
-    hi = hi > nbins ? nbins : hi;
-    for (int k = lo + 1; k <= hi; ++k) bin_start[k] = i;
+  // 64-bit counter: with np just below 2^31 the last strides pass INT_MAX
+  for (long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x; i0 <= np; i0 += (long long)UB * stride) {
+    int lo[UB], hi[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const long long i = i0 + (long long)u * stride;
+      lo[u] = -1;
+      hi[u] = -1;  // no entry for i beyond np
+      if (i <= np) {
+        lo[u] = i == 0 ? -1 : (int)skeys[i - 1];
+        hi[u] = i == np ? nbins : (int)skeys[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = (int)(i0 + (long long)u * stride);  // used only where i <= np
+      const int h = hi[u] > nbins ? nbins : hi[u];
+      for (int k = lo[u] + 1; k <= h; ++k) bin_start[k] = i;
+    }
   }
 }
 
