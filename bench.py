@@ -7,8 +7,9 @@ every species of the workload: binning (stable counting sort by support
 group), per-bin matrix-core contraction, and stencil deposition. Inputs are
 seeded synthetic particles already resident in HBM when timing starts.
 
-Default workload: CIC ECSIM fp64 on a 32^3 periodic grid with 64 particles
-per cell (2,097,152 particles), beta = 0.5, sigma = 1.
+Default workload: TSC ECSIM fp64 on a 128^3 periodic grid with a clustered
+density (134,217,728 particles, mean 64 per cell, four Gaussian clusters),
+beta = 0.5, sigma = 1: the largest of the five workloads, one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--kind K]
                     [--dtype f64|f32] [--shuffled] [--algo A] [--no-cpu-baseline]
@@ -186,6 +187,72 @@ def onbox_peaks(dev, stream):
                    "1 GiB torch copy_, read + write bytes"}
 
 
+def host_info():
+    """Where the CPU baseline ran: logical CPUs of the host, CPUs this process
+    may use, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def sampled_rows_parity(case, M, nof, ncomp, Fgrid=None, nsample=44, seed=55):
+    """Exact oracle rows of the assembled matrix for sampled nodes: random nodes,
+    the two corner nodes and, on the clustered workload, the four cluster
+    centres (the densest bins). Only particles whose cell lies within three
+    cells of a sampled node along every axis (periodically) can reach those
+    rows, so only they are passed to the oracle. Single species, field per
+    particle."""
+    import numpy as np
+    import torch
+    import oracle
+    sp = case.species[0]
+    n = [int(v) for v in case.grid.n]
+    nn = case.grid.ncells
+    rng = np.random.default_rng(seed)
+    extra = [0, nn - 1]
+    if case.name.startswith("c5"):
+        q = n[0] // 4
+        extra += [x + n[0] * (y + n[1] * z) for (x, y, z) in
+                  ((q, q, q), (3 * q, 3 * q, q), (3 * q, q, 3 * q), (q, 3 * q, 3 * q))]
+    nodes = np.unique(np.concatenate([rng.integers(0, nn, nsample), extra]).astype(np.int64))
+    near = np.zeros(nn, dtype=bool).reshape(n[2], n[1], n[0])
+    span = np.arange(-3, 4)
+    for g in nodes:
+        gx, gy, gz = g % n[0], (g // n[0]) % n[1], g // (n[0] * n[1])
+        near[np.ix_((gz + span) % n[2], (gy + span) % n[1], (gx + span) % n[0])] = True
+    pos = np.asarray(sp.pos, dtype=np.float64)
+    cell = np.zeros(pos.shape[0], dtype=np.int64)
+    for d in (2, 1, 0):
+        j = np.floor((pos[:, d] - case.grid.origin[d]) / case.grid.h[d]).astype(np.int64) % n[d]
+        cell = cell * n[d] + j
+    sel = np.flatnonzero(near.reshape(-1)[cell])
+    beta, sigma = sp.beta, case.sigma
+    if case.dtype == "f32":
+        beta, sigma = float(np.float32(beta)), float(np.float32(sigma))
+    B = None
+    if case.kind == "ecsim":
+        B = sp.B[sel] if Fgrid is None else oracle.interp_field(case.order, n, case.grid.origin, case.grid.h,
+                                                                pos[sel], Fgrid)
+    ref = oracle.rows(case.order, n, case.grid.origin, case.grid.h, pos[sel], np.asarray(sp.w, np.float64)[sel],
+                      nodes, B, beta, sigma)
+    got = M.view(nn, nof * ncomp)[torch.from_numpy(nodes).to(M.device)].double().cpu().numpy().reshape(ref.shape)
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    emax = float(np.abs(got - ref).max() / np.abs(ref).max())
+    return {"kind": "exact oracle rows of sampled nodes", "nodes": int(nodes.size), "particles_scanned": int(sel.size),
+            "rel_fro": err, "max_abs_err_over_max_abs": emax}
+
+
 def cpu_baseline(case, budget_s: float, Fgrid=None):
     """The oracle as it stands, on the host cores, on a bounded sample. With a
     field on the grid nodes the oracle gathers it at the particles first, and
@@ -199,14 +266,13 @@ def cpu_baseline(case, budget_s: float, Fgrid=None):
             return None
         if Fgrid is None:
             return sp.B[:k]
-        return oracle.interp_field(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:k], Fgrid,
-                                   prec32=case.dtype == "f32")
+        return oracle.interp_field(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:k], Fgrid)
     # whole species if it fits the budget estimate, else a cell-sorted prefix (a slab of cells)
     sample = sp.np
     t0 = time.perf_counter()
     probe = min(sp.np, 200_000)
     oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:probe], sp.w[:probe],
-                    field(probe), sp.beta, case.sigma, prec32=case.dtype == "f32")
+                    field(probe), sp.beta, case.sigma)
     rate_guess = probe / max(time.perf_counter() - t0, 1e-6)
     if sp.np / rate_guess > budget_s:
         sample = int(rate_guess * budget_s)
@@ -214,7 +280,7 @@ def cpu_baseline(case, budget_s: float, Fgrid=None):
     while True:
         t0 = time.perf_counter()
         Mref = oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos[:sample],
-                               sp.w[:sample], field(sample), sp.beta, case.sigma, prec32=case.dtype == "f32")
+                               sp.w[:sample], field(sample), sp.beta, case.sigma)
         total_t += time.perf_counter() - t0
         reps += 1
         if total_t >= budget_s or reps >= 100:
@@ -222,8 +288,9 @@ def cpu_baseline(case, budget_s: float, Fgrid=None):
     value = sample * reps / total_t
     desc = (f"species 0 of the workload, {'all' if sample == sp.np else 'first'} {sample:,} particles"
             f"{'' if sample == sp.np else ' (cell-sorted prefix: a slab of cells)'}, {reps} run(s)")
-    return {"value": value, "unit": "particles/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": desc}, (Mref if sample == sp.np else None)
+    out = {"value": value, "unit": "particles/s", "cores": oracle.max_threads(), "kind": "oracle", "sample": desc}
+    out.update(host_info())
+    return out, (Mref if sample == sp.np else None)
 
 
 def main():
@@ -231,7 +298,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--kind", default=None, help="scalar|ecsim where the config offers both (config 4)")
     ap.add_argument("--dtype", default="f64", choices=("f64", "f32", "mix"),
                     help="f64, f32, or mix: fp32 positions and fields with fp64 weights, matrix and arithmetic")
@@ -606,6 +673,7 @@ def main():
     # parity of this run's output against the oracle (and the CPU baseline timing)
     cpu = None
     parity = None
+    parity_rows = None
     if not args.no_cpu_baseline:
         cpu, Mref = cpu_baseline(case, args.cpu_budget, Fgrid)
         if Mref is not None and len(spec) == 1:
@@ -614,6 +682,9 @@ def main():
                 import oracle
                 Mref = oracle.canonical_half(order, Mref)
             parity = float(np.linalg.norm(got - Mref.reshape(got.shape)) / np.linalg.norm(Mref))
+        elif len(spec) == 1 and not args.canonical and args.dims == 3:
+            parity_rows = sampled_rows_parity(case, M, nof, ncomp, Fgrid)
+        print("[bench] cpu baseline and parity done", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -646,6 +717,7 @@ def main():
         "cold_mall": cold,
         "cpu_baseline": cpu,
         "parity_rel_fro_vs_oracle": parity,
+        "parity_sampled_rows_vs_oracle": parity_rows,
     }
     print(json.dumps(line), flush=True)
 

@@ -34,9 +34,13 @@
  *           mm_assemble_ecsim, mm_contract_bins and mm_deposit_records (the
  *           records are fp64); every other combination is
  *           MM_ERR_UNSUPPORTED.
- *  dtype:   MM_F64: pos, w, B and M are double. MM_F32: all four are float,
- *           the cell decision, weights and matrix-core accumulation run in
- *           fp32 (sigma and beta are rounded to fp32). MM_MIX: the
+ *  dtype:   MM_F64: pos, w, B and M are double. MM_F32: all four are float;
+ *           the cell decision (floor of u, the TSC half-cell test, the bin
+ *           key) is taken in fp64 on the stored fp32 position, which fp64
+ *           holds exactly, so a particle is placed as its exact value is;
+ *           the weights, the response tensor and the matrix-core
+ *           accumulation run in fp32 (sigma and beta are rounded to fp32).
+ *           MM_MIX: the
  *           production layout of Sec. 5 ("Exactness and precision"):
  *           positions and fields (pos, B, Bgrid) are float, weights w,
  *           quantities Q, vectors x, y and the outputs M, m are double, and
@@ -71,7 +75,9 @@ typedef enum {
   MM_OK = 0,
   MM_ERR_NULL = 1,        /* a required pointer is NULL */
   MM_ERR_ARG = 2,         /* order, dtype, grid, sigma/beta or algo out of range */
-  MM_ERR_UNSUPPORTED = 3, /* np or node count at or above 2^31 */
+  MM_ERR_UNSUPPORTED = 3, /* np or node count at or above 2^31, or a combination of dtype,
+                             algorithm, field placement and grid dimension that is not
+                             implemented (each entry point lists its own) */
   MM_ERR_WORKSPACE = 4,   /* *ws_bytes smaller than required */
   MM_ERR_HIP = 5          /* a HIP launch or runtime call failed */
 } mm_status;
@@ -201,6 +207,18 @@ mm_status mm_contract_bins_gridB(const mm_grid* grid, int order, mm_dtype dt, in
                                  double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream);
 mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
                              int accumulate, void* M, mm_stream_t stream);
+
+/*
+ * mm_record_bytes - size in bytes of the records that mm_deposit_records,
+ * mm_deposit_records_canonical and mm_deposit_records_multi read for this
+ * grid, order, dtype (of M) and kind: the first part of the buffer that
+ * mm_contract_bins fills (its own size query may add room after them). The
+ * deposit entry points take no record length, so a caller that holds records
+ * of unknown origin checks their size against this first. Nothing is enqueued.
+ *  bytes  host output; NULL -> MM_ERR_NULL. Grid, order and dtype errors as
+ *         for mm_deposit_records.
+ */
+mm_status mm_record_bytes(const mm_grid* grid, int order, mm_dtype dt, int tensorial, size_t* bytes);
 
 /*
  * mm_deposit_records_canonical - mm_deposit_records into the canonical half of

@@ -51,13 +51,13 @@ def _load():
     I64 = ctypes.c_int64
     D = ctypes.c_double
     lib.oracle_alpha.argtypes = [P, D, P]
-    lib.oracle_support.argtypes = [I, I, P, P, P, P, P, P]
-    lib.oracle_assemble.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I, P, I]
-    lib.oracle_bin.argtypes = [I, I, P, P, P, I64, P, P, P]
-    lib.oracle_bilinear.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, P, P, P]
-    lib.oracle_rows.argtypes = [I, I, P, P, P, I64, P, P, P, D, D, I64, P, P]
-    lib.oracle_interp_field.argtypes = [I, I, P, P, P, I64, P, P, P]
-    lib.oracle_moments.argtypes = [I, I, P, P, P, I64, P, I, P, I, P]
+    lib.oracle_support.argtypes = [I, P, P, P, P, P, P]
+    lib.oracle_assemble.argtypes = [I, P, P, P, I64, P, P, P, D, D, I, P, I]
+    lib.oracle_bin.argtypes = [I, P, P, P, I64, P, P, P]
+    lib.oracle_bilinear.argtypes = [I, P, P, P, I64, P, P, P, D, D, P, P, P]
+    lib.oracle_rows.argtypes = [I, P, P, P, I64, P, P, P, D, D, I64, P, P]
+    lib.oracle_interp_field.argtypes = [I, P, P, P, I64, P, P, P]
+    lib.oracle_moments.argtypes = [I, P, P, P, I64, P, I, P, I, P]
     lib.oracle_max_threads.argtypes = []
     for f in (lib.oracle_alpha, lib.oracle_support, lib.oracle_assemble, lib.oracle_bin,
               lib.oracle_bilinear, lib.oracle_rows, lib.oracle_interp_field, lib.oracle_moments,
@@ -107,19 +107,19 @@ def alpha(B, beta: float) -> np.ndarray:
     return out.reshape(3, 3)
 
 
-def support(order, n, origin, h, x, prec32=False):
+def support(order, n, origin, h, x):
     """First support node (wrapped) and per-dimension 1D weights ``[3, 3]``."""
     n_, o_, h_ = _grid_args(n, origin, h)
     x = _f64(x)
     first = np.empty(3, dtype=np.int32)
     w1d = np.empty(9)
-    _check(_load().oracle_support(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), _ptr(x), _ptr(first),
+    _check(_load().oracle_support(order, _ptr(n_), _ptr(o_), _ptr(h_), _ptr(x), _ptr(first),
                                   _ptr(w1d)), "support")
     return first, w1d.reshape(3, 3)
 
 
 def assemble(order, n, origin, h, pos, w, B=None, beta=0.0, sigma=1.0, M=None, accumulate=False,
-             prec32=False, nthreads=0) -> np.ndarray:
+             nthreads=0) -> np.ndarray:
     """Mass matrix ``[nnodes, noff, ncomp]`` by direct scatter (scalar if ``B is None``)."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos, w, B = _f64(pos), _f64(w), _f64(B)
@@ -131,13 +131,13 @@ def assemble(order, n, origin, h, pos, w, B=None, beta=0.0, sigma=1.0, M=None, a
         M = np.zeros(shape)
         accumulate = False
     assert M.shape == shape and M.dtype == np.float64 and M.flags.c_contiguous
-    _check(_load().oracle_assemble(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
+    _check(_load().oracle_assemble(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
                                    _ptr(B), float(beta), float(sigma), int(bool(accumulate)), _ptr(M),
                                    int(nthreads)), "assemble")
     return M
 
 
-def bin_particles(order, n, origin, h, pos, prec32=False):
+def bin_particles(order, n, origin, h, pos):
     """Stable counting sort by first support node: ``(bin_start[nbins+1], perm[np])``."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos = _f64(pos)
@@ -145,23 +145,23 @@ def bin_particles(order, n, origin, h, pos, prec32=False):
     nbins = int(np.prod(n_.astype(np.int64)))
     bin_start = np.empty(nbins + 1, dtype=np.int32)
     perm = np.empty(max(npart, 1), dtype=np.int32)
-    _check(_load().oracle_bin(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(bin_start),
+    _check(_load().oracle_bin(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(bin_start),
                               _ptr(perm)), "bin")
     return bin_start, perm[:npart]
 
 
-def bilinear(order, n, origin, h, pos, w, u, v, B=None, beta=0.0, sigma=1.0, prec32=False) -> float:
+def bilinear(order, n, origin, h, pos, w, u, v, B=None, beta=0.0, sigma=1.0) -> float:
     """``sigma * sum_p (W_p u)^T s_p (W_p v)``; u, v are ``[nnodes, 3]`` (tensorial) or ``[nnodes]``."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos, w, B, u, v = _f64(pos), _f64(w), _f64(B), _f64(u), _f64(v)
     npart = pos.reshape(-1, 3).shape[0]
     out = np.zeros(1)
-    _check(_load().oracle_bilinear(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
+    _check(_load().oracle_bilinear(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w),
                                    _ptr(B), float(beta), float(sigma), _ptr(u), _ptr(v), _ptr(out)), "bilinear")
     return float(out[0])
 
 
-def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32=False) -> np.ndarray:
+def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0) -> np.ndarray:
     """Exact stencil rows ``[len(nodes), noff, ncomp]`` for selected nodes."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos, w, B = _f64(pos), _f64(w), _f64(B)
@@ -169,12 +169,12 @@ def rows(order, n, origin, h, pos, w, nodes, B=None, beta=0.0, sigma=1.0, prec32
     npart = pos.reshape(-1, 3).shape[0]
     ncomp = 1 if B is None else 9
     out = np.zeros((len(nodes), noff_grid(order, n_), ncomp))
-    _check(_load().oracle_rows(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
+    _check(_load().oracle_rows(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(w), _ptr(B),
                                float(beta), float(sigma), len(nodes), _ptr(nodes), _ptr(out)), "rows")
     return out
 
 
-def moments(order, n, origin, h, pos, Q, m=None, accumulate=False, prec32=False) -> np.ndarray:
+def moments(order, n, origin, h, pos, Q, m=None, accumulate=False) -> np.ndarray:
     """Deposit of per-particle quantities ``Q [np, nq]``: ``m[g][k] = sum_p W_pg Q_p[k]``, ``[nnodes, nq]``."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos, Q = _f64(pos), _f64(Q)
@@ -185,18 +185,18 @@ def moments(order, n, origin, h, pos, Q, m=None, accumulate=False, prec32=False)
         m = np.zeros((nnodes, nq))
         accumulate = False
     assert m.shape == (nnodes, nq) and m.dtype == np.float64 and m.flags.c_contiguous
-    _check(_load().oracle_moments(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), int(nq),
+    _check(_load().oracle_moments(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), int(nq),
                                   _ptr(Q), int(bool(accumulate)), _ptr(m)), "moments")
     return m
 
 
-def interp_field(order, n, origin, h, pos, F, prec32=False) -> np.ndarray:
+def interp_field(order, n, origin, h, pos, F) -> np.ndarray:
     """Particle values ``[np, 3]`` of the nodal field ``F[nnodes, 3]``: sum_a W_pa F[g_a]."""
     n_, o_, h_ = _grid_args(n, origin, h)
     pos, F = _f64(pos), _f64(F)
     npart = pos.reshape(-1, 3).shape[0]
     out = np.zeros((npart, 3))
-    _check(_load().oracle_interp_field(order, int(prec32), _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(F),
+    _check(_load().oracle_interp_field(order, _ptr(n_), _ptr(o_), _ptr(h_), npart, _ptr(pos), _ptr(F),
                                        _ptr(out)), "interp_field")
     return out
 

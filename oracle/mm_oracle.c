@@ -31,9 +31,9 @@
  *    offset = (dx+R) + (2R+1)*((dy+R) + (2R+1)*(dz+R)) for the node-pair
  *    displacement d = g' - g in [-R, R]^3; comp = 3*i + j (ncomp = 9) or 0.
  *
- * Precision: fp64 throughout. When prec32 != 0 the inputs hold fp32 values and
- * the cell index and fraction are found in fp32 arithmetic (the precision in
- * which the fp32 kernels take that integer decision); weights and sums stay fp64.
+ * Precision: fp64 throughout, on the values passed in. An fp32 workload is
+ * given to the oracle as its fp32-rounded inputs (exact in fp64), so the
+ * oracle is fp64 arithmetic on the fp32 inputs, the cell decision included.
  *
  * Determinism: the parallel scatter runs z-slabs of particles in two colours;
  * slabs of one colour touch disjoint node planes, so every entry's summation
@@ -53,7 +53,6 @@
 
 typedef struct {
   int order;          /* 1 = CIC, 2 = TSC */
-  int prec32;         /* take the cell decision in fp32 */
   int32_t n[3];
   double origin[3];
   double h[3];
@@ -79,19 +78,13 @@ static int32_t wrap_index(int64_t k, int32_t n) {
   return (int32_t)(r < 0 ? r + n : r);
 }
 
-/* Cell index j (unwrapped) and fraction xi in [0,1) of one coordinate. */
+/* Cell index j (unwrapped) and fraction xi in [0,1) of one coordinate, in fp64
+ * (IEEE division, as Sec. 2.3 reads: u = (x - origin) / h). */
 static void cell_and_fraction(const or_grid* g, int d, double x, int64_t* j, double* xi) {
-  if (g->prec32) {
-    float u = ((float)x - (float)g->origin[d]) / (float)g->h[d];
-    float fl = floorf(u);
-    *j = (int64_t)fl;
-    *xi = (double)u - (double)fl; /* exact: u - floor(u) is representable */
-  } else {
-    double u = (x - g->origin[d]) / g->h[d];
-    double fl = floor(u);
-    *j = (int64_t)fl;
-    *xi = u - fl;
-  }
+  double u = (x - g->origin[d]) / g->h[d];
+  double fl = floor(u);
+  *j = (int64_t)fl;
+  *xi = u - fl;
 }
 
 /* Support rule and 1D B-spline weights (Sec. 2.3). */
@@ -162,11 +155,10 @@ int oracle_alpha(const double* B, double beta, double* alpha) {
 }
 
 /* Support of one particle, exported for tests: first[3] and w1d[3][3]. */
-int oracle_support(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_support(int order, const int32_t* n, const double* origin, const double* h,
                    const double* x, int32_t* first, double* w1d) {
   or_grid g;
   g.order = order;
-  g.prec32 = prec32;
   for (int d = 0; d < 3; ++d) {
     g.n[d] = n[d];
     g.origin[d] = origin[d];
@@ -224,11 +216,10 @@ static void scatter_particle(const or_grid* g, const double* x, double w, const 
   }
 }
 
-static int fill_grid(or_grid* g, int order, int prec32, const int32_t* n, const double* origin,
+static int fill_grid(or_grid* g, int order, const int32_t* n, const double* origin,
                      const double* h) {
   if (!n || !origin || !h) return 0;
   g->order = order;
-  g->prec32 = prec32;
   for (int d = 0; d < 3; ++d) {
     g->n[d] = n[d];
     g->origin[d] = origin[d];
@@ -243,11 +234,11 @@ static int fill_grid(or_grid* g, int order, int prec32, const int32_t* n, const 
  * M has nnodes*noff*ncomp doubles; it is zeroed first unless accumulate != 0.
  * nthreads <= 0 uses the OpenMP default.
  */
-int oracle_assemble(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_assemble(int order, const int32_t* n, const double* origin, const double* h,
                     int64_t np, const double* pos, const double* w, const double* B, double beta,
                     double sigma, int accumulate, double* M, int nthreads) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || !M || np < 0) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || !M || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
   const int R = order;
   const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];
@@ -329,10 +320,10 @@ int oracle_max_threads(void) {
  * bin_start[k] = number of particles with key < k (nbins+1 entries),
  * perm lists particle indices bin by bin, ascending within a bin.
  */
-int oracle_bin(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_bin(int order, const int32_t* n, const double* origin, const double* h,
                int64_t np, const double* pos, int32_t* bin_start, int32_t* perm) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || !bin_start || np < 0) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || !bin_start || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !perm)) return OR_ERR_ARG;
   const int64_t nbins = (int64_t)n[0] * n[1] * n[2];
   int32_t* key = (int32_t*)malloc((size_t)(np > 0 ? np : 1) * sizeof(int32_t));
@@ -361,11 +352,11 @@ int oracle_bin(int order, int prec32, const int32_t* n, const double* origin, co
  *   out = sigma * sum_p (W_p u)^T s_p (W_p v),   (W_p u)_i = sum_a W_pa u[g_a][i]
  * u, v hold nnodes*ncomp_vec values (ncomp_vec = 3 tensorial, 1 scalar).
  */
-int oracle_bilinear(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_bilinear(int order, const int32_t* n, const double* origin, const double* h,
                     int64_t np, const double* pos, const double* w, const double* B, double beta,
                     double sigma, const double* u, const double* v, double* out) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || !u || !v || !out || np < 0) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || !u || !v || !out || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
   const int NS = order + 1, nsup = nsup_of(&g);
   const int nv = B ? 3 : 1;
@@ -405,11 +396,11 @@ int oracle_bilinear(int order, int prec32, const int32_t* n, const double* origi
  * particle: rows[s][offset][comp] for node sel[s]. Used where the full output
  * is too large to hold on the host.
  */
-int oracle_rows(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_rows(int order, const int32_t* n, const double* origin, const double* h,
                 int64_t np, const double* pos, const double* w, const double* B, double beta,
                 double sigma, int64_t nsel, const int64_t* sel, double* rows) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || !rows || np < 0 || nsel < 0) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || !rows || np < 0 || nsel < 0) return OR_ERR_ARG;
   if (nsel > 0 && !sel) return OR_ERR_ARG;
   if (np > 0 && (!pos || !w)) return OR_ERR_ARG;
   const int R = order, NS = R + 1, NO = 2 * R + 1, nsup = nsup_of(&g), noff = noff_of(&g), RZ = is2d(&g) ? 0 : R;
@@ -485,10 +476,10 @@ int oracle_rows(int order, int prec32, const int32_t* n, const double* origin, c
  * nodes as M and is gathered with the same weights is a reading, the plainest
  * one the page supports.
  */
-int oracle_interp_field(int order, int prec32, const int32_t* n, const double* origin, const double* h,
+int oracle_interp_field(int order, const int32_t* n, const double* origin, const double* h,
                         int64_t np, const double* pos, const double* F, double* out) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || np < 0) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || np < 0) return OR_ERR_ARG;
   if (np > 0 && (!pos || !F || !out)) return OR_ERR_ARG;
   const int NS = order + 1, nsup = nsup_of(&g);
 #pragma omp parallel for schedule(static)
@@ -517,10 +508,10 @@ int oracle_interp_field(int order, int prec32, const int32_t* n, const double* o
  * Q holds np*nq values (particle-major), m holds nnodes*nq and is zeroed
  * first unless accumulate != 0. Serial, particle by particle.
  */
-int oracle_moments(int order, int prec32, const int32_t* n, const double* origin, const double* h, int64_t np,
+int oracle_moments(int order, const int32_t* n, const double* origin, const double* h, int64_t np,
                    const double* pos, int nq, const double* Q, int accumulate, double* m) {
   or_grid g;
-  if (!fill_grid(&g, order, prec32, n, origin, h) || !m || np < 0 || nq < 1) return OR_ERR_ARG;
+  if (!fill_grid(&g, order, n, origin, h) || !m || np < 0 || nq < 1) return OR_ERR_ARG;
   if (np > 0 && (!pos || !Q)) return OR_ERR_ARG;
   const int NS = order + 1, nsup = nsup_of(&g);
   const int64_t nnodes = (int64_t)n[0] * n[1] * n[2];

@@ -64,6 +64,16 @@ def _check_tensor(t: torch.Tensor, name: str, dtype, shape_tail=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_bins(bin_start: torch.Tensor, perm: torch.Tensor, nnodes: int, npart: int):
+    """The binning arrays must match the grid and the particles they index:
+    bin_start holds nnodes + 1 entries and perm at least one per particle
+    (the kernels read bin_start[0..nnodes] and perm[bin_start[k] ..])."""
+    if bin_start.numel() != nnodes + 1:
+        raise ValueError(f"bin_start has {bin_start.numel()} entries, expected nnodes + 1 = {nnodes + 1}")
+    if perm.numel() < npart:
+        raise ValueError(f"perm has {perm.numel()} entries, fewer than the {npart} particles")
+
+
 def _call(fn, what, *args):
     st = fn(*args)
     if st != _lib.MM_OK:
@@ -92,9 +102,10 @@ def noff(order: int) -> int:
 def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch.Tensor] = None,
                   perm: Optional[torch.Tensor] = None, mixed: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Stable counting sort by first support node -> ``(bin_start[nbins+1], perm[np])`` (int32).
-    ``mixed``: float32 positions binned in fp64 arithmetic, as the mixed layout
-    (fp32 positions, fp64 weights) assembles them; otherwise float32 positions
-    are binned in fp32."""
+    The key is found in fp64 arithmetic for float32 positions too (the
+    stored value read exactly), as every assembly path places particles;
+    ``mixed`` names the mixed layout (float32 positions, float64 weights)
+    and bins the same way."""
     lib = _lib.load()
     g = _grid_of(grid)
     dt = pos.dtype
@@ -111,6 +122,7 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
         perm = torch.empty(max(npart, 1), dtype=torch.int32, device=dev)
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
+    _check_bins(bin_start, perm, _nnodes(g), npart)
     s = _stream(dev)
     head = (ctypes.byref(g), int(order), _lib.MM_MIX if mixed else _DT[dt], npart, _ptr(pos), _ptr(bin_start),
             _ptr(perm))
@@ -141,6 +153,7 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
             raise ValueError("the matrix-core algorithms need bin_start and perm from bin_particles")
         _check_tensor(bin_start, "bin_start", torch.int32)
         _check_tensor(perm, "perm", torch.int32)
+        _check_bins(bin_start, perm, _nnodes(g), npart)
     ncomp = 9 if kind == "ecsim" else 1
     nof = noff_grid(order, g)
     shape = (_nnodes(g), nof, ncomp) if ncomp == 9 else (_nnodes(g), nof)
@@ -214,6 +227,9 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
     npart = pos.numel() // 3
+    if w.numel() != npart or (B is not None and B.numel() != 3 * npart):
+        raise ValueError("pos, w and B disagree on the particle count")
+    _check_bins(bin_start, perm, _nnodes(g), npart)
     s = _stream(pos.device)
     if Bgrid is not None:
         fn, name = lib.mm_contract_bins_gridB, "mm_contract_bins_gridB"
@@ -239,6 +255,34 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     return rec
 
 
+def record_bytes(grid, order: int, dtype: torch.dtype, tensorial: bool) -> int:
+    """Bytes of the per-bin records that a deposition of this grid, order, output
+    dtype and kind reads (the records mm_contract_bins writes first)."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    nbytes = ctypes.c_size_t(0)
+    _call(lib.mm_record_bytes, "mm_record_bytes", ctypes.byref(g), int(order), _DT[dtype], int(bool(tensorial)),
+          ctypes.byref(nbytes))
+    return int(nbytes.value)
+
+
+def _check_records(lib, g, order, dtype, tensorial, rec, M):
+    """A record set must be a device tensor on M's device holding at least the
+    bytes the deposition reads (records of another grid, order, dtype or kind
+    would be read out of bounds)."""
+    if not isinstance(rec, torch.Tensor) or not rec.is_cuda or rec.device != M.device:
+        raise ValueError("record sets must be device tensors on M's device")
+    if not rec.is_contiguous():
+        raise ValueError("record sets must be contiguous")
+    need = record_bytes(g, order, dtype, tensorial)
+    have = rec.numel() * rec.element_size()
+    if have < need:
+        raise ValueError(f"record set holds {have} bytes, the deposition reads {need} "
+                         f"(records of another grid, order, dtype or kind?)")
+
+
 def noff_canonical(order: int) -> int:
     """Offsets kept in the canonical half of the stencil: 14 (CIC) or 63 (TSC)."""
     return (noff(order) + 1) // 2
@@ -261,6 +305,7 @@ def deposit_records(grid, order: int, rec, M: torch.Tensor, tensorial: bool,
     nof = noff_canonical(order) if canonical else noff_grid(order, g)
     if M.numel() != _nnodes(g) * nof * ncomp:
         raise ValueError("M has the wrong number of elements")
+    _check_records(lib, g, order, M.dtype, tensorial, rec, M)
     fn, name = ((lib.mm_deposit_records_canonical, "mm_deposit_records_canonical") if canonical
                 else (lib.mm_deposit_records, "mm_deposit_records"))
     _call(fn, name, ctypes.byref(g), int(order), _DT[M.dtype], int(bool(tensorial)), _ptr(rec),
@@ -280,8 +325,7 @@ def _deposit_multi(lib, grid, order, recs, M, tensorial, accumulate, canonical):
     if M.numel() != _nnodes(g) * nof * ncomp:
         raise ValueError("M has the wrong number of elements")
     for r in recs:
-        if not r.is_cuda or r.device != M.device:
-            raise ValueError("record sets must be device tensors on M's device")
+        _check_records(lib, g, order, M.dtype, tensorial, r, M)
     arr = (ctypes.c_void_p * len(recs))(*[r.data_ptr() for r in recs])
     _call(lib.mm_deposit_records_multi, "mm_deposit_records_multi", ctypes.byref(g), int(order), _DT[M.dtype],
           int(bool(tensorial)), int(bool(canonical)), len(recs), arr, int(bool(accumulate)), _ptr(M),
@@ -336,6 +380,7 @@ def deposit_moments(grid, order: int, pos: torch.Tensor, Q: torch.Tensor, bin_st
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
     nn = _nnodes(g)
+    _check_bins(bin_start, perm, nn, npart)
     if m is None:
         m = torch.empty((nn, nq), dtype=dt, device=pos.device)
         accumulate = False

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restric
     for (int i = 0; i < KB; ++i) {
       const size_t idx = base + (size_t)i * BT + tid;
       const bool valid = idx < (size_t)np;
-      const uint32_t key = (uint32_t)particle_key<T, R>(x[i], g);
+      const uint32_t key = (uint32_t)particle_key<R>(x[i], g);
       kv[i] = key;
       if (valid) keys[idx] = key;
       count_digit_runs(h, (int)(key & 255u), valid, lane);
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restric
     int kb = -1;
     if (base > 0) {
       const T xb[3] = {(T)pos[3 * (base - 1)], (T)pos[3 * (base - 1) + 1], (T)pos[3 * (base - 1) + 2]};
-      kb = particle_key<T, R>(xb, g);
+      kb = particle_key<R>(xb, g);
     }
     kbefore = kb;
   }
@@ -512,9 +512,10 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
   BinWs w = bin_layout(ws, np, nbins);
   const int npass = digit_passes(nbins);
   const int ntiles = (np + TILE - 1) / TILE;
-  hipError_t e = f32     ? keys_t<float, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
-                 : pos32 ? keys_t<double, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
-                         : keys_t<double, double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
+  // fp32 positions (MM_F32 and the mixed layout) are read exactly into fp64:
+  // the key is found in fp64 arithmetic, as every kernel finds the support
+  hipError_t e = (f32 || pos32) ? keys_t<double, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
+                                : keys_t<double, double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
   if (e != hipSuccess) return e;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;

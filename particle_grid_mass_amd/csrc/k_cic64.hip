@@ -150,9 +150,9 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
 #pragma unroll
   for (int c = 0; c < NC; ++c) t[c] = 0.0;
   if (r.valid) {
-    axis_support<double, 1>(grid_coord<double, 0>(r.x, g), g.n0, wx);
-    axis_support<double, 1>(grid_coord<double, 1>(r.y, g), g.n1, wy);
-    axis_support<double, 1>(grid_coord<double, 2>(r.z, g), g.n2, wz);
+    support_axis<double, 1, 0>((double)r.x, g, wx);
+    support_axis<double, 1, 1>((double)r.y, g, wy);
+    support_axis<double, 1, 2>((double)r.z, g, wz);
     const double f = sigma * r.w;
     double bx = r.bx, by = r.by, bz = r.bz;
     if (NC == 9 && GB) {

@@ -169,9 +169,9 @@ __device__ __forceinline__ void stage_particle(const Raw<T>& r, const GridDev& g
 #pragma unroll
   for (int c = 0; c < NC; ++c) t[c] = T(0);
   if (r.valid) {
-    axis_support<T, R>(grid_coord<T, 0>(r.x, g), g.n0, wx);
-    axis_support<T, R>(grid_coord<T, 1>(r.y, g), g.n1, wy);
-    axis_support<T, R>(grid_coord<T, 2>(r.z, g), g.n2, wz);
+    support_axis<T, R, 0>((double)r.x, g, wx);
+    support_axis<T, R, 1>((double)r.y, g, wy);
+    support_axis<T, R, 2>((double)r.z, g, wz);
     T f = sigma * r.w;
     if (NC == 9)
       response<T>(r.bx, r.by, r.bz, beta, f, t);

@@ -21,9 +21,9 @@ __global__ __launch_bounds__(256) void k_interp_field(GridDev g, const PT* __res
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= np) return;
   T wx[3], wy[3], wz[3];
-  const int fx = axis_support<T, R>(grid_coord<T, 0>((T)pos[3 * (size_t)p], g), g.n0, wx);
-  const int fy = axis_support<T, R>(grid_coord<T, 1>((T)pos[3 * (size_t)p + 1], g), g.n1, wy);
-  const int fz = axis_support<T, R>(grid_coord<T, 2>((T)pos[3 * (size_t)p + 2], g), g.n2, wz);
+  const int fx = support_axis<T, R, 0>((double)pos[3 * (size_t)p], g, wx);
+  const int fy = support_axis<T, R, 1>((double)pos[3 * (size_t)p + 1], g, wy);
+  const int fz = support_axis<T, R, 2>((double)pos[3 * (size_t)p + 2], g, wz);
   T b[3] = {T(0), T(0), T(0)};
 #pragma unroll
   for (int az = 0; az < NS; ++az) {

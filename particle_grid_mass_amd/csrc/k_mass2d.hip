@@ -106,8 +106,8 @@ __global__ __launch_bounds__(64) void k_mass2d(GridDev g, const PT* __restrict__
 #pragma unroll
     for (int c = 0; c < NC; ++c) t[c] = 0.0;
     if (raw.valid) {
-      axis_support<double, R>(grid_coord<double, 0>(raw.x, g), g.n0, wx);
-      axis_support<double, R>(grid_coord<double, 1>(raw.y, g), g.n1, wy);
+      support_axis<double, R, 0>((double)raw.x, g, wx);
+      support_axis<double, R, 1>((double)raw.y, g, wy);
       const double f = sigma * raw.w;
       if (NC == 9)
         response<double>(raw.bx, raw.by, raw.bz, beta, f, t);

@@ -130,9 +130,9 @@ __global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict_
     {
       T wx[3] = {T(0), T(0), T(0)}, wy[3] = {T(0), T(0), T(0)}, wz[3] = {T(0), T(0), T(0)};
       if (raw.valid) {
-        axis_support<T, R>(grid_coord<T, 0>(raw.x, g), g.n0, wx);
-        axis_support<T, R>(grid_coord<T, 1>(raw.y, g), g.n1, wy);
-        axis_support<T, R>(grid_coord<T, 2>(raw.z, g), g.n2, wz);
+        support_axis<T, R, 0>((double)raw.x, g, wx);
+        support_axis<T, R, 1>((double)raw.y, g, wy);
+        support_axis<T, R, 2>((double)raw.z, g, wz);
       }
       double* sw = sm + w_base<R>(lane);
       if (R == 2) {

@@ -39,9 +39,9 @@ __global__ __launch_bounds__(256) void k_atomic_scatter(GridDev g, const T* __re
   if (p >= np) return;
   T x[3] = {pos[3 * (size_t)p], pos[3 * (size_t)p + 1], pos[3 * (size_t)p + 2]};
   T wx[3], wy[3], wz[3];
-  int fx = axis_support<T, R>(grid_coord<T, 0>(x[0], g), g.n0, wx);
-  int fy = axis_support<T, R>(grid_coord<T, 1>(x[1], g), g.n1, wy);
-  int fz = axis_support<T, R>(grid_coord<T, 2>(x[2], g), g.n2, wz);
+  int fx = support_axis<T, R, 0>((double)x[0], g, wx);
+  int fy = support_axis<T, R, 1>((double)x[1], g, wy);
+  int fz = support_axis<T, R, 2>((double)x[2], g, wz);
   T t[NC];
   if (NC == 9) {
     response<T>(Bf[3 * (size_t)p], Bf[3 * (size_t)p + 1], Bf[3 * (size_t)p + 2], beta, sigma * w[p], t);

@@ -171,9 +171,9 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
                                       double* sW, const double* sF, int lane) {
   double wx[3] = {0, 0, 0}, wy[3] = {0, 0, 0}, wz[3] = {0, 0, 0}, t[3] = {0, 0, 0};
   if (r.valid) {
-    axis_support<double, 2>(grid_coord<double, 0>(r.x, g), g.n0, wx);
-    axis_support<double, 2>(grid_coord<double, 1>(r.y, g), g.n1, wy);
-    axis_support<double, 2>(grid_coord<double, 2>(r.z, g), g.n2, wz);
+    support_axis<double, 2, 0>((double)r.x, g, wx);
+    support_axis<double, 2, 1>((double)r.y, g, wy);
+    support_axis<double, 2, 2>((double)r.z, g, wz);
     double bx = r.bx, by = r.by, bz = r.bz;
     if (GB) {
       const double* fb = sF + (lane >> 4) * (3 * N);

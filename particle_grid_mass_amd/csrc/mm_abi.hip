@@ -254,6 +254,18 @@ mm_status mm_contract_bins_gridB(const mm_grid* grid, int order, mm_dtype dt, in
                          stream);
 }
 
+mm_status mm_record_bytes(const mm_grid* grid, int order, mm_dtype dt, int tensorial, size_t* bytes) {
+  if (!bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (is2d(grid) && dt == MM_F32) return MM_ERR_UNSUPPORTED;
+  *bytes = is2d(grid) ? record_bytes_2d(order, tensorial != 0, nnodes)
+                      : record_bytes(order, dt == MM_F32, tensorial != 0, nnodes);
+  return MM_OK;
+}
+
 mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int tensorial, const void* rec,
                              int accumulate, void* M, mm_stream_t stream) {
   int64_t nnodes = 0;
@@ -352,8 +364,10 @@ const char* mm_status_string(mm_status s) {
   switch (s) {
     case MM_OK: return "ok";
     case MM_ERR_NULL: return "a required pointer is NULL";
-    case MM_ERR_ARG: return "argument out of range (order, dtype, grid, sigma/beta or algo)";
-    case MM_ERR_UNSUPPORTED: return "particle or node count at or above 2^31";
+    case MM_ERR_ARG: return "argument out of range (order, dtype, grid, sigma/beta, algo or alignment)";
+    case MM_ERR_UNSUPPORTED:
+      return "unsupported: particle or node count at or above 2^31, or a combination of dtype, algorithm, "
+             "field placement and grid dimension that the library does not implement";
     case MM_ERR_WORKSPACE: return "workspace smaller than required";
     case MM_ERR_HIP: return "HIP launch or runtime error";
   }

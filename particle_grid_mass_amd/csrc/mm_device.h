@@ -14,7 +14,8 @@ namespace mmk {
 typedef double v4d __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Grid passed by value to every kernel (origin/h in fp64; fp32 kernels round them).
+// Grid passed by value to every kernel (origin and h in fp64; the support of a
+// particle is always found in fp64, see support_axis).
 // Bit d of `exact` is set when h_d is a power of two: then (x - o) * (1/h)
 // equals the IEEE quotient (x - o) / h bit for bit, and the cheaper product is used.
 struct GridDev {
@@ -34,41 +35,43 @@ __device__ __forceinline__ T grid_coord(T x, const GridDev& g) {
   return dx / (T)(D == 0 ? g.h0 : D == 1 ? g.h1 : g.h2);
 }
 
-template <typename T>
-__device__ __forceinline__ T dev_floor(T x);
-template <>
-__device__ __forceinline__ double dev_floor<double>(double x) { return floor(x); }
-template <>
-__device__ __forceinline__ float dev_floor<float>(float x) { return floorf(x); }
-
 __device__ __forceinline__ int wrap_node(int j, int n) {
   int r = j % n;
   return r < 0 ? r + n : r;
 }
 
-// One axis of the support from the grid coordinate u = (x - origin)/h:
-// returns the first support node (wrapped) and writes the R+1
-// one-dimensional B-spline weights. j = floor(u), xi = u - j.
+// One axis of the support of a stored coordinate x (read exactly into fp64,
+// whatever its storage type): returns the first support node (wrapped) and
+// writes the R+1 one-dimensional B-spline weights in the precision T.
+// The grid coordinate u = (x - origin)/h, j = floor(u), xi = u - j and the
+// TSC half-cell decision are taken in fp64 arithmetic for every T, so the
+// binning and every kernel agree on each particle's support, and an fp32
+// position is placed as its exact value is; the weights are then formed in T
+// from the fraction rounded to T.
 //   CIC: nodes j, j+1 with (1 - xi, xi).
 //   TSC: centre m = j (xi < 1/2) or j+1 (xi >= 1/2); delta = offset from m;
 //        nodes m-1, m, m+1 with (1/2 (1/2 - delta)^2, 3/4 - delta^2, 1/2 (1/2 + delta)^2).
-template <typename T, int R>
-__device__ __forceinline__ int axis_support(T u, int n, T* wt) {
-  T fl = dev_floor<T>(u);
-  int j = (int)fl;
-  T xi = u - fl;
+template <typename T, int R, int D>
+__device__ __forceinline__ int support_axis(double x, const GridDev& g, T* wt) {
+  const int n = D == 0 ? g.n0 : D == 1 ? g.n1 : g.n2;
+  const double u = grid_coord<double, D>(x, g);
+  const double fl = floor(u);
+  const int j = (int)fl;
+  const double xi = u - fl;
   if (R == 1) {
-    wt[0] = T(1) - xi;
-    wt[1] = xi;
+    const T t = (T)xi;
+    wt[0] = T(1) - t;
+    wt[1] = t;
     return wrap_node(j, n);
   } else {
     int m = j;
-    T d = xi;
-    if (!(xi < T(0.5))) {
+    double dd = xi;
+    if (!(xi < 0.5)) {
       m = j + 1;
-      d = xi - T(1);
+      dd = xi - 1.0;
     }
-    T p = T(0.5) - d, q = T(0.5) + d;
+    const T d = (T)dd;
+    const T p = T(0.5) - d, q = T(0.5) + d;
     wt[0] = T(0.5) * p * p;
     wt[1] = T(0.75) - d * d;
     wt[2] = T(0.5) * q * q;
@@ -76,14 +79,15 @@ __device__ __forceinline__ int axis_support(T u, int n, T* wt) {
   }
 }
 
-// First support node of a particle as a linear node index (the bin key).
+// First support node of a particle as a linear node index (the bin key),
+// decided in fp64 on the stored position (see support_axis).
 // On a 2D grid (n2 == 1) z is ignored and the key is the node in the plane.
-template <typename T, int R>
-__device__ __forceinline__ int particle_key(const T* p3, const GridDev& g) {
-  T wt[3];
-  int fx = axis_support<T, R>(grid_coord<T, 0>(p3[0], g), g.n0, wt);
-  int fy = axis_support<T, R>(grid_coord<T, 1>(p3[1], g), g.n1, wt);
-  int fz = g.n2 == 1 ? 0 : axis_support<T, R>(grid_coord<T, 2>(p3[2], g), g.n2, wt);
+template <int R, typename PT>
+__device__ __forceinline__ int particle_key(const PT* p3, const GridDev& g) {
+  double wt[3];
+  int fx = support_axis<double, R, 0>((double)p3[0], g, wt);
+  int fy = support_axis<double, R, 1>((double)p3[1], g, wt);
+  int fz = g.n2 == 1 ? 0 : support_axis<double, R, 2>((double)p3[2], g, wt);
   return fx + g.n0 * (fy + g.n1 * fz);
 }
 

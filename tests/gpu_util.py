@@ -24,6 +24,26 @@ def rel_fro(a, b):
     return np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a)
 
 
+def max_entry_err(a, b):
+    """Largest entry error relative to the largest reference entry."""
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    mb = np.abs(b).max() if b.size else 0.0
+    d = np.abs(a - b).max() if a.size else 0.0
+    return d / mb if mb > 0 else d
+
+
+def assert_match(got, ref, dtype):
+    """The parity bar: relative Frobenius error within the budget of the dtype,
+    and no single entry off by more than that budget times the largest entry
+    (a norm alone would let a few large errors hide among millions of
+    entries)."""
+    e_fro = rel_fro(got, ref)
+    e_max = max_entry_err(got, ref)
+    assert e_fro <= TOL[dtype], f"relative Frobenius error {e_fro:.3e} > {TOL[dtype]:.0e}"
+    assert e_max <= TOL[dtype], f"max entry error {e_max:.3e} of max|ref| > {TOL[dtype]:.0e}"
+
+
 def species_scalars(case, sp):
     beta, sigma = sp.beta, case.sigma
     if case.dtype == "f32":
@@ -59,8 +79,7 @@ def oracle_assemble(case, species=None):
     for si, sp in enumerate(case.species if species is None else species):
         beta, sigma = species_scalars(case, sp)
         M = oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w,
-                            sp.B if case.kind == "ecsim" else None, beta, sigma, M=M, accumulate=si > 0,
-                            prec32=case.dtype == "f32")
+                            sp.B if case.kind == "ecsim" else None, beta, sigma, M=M, accumulate=si > 0)
     return M
 
 

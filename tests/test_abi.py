@@ -198,3 +198,42 @@ def test_deposit_records_multi_validation():
     assert dep(G8, order=3) == _lib.MM_ERR_ARG
     assert dep(G8, dt=7) == _lib.MM_ERR_ARG
     assert dep(_lib.make_grid((8, 8, 1))) == _lib.MM_ERR_UNSUPPORTED
+
+
+def test_record_bytes_query():
+    """mm_record_bytes returns the record size the deposition reads, with the
+    usual host-side argument checks, and enqueues nothing."""
+    lib = _lib.load()
+
+    def q(g, order=1, dt=_lib.MM_F64, ten=1):
+        nb = ctypes.c_size_t(0)
+        st = lib.mm_record_bytes(ctypes.byref(g) if g is not None else None, order, dt, ten, ctypes.byref(nb))
+        return st, nb.value
+
+    assert q(G8) == (_lib.MM_OK, 512 * 36 * 9 * 8)
+    assert q(G8, ten=0) == (_lib.MM_OK, 512 * 36 * 8)
+    assert q(G8, dt=_lib.MM_F32) == (_lib.MM_OK, 512 * 36 * 9 * 4)
+    st, nb2 = q(_lib.make_grid((8, 8, 8)), order=2)
+    assert st == _lib.MM_OK and nb2 >= 512 * 378 * 9 * 8
+    assert q(None)[0] == _lib.MM_ERR_NULL
+    assert q(G8, order=3)[0] == _lib.MM_ERR_ARG
+    assert q(G8, dt=9)[0] == _lib.MM_ERR_ARG
+    assert lib.mm_record_bytes(ctypes.byref(G8), 1, 0, 1, None) == _lib.MM_ERR_NULL
+    assert "unsupported" in lib.mm_status_string(_lib.MM_ERR_UNSUPPORTED).decode()
+
+
+def test_binding_checks_bin_arrays():
+    """The binding rejects binning arrays that do not fit the grid or the
+    particles before any call reaches the library (host tensors suffice: the
+    size check runs on shapes only)."""
+    import torch
+    from particle_grid_mass_amd import api
+    bs = torch.zeros(513, dtype=torch.int32)
+    perm = torch.zeros(100, dtype=torch.int32)
+    api._check_bins(bs, perm, 512, 100)
+    with pytest.raises(ValueError):
+        api._check_bins(torch.zeros(512, dtype=torch.int32), perm, 512, 100)  # one short
+    with pytest.raises(ValueError):
+        api._check_bins(torch.zeros(1001, dtype=torch.int32), perm, 512, 100)  # another grid
+    with pytest.raises(ValueError):
+        api._check_bins(bs, torch.zeros(99, dtype=torch.int32), 512, 100)  # short perm

@@ -25,10 +25,9 @@ def oracle_gridB(case, F):
     M = None
     for si, sp in enumerate(case.species):
         beta, sigma = species_scalars(case, sp)
-        Bp = oracle.interp_field(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos, F,
-                                 prec32=case.dtype == "f32")
+        Bp = oracle.interp_field(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos, F)
         M = oracle.assemble(case.order, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w, Bp, beta, sigma,
-                            M=M, accumulate=si > 0, prec32=case.dtype == "f32")
+                            M=M, accumulate=si > 0)
     return M
 
 

@@ -44,7 +44,7 @@ def test_moments_small(seed, order, n, npart, nq, dtype):
     Q = quantities(seed, npart, nq, dtype)
     print(f"[case] moments order={order} n={n} np={npart} nq={nq} {dtype}", flush=True)
     got = gpu_moments(case.grid, order, pos, Q, dtype).double().cpu().numpy()
-    ref = oracle.moments(order, n, case.grid.origin, case.grid.h, pos, Q, prec32=dtype == "f32")
+    ref = oracle.moments(order, n, case.grid.origin, case.grid.h, pos, Q)
     assert rel_fro(got, ref) <= TOL[dtype]
 
 

@@ -14,8 +14,8 @@ import torch
 import oracle
 import particle_grid_mass_amd as mm
 from tests import dense_ref
-from tests.gpu_util import (TOL, TDT, as_numpy_M, gpu_assemble, oracle_assemble, rel_fro, require_gpu, to_dev,
-                            species_scalars)
+from tests.gpu_util import (TOL, TDT, as_numpy_M, assert_match, gpu_assemble, oracle_assemble, rel_fro,
+                            require_gpu, to_dev, species_scalars)
 from workloads import make_config, random_case, Case, Species, Grid
 
 pytestmark = pytest.mark.gpu
@@ -52,8 +52,7 @@ def test_bin_parity(seed, order, n, npart, spread, srt, dtype):
                        origin=(-1.5, 0.25, 3.0), h=(0.5, 0.75, 1.25))
     _print_case("bin", case)
     sp = case.species[0]
-    bs_ref, perm_ref = oracle.bin_particles(order, n, case.grid.origin, case.grid.h, sp.pos,
-                                            prec32=dtype == "f32")
+    bs_ref, perm_ref = oracle.bin_particles(order, n, case.grid.origin, case.grid.h, sp.pos)
     bs, perm = mm.bin_particles(case.grid, order, to_dev(sp.pos, TDT[dtype]))
     torch.cuda.synchronize()
     assert np.array_equal(bs.cpu().numpy(), bs_ref)
@@ -143,7 +142,7 @@ def test_assemble_small(seed, order, n, npart, kind, dtype, algo):
     _print_case(f"small/{algo}", case)
     M = as_numpy_M(gpu_assemble(case, algo), case)
     ref = oracle_assemble(case)
-    assert rel_fro(M, ref) <= TOL[dtype]
+    assert_match(M, ref, dtype)
 
 
 @pytest.mark.parametrize("order", [1, 2])
@@ -161,7 +160,7 @@ def test_one_heavy_bin(order, dtype):
     case = Case("heavy", Grid((6, 6, 7)), order, "ecsim", [Species(pos, w, B, 0.5)], dtype=dtype)
     _print_case("heavy", case)
     M = as_numpy_M(gpu_assemble(case, "mfma"), case)
-    assert rel_fro(M, oracle_assemble(case)) <= TOL[dtype]
+    assert_match(M, oracle_assemble(case), dtype)
 
 
 def test_accumulate_and_empty():
@@ -209,14 +208,14 @@ def test_gpu_symmetry_and_partition_of_unity():
 def test_config1_full(algo):
     case = make_config(1)
     _print_case(f"c1/{algo}", case)
-    assert rel_fro(as_numpy_M(gpu_assemble(case, algo), case), oracle_assemble(case)) <= 1e-12
+    assert_match(as_numpy_M(gpu_assemble(case, algo), case), oracle_assemble(case), "f64")
 
 
 @pytest.mark.parametrize("algo", ["mfma", "atomic"])
 def test_config2_full(algo):
     case = make_config(2)
     _print_case(f"c2/{algo}", case)
-    assert rel_fro(as_numpy_M(gpu_assemble(case, algo), case), oracle_assemble(case)) <= 1e-12
+    assert_match(as_numpy_M(gpu_assemble(case, algo), case), oracle_assemble(case), "f64")
 
 
 @pytest.mark.parametrize("shuffled", [False, True])
@@ -225,7 +224,7 @@ def test_config3_full(shuffled):
     _print_case("c3/mfma", case)
     M, bins = gpu_assemble(case, "mfma", return_bins=True)
     ref = oracle_assemble(case)
-    assert rel_fro(as_numpy_M(M, case), ref) <= 1e-12
+    assert_match(as_numpy_M(M, case), ref, "f64")
     for (bs, perm), sp in zip(bins, case.species):  # binning of each species, bit-exact
         bs_ref, perm_ref = oracle.bin_particles(1, case.grid.n, case.grid.origin, case.grid.h, sp.pos)
         assert np.array_equal(bs.cpu().numpy(), bs_ref)
@@ -236,7 +235,7 @@ def test_config3_full(shuffled):
 def test_config4_full(kind):
     case = make_config(4, kind=kind)
     _print_case("c4/mfma", case)
-    assert rel_fro(as_numpy_M(gpu_assemble(case, "mfma"), case), oracle_assemble(case)) <= 1e-12
+    assert_match(as_numpy_M(gpu_assemble(case, "mfma"), case), oracle_assemble(case), "f64")
 
 
 @pytest.fixture(scope="module")
@@ -264,16 +263,14 @@ def test_config5_sampled(dtype, config5_f64):
     nodes = np.concatenate([rng.integers(0, nn, 44), [0, nn - 1],
                             [x + n * (y + n * z) for (x, y, z) in centres]]).astype(np.int64)
     beta, sigma = species_scalars(case, sp)
-    rows_ref = oracle.rows(2, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w, nodes, sp.B, beta, sigma,
-                           prec32=dtype == "f32")
+    rows_ref = oracle.rows(2, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w, nodes, sp.B, beta, sigma)
     rows = M[torch.from_numpy(nodes).cuda()].double().cpu().numpy().reshape(rows_ref.shape)
-    assert rel_fro(rows, rows_ref) <= TOL[dtype]
+    assert_match(rows, rows_ref, dtype)
     # bilinear form u^T M v over the whole matrix (stencil contraction with torch on the GPU
     # output) against the oracle's O(np N) evaluation from the particles.
     u = rng.standard_normal((nn, 3))
     v = rng.standard_normal((nn, 3))
-    ref = oracle.bilinear(2, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w, u, v, sp.B, beta, sigma,
-                          prec32=dtype == "f32")
+    ref = oracle.bilinear(2, case.grid.n, case.grid.origin, case.grid.h, sp.pos, sp.w, u, v, sp.B, beta, sigma)
     got = _stencil_bilinear_torch(M, case, u, v)
     del M
     torch.cuda.empty_cache()

@@ -300,15 +300,46 @@ def test_binning_stable_and_supports(order):
             assert supp <= allowed
 
 
-def test_prec32_decision():
-    """fp32 inputs: the cell decision is taken in fp32 arithmetic."""
-    x = np.float32(0.1) * np.float32(3.0)  # fp32 value near a cell boundary for h = 0.1
-    pos = np.array([[float(x), 0.05, 0.05]])
-    h = (float(np.float32(0.1)),) * 3
-    f32 = oracle.support(1, (8, 8, 8), (0, 0, 0), h, pos[0], prec32=True)
-    u32 = np.float32(np.float32(pos[0, 0]) - np.float32(0.0)) / np.float32(h[0])
-    assert f32[0][0] == int(np.floor(u32)) % 8
-    assert f32[1][0, 1] == float(u32) - np.floor(float(u32))
+def _fp32_faces():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp32_faces.json")) as f:
+        return json.load(f)
+
+
+def test_fp32_positions_decided_exactly():
+    """fp32 positions are placed as their exact values are (Sec. 2.3 support
+    rule on the stored value): next to a cell face or a TSC half-cell tie,
+    where fp32 arithmetic on the quotient would land on the face or the tie,
+    the oracle's cell, fraction and TSC centre equal the exact rational ones
+    (tests/golden/fp32_faces.json, written by make_fp32_faces.py with
+    fractions.Fraction, never by the oracle), and each case contradicts the
+    fp32-arithmetic reading."""
+    from fractions import Fraction
+    d = _fp32_faces()
+    assert len(d["faces"]) >= 4 and len(d["ties"]) >= 4
+    for c in d["faces"]:
+        n = (c["n"],) * 3
+        x = np.array([float.fromhex(c["x_hex"]), 0.0, 0.0], dtype=np.float64)
+        assert np.float32(x[0]) == x[0]  # an fp32 value
+        first, w1d = oracle.support(1, n, (c["origin"],) * 3, (c["h"],) * 3, x)
+        assert first[0] == c["exact_cell"] != c["fp32_cell"]
+        xi = Fraction(c["exact_xi"])
+        assert abs(Fraction(w1d[0, 1]) - xi) <= Fraction(1, 2 ** 50)
+        assert abs(Fraction(w1d[0, 0]) - (1 - xi)) <= Fraction(1, 2 ** 50)
+    for c in d["ties"]:
+        n = (c["n"],) * 3
+        x = np.array([float.fromhex(c["x_hex"]), 0.0, 0.0], dtype=np.float64)
+        first, w1d = oracle.support(2, n, (c["origin"],) * 3, (c["h"],) * 3, x)
+        assert c["exact_tsc_centre"] != c["fp32_tsc_centre"]
+        assert first[0] == (c["exact_tsc_centre"] - 1) % c["n"]
+        # centred on j (xi just below 1/2): delta = xi, so the upper weight 1/2 (1/2 + delta)^2 is just below 1/2
+        delta = Fraction(c["exact_xi"])
+        assert abs(Fraction(w1d[0, 2]) - Fraction(1, 2) * (Fraction(1, 2) + delta) ** 2) <= Fraction(1, 2 ** 50)
+        # binning keys follow the same decision
+        bs, perm = oracle.bin_particles(2, n, (c["origin"],) * 3, (c["h"],) * 3, x[None, :])
+        key = int(np.searchsorted(bs, 0, side="right") - 1)
+        assert key % c["n"] == (c["exact_tsc_centre"] - 1) % c["n"]
 
 
 def test_config_generators_shapes():
