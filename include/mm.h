@@ -50,7 +50,9 @@
  *  Memory:  every array argument is a device pointer (hipMalloc or an
  *           allocator on top of it, e.g. torch) on the current device,
  *           owned by the caller. The library allocates nothing and keeps no
- *           mutable global state; calls are reentrant.
+ *           mutable global state; calls are reentrant. The one exception is
+ *           mm_assemble_ecsim_noalloc, which uses a fixed scratch array of the
+ *           library per GPU (see there).
  *  Streams: all work is enqueued asynchronously on `stream` (a hipStream_t,
  *           NULL = default stream); no call synchronizes the host.
  *  Workspace (CUB style): call with ws == NULL to receive the required byte
@@ -79,7 +81,9 @@ typedef enum {
                              algorithm, field placement and grid dimension that is not
                              implemented (each entry point lists its own) */
   MM_ERR_WORKSPACE = 4,   /* *ws_bytes smaller than required */
-  MM_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+  MM_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
+  MM_ERR_SCRATCH = 6      /* the workload needs more than the fixed scratch of
+                             mm_assemble_ecsim_noalloc (MM_NOALLOC_SCRATCH_BYTES) */
 } mm_status;
 
 typedef enum { MM_F64 = 0, MM_F32 = 1, MM_MIX = 2 } mm_dtype;
@@ -305,6 +309,32 @@ mm_status mm_stencil_matvec(const mm_grid* grid, int order, mm_dtype dt, int ten
  * out of range -> MM_ERR_ARG.
  */
 mm_status mm_probe_mfma_f64(int nblocks, int iters, double* out, mm_stream_t stream);
+
+/*
+ * mm_assemble_ecsim_noalloc - mm_assemble_ecsim with MM_ALGO_MFMA for callers
+ * that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid allocation. It calls
+ * no allocating routine. The per-bin records live in a fixed device array of
+ * MM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * library's first use on that GPU until the process ends; its address is
+ * looked up once per device, on the first call with that device current.
+ *
+ *  Arguments as for mm_assemble_ecsim (algorithm MM_ALGO_MFMA, field per
+ *  particle); the caller still owns pos, w, B, bin_start, perm and M, all on
+ *  the current device.
+ *  Limit: the records of the grid must fit the scratch: record bytes (see
+ *  mm_record_bytes; rounded up to 256) <= MM_NOALLOC_SCRATCH_BYTES, e.g. CIC
+ *  3x3 fp64 up to 25,890 nodes (29^3), CIC 3x3 fp32 up to 51,781 nodes, else
+ *  MM_ERR_SCRATCH, before anything is enqueued.
+ *  Every call on one GPU uses that GPU's one scratch array, whatever the
+ *  stream: calls whose work overlaps on one GPU (other streams or threads)
+ *  race on it and must be serialised by the caller. Each call writes the
+ *  records it reads, so nothing left by an earlier call is read.
+ */
+#define MM_NOALLOC_SCRATCH_BYTES (64u << 20)
+mm_status mm_assemble_ecsim_noalloc(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                    const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                                    double beta, double sigma, int accumulate, void* M, mm_stream_t stream);
 
 /* Static description of a status code. */
 const char* mm_status_string(mm_status s);

@@ -3,10 +3,12 @@
 The computation lives in ``libmm.so`` (hand-written HIP kernels behind the C
 ABI of ``include/mm.h``); this package is its thin torch binding.
 """
-from .api import (MMError, assemble_ecsim, assemble_ecsim_gridB, assemble_scalar, bin_particles,  # noqa: F401
+from .api import (MMError, assemble_ecsim, assemble_ecsim_gridB, assemble_ecsim_noalloc, assemble_scalar,  # noqa: F401
+                  bin_particles,
                   contract_bins, deposit_moments, deposit_records, noff, noff_canonical, noff_grid,
-                  probe_mfma_f64, stencil_matvec)
+                  probe_mfma_f64, record_bytes, stencil_matvec)
 
-__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "assemble_ecsim_gridB", "contract_bins",
+__all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "assemble_ecsim_gridB", "assemble_ecsim_noalloc",
+           "contract_bins",
            "deposit_records", "deposit_moments", "stencil_matvec", "probe_mfma_f64", "noff", "noff_canonical",
-           "noff_grid", "MMError"]
+           "noff_grid", "record_bytes", "MMError"]

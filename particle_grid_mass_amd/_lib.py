@@ -7,7 +7,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmm.so")
 
-MM_OK, MM_ERR_NULL, MM_ERR_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP = range(6)
+MM_OK, MM_ERR_NULL, MM_ERR_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP, MM_ERR_SCRATCH = range(7)
+MM_NOALLOC_SCRATCH_BYTES = 64 << 20
 MM_F64, MM_F32, MM_MIX = 0, 1, 2
 MM_MAX_RECORD_SETS = 4
 ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
@@ -15,7 +16,7 @@ ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
 # Every symbol the public header include/mm.h declares.
 EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_assemble_ecsim_gridB",
             "mm_contract_bins", "mm_contract_bins_gridB", "mm_deposit_records", "mm_deposit_records_canonical",
-            "mm_deposit_records_multi", "mm_record_bytes", "mm_deposit_moments", "mm_stencil_matvec", "mm_probe_mfma_f64", "mm_status_string", "mm_version")
+            "mm_deposit_records_multi", "mm_record_bytes", "mm_deposit_moments", "mm_stencil_matvec", "mm_assemble_ecsim_noalloc", "mm_probe_mfma_f64", "mm_status_string", "mm_version")
 
 
 class MMGrid(ctypes.Structure):
@@ -59,11 +60,12 @@ def load():
     lib.mm_stencil_matvec.argtypes = [G, I, I, I, I, P, P, P, P]
     lib.mm_deposit_moments.argtypes = [G, I, I, I64, P, P, I, P, P, I, P, P, SZ, P]
     lib.mm_probe_mfma_f64.argtypes = [I, I, P, P]
+    lib.mm_assemble_ecsim_noalloc.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, P, P]
     for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim, lib.mm_assemble_ecsim_gridB,
               lib.mm_contract_bins, lib.mm_contract_bins_gridB, lib.mm_deposit_records,
               lib.mm_deposit_records_canonical, lib.mm_deposit_records_multi, lib.mm_record_bytes,
               lib.mm_stencil_matvec, lib.mm_deposit_moments,
-              lib.mm_probe_mfma_f64):
+              lib.mm_probe_mfma_f64, lib.mm_assemble_ecsim_noalloc):
         f.restype = ctypes.c_int
     lib.mm_status_string.argtypes = [ctypes.c_int]
     lib.mm_status_string.restype = ctypes.c_char_p

@@ -206,6 +206,38 @@ def assemble_ecsim_gridB(grid, order: int, pos, w, Bgrid, bin_start=None, perm=N
                      Bgrid=Bgrid)
 
 
+def assemble_ecsim_noalloc(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.0, sigma: float = 1.0,
+                           M: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+    """``assemble_ecsim`` (matrix-core algorithm) through the entry point that
+    allocates nothing: the per-bin records live in the library's fixed device
+    scratch (``MM_NOALLOC_SCRATCH_BYTES`` per GPU), so no workspace is
+    allocated; M is allocated here only when not given. Calls that overlap on
+    one GPU race on that scratch."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    code, fdt, dt = _modes(pos, w)
+    _check_tensor(pos, "pos", fdt)
+    _check_tensor(w, "w", dt)
+    _check_tensor(B, "B", fdt)
+    npart = pos.numel() // 3
+    if w.numel() != npart or B.numel() != 3 * npart:
+        raise ValueError("pos, w and B disagree on the particle count")
+    _check_tensor(bin_start, "bin_start", torch.int32)
+    _check_tensor(perm, "perm", torch.int32)
+    _check_bins(bin_start, perm, _nnodes(g), npart)
+    nof = noff_grid(order, g)
+    if M is None:
+        M = torch.empty((_nnodes(g), nof, 9), dtype=dt, device=pos.device)
+        accumulate = False
+    _check_tensor(M, "M", dt)
+    if M.numel() != _nnodes(g) * nof * 9:
+        raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * nof * 9}")
+    _call(lib.mm_assemble_ecsim_noalloc, "mm_assemble_ecsim_noalloc", ctypes.byref(g), int(order), code, npart,
+          _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm), float(beta), float(sigma),
+          int(bool(accumulate)), _ptr(M), _stream(pos.device))
+    return M
+
+
 def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.0, sigma: float = 1.0,
                   rec: Optional[torch.Tensor] = None, Bgrid: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Phase 1 of the matrix-core assembly: packed per-bin local matrices (uint8

@@ -2,6 +2,9 @@
 // and kernel dispatch. Every argument error is reported before any HIP call.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mm.h"
 #include "mm_contract.h"
 
@@ -62,13 +65,51 @@ bool is2d(const mm_grid* g) { return g->n[2] == 1; }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// ------------------------------------------------------------ fixed scratch
+// Device scratch of the allocation-free entry point mm_assemble_ecsim_noalloc:
+// the per-bin records of the two-phase assembly live here instead of in a
+// caller workspace. One copy per GPU, created when the library's code object
+// is loaded there and held until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: kernels and copies take
+// the address hipGetSymbolAddress returns for the current device, looked up
+// once per device and kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)MM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The scratch address on the current device (looked up on the first call there).
+mm_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MM_ERR_HIP;
+  if (dev >= kMaxDevices) return MM_ERR_UNSUPPORTED;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MM_ERR_HIP;
+      scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return MM_OK;
+}
+
 // Shared argument checks of the assembly entry points. The tensorial field is
 // per particle (B) or on the grid nodes (Bgrid, gathered at each particle).
+// fixed_max > 0: ws is the library's own fixed device scratch of fixed_max
+// bytes (the allocation-free entry point): no size query, and a workload that
+// needs more is MM_ERR_SCRATCH.
 mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
                           const void* B, const void* Bgrid, bool tensorial, const int32_t* bin_start,
                           const int32_t* perm, double beta, double sigma, mm_algo algo, void* M, void* ws,
-                          size_t* ws_bytes, mm_stream_t stream, int accumulate) {
-  if (!ws_bytes) return MM_ERR_NULL;
+                          size_t* ws_bytes, mm_stream_t stream, int accumulate, size_t fixed_max = 0) {
+  if (!ws_bytes && fixed_max == 0) return MM_ERR_NULL;
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
@@ -100,12 +141,17 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   // fp32 positions with an fp64 interpolated field: not a combination the kernels take
   if (interp && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
   const size_t need = rec_need + (interp ? (size_t)np * 3 * elem : 0);
-  if (!ws) {
-    *ws_bytes = need;
-    return MM_OK;
+  if (fixed_max > 0) {
+    if (need > fixed_max) return MM_ERR_SCRATCH;
+    if (need > 0 && (st = scratch_of_current_device(&ws)) != MM_OK) return st;
+  } else {
+    if (!ws) {
+      *ws_bytes = need;
+      return MM_OK;
+    }
+    if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+    if (need > 0 && ((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
   }
-  if (*ws_bytes < need) return MM_ERR_WORKSPACE;
-  if (need > 0 && ((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
 
   const int noff = is2d(grid) ? (order == 1 ? 9 : 25) : (order == 1 ? 27 : 125);
   const size_t count = (size_t)nnodes * noff * (tensorial ? 9 : 1);
@@ -193,6 +239,14 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
 }  // namespace
 
 extern "C" {
+
+mm_status mm_assemble_ecsim_noalloc(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                    const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                                    double beta, double sigma, int accumulate, void* M, mm_stream_t stream) {
+  // the scratch address is looked up inside, after every argument check passed
+  return assemble_common(grid, order, dt, np, pos, w, B, nullptr, true, bin_start, perm, beta, sigma, MM_ALGO_MFMA,
+                         M, nullptr, nullptr, stream, accumulate, kScratchBytes);
+}
 
 mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
                            int32_t* bin_start, int32_t* perm, void* ws, size_t* ws_bytes, mm_stream_t stream) {
@@ -370,6 +424,9 @@ const char* mm_status_string(mm_status s) {
              "field placement and grid dimension that the library does not implement";
     case MM_ERR_WORKSPACE: return "workspace smaller than required";
     case MM_ERR_HIP: return "HIP launch or runtime error";
+    case MM_ERR_SCRATCH:
+      return "the records of this workload exceed the fixed device scratch of the allocation-free entry point "
+             "(MM_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

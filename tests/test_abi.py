@@ -28,7 +28,7 @@ def test_library_exports_all_symbols():
     for name in declared_symbols():
         assert hasattr(lib, name), name
     assert lib.mm_version().decode().startswith("mm ")
-    for code in range(6):
+    for code in range(7):
         assert lib.mm_status_string(code)
 
 
@@ -237,3 +237,27 @@ def test_binding_checks_bin_arrays():
         api._check_bins(torch.zeros(1001, dtype=torch.int32), perm, 512, 100)  # another grid
     with pytest.raises(ValueError):
         api._check_bins(bs, torch.zeros(99, dtype=torch.int32), 512, 100)  # short perm
+
+
+def test_noalloc_validation():
+    """The allocation-free entry point checks its arguments and the size of the
+    records against its fixed scratch on the host, before it looks up the
+    scratch or enqueues anything."""
+    lib = _lib.load()
+
+    def call(g, order=1, dt=_lib.MM_F64, np_=10, pos=FAKE, B=FAKE, bs=FAKE, M=FAKE):
+        return lib.mm_assemble_ecsim_noalloc(ctypes.byref(g) if g is not None else None, order, dt, np_, pos, FAKE,
+                                             B, bs, FAKE, 0.5, 1.0, 0, M, None)
+
+    big = _lib.make_grid((64, 64, 64))  # 262,144 nodes: CIC 3x3 fp64 records of 679 MB
+    assert call(big) == _lib.MM_ERR_SCRATCH
+    assert call(_lib.make_grid((32, 32, 32)), order=2) == _lib.MM_ERR_SCRATCH
+    assert call(None) == _lib.MM_ERR_NULL
+    assert call(G8, M=None) == _lib.MM_ERR_NULL
+    assert call(G8, B=None) == _lib.MM_ERR_NULL
+    assert call(G8, bs=None) == _lib.MM_ERR_NULL
+    assert call(G8, order=3) == _lib.MM_ERR_ARG
+    assert call(G8, dt=9) == _lib.MM_ERR_ARG
+    assert call(G8, np_=-1) == _lib.MM_ERR_ARG
+    assert _lib.MM_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert "scratch" in lib.mm_status_string(_lib.MM_ERR_SCRATCH).decode()
