@@ -44,9 +44,10 @@ HEADERS = ("mm_device.h", "mm_contract.h", "mm_internal.h")
 # Source files that define each kernel the roofline may name.
 KERNEL_FILES = {
     "k_cic64": ("k_cic64.hip",) + HEADERS,
-    "k_tsc64": ("k_tsc64.hip",) + HEADERS,
+    "k_tsc64": ("k_tsc64.hip", "mm_run.h") + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
+    "k_gather_run": ("k_gather_run.hip", "mm_run.h") + HEADERS,
     "k_mass2d": ("k_mass2d.hip",) + HEADERS,
     "k_gather2d": ("k_mass2d.hip",) + HEADERS,
     "k_atomic_scatter": ("k_scatter.hip",) + HEADERS,
@@ -55,9 +56,10 @@ KERNEL_FILES = {
 
 KERNEL_LABELS = {
     "k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
-    "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+    "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block, run records)",
     "k_contract": "k_contract (per-bin MFMA contraction)",
     "k_gather": "k_gather (stencil deposition of the per-bin records)",
+    "k_gather_run": "k_gather_run (stencil deposition of the records of x-runs of four bins)",
     "k_mass2d": "k_mass2d (2D per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
     "k_gather2d": "k_gather2d (2D stencil deposition of the per-bin records)",
     "k_atomic_scatter": "k_atomic_scatter (per-particle atomic scatter, comparison only)",
@@ -86,25 +88,27 @@ def flops_per_particle(order: int, tensorial: bool, dims: int = 3) -> int:
 
 
 def contract_bytes(order: int, tensorial: bool, elem: int, np_: int, nbins: int, field_on_grid: bool = False,
-                   pelem: int = 0, dims: int = 3, rec_elem: int = 0) -> int:
+                   pelem: int = 0, dims: int = 3, rec_elem: int = 0, rec_total: int = 0) -> int:
     """Algorithmic HBM bytes of one contraction launch: each particle's
     position, weight (and field) and permutation entry read once, bin bounds
     read once, one packed upper-triangle record written per bin; a field on
     the grid nodes is read once instead of the per-particle field. pelem: bytes
     of a stored position or field value when it differs from elem (the mixed
     layout's fp32 positions); rec_elem: bytes of a record value (fp64 records
-    of the 2D problem)."""
+    of the 2D problem); rec_total: the records' total bytes when they are not
+    one packed triangle per bin (the run records of second-order fp64 3x3
+    assembly, summed over runs of four bins along x)."""
     pelem = pelem or elem
     rec_elem = rec_elem or elem
     n = (order + 1) ** dims
     per_particle = (3 + (3 if tensorial and not field_on_grid else 0)) * pelem + elem + 4
     record = n * (n + 1) // 2 * (9 if tensorial else 1) * rec_elem
     field = nbins * 3 * pelem if tensorial and field_on_grid else 0
-    return np_ * per_particle + (nbins + 1) * 4 + nbins * record + field
+    return np_ * per_particle + (nbins + 1) * 4 + (rec_total or nbins * record) + field
 
 
 def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate: bool,
-                  canonical: bool = False, dims: int = 3, rec_elem: int = 0, nrec: int = 1) -> int:
+                  canonical: bool = False, dims: int = 3, rec_elem: int = 0, nrec: int = 1, rec_total: int = 0) -> int:
     """Algorithmic HBM bytes of one deposition launch: every record of the
     nrec record sets (one per species) read once, every stencil entry written
     once (read too when accumulating); the canonical half stores
@@ -116,7 +120,8 @@ def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate
         noff = (noff + 1) // 2
     nc = 9 if tensorial else 1
     out = nbins * noff * nc * elem
-    return nrec * nbins * n * (n + 1) // 2 * nc * rec_elem + out * (2 if accumulate else 1)
+    rec = rec_total or nbins * n * (n + 1) // 2 * nc * rec_elem
+    return nrec * rec + out * (2 if accumulate else 1)
 
 
 def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
@@ -554,20 +559,25 @@ def main():
     np_launch = np_total / len(spec)
     t_dom = dom_ms / launches * 1e-3
     flops = flops_per_particle(order, tensorial, args.dims) * np_launch
+    # records as the library lays them out for this grid (run records, or one packed triangle per bin)
+    rec_total = 0
+    if args.algo == "mfma" and args.dims == 3 and order == 2 and tensorial and case.dtype == "f64":
+        rec_total = mm.record_bytes(case.grid, order, torch.float64, True)
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem, args.dims,
-                            8 if args.dims == 2 else 0)
+                            8 if args.dims == 2 else 0, rec_total=rec_total)
     # one deposition of every species' record sets, or the average over the
     # species' launches: the first overwrites M, the others accumulate into it
     # (read and write)
     if multi:
         dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False, canonical=args.canonical,
-                               nrec=len(spec))
+                               nrec=len(spec), rec_total=rec_total)
     else:
         dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
-                                   dims=args.dims, rec_elem=8 if args.dims == 2 else 0)
+                                   dims=args.dims, rec_elem=8 if args.dims == 2 else 0, rec_total=rec_total)
                      for si in range(len(spec))) / len(spec)
+    run_records = rec_total > 0 and case.grid.n[0] % 4 == 0
     if dom == "deposit":
-        kname = "k_gather2d" if args.dims == 2 else "k_gather"
+        kname = "k_gather2d" if args.dims == 2 else ("k_gather_run" if run_records else "k_gather")
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
                 "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
         roof["algorithmic_bytes_per_launch"] = dbytes

@@ -35,6 +35,7 @@
 //  MODE_ATOMIC - every local entry is added into the stencil matrix with a
 //    hardware atomic ((a,b) and (b,a) for off-diagonal tiles).
 #include "mm_contract.h"
+#include "mm_run.h"
 
 namespace mmk {
 
@@ -509,7 +510,10 @@ bool contract_gathers_field(int order, bool f32, int mode) {
   return mode == MODE_RECORD && !f32 && (order == 1 || order == 2);  // k_cic64, k_tsc64
 }
 
-size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins) {
+size_t record_bytes(int order, bool f32, bool tensorial, const GridDev& g) {
+  const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
+  if (order == 2 && !f32 && tensorial && tsc_run_records(g))  // one record per run of four bins
+    return (size_t)(nbins / run::RUN) * run::RUNREC * sizeof(double);
   const int npair = order == 1 ? Geo<1>::NPAIR : Geo<2>::NPAIR;
   const size_t recb = (size_t)nbins * npair * (tensorial ? 9 : 1) * (f32 ? 4 : 8);
   if (order == 2 && !f32 && tensorial)  // k_tsc64 keeps its bin order after the records
@@ -758,6 +762,8 @@ static hipError_t gather_dispatch(const GridDev& g, int order, bool f32, bool te
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
                          int accumulate,
                          void* M, hipStream_t s, bool canonical) {
+  if (order == 2 && !f32 && tensorial && tsc_run_records(g))  // run records of k_tsc64
+    return launch_gather_run(g, rec, nrec, accumulate, M, s, canonical);
   return canonical ? gather_dispatch<true>(g, order, f32, tensorial, rec, nrec, accumulate, M, s)
                    : gather_dispatch<false>(g, order, f32, tensorial, rec, nrec, accumulate, M, s);
 }

@@ -29,6 +29,7 @@
 //    three components a wave owns per pair are written as one 24-byte piece
 //    (the three waves of a group fill the 72 bytes of a pair in the XCD's L2).
 #include "mm_contract.h"
+#include "mm_run.h"
 
 namespace mmk {
 
@@ -211,7 +212,15 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
-template <typename PT, bool GB>
+// Run records (RUNS): the group is the run of bins 4 grp .. 4 grp + 3 (consecutive
+// x; the launcher passes no bin order). For each of its three components a
+// wave stores the four bins' pair values in LDS (one packed triangle per bin,
+// each lane its own entries: no conflicts), then every lane sums the one to
+// three bin values of its union entries (mm_run.h) in bin order and writes
+// the component's plane of the run record, 999 consecutive values.
+static __constant__ run::Tables kRun = run::make_tables();
+
+template <typename PT, bool GB, bool RUNS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
     GridDev g, const PT* __restrict__ pos, const double* __restrict__ w, const PT* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
@@ -299,9 +308,54 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 
   // D_blk[i][j] of block (I, J) sits in lane (i << 4) | (blk << 2) | j: local
-  // entry (4I + i, 4J + j) of bin 4 grp + blk. Stage each bin's CPW * NPAIR
-  // record values (contiguous in rec) in LDS, then write them with 16-byte stores.
+  // entry (4I + i, 4J + j) of bin 4 grp + blk.
   const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
+  if constexpr (RUNS) {
+    constexpr int ZSLOT = NB * NPAIR;  // a zero in LDS, read for the bins an entry does not have
+    constexpr int DUMP = ZSLOT + 1;    // written by the block entries below the diagonal or in the padding row
+    static_assert(DUMP + 1 <= SMEM, "the four bins' pair values of one component fit the W region");
+    constexpr int NIT = (run::NENT + 63) / 64;  // entries per lane
+    int tb[NIT];  // the lane's entries and their bins, read once for the three components
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      const int e = lane + 64 * q;
+      tb[q] = kRun.contrib[e < run::NENT ? e : run::NENT - 1];
+    }
+    double* pv = sW;  // [bin of the run][pair], then the zero slot
+    if (lane == 0) pv[ZSLOT] = 0.0;
+    double* dst = rec + (size_t)grp * run::RUNREC + (size_t)(CPW * row) * run::PLANE;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      int k = 0;
+#pragma unroll
+      for (int I = 0; I < NBLK; ++I)
+#pragma unroll
+        for (int J = I; J < NBLK; ++J, ++k) {
+          const int a = 4 * I + di, bb = 4 * J + dj;
+          const bool pair = a < N && bb < N && (I < J || di <= dj);
+          pv[pair ? db * NPAIR + run::pair_index(a, bb) : DUMP] = acc[c][k];
+        }
+      wave_sync();
+      // Each entry adds its first bin's value and those of up to two more bins
+      // (both nodes one column further left in each: pair index + NPAIR - 28 +
+      // a, a one less), reading the zero slot where it has fewer; no branches,
+      // so every lane's reads are in flight together.
+#pragma unroll
+      for (int q = 0; q < NIT; ++q) {
+        const int t = tb[q];
+        const int q0 = t & 2047, a = (t >> 11) & 31, n = t >> 16;
+        const int q1 = n > 1 ? q0 + NPAIR - 28 + a : ZSLOT;
+        const int q2 = n > 2 ? q0 + 2 * (NPAIR - 28) + 2 * a - 1 : ZSLOT;
+        const double v = (pv[q0] + pv[q1]) + pv[q2];
+        const int e = lane + 64 * q;
+        if (q < NIT - 1 || e < run::NENT) dst[c * run::PLANE + e] = v;
+      }
+      wave_sync();
+    }
+    return;
+  }
+  // Per-bin records: stage each bin's CPW * NPAIR record values (contiguous in
+  // rec) in LDS, then write them with 16-byte stores.
 #pragma unroll 1
   for (int b = 0; b < NB; ++b) {
     const int bin = group_bin(order, grp, b, nbins);
@@ -361,32 +415,38 @@ __global__ __launch_bounds__(OWIN) void k_order_window(const int32_t* __restrict
 
 size_t tsc64_order_bytes(int64_t nbins) { return ((size_t)nbins * 4 + 255) / 256 * 256; }
 
-template <typename PT>
+template <typename PT, bool RUNS>
 static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                           double beta, double sigma, double* rec, int32_t* order, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // NQ single-wave workgroups per group of four bins
-  hipLaunchKernelGGL(k_order_window, dim3((nbins + OWIN - 1) / OWIN), dim3(OWIN), 0, s, bin_start, nbins, order);
+  // run records need the groups to be runs of consecutive x: no bin order
+  if (!RUNS)
+    hipLaunchKernelGGL(k_order_window, dim3((nbins + OWIN - 1) / OWIN), dim3(OWIN), 0, s, bin_start, nbins, order);
+  const int32_t* ord = RUNS ? nullptr : (const int32_t*)order;
   if (P.Bgrid)
-    hipLaunchKernelGGL((k_tsc64<PT, true>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec,
-                       (const int32_t*)order);
+    hipLaunchKernelGGL((k_tsc64<PT, true, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord);
   else
-    hipLaunchKernelGGL((k_tsc64<PT, false>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec,
-                       (const int32_t*)order);
+    hipLaunchKernelGGL((k_tsc64<PT, false, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord);
   return hipGetLastError();
 }
+
+bool tsc_run_records(const GridDev& g) { return g.n2 > 1 && g.n0 % run::RUN == 0; }
 
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s) {
   if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
-  // the bin order lives after the records (record_bytes counts it)
+  if (tsc_run_records(g))
+    return P.pos32 ? tsc64_t<float, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s)
+                   : tsc64_t<double, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s);
+  // per-bin records; the bin order lives after them (record_bytes counts it)
   const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
   const size_t recb = (size_t)nbins * NPAIR * NC * 8;
   int32_t* order = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(rec) + (recb + 255) / 256 * 256);
-  return P.pos32 ? tsc64_t<float>(g, P, bin_start, perm, beta, sigma, rec, order, s)
-                 : tsc64_t<double>(g, P, bin_start, perm, beta, sigma, rec, order, s);
+  return P.pos32 ? tsc64_t<float, false>(g, P, bin_start, perm, beta, sigma, rec, order, s)
+                 : tsc64_t<double, false>(g, P, bin_start, perm, beta, sigma, rec, order, s);
 }
 
 }  // namespace mmk

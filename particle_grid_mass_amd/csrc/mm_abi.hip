@@ -134,7 +134,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   // gather itself is first interpolated to the particles, after the records.
   const bool records = algo == MM_ALGO_MFMA && np > 0;
   const size_t rec_need =
-      records ? align256(is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, nnodes))
+      records ? align256(is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, to_dev(grid)))
               : 0;
   const bool interp = Bgrid && np > 0 &&
                       !(records && contract_gathers_field(order, f32, MODE_RECORD));
@@ -209,7 +209,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   const bool f32 = dt == MM_F32;
   const bool tensorial = B != nullptr || Bgrid != nullptr;
   if (is2d(grid) && (f32 || Bgrid)) return MM_ERR_UNSUPPORTED;
-  const size_t rec_need = is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, nnodes);
+  const size_t rec_need = is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, to_dev(grid));
   const bool interp = Bgrid && np > 0 && !contract_gathers_field(order, f32, MODE_RECORD);
   const size_t need = interp ? align256(rec_need) + (size_t)np * 3 * (f32 ? 4 : 8) : rec_need;
   if (!rec) {
@@ -316,7 +316,7 @@ mm_status mm_record_bytes(const mm_grid* grid, int order, mm_dtype dt, int tenso
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (is2d(grid) && dt == MM_F32) return MM_ERR_UNSUPPORTED;
   *bytes = is2d(grid) ? record_bytes_2d(order, tensorial != 0, nnodes)
-                      : record_bytes(order, dt == MM_F32, tensorial != 0, nnodes);
+                      : record_bytes(order, dt == MM_F32, tensorial != 0, to_dev(grid));
   return MM_OK;
 }
 

@@ -22,8 +22,12 @@ hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin
 // per (group of four bins, row of alpha).
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
-// Bytes k_tsc64 uses after its records (rounded up to 256) for the bin order.
+// Bytes k_tsc64 uses after its per-bin records (rounded up to 256) for the bin order.
 size_t tsc64_order_bytes(int64_t nbins);
+// Whether the order-2 fp64 tensorial records of this grid are run records
+// (mm_run.h: x-runs of four bins; 3D grids with n0 a multiple of 4) rather
+// than per-bin pair records.
+bool tsc_run_records(const GridDev& g);
 
 // Whether launch_contract gathers a grid field itself (Particles::Bgrid) for
 // this order, precision and mode; otherwise the field must first be
@@ -34,8 +38,10 @@ bool contract_gathers_field(int order, bool f32, int mode);
 // 16 * iters instructions per wave; out holds nblocks * 256 doubles.
 hipError_t launch_probe_mfma_f64(int nblocks, int iters, double* out, hipStream_t s);
 
-// Bytes of the packed per-bin records: nbins * N(N+1)/2 * ncomp * sizeof(T).
-size_t record_bytes(int order, bool f32, bool tensorial, int64_t nbins);
+// Bytes of the records of this grid: packed per-bin records, nbins * N(N+1)/2 *
+// ncomp * sizeof(T) (plus the TSC bin order), or the run records of order-2
+// fp64 tensorial grids (tsc_run_records).
+size_t record_bytes(int order, bool f32, bool tensorial, const GridDev& g);
 
 // Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o,
 // over nrec (1 .. MAX_REC) record sets rec[0..nrec-1] (one per species).
@@ -48,6 +54,11 @@ struct RecSet {
 };
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
                          int accumulate, void* M, hipStream_t s, bool canonical = false);
+
+// Phase 2 for run records (order 2, fp64, tensorial, tsc_run_records(g)):
+// the same sums as launch_gather, read from the records of x-runs of four bins.
+hipError_t launch_gather_run(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
+                             hipStream_t s, bool canonical);
 
 // The 2D problem (n2 == 1): per-bin fp64 records rec[bin][pair][comp] of the
 // (R+1)^2 support, and their fixed-order sum into M [nnodes][(2R+1)^2][comp]

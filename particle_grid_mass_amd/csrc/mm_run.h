@@ -1,0 +1,110 @@
+// Records of x-runs of four second-order bins: the layout shared by the TSC
+// contraction that writes them (k_tsc64.hip) and the deposit that reads them
+// (k_gather_run.hip).
+//
+// Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
+// Particle-In-Cell Methods": each support group's local matrix (Sec. 3.1,
+// Eq. 15) is scattered into the stencil storage (Sec. 3.4), and the matrix is
+// symmetric node pair by node pair (Table 1 and its footnote), so only the
+// canonical half of the pairs is kept.
+//
+// A run is four bins with consecutive x (first support nodes kx = 4r .. 4r+3,
+// same y and z). Their supports cover the 6 x 3 x 3 union nodes (X, Y, Z),
+// X in [0, 6) relative to node 4r. A run record holds, for every canonical
+// node pair of the union that some bin of the run covers, the sum of the
+// bins' local matrices: 999 entries instead of 4 x 378 pair records, a third
+// fewer bytes to write and to read back.
+//
+// Entry numbering: by the row node's Z and Y, then the (dY, dZ) row of the
+// canonical offset d = (dX, dY, dZ) >= 0 ((dZ, dY, dX) lexicographic; 13 rows,
+// the first, d = (dX, 0, 0), holding dX >= 0 only), then X, then dX. For
+// fixed (Z, Y, row) the valid (X, dX) (X and X + dX in [0, 6)) form one
+// segment. A deposit wave shares the (dY, dZ) row and covers nodes x times
+// the five dX, so each term it reads is one contiguous stretch.
+//
+// Storage (doubles): rec[run][c][entry] for component c = 3 i + j of the 3x3
+// block: one plane of 999 values per component, padded to PLANE (16-byte
+// aligned). A contraction wave owning row i writes its three planes one after
+// the other, each a contiguous stretch (writing the three components of an
+// entry side by side, one component per pass, left partial cache lines that
+// reached HBM 2.7 times over); a deposit wave reads each plane over
+// consecutive entries.
+#pragma once
+
+#include <stdint.h>
+
+namespace mmk {
+namespace run {
+
+constexpr int RUN = 4;                 // bins per run (consecutive x)
+constexpr int UX = RUN + 2;            // node columns of the union support
+constexpr int NENT = 999;              // canonical union entries per run
+constexpr int PLANE = 1000;            // doubles per component plane (999, padded to 16 bytes)
+constexpr int RUNREC = 9 * PLANE;      // doubles per run record
+constexpr int CENTRE = 62;             // full offset index of d = 0
+constexpr int ROW0 = CENTRE / 5;       // (dY, dZ) row of d = (dX, 0, 0): full offset index / 5
+constexpr int NROW = 25 - ROW0;        // (dY, dZ) rows holding canonical offsets
+constexpr int NPAIR = 378;             // packed upper triangle of one bin's 27 x 27 matrix
+
+// Packed upper triangle of a bin's 27 support rows: pair(a, b), a <= b.
+constexpr int pair_index(int a, int b) { return a * 27 - (a * (a - 1)) / 2 + (b - a); }
+
+// Smallest dX of node column X (X + dX >= 0; dX >= 0 in the first row).
+constexpr int dx_min(int X, bool first_row) { return first_row ? 0 : (X < 2 ? -X : -2); }
+// Largest dX of node column X (X + dX < 6).
+constexpr int dx_max(int X) { return 5 - X < 2 ? 5 - X : 2; }
+
+struct Tables {
+  short seg_start[9 * NROW];  // first entry of segment (Z, Y, row): [(3 Z + Y) * NROW + row - ROW0]; -1: none
+  unsigned char col_start[2][UX + 1];  // entries before column X in a segment: [first row?][X]
+  // per entry: the bins b0 .. b0 + n - 1 of the run that hold both nodes:
+  // q0 = b0 * NPAIR + pair(a, a') (bits 0..10), a = the row node's support
+  // index in bin b0 (bits 11..15), n (bits 16..17); the next bin's index is
+  // q + NPAIR - 28 + a with a one less (both nodes one column further left)
+  int contrib[NENT];
+  int count;  // entries numbered
+};
+
+constexpr Tables make_tables() {
+  Tables t{};
+  for (int f = 0; f < 2; ++f) {
+    int c = 0;
+    for (int X = 0; X < UX; ++X) {
+      t.col_start[f][X] = (unsigned char)c;
+      c += dx_max(X) - dx_min(X, f == 1) + 1;
+    }
+    t.col_start[f][UX] = (unsigned char)c;
+  }
+  int e = 0;
+  for (int Z = 0; Z < 3; ++Z)
+    for (int Y = 0; Y < 3; ++Y)
+      for (int row = ROW0; row < 25; ++row) {
+        const int dy = row % 5 - 2, dz = row / 5 - 2;
+        const bool ok = Z + dz >= 0 && Z + dz < 3 && Y + dy >= 0 && Y + dy < 3;
+        t.seg_start[(3 * Z + Y) * NROW + row - ROW0] = ok ? (short)e : (short)-1;
+        if (!ok) continue;
+        for (int X = 0; X < UX; ++X)
+          for (int dx = dx_min(X, row == ROW0); dx <= dx_max(X); ++dx, ++e) {
+            int b0 = -1, n = 0, q0 = 0, a0 = 0;
+            for (int b = 0; b < RUN; ++b) {
+              const int ax = X - b, bx = X + dx - b;
+              if (ax < 0 || ax > 2 || bx < 0 || bx > 2) continue;
+              if (b0 < 0) {
+                b0 = b;
+                a0 = ax + 3 * Y + 9 * Z;
+                q0 = b * NPAIR + pair_index(a0, bx + 3 * (Y + dy) + 9 * (Z + dz));
+              }
+              ++n;
+            }
+            t.contrib[e] = q0 | (a0 << 11) | (n << 16);
+          }
+      }
+  t.count = e;
+  return t;
+}
+
+static_assert(make_tables().count == NENT, "canonical union entries of a run of four bins");
+static_assert(make_tables().col_start[0][UX] == 24 && make_tables().col_start[1][UX] == 15, "segment lengths");
+
+}  // namespace run
+}  // namespace mmk

@@ -213,8 +213,13 @@ def test_record_bytes_query():
     assert q(G8) == (_lib.MM_OK, 512 * 36 * 9 * 8)
     assert q(G8, ten=0) == (_lib.MM_OK, 512 * 36 * 8)
     assert q(G8, dt=_lib.MM_F32) == (_lib.MM_OK, 512 * 36 * 9 * 4)
-    st, nb2 = q(_lib.make_grid((8, 8, 8)), order=2)
-    assert st == _lib.MM_OK and nb2 >= 512 * 378 * 9 * 8
+    # second order, fp64, 3x3: run records of four bins along x (999 canonical
+    # entries x 9 components, planes padded to 3000 values) when n0 % 4 == 0 ...
+    assert q(_lib.make_grid((8, 8, 8)), order=2) == (_lib.MM_OK, 512 // 4 * 9000 * 8)
+    # ... and one packed triangle per bin (plus the bin order) otherwise
+    st, nb2 = q(_lib.make_grid((7, 8, 8)), order=2)
+    assert st == _lib.MM_OK and nb2 >= 448 * 378 * 9 * 8
+    assert q(_lib.make_grid((8, 8, 8)), order=2, dt=_lib.MM_F32) == (_lib.MM_OK, 512 * 378 * 9 * 4)
     assert q(None)[0] == _lib.MM_ERR_NULL
     assert q(G8, order=3)[0] == _lib.MM_ERR_ARG
     assert q(G8, dt=9)[0] == _lib.MM_ERR_ARG

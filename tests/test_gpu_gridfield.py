@@ -60,6 +60,8 @@ SMALL = [
     (54, 2, (5, 6, 7), 3),
     (55, 2, (7, 6, 5), 1500),
     (56, 2, (9, 8, 7), 20000),
+    (57, 2, (8, 6, 7), 15000),  # run records (x extent a multiple of 4) for fp64
+    (58, 2, (12, 5, 5), 7),
 ]
 
 

@@ -33,7 +33,8 @@ def widen(a):
     return np.ascontiguousarray(a, dtype=np.float32).astype(np.float64)
 
 
-CASES = [(151, 1, (5, 6, 7), 37), (152, 1, (9, 8, 7), 20000), (153, 2, (7, 6, 5), 1500), (154, 2, (9, 8, 7), 20000)]
+CASES = [(151, 1, (5, 6, 7), 37), (152, 1, (9, 8, 7), 20000), (153, 2, (7, 6, 5), 1500), (154, 2, (9, 8, 7), 20000),
+         (155, 2, (8, 7, 6), 20000)]  # run records (x extent a multiple of 4)
 
 
 @pytest.mark.parametrize("algo", ["mfma", "mfma_atomic"])

@@ -129,6 +129,10 @@ SMALL = [
     (14, 2, (5, 6, 7), 3),
     (15, 2, (7, 6, 5), 1500),
     (16, 2, (9, 8, 7), 20000),
+    # x extent a multiple of 4: the second-order fp64 3x3 path writes run records
+    (17, 2, (8, 6, 5), 3),
+    (18, 2, (12, 7, 6), 20000),
+    (19, 2, (16, 5, 5), 1),
 ]
 
 

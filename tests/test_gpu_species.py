@@ -53,7 +53,9 @@ def new_M(case, canonical, fill=None):
 
 
 CASES = [(201, 1, (5, 6, 7), (3000, 1200)), (202, 2, (7, 6, 5), (2500, 900, 40)),
-         (203, 2, (9, 8, 7), (20000, 7000, 3, 500)), (204, 1, (6, 5, 5), (0, 800))]
+         (203, 2, (9, 8, 7), (20000, 7000, 3, 500)), (204, 1, (6, 5, 5), (0, 800)),
+         # x extent a multiple of 4: second-order fp64 3x3 records are run records
+         (205, 2, (8, 6, 5), (6000, 2000, 0)), (206, 2, (12, 5, 7), (9000, 31))]
 
 
 @pytest.mark.parametrize("canonical", [False, True])

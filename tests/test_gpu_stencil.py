@@ -35,7 +35,8 @@ def records_and_M(case, canonical):
     return M.view(case.grid.ncells, nof, nc)
 
 
-CASES = [(101, 1, (5, 6, 7), 3000), (102, 2, (7, 6, 5), 3000), (103, 2, (9, 8, 7), 20000)]
+CASES = [(101, 1, (5, 6, 7), 3000), (102, 2, (7, 6, 5), 3000), (103, 2, (9, 8, 7), 20000),
+         (104, 2, (8, 7, 6), 20000)]  # run records (x extent a multiple of 4) for fp64 3x3
 
 
 @pytest.mark.parametrize("dtype", ["f64", "f32"])
