@@ -91,7 +91,10 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<doub
         if (Y + oy < 0 || Y + oy > 2) continue;
         const int ky = gy - Y < 0 ? gy - Y + g.n1 : gy - Y;
         const size_t rowrun = (size_t)nruns * ((size_t)ky + (size_t)g.n1 * kz);
-        const int seg = kRunG.seg_start[(3 * Z + Y) * run::NROW + oyz - run::ROW0] + 3 * i * run::PLANE;
+        // slice 3 Z + Y of the record: its component planes of slice_stride values
+        const int sl = 3 * Z + Y;
+        const int stride = kRunG.slice_stride[sl];
+        const int seg = kRunG.seg_start[sl * run::NROW + oyz - run::ROW0] + kRunG.slice_off[sl] + 3 * i * stride;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if (h == 0 ? !use1 : !use2) continue;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<doub
             if (q == 0 || q < recs.n) {  // (uniform)
               const double* src = recs.r[q] + off;
 #pragma unroll
-              for (int j = 0; j < 3; ++j) sum[j] += src[j * run::PLANE];
+              for (int j = 0; j < 3; ++j) sum[j] += src[j * stride];
             }
           }
         }

@@ -217,7 +217,7 @@ __device__ __forceinline__ void wave_sync() {
 // wave stores the four bins' pair values in LDS (one packed triangle per bin,
 // each lane its own entries: no conflicts), then every lane sums the one to
 // three bin values of its union entries (mm_run.h) in bin order and writes
-// the component's plane of the run record, 999 consecutive values.
+// the component's nine line-aligned stretches of the run record.
 static __constant__ run::Tables kRun = run::make_tables();
 
 template <typename PT, bool GB, bool RUNS>
@@ -315,15 +315,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     constexpr int DUMP = ZSLOT + 1;    // written by the block entries below the diagonal or in the padding row
     static_assert(DUMP + 1 <= SMEM, "the four bins' pair values of one component fit the W region");
     constexpr int NIT = (run::NENT + 63) / 64;  // entries per lane
-    int tb[NIT];  // the lane's entries and their bins, read once for the three components
+    int tb[NIT], ts[NIT];  // the lane's entries: their bins and where they are stored (read once)
 #pragma unroll
     for (int q = 0; q < NIT; ++q) {
-      const int e = lane + 64 * q;
-      tb[q] = kRun.contrib[e < run::NENT ? e : run::NENT - 1];
+      const int e = lane + 64 * q < run::NENT ? lane + 64 * q : run::NENT - 1;
+      tb[q] = kRun.contrib[e];
+      ts[q] = kRun.store[e];
     }
     double* pv = sW;  // [bin of the run][pair], then the zero slot
     if (lane == 0) pv[ZSLOT] = 0.0;
-    double* dst = rec + (size_t)grp * run::RUNREC + (size_t)(CPW * row) * run::PLANE;
+    double* dst = rec + (size_t)grp * run::RUNREC;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       int k = 0;
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int q2 = n > 2 ? q0 + 2 * (NPAIR - 28) + 2 * a - 1 : ZSLOT;
         const double v = (pv[q0] + pv[q1]) + pv[q2];
         const int e = lane + 64 * q;
-        if (q < NIT - 1 || e < run::NENT) dst[c * run::PLANE + e] = v;
+        const int comp = CPW * row + c;
+        if (q < NIT - 1 || e < run::NENT) dst[(ts[q] & 16383) + comp * 16 * (ts[q] >> 14)] = v;
       }
       wave_sync();
     }

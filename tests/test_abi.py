@@ -214,8 +214,9 @@ def test_record_bytes_query():
     assert q(G8, ten=0) == (_lib.MM_OK, 512 * 36 * 8)
     assert q(G8, dt=_lib.MM_F32) == (_lib.MM_OK, 512 * 36 * 9 * 4)
     # second order, fp64, 3x3: run records of four bins along x (999 canonical
-    # entries x 9 components, planes padded to 3000 values) when n0 % 4 == 0 ...
-    assert q(_lib.make_grid((8, 8, 8)), order=2) == (_lib.MM_OK, 512 // 4 * 9000 * 8)
+    # entries x 9 components, each slice plane padded to 16 values: 9360 values
+    # per run) when n0 % 4 == 0 ...
+    assert q(_lib.make_grid((8, 8, 8)), order=2) == (_lib.MM_OK, 512 // 4 * 9360 * 8)
     # ... and one packed triangle per bin (plus the bin order) otherwise
     st, nb2 = q(_lib.make_grid((7, 8, 8)), order=2)
     assert st == _lib.MM_OK and nb2 >= 448 * 378 * 9 * 8
