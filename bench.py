@@ -44,6 +44,7 @@ HEADERS = ("mm_device.h", "mm_contract.h", "mm_internal.h")
 # Source files that define each kernel the roofline may name.
 KERNEL_FILES = {
     "k_cic64": ("k_cic64.hip",) + HEADERS,
+    "k_cic32": ("k_cic32.hip",) + HEADERS,
     "k_tsc64": ("k_tsc64.hip", "mm_run.h") + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
@@ -56,6 +57,7 @@ KERNEL_FILES = {
 
 KERNEL_LABELS = {
     "k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
+    "k_cic32": "k_cic32 (CIC fp32 per-bin MFMA contraction, 4x4x1 f32, one bin per block)",
     "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block, run records)",
     "k_contract": "k_contract (per-bin MFMA contraction)",
     "k_gather": "k_gather (stencil deposition of the per-bin records)",
@@ -77,6 +79,8 @@ def kernel_source_hash(kernel: str) -> str:
 def contract_kernel(order: int, dtype: str, tensorial: bool) -> str:
     if dtype == "f64" and order == 1:
         return "k_cic64"
+    if dtype == "f32" and order == 1:
+        return "k_cic32"
     if dtype == "f64" and tensorial:
         return "k_tsc64"
     return "k_contract"

@@ -496,6 +496,8 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
   if (mode == MODE_RECORD && order == 1 && !f32)
     return launch_cic64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
+  if (mode == MODE_RECORD && order == 1 && f32 && !P.Bgrid)
+    return launch_cic32(g, P, bin_start, perm, beta, sigma, (float*)out, s);
   if (mode == MODE_RECORD && order == 2 && !f32 && (P.B || P.Bgrid))
     return launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
   if (P.Bgrid) return hipErrorInvalidValue;  // the other kernels take a per-particle field (interp first)
