@@ -93,7 +93,11 @@ typedef enum {
   MM_ALGO_MFMA = 0,          /* per-bin matrix-core contraction + the library's default deposit */
   MM_ALGO_ATOMIC = 1,        /* conventional per-particle atomic scatter (comparison kernel);
                                 ignores bin_start/perm, which may be NULL */
-  MM_ALGO_MFMA_ATOMIC = 2    /* per-bin matrix-core contraction, global-atomic deposit */
+  MM_ALGO_MFMA_ATOMIC = 2,   /* per-bin matrix-core contraction, global-atomic deposit */
+  MM_ALGO_VALU = 3           /* the same per-bin contraction and deposit as MM_ALGO_MFMA with the
+                                products formed by fp64 vector FMAs instead of matrix instructions
+                                (comparison kernel for the matrix cores); order 1 with MM_F64 or
+                                MM_MIX and the field per particle only, else MM_ERR_UNSUPPORTED */
 } mm_algo;
 
 typedef struct {

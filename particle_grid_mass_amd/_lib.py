@@ -11,7 +11,7 @@ MM_OK, MM_ERR_NULL, MM_ERR_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP
 MM_NOALLOC_SCRATCH_BYTES = 64 << 20
 MM_F64, MM_F32, MM_MIX = 0, 1, 2
 MM_MAX_RECORD_SETS = 4
-ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2}
+ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2, "valu": 3}
 
 # Every symbol the public header include/mm.h declares.
 EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_assemble_ecsim_gridB",

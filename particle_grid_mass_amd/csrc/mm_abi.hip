@@ -114,8 +114,11 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
-  if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC) return MM_ERR_ARG;
+  if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC && algo != MM_ALGO_VALU)
+    return MM_ERR_ARG;
   if (algo == MM_ALGO_ATOMIC && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
+  // the vector-FMA comparison contraction: CIC, fp64 arithmetic, 3D, field per particle
+  if (algo == MM_ALGO_VALU && (order != 1 || dt == MM_F32 || is2d(grid) || Bgrid)) return MM_ERR_UNSUPPORTED;
   // 2D: the matrix-core path in fp64 (or the mixed layout), field per particle
   if (is2d(grid) && (algo != MM_ALGO_MFMA || dt == MM_F32 || Bgrid)) return MM_ERR_UNSUPPORTED;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
@@ -132,7 +135,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   // The two-phase deposit keeps one packed record per bin; the atomic
   // deposits need no workspace. A grid field that the chosen kernel does not
   // gather itself is first interpolated to the particles, after the records.
-  const bool records = algo == MM_ALGO_MFMA && np > 0;
+  const bool records = (algo == MM_ALGO_MFMA || algo == MM_ALGO_VALU) && np > 0;
   const size_t rec_need =
       records ? align256(is2d(grid) ? record_bytes_2d(order, tensorial, nnodes) : record_bytes(order, f32, tensorial, to_dev(grid)))
               : 0;
@@ -176,7 +179,8 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     return hip_status(e);
   }
   if (records) {
-    e = launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
+    e = algo == MM_ALGO_VALU ? launch_cic64_valu(g, P, bin_start, perm, beta, sigma, (double*)ws, s)
+                             : launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
     if (e == hipSuccess) {
       const void* recs[1] = {ws};
       e = launch_gather(g, order, f32, tensorial, recs, 1, accumulate, M, s);

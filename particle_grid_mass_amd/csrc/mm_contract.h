@@ -18,6 +18,11 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
 hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
 
+// Phase 1 for CIC fp64 records on vector FMAs (the comparison kernel of MM_ALGO_VALU):
+// 16 bins per wave, four lanes per bin splitting its 36 pairs.
+hipError_t launch_cic64_valu(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                             double beta, double sigma, double* rec, hipStream_t s);
+
 // Phase 1 for CIC fp32 records: 16 bins per wave, one per block of v_mfma_f32_4x4x1_16b.
 hipError_t launch_cic32(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, float* rec, hipStream_t s);

@@ -267,3 +267,12 @@ def test_noalloc_validation():
     assert call(G8, np_=-1) == _lib.MM_ERR_ARG
     assert _lib.MM_NOALLOC_SCRATCH_BYTES == 64 << 20
     assert "scratch" in lib.mm_status_string(_lib.MM_ERR_SCRATCH).decode()
+
+
+def test_valu_algo_validation():
+    """MM_ALGO_VALU is CIC with fp64 arithmetic, 3D and the field per particle only."""
+    assert _ecsim(G8, algo=3)[0] == _lib.MM_OK  # workspace query
+    assert _ecsim(G8, order=2, algo=3)[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _ecsim(G8, dt=_lib.MM_F32, algo=3)[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _ecsim(_lib.make_grid((8, 8, 1)), algo=3)[0] == _lib.MM_ERR_UNSUPPORTED
+    assert _ecsim(G8, algo=4)[0] == _lib.MM_ERR_ARG

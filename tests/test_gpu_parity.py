@@ -295,3 +295,39 @@ def _stencil_bilinear_torch(M, case, u, v):
         blk = Md[:, :, :, o].reshape(-1, 3, 3).double()
         total += torch.einsum("gi,gij,gj->", ud, blk, vs)
     return float(total)
+
+
+# ------------------------------------------------------------------ vector-FMA comparison contraction
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+@pytest.mark.parametrize("seed,order,n,npart", [c for c in SMALL if c[1] == 1])
+def test_valu_contraction_small(seed, order, n, npart, kind):
+    """MM_ALGO_VALU: the binned CIC contraction on vector FMAs, same records
+    and deposit as the matrix-core path."""
+    case = random_case(seed, order, n, npart, kind=kind, dtype="f64", beta=0.7, sigma=1.3,
+                       origin=(0.25, -2.0, 1.0), h=(0.5, 1.0, 0.75), spread=0.8)
+    _print_case("small/valu", case)
+    assert_match(as_numpy_M(gpu_assemble(case, "valu"), case), oracle_assemble(case), "f64")
+
+
+def test_valu_contraction_config2():
+    case = make_config(2)
+    _print_case("c2/valu", case)
+    assert_match(as_numpy_M(gpu_assemble(case, "valu"), case), oracle_assemble(case), "f64")
+
+
+def test_valu_unsupported_combinations():
+    from particle_grid_mass_amd import _lib
+    case = random_case(61, 2, (6, 6, 6), 100, kind="ecsim")
+    sp = case.species[0]
+    pos, w, B = (to_dev(a, torch.float64) for a in (sp.pos, sp.w, sp.B))
+    bs, perm = mm.bin_particles(case.grid, 2, pos)
+    with pytest.raises(mm.MMError) as ei:  # second order
+        mm.assemble_ecsim(case.grid, 2, pos, w, B, bs, perm, beta=0.5, algo="valu")
+    assert ei.value.status == _lib.MM_ERR_UNSUPPORTED
+    c1 = random_case(62, 1, (6, 6, 6), 100, kind="ecsim", dtype="f32")
+    s1 = c1.species[0]
+    p1, w1, B1 = (to_dev(a, torch.float32) for a in (s1.pos, s1.w, s1.B))
+    b1, q1 = mm.bin_particles(c1.grid, 1, p1)
+    with pytest.raises(mm.MMError) as ei:  # fp32
+        mm.assemble_ecsim(c1.grid, 1, p1, w1, B1, b1, q1, beta=0.5, algo="valu")
+    assert ei.value.status == _lib.MM_ERR_UNSUPPORTED
