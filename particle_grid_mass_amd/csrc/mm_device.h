@@ -148,4 +148,17 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Hardware block b runs on XCD b % 8. Give XCD x the chunks x, x + 8, x + 16,
+// ... of CH consecutive logical blocks: neighbouring blocks still share an
+// XCD (and its L2) inside a chunk, and every XCD sweeps the whole grid, so
+// work whose cost varies across the grid (clustered particles) is spread
+// evenly over the XCDs. Bijective on [0, nb); the last nb mod (8 CH) blocks
+// map to themselves.
+__device__ __forceinline__ int xcd_chunk_remap(int b, int nb, int CH) {
+  const int full = nb - nb % (8 * CH);
+  if (b >= full) return b;
+  const int x = b % 8, idx = b / 8;
+  return ((idx / CH) * 8 + x) * CH + idx % CH;
+}
+
 }  // namespace mmk
