@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64) void k_cic32(GridDev g, const float* __restrict
   __shared__ __attribute__((aligned(16))) float sm[Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
-  const int grp = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = xcd_chunk_remap(blockIdx.x, gridDim.x, 16);  // chunks of groups dealt round the XCDs
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, grp, nbins, np, lane);
 

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(64) void k_cic64v(GridDev g, const PT* __restrict__
   __shared__ __attribute__((aligned(16))) double sm[Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
-  const int grp = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = xcd_chunk_remap(blockIdx.x, gridDim.x, 16);  // chunks of groups dealt round the XCDs
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, grp, nbins, np, lane);
   const int bl = lane >> 2, q = lane & 3;  // the lane's bin in the group and quarter of its pairs

@@ -34,7 +34,7 @@ namespace {
 
 static __constant__ run::Tables kRunG = run::make_tables();
 
-constexpr int ZB = 4;  // rows visited in z-blocks of ZB planes (the 9 record rows a node row reads stay in L2)
+constexpr int ZB = 1;  // node rows in plain order, y fastest: consecutive rows read adjacent slices of a record row
 
 constexpr int PAIRS = 64;  // (node, offset) pairs per block, one per lane of each wave
 

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64) void k_mass2d(GridDev g, const PT* __restrict__
   __shared__ __attribute__((aligned(16))) double sm[TOFF + 64 * TS + NB * 2];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
-  const int grp = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = xcd_chunk_remap(blockIdx.x, gridDim.x, 16);  // chunks of groups dealt round the XCDs
   if (grp >= ngroups) return;
   const int bin_l = NB * grp + (lane >> 4);
   int s0 = 0, e0 = 0;

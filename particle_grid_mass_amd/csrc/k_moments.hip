@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64) void k_moments(GridDev g, const PT* __restrict_
   __shared__ __attribute__((aligned(16))) double sm[SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
-  const int grp = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = xcd_chunk_remap(blockIdx.x, gridDim.x, 16);  // chunks of groups dealt round the XCDs
   if (grp >= ngroups) return;
   // prep lane l serves bin 4 grp + (l >> 4)
   const int bin_l = NB * grp + (lane >> 4);
