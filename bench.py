@@ -45,6 +45,7 @@ HEADERS = ("mm_device.h", "mm_contract.h", "mm_internal.h")
 KERNEL_FILES = {
     "k_cic64": ("k_cic64.hip",) + HEADERS,
     "k_cic32": ("k_cic32.hip",) + HEADERS,
+    "k_cic64v": ("k_cic64v.hip", "k_contract.hip") + HEADERS,
     "k_tsc64": ("k_tsc64.hip", "mm_run.h") + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
@@ -58,6 +59,8 @@ KERNEL_FILES = {
 KERNEL_LABELS = {
     "k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
     "k_cic32": "k_cic32 (CIC fp32 per-bin MFMA contraction, 4x4x1 f32, one bin per block)",
+    "k_cic64v": "k_cic64v + k_gather (CIC fp64 per-bin contraction on vector FMAs and its deposit, "
+                "timed together as one MM_ALGO_VALU assembly call)",
     "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block, run records)",
     "k_contract": "k_contract (per-bin MFMA contraction)",
     "k_gather": "k_gather (stencil deposition of the per-bin records)",
@@ -319,7 +322,8 @@ def main():
                     help="several species: deposit each species' records on its own (accumulating into M) "
                          "instead of one deposition of all species' records")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
-    ap.add_argument("--algo", default="mfma", help="mfma (default) | mfma_atomic | atomic")
+    ap.add_argument("--algo", default="mfma",
+                    help="mfma (default) | mfma_atomic | atomic | valu (the CIC contraction on vector FMAs)")
     ap.add_argument("--canonical", action="store_true",
                     help="deposit into the canonical half of the stencil (14 / 63 offsets) instead of the full one")
     ap.add_argument("--matvec", action="store_true",
@@ -503,11 +507,13 @@ def main():
     phase_per_launch_ms = {p: phase_ms[p] / (psteps * nlaunch[p]) for p in phases}
     if args.algo == "mfma":
         dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
-    elif args.algo == "mfma_atomic":
-        dom = "contract"
+    elif args.algo in ("mfma_atomic", "valu"):
+        dom = "contract"  # one assembly call: its contraction with the deposit that follows it
     else:  # one kernel per species: the per-particle atomic scatter, bracketed by marks 0 and 1
         dom = "atomic"
         phase_per_launch_ms = {"atomic_scatter": phase_per_launch_ms["bin"]}
+    if args.algo in ("mfma_atomic", "valu"):  # the assembly call holds the contraction and its deposit
+        phase_per_launch_ms = {"bin": phase_per_launch_ms["bin"], "assemble": phase_per_launch_ms["contract"]}
     bracket = {"contract": (1, 2), "deposit": (2, 3), "atomic": (0, 1)}[dom]
 
     # Timed pass: whole-step time between t_start and t_end, and the dominant
@@ -591,6 +597,8 @@ def main():
             kname = "k_mass2d"
         if args.algo == "mfma_atomic":
             kname = "k_contract"
+        if args.algo == "valu":
+            kname = "k_cic64v"
         peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
         label = KERNEL_LABELS[kname]
         # the binding roof follows the arithmetic intensity: below the ridge
