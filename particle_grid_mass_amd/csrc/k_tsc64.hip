@@ -224,15 +224,15 @@ template <typename PT, bool GB, bool RUNS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
     GridDev g, const PT* __restrict__ pos, const double* __restrict__ w, const PT* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
-    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order) {
+    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order, int xch) {
   __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
   double* sW = smem;
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
-  // chunks of 16 groups (the NQ waves of a group share an XCD) dealt round
-  // the XCDs: a clustered density put 1.3 times the mean work on the XCDs
-  // whose contiguous range held a cluster
-  const int lid = xcd_chunk_remap(blockIdx.x, gridDim.x, 16 * NQ);
+  // chunks of xch blocks (whole groups: the NQ waves of a group share an XCD)
+  // dealt round the XCDs: a contiguous range per XCD put 1.3 times the mean
+  // work on the XCDs whose range held a cluster of a clustered density
+  const int lid = xcd_chunk_remap(blockIdx.x, gridDim.x, xch);
   const int grp = lid / NQ, row = lid - grp * NQ;     // row of alpha: components CPW*row ..
   if (grp >= ngroups) return;
   const Group G = load_group(bin_start, order, grp, nbins, np, lane);
@@ -314,46 +314,47 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // entry (4I + i, 4J + j) of bin 4 grp + blk.
   const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
   if constexpr (RUNS) {
-    constexpr int ZSLOT = NB * NPAIR;  // a zero in LDS, read for the bins an entry does not have
-    constexpr int DUMP = ZSLOT + 1;    // written by the block entries below the diagonal or in the padding row
-    static_assert(DUMP + 1 <= SMEM, "the four bins' pair values of one component fit the W region");
+    static_assert(run::RUN * run::BSTRIDE <= SMEM, "the four bins' blocks of one component fit the W region");
     constexpr int NIT = (run::NENT + 63) / 64;  // entries per lane
-    int tb[NIT], ts[NIT];  // the lane's entries: their bins and where they are stored (read once)
+    unsigned tb[NIT], ts[NIT];  // the lane's entries: their block slots and where they are stored (read once)
 #pragma unroll
     for (int q = 0; q < NIT; ++q) {
       const int e = lane + 64 * q < run::NENT ? lane + 64 * q : run::NENT - 1;
       tb[q] = kRun.contrib[e];
-      ts[q] = kRun.store[e];
+      ts[q] = kRun.store_bytes[e];
     }
-    double* pv = sW;  // [bin of the run][pair], then the zero slot
-    if (lane == 0) pv[ZSLOT] = 0.0;
-    double* dst = rec + (size_t)grp * run::RUNREC;
+    double* pv = sW;                                           // [bin][upper block][i][j] (mm_run.h)
+    double* pl = pv + db * run::BSTRIDE + 4 * di + dj;         // this lane's entry of block 0
+    char* dst = reinterpret_cast<char*>(rec + (size_t)grp * run::RUNREC);
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      int k = 0;
 #pragma unroll
-      for (int I = 0; I < NBLK; ++I)
-#pragma unroll
-        for (int J = I; J < NBLK; ++J, ++k) {
-          const int a = 4 * I + di, bb = 4 * J + dj;
-          const bool pair = a < N && bb < N && (I < J || di <= dj);
-          pv[pair ? db * NPAIR + run::pair_index(a, bb) : DUMP] = acc[c][k];
-        }
+      for (int k = 0; k < NBP; ++k) pl[16 * k] = acc[c][k];
       wave_sync();
       // Each entry adds its first bin's value and those of up to two more bins
-      // (both nodes one column further left in each: pair index + NPAIR - 28 +
-      // a, a one less), reading the zero slot where it has fewer; no branches,
-      // so every lane's reads are in flight together.
+      // (both nodes one column further left in each), reading an exact zero
+      // where it has fewer; no branches, so every lane's reads are in flight
+      // together.
+      const unsigned comp = CPW * row + c;
+      constexpr int HB = NIT / 2;  // entries read before any is summed
 #pragma unroll
-      for (int q = 0; q < NIT; ++q) {
-        const int t = tb[q];
-        const int q0 = t & 2047, a = (t >> 11) & 31, n = t >> 16;
-        const int q1 = n > 1 ? q0 + NPAIR - 28 + a : ZSLOT;
-        const int q2 = n > 2 ? q0 + 2 * (NPAIR - 28) + 2 * a - 1 : ZSLOT;
-        const double v = (pv[q0] + pv[q1]) + pv[q2];
-        const int e = lane + 64 * q;
-        const int comp = CPW * row + c;
-        if (q < NIT - 1 || e < run::NENT) dst[(ts[q] & 16383) + comp * 16 * (ts[q] >> 14)] = v;
+      for (int h = 0; h < NIT; h += HB) {
+        double x[HB][3];
+#pragma unroll
+        for (int q = 0; q < HB; ++q) {
+          const unsigned t = tb[h + q];
+          x[q][0] = pv[t & 2047u];
+          x[q][1] = pv[((t >> 11) & 2047u) + run::ZERO0];
+          x[q][2] = pv[(t >> 22) + run::ZERO1];
+        }
+#pragma unroll
+        for (int q = 0; q < HB; ++q) {
+          const double v = (x[q][0] + x[q][1]) + x[q][2];
+          const int e = lane + 64 * (h + q);
+          // byte offset of the entry's component-0 value plus comp planes of its slice
+          const unsigned o = (ts[h + q] & 0x1ffffu) + comp * 128u * (ts[h + q] >> 17);
+          if (h + q < NIT - 1 || e < run::NENT) *reinterpret_cast<double*>(dst + o) = v;
+        }
       }
       wave_sync();
     }
@@ -399,6 +400,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // about 4% of the work as padding. Each bin's record depends only on its own
 // particles, so the records are the same in any order.
 constexpr int OWIN = 256;
+constexpr int XPLANES = 1;  // planes of runs per XCD chunk
 
 __global__ __launch_bounds__(OWIN) void k_order_window(const int32_t* __restrict__ bin_start, int nbins,
                                                        int32_t* __restrict__ order) {
@@ -429,12 +431,19 @@ static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* b
   if (!RUNS)
     hipLaunchKernelGGL(k_order_window, dim3((nbins + OWIN - 1) / OWIN), dim3(OWIN), 0, s, bin_start, nbins, order);
   const int32_t* ord = RUNS ? nullptr : (const int32_t*)order;
+  // XCD chunks. Runs: whole planes of runs, so that the bins one row and one
+  // plane apart in y, which read the same cells' particles, run on one XCD
+  // and find them in its L2 (chunks of 16 runs put them on other XCDs and the
+  // particle data was fetched 4.5 times on a 128^3 grid); the planes dealt
+  // round the XCDs still balance a clustered density. Per-bin records follow
+  // the windowed bin order: chunks of 16 groups.
+  const int xch = RUNS ? NQ * XPLANES * (g.n0 / run::RUN) * g.n1 : 16 * NQ;
   if (P.Bgrid)
     hipLaunchKernelGGL((k_tsc64<PT, true, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord);
+                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch);
   else
     hipLaunchKernelGGL((k_tsc64<PT, false, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord);
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch);
   return hipGetLastError();
 }
 

@@ -63,6 +63,26 @@ constexpr int NPAIR = 378;             // packed upper triangle of one bin's 27 
 // Packed upper triangle of a bin's 27 support rows: pair(a, b), a <= b.
 constexpr int pair_index(int a, int b) { return a * 27 - (a * (a - 1)) / 2 + (b - a); }
 
+// Where the contraction parks one component of the four bins' local matrices
+// for the summation over bins: the 4x4 blocks (I, J), I <= J, of the 27 rows
+// padded to 28, as the matrix instruction leaves them, block k (row-major over
+// the upper blocks) of bin b at b * BSTRIDE + 16 k, entry (i, j) of the block
+// at 4 i + j. Each lane then stores its 28 accumulators at one base address
+// plus constant offsets. Entry (27, 27), the padding row against the padding
+// column, is an exact zero: it is the slot read for a bin that does not hold
+// an entry. BSTRIDE = 448 + 16 puts the four bins of one store on alternate
+// halves of the LDS banks.
+constexpr int NBLKR = 7;                              // row blocks of 4
+constexpr int BSTRIDE = 464;                          // slots per bin
+constexpr int ZERO0 = 27 * 16 + 15;                   // bin 0's (27, 27)
+constexpr int ZERO1 = BSTRIDE + ZERO0;                // bin 1's (27, 27)
+constexpr int upper_block(int I, int J) { return I * NBLKR - (I * (I - 1)) / 2 + (J - I); }
+constexpr int block_slot(int bin, int a, int b) {
+  return bin * BSTRIDE + 16 * upper_block(a / 4, b / 4) + 4 * (a % 4) + b % 4;
+}
+static_assert(upper_block(6, 6) == 27 && block_slot(0, 27, 27) == ZERO0 && block_slot(1, 27, 27) == ZERO1,
+              "the padding entries serve as zero slots");
+
 // Smallest dX of node column X (X + dX >= 0; dX >= 0 in the first row).
 constexpr int dx_min(int X, bool first_row) { return first_row ? 0 : (X < 2 ? -X : -2); }
 // Largest dX of node column X (X + dX < 6).
@@ -71,14 +91,16 @@ constexpr int dx_max(int X) { return 5 - X < 2 ? 5 - X : 2; }
 struct Tables {
   short seg_start[9 * NROW];  // first entry of segment (Z, Y, row): [(3 Z + Y) * NROW + row - ROW0]; -1: none
   unsigned char col_start[2][UX + 1];  // entries before column X in a segment: [first row?][X]
-  // per entry: the bins b0 .. b0 + n - 1 of the run that hold both nodes:
-  // q0 = b0 * NPAIR + pair(a, a') (bits 0..10), a = the row node's support
-  // index in bin b0 (bits 11..15), n (bits 16..17); the next bin's index is
-  // q + NPAIR - 28 + a with a one less (both nodes one column further left)
-  int contrib[NENT];
-  // per entry: where component 0 is stored (bits 0..13) and the plane stride
-  // of its slice / 16 (bits 14..17); component c is at that offset + c * stride
-  int store[NENT];
+  // per entry: the block slots (block_slot) of its value in the bins b0 ..
+  // b0 + n - 1 of the run that hold both nodes, both nodes one column further
+  // left in each next bin: q0 (bits 0..10), q1 - ZERO0 (bits 11..21) and
+  // q2 - ZERO1 (bits 22..31), q1 = ZERO0 when n < 2 and q2 = ZERO1 when n < 3
+  unsigned contrib[NENT];
+  // per entry: the byte offset of its component 0 in the run record (bits
+  // 0..16) and the plane stride of its slice in 128-byte lines (bits 17..21);
+  // component c is stored c plane strides further on
+  unsigned store_bytes[NENT];
+  unsigned char nbins[NENT];  // n of each entry (1 to 3)
   int slice_off[9];  // storage offset of slice s minus its first entry index
   int slice_stride[9];  // plane stride of slice s (slice_pad)
   int count;  // entries numbered
@@ -104,20 +126,16 @@ constexpr Tables make_tables() {
         if (!ok) continue;
         for (int X = 0; X < UX; ++X)
           for (int dx = dx_min(X, row == ROW0); dx <= dx_max(X); ++dx, ++e) {
-            int b0 = -1, n = 0, q0 = 0, a0 = 0;
+            int q[3] = {0, ZERO0, ZERO1}, n = 0;
             for (int b = 0; b < RUN; ++b) {
               const int ax = X - b, bx = X + dx - b;
               if (ax < 0 || ax > 2 || bx < 0 || bx > 2) continue;
-              if (b0 < 0) {
-                b0 = b;
-                a0 = ax + 3 * Y + 9 * Z;
-                q0 = b * NPAIR + pair_index(a0, bx + 3 * (Y + dy) + 9 * (Z + dz));
-              }
-              ++n;
+              q[n++] = block_slot(b, ax + 3 * Y + 9 * Z, bx + 3 * (Y + dy) + 9 * (Z + dz));
             }
-            t.contrib[e] = q0 | (a0 << 11) | (n << 16);
+            t.contrib[e] = (unsigned)q[0] | ((unsigned)(q[1] - ZERO0) << 11) | ((unsigned)(q[2] - ZERO1) << 22);
+            t.nbins[e] = (unsigned char)n;
             const int sl = 3 * Z + Y;
-            t.store[e] = (slice_base(sl) + e - slice_start(sl)) | ((slice_pad(sl) / 16) << 14);
+            t.store_bytes[e] = (unsigned)(8 * (slice_base(sl) + e - slice_start(sl))) | ((unsigned)(slice_pad(sl) / 16) << 17);
           }
       }
   for (int sl = 0; sl < 9; ++sl) {
@@ -129,7 +147,31 @@ constexpr Tables make_tables() {
 }
 
 static_assert(make_tables().count == NENT, "canonical union entries of a run of four bins");
+
+// Every encoded slot fits its field, and every entry gathers the first slot
+// of its bins in the upper triangle of a block (i <= j on the diagonal).
+constexpr bool contrib_fits() {
+  const Tables t = make_tables();
+  int total = 0;
+  for (int e = 0; e < NENT; ++e) {
+    const unsigned c = t.contrib[e];
+    const int q0 = (int)(c & 2047u), q1 = (int)((c >> 11) & 2047u) + ZERO0, q2 = (int)(c >> 22) + ZERO1;
+    const int n = t.nbins[e];
+    if (n < 1 || n > 3 || q0 >= RUN * BSTRIDE || q1 >= RUN * BSTRIDE || q2 >= RUN * BSTRIDE) return false;
+    if ((n < 2) != (q1 == ZERO0) || (n < 3) != (q2 == ZERO1)) return false;
+    if (q0 % 16 / 4 > q0 % 4 && (q0 % BSTRIDE) / 16 < NBLKR * (NBLKR + 1) / 2) {
+      // a slot left of the diagonal inside a diagonal block is never read
+      const int k = (q0 % BSTRIDE) / 16;
+      for (int I = 0; I < NBLKR; ++I)
+        if (upper_block(I, I) == k) return false;
+    }
+    total += n;
+  }
+  return total == RUN * NPAIR;  // each bin value is read exactly once
+}
+static_assert(contrib_fits(), "run table encoding");
 static_assert(slice_start(9) == NENT && RUNREC == 9 * 1040 && RUNREC % 2 == 0, "slices of a run record");
+static_assert(8 * RUNREC < (1 << 17), "record byte offsets fit the store table's field");
 static_assert(make_tables().col_start[0][UX] == 24 && make_tables().col_start[1][UX] == 15, "segment lengths");
 
 }  // namespace run
