@@ -41,6 +41,14 @@ constexpr int WITEMS = TILE / NWV;     // particles per wave in the scatter
 
 __device__ __forceinline__ unsigned long long lanemask_lt() { return __lanemask_lt(); }
 
+// Tile of this block in the per-tile kernels (one block per tile). The digit
+// counts are stored column by column (ghist[digit][tile]), so every tile
+// writes, and the scatter reads, one value in each of 256 columns; chunks of
+// 32 consecutive tiles on one XCD let its L2 gather those values into whole
+// lines (dealt round the XCDs, tiles are spread one per XCD and every column
+// value went to memory as a partial line).
+__device__ __forceinline__ int tile_of_block() { return xcd_chunk_remap(blockIdx.x, gridDim.x, 32); }
+
 // Lanes of the wave whose 8-bit digit equals this lane's (among `valid` lanes).
 __device__ __forceinline__ unsigned long long match_digit(int d, bool valid) {
   unsigned long long peers = __ballot(valid);
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   h[tid] = 0;
   __syncthreads();
-  const int tile = blockIdx.x;
+  const int tile = tile_of_block();
   const size_t base = (size_t)tile * TILE;
   bool desc = false;
   uint32_t kv[BI];
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, 
   if (*unsorted == 0) return;  // already in key order
   const int tid = threadIdx.x, lane = tid & 63;
   h[tid] = 0;
-  const int tile = blockIdx.x;
+  const int tile = tile_of_block();
   const size_t base = (size_t)tile * TILE;
   uint32_t kk[BI];
 #pragma unroll
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(BT) void k_scatter(const uint32_t* __restrict__ key
   __shared__ uint32_t sk[TILE];      // the tile's keys and values in digit order
   __shared__ int32_t sv[TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x;
+  const int tile = tile_of_block();
 
   // digit base of this tile: exclusive prefix of the pass totals over digits
   // plus this tile's prefix within the digit's column
