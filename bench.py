@@ -46,6 +46,7 @@ KERNEL_FILES = {
     "k_cic64": ("k_cic64.hip",) + HEADERS,
     "k_cic32": ("k_cic32.hip",) + HEADERS,
     "k_cic64v": ("k_cic64v.hip", "k_contract.hip") + HEADERS,
+    "k_cic64_reorder": ("k_cic64.hip",) + HEADERS,
     "k_tsc64": ("k_tsc64.hip", "mm_run.h") + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
@@ -59,6 +60,8 @@ KERNEL_FILES = {
 KERNEL_LABELS = {
     "k_cic64": "k_cic64 (CIC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block)",
     "k_cic32": "k_cic32 (CIC fp32 per-bin MFMA contraction, 4x4x1 f32, one bin per block)",
+    "k_cic64_reorder": "torch index_select of pos, w and B into bin order, then k_cic64 through the identity "
+                       "permutation (packed-reorder comparison, timed together)",
     "k_cic64v": "k_cic64v + k_gather (CIC fp64 per-bin contraction on vector FMAs and its deposit, "
                 "timed together as one MM_ALGO_VALU assembly call)",
     "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block, run records)",
@@ -145,7 +148,8 @@ def workload_key(args) -> str:
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
             + ("-perspecies" if args.deposit_per_species else "")
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
-            + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else ""))
+            + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else "")
+            + ("-reorder" if getattr(args, "reorder", False) else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -324,6 +328,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--algo", default="mfma",
                     help="mfma (default) | mfma_atomic | atomic | valu (the CIC contraction on vector FMAs)")
+    ap.add_argument("--reorder", action="store_true",
+                    help="comparison: after binning, gather pos, w and B into bin order (torch index_select) and "
+                         "contract through the identity permutation; the gather is timed with the contraction")
     ap.add_argument("--canonical", action="store_true",
                     help="deposit into the canonical half of the stencil (14 / 63 offsets) instead of the full one")
     ap.add_argument("--matvec", action="store_true",
@@ -375,6 +382,9 @@ def main():
             sp.pos = sp.pos.astype(np.float32).astype(np.float64)
             if sp.B is not None:
                 sp.B = sp.B.astype(np.float32).astype(np.float64)
+    if args.reorder and (args.algo != "mfma" or args.dims != 3 or args.field == "grid"):
+        print("bench.py: --reorder compares the matrix-core path with the field per particle (3D)", file=sys.stderr)
+        sys.exit(2)
     if args.canonical and args.algo != "mfma":
         print("bench.py: --canonical deposits the records of the matrix-core path (--algo mfma)", file=sys.stderr)
         sys.exit(2)
@@ -407,6 +417,11 @@ def main():
                          beta=sp.beta,
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
+        if args.reorder:  # bin-ordered copies and the identity permutation they are read through
+            d = spec[-1]
+            d["pos_r"], d["w_r"] = torch.empty_like(d["pos"]), torch.empty_like(d["w"])
+            d["B_r"] = torch.empty_like(d["B"]) if d["B"] is not None else None
+            d["ident"] = torch.arange(max(sp.np, 1), dtype=torch.int32, device=dev)
     ncomp = 9 if tensorial else 1
     nof = mm.noff_canonical(order) if args.canonical else mm.noff_grid(order, case.grid)
     M = torch.empty(nbins * nof * ncomp, dtype=tdt, device=dev)
@@ -458,8 +473,17 @@ def main():
             mark(si, 1)
             if args.algo == "mfma":
                 rec = recs[si] if multi else recs[0]
-                mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma, rec=rec,
-                                 Bgrid=Fd)
+                if args.reorder:
+                    pidx = perm[:s["pos"].shape[0]]
+                    torch.index_select(s["pos"], 0, pidx, out=s["pos_r"])
+                    torch.index_select(s["w"], 0, pidx, out=s["w_r"])
+                    if s["B"] is not None:
+                        torch.index_select(s["B"], 0, pidx, out=s["B_r"])
+                    mm.contract_bins(case.grid, order, s["pos_r"], s["w_r"], s["B_r"], bs, s["ident"], s["beta"],
+                                     case.sigma, rec=rec)
+                else:
+                    mm.contract_bins(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"], case.sigma,
+                                     rec=rec, Bgrid=Fd)
                 mark(si, 2)
                 if not multi:
                     mm.deposit_records(case.grid, order, rec, M, tensorial, accumulate=si > 0,
@@ -599,6 +623,8 @@ def main():
             kname = "k_contract"
         if args.algo == "valu":
             kname = "k_cic64v"
+        if args.reorder and dom == "contract":
+            kname = "k_cic64_reorder" if kname == "k_cic64" else kname
         peak = PEAK_FP64_MFMA if case.dtype == "f64" else PEAK_FP32_MFMA
         label = KERNEL_LABELS[kname]
         # the binding roof follows the arithmetic intensity: below the ridge
@@ -725,7 +751,7 @@ def main():
                    "order": order, "kind": case.kind, "field": args.field if tensorial else None,
                    "storage": "fp32 positions and fields, fp64 weights and matrix" if mix else case.dtype,
                    "np": np_total,
-                   "species": len(spec), "algo": args.algo, "stencil": "canonical half" if args.canonical else "full",
+                   "species": len(spec), "algo": args.algo + ("+reorder" if args.reorder else ""), "stencil": "canonical half" if args.canonical else "full",
                    "step": ("bin + contract per species, one deposit of all species' records" if multi else
                             "bin + contract + deposit per species") if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
