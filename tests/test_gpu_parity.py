@@ -133,6 +133,9 @@ SMALL = [
     (17, 2, (8, 6, 5), 3),
     (18, 2, (12, 7, 6), 20000),
     (19, 2, (16, 5, 5), 1),
+    # an odd number of runs (105): a wave of the run-record contraction that takes
+    # consecutive runs is left with one
+    (20, 2, (12, 5, 7), 9000),
 ]
 
 
