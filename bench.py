@@ -48,6 +48,7 @@ KERNEL_FILES = {
     "k_cic64v": ("k_cic64v.hip", "k_contract.hip") + HEADERS,
     "k_cic64_reorder": ("k_cic64.hip",) + HEADERS,
     "k_tsc64": ("k_tsc64.hip", "mm_run.h") + HEADERS,
+    "k_tsc32": ("k_tsc32.hip", "mm_run.h") + HEADERS,
     "k_contract": ("k_contract.hip",) + HEADERS,
     "k_gather": ("k_contract.hip",) + HEADERS,
     "k_gather_run": ("k_gather_run.hip", "mm_run.h") + HEADERS,
@@ -65,6 +66,8 @@ KERNEL_LABELS = {
     "k_cic64v": "k_cic64v + k_gather (CIC fp64 per-bin contraction on vector FMAs and its deposit, "
                 "timed together as one MM_ALGO_VALU assembly call)",
     "k_tsc64": "k_tsc64 (TSC fp64 per-bin MFMA contraction, 4x4x4 f64, one bin per block, run records)",
+    "k_tsc32": "k_tsc32 (TSC fp32 per-bin MFMA contraction, 4x4x1 f32, one bin and component per block, "
+               "run records)",
     "k_contract": "k_contract (per-bin MFMA contraction)",
     "k_gather": "k_gather (stencil deposition of the per-bin records)",
     "k_gather_run": "k_gather_run (stencil deposition of the records of x-runs of four bins)",
@@ -595,8 +598,9 @@ def main():
     flops = flops_per_particle(order, tensorial, args.dims) * np_launch
     # records as the library lays them out for this grid (run records, or one packed triangle per bin)
     rec_total = 0
-    if args.algo == "mfma" and args.dims == 3 and order == 2 and tensorial and case.dtype == "f64":
-        rec_total = mm.record_bytes(case.grid, order, torch.float64, True)
+    if args.algo == "mfma" and args.dims == 3 and order == 2 and tensorial:
+        rec_total = mm.record_bytes(case.grid, order, tdt, True)
+    run_records = rec_total > 0 and case.grid.n[0] % 4 == 0
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem, args.dims,
                             8 if args.dims == 2 else 0, rec_total=rec_total)
     # one deposition of every species' record sets, or the average over the
@@ -609,7 +613,6 @@ def main():
         dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
                                    dims=args.dims, rec_elem=8 if args.dims == 2 else 0, rec_total=rec_total)
                      for si in range(len(spec))) / len(spec)
-    run_records = rec_total > 0 and case.grid.n[0] % 4 == 0
     if dom == "deposit":
         kname = "k_gather2d" if args.dims == 2 else ("k_gather_run" if run_records else "k_gather")
         roof = {"kernel": KERNEL_LABELS[kname], "bound": "hbm",
@@ -617,6 +620,8 @@ def main():
         roof["algorithmic_bytes_per_launch"] = dbytes
     else:
         kname = contract_kernel(order, case.dtype, tensorial) if dom == "contract" else "k_atomic_scatter"
+        if kname == "k_contract" and run_records and case.dtype == "f32":
+            kname = "k_tsc32"
         if args.dims == 2 and dom == "contract":
             kname = "k_mass2d"
         if args.algo == "mfma_atomic":

@@ -187,6 +187,15 @@ mm_status mm_assemble_ecsim_gridB(const mm_grid* grid, int order, mm_dtype dt, i
  * for support rows a <= b (upper triangle, pair(a,b) = a*N - a(a-1)/2 + b - a,
  * N = 8 or 27), comp as in M. B == NULL selects the scalar matrix (one comp);
  * with np == 0 a tensorial call still passes a non-NULL B (it is not read).
+ * Order 2 tensorial on a 3D grid whose n[0] is a multiple of 4 (MM_F64,
+ * MM_MIX, and MM_F32 with the field per particle or interpolated): the
+ * records are instead summed over runs of four bins along x (first support
+ * nodes 4r .. 4r+3, same y and z): one record per run holding the 999
+ * canonical node pairs of the runs' 6 x 3 x 3 union support that some bin of
+ * the run covers, 9,360 values per run (grouped by the row node's y and z,
+ * each group's nine component planes padded to 16 values). The layout is the
+ * library's own; the deposit entry points read it, and mm_record_bytes gives
+ * its size.
  *  rec       device buffer of *rec_bytes bytes (query with rec == NULL),
  *            16-byte aligned (else MM_ERR_ARG). The records start at rec.
  *            For order 2 tensorial fp64 (and MM_MIX) the query also counts

@@ -500,6 +500,8 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
     return launch_cic32(g, P, bin_start, perm, beta, sigma, (float*)out, s);
   if (mode == MODE_RECORD && order == 2 && !f32 && (P.B || P.Bgrid))
     return launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
+  if (mode == MODE_RECORD && order == 2 && f32 && P.B && !P.Bgrid && tsc_run_records(g))
+    return launch_tsc32(g, P, bin_start, perm, beta, sigma, (float*)out, s);
   if (P.Bgrid) return hipErrorInvalidValue;  // the other kernels take a per-particle field (interp first)
   if (mode == MODE_RECORD)
     return f32 ? contract_t<float, MODE_RECORD>(g, order, P, bin_start, perm, beta, sigma, out, s)
@@ -514,8 +516,8 @@ bool contract_gathers_field(int order, bool f32, int mode) {
 
 size_t record_bytes(int order, bool f32, bool tensorial, const GridDev& g) {
   const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
-  if (order == 2 && !f32 && tensorial && tsc_run_records(g))  // one record per run of four bins
-    return (size_t)(nbins / run::RUN) * run::RUNREC * sizeof(double);
+  if (order == 2 && tensorial && tsc_run_records(g))  // one record per run of four bins
+    return (size_t)(nbins / run::RUN) * run::RUNREC * (f32 ? 4 : 8);
   const int npair = order == 1 ? Geo<1>::NPAIR : Geo<2>::NPAIR;
   const size_t recb = (size_t)nbins * npair * (tensorial ? 9 : 1) * (f32 ? 4 : 8);
   if (order == 2 && !f32 && tensorial)  // k_tsc64 keeps its bin order after the records
@@ -764,8 +766,8 @@ static hipError_t gather_dispatch(const GridDev& g, int order, bool f32, bool te
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
                          int accumulate,
                          void* M, hipStream_t s, bool canonical) {
-  if (order == 2 && !f32 && tensorial && tsc_run_records(g))  // run records of k_tsc64
-    return launch_gather_run(g, rec, nrec, accumulate, M, s, canonical);
+  if (order == 2 && tensorial && tsc_run_records(g))  // run records of k_tsc64 / k_tsc32
+    return launch_gather_run(g, rec, nrec, accumulate, M, s, canonical, f32);
   return canonical ? gather_dispatch<true>(g, order, f32, tensorial, rec, nrec, accumulate, M, s)
                    : gather_dispatch<false>(g, order, f32, tensorial, rec, nrec, accumulate, M, s);
 }

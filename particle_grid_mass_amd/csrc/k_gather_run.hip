@@ -1,6 +1,6 @@
 // Deposit of run records (mm_run.h) into the stencil matrix, phase 2 of the
-// second-order fp64 tensorial assembly on grids whose x extent is a multiple
-// of four.
+// second-order tensorial assembly (fp64, and fp32 with the field per
+// particle) on grids whose x extent is a multiple of four.
 //
 // Pennati & Markidis, "Mass Matrix Assembly on Tensor Cores for Implicit
 // Particle-In-Cell Methods", Sec. 3.4: every stencil entry M[g][o] is the sum
@@ -38,12 +38,12 @@ constexpr int ZB = 1;  // node rows in plain order, y fastest: consecutive rows 
 
 constexpr int PAIRS = 64;  // (node, offset) pairs per block, one per lane of each wave
 
-template <bool CANON, int NR>
-__global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<double> recs, int accumulate,
-                                                          double* __restrict__ M, int blocks_per_row) {
+template <typename T, bool CANON, int NR>
+__global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<T> recs, int accumulate,
+                                                          T* __restrict__ M, int blocks_per_row) {
   constexpr int NC = 9;
   constexpr int NOFF = 125;
-  __shared__ double st[PAIRS * NC];
+  __shared__ T st[PAIRS * NC];
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int rv = blk / blocks_per_row;  // visit order of the node row
   const int lane = threadIdx.x & 63, i = threadIdx.x >> 6;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<doub
   const int c1 = kRunG.col_start[first][x1] + ox - run::dx_min(x1, first);
   const int c2 = x2 < run::UX ? kRunG.col_start[first][x2] + ox - run::dx_min(x2, first) : 0;
 
-  double sum[3] = {0.0, 0.0, 0.0};
+  T sum[3] = {T(0), T(0), T(0)};
   if (active) {
 #pragma unroll
     for (int Z = 0; Z < 3; ++Z) {
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<doub
 #pragma unroll
           for (int q = 0; q < NR; ++q) {
             if (q == 0 || q < recs.n) {  // (uniform)
-              const double* src = recs.r[q] + off;
+              const T* src = recs.r[q] + off;
 #pragma unroll
               for (int j = 0; j < 3; ++j) sum[j] += src[j * stride];
             }
@@ -123,43 +123,51 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<doub
     const int qx = qrem / 5, qxi = qrem - qx * 5;
     const int qo = qxi + 5 * qyz;
     if (pp >= run::NROW * per || qo < run::CENTRE) continue;
-    const double v = st[idx];
+    const T v = st[idx];
     const size_t node = (size_t)qx + (size_t)g.n0 * ((size_t)gy + (size_t)g.n1 * gz);
-    double* dst = CANON ? M + (node * 63 + (qo - run::CENTRE)) * NC + c : M + (node * NOFF + qo) * NC + c;
+    T* dst = CANON ? M + (node * 63 + (qo - run::CENTRE)) * NC + c : M + (node * NOFF + qo) * NC + c;
     *dst = accumulate ? *dst + v : v;
     if (!CANON && qo != run::CENTRE) {  // the mirrored entry M[g + d][-o]
       int mx = qx + qxi - 2, my = gy + qyz % 5 - 2, mz = gz + qyz / 5 - 2;
       mx = mx < 0 ? mx + g.n0 : (mx >= g.n0 ? mx - g.n0 : mx);
       my = my < 0 ? my + g.n1 : (my >= g.n1 ? my - g.n1 : my);
       mz = mz < 0 ? mz + g.n2 : (mz >= g.n2 ? mz - g.n2 : mz);
-      double* mdst =
+      T* mdst =
           M + (((size_t)mx + (size_t)g.n0 * ((size_t)my + (size_t)g.n1 * mz)) * NOFF + (NOFF - 1 - qo)) * NC + c;
       *mdst = accumulate ? *mdst + v : v;
     }
   }
 }
 
-template <bool CANON, int NR>
-hipError_t go(const GridDev& g, const RecSet<double>& rs, int accumulate, void* M, hipStream_t s) {
+template <typename T, bool CANON, int NR>
+hipError_t go(const GridDev& g, const RecSet<T>& rs, int accumulate, void* M, hipStream_t s) {
   const size_t row_pairs = (size_t)run::NROW * 5 * g.n0;  // (dY, dZ) rows x dX x nodes of a node row
   const int bpr = (int)((row_pairs + PAIRS - 1) / PAIRS);
   const size_t blocks = (size_t)bpr * g.n1 * g.n2;
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gather_run<CANON, NR>), dim3((unsigned)blocks), dim3(3 * PAIRS), 0, s, g, rs, accumulate,
-                     (double*)M, bpr);
+  hipLaunchKernelGGL((k_gather_run<T, CANON, NR>), dim3((unsigned)blocks), dim3(3 * PAIRS), 0, s, g, rs, accumulate,
+                     (T*)M, bpr);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t gather_run_t(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M, hipStream_t s,
+                        bool canonical) {
+  RecSet<T> rs{};
+  for (int q = 0; q < nrec; ++q) rs.r[q] = (const T*)rec[q];
+  rs.n = nrec;
+  if (nrec > 1)
+    return canonical ? go<T, true, MAX_REC>(g, rs, accumulate, M, s) : go<T, false, MAX_REC>(g, rs, accumulate, M, s);
+  return canonical ? go<T, true, 1>(g, rs, accumulate, M, s) : go<T, false, 1>(g, rs, accumulate, M, s);
 }
 
 }  // namespace
 
 hipError_t launch_gather_run(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
-                             hipStream_t s, bool canonical) {
+                             hipStream_t s, bool canonical, bool f32) {
   if (nrec < 1 || nrec > MAX_REC || !tsc_run_records(g)) return hipErrorInvalidValue;
-  RecSet<double> rs{};
-  for (int q = 0; q < nrec; ++q) rs.r[q] = (const double*)rec[q];
-  rs.n = nrec;
-  if (nrec > 1) return canonical ? go<true, MAX_REC>(g, rs, accumulate, M, s) : go<false, MAX_REC>(g, rs, accumulate, M, s);
-  return canonical ? go<true, 1>(g, rs, accumulate, M, s) : go<false, 1>(g, rs, accumulate, M, s);
+  return f32 ? gather_run_t<float>(g, rec, nrec, accumulate, M, s, canonical)
+             : gather_run_t<double>(g, rec, nrec, accumulate, M, s, canonical);
 }
 
 }  // namespace mmk

@@ -31,11 +31,15 @@ hipError_t launch_cic32(const GridDev& g, const Particles& P, const int32_t* bin
 // per (group of four bins, row of alpha).
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
+// Phase 1 for TSC fp32 ECSIM run records (tsc_run_records(g), field per
+// particle): 4x4x1 fp32 blocks, 8 bins and two components per wave.
+hipError_t launch_tsc32(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                        double beta, double sigma, float* rec, hipStream_t s);
 // Bytes k_tsc64 uses after its per-bin records (rounded up to 256) for the bin order.
 size_t tsc64_order_bytes(int64_t nbins);
-// Whether the order-2 fp64 tensorial records of this grid are run records
-// (mm_run.h: x-runs of four bins; 3D grids with n0 a multiple of 4) rather
-// than per-bin pair records.
+// Whether the order-2 tensorial records of this grid (fp64, and fp32 with the
+// field per particle) are run records (mm_run.h: x-runs of four bins; 3D
+// grids with n0 a multiple of 4) rather than per-bin pair records.
 bool tsc_run_records(const GridDev& g);
 
 // Whether launch_contract gathers a grid field itself (Particles::Bgrid) for
@@ -49,7 +53,7 @@ hipError_t launch_probe_mfma_f64(int nblocks, int iters, double* out, hipStream_
 
 // Bytes of the records of this grid: packed per-bin records, nbins * N(N+1)/2 *
 // ncomp * sizeof(T) (plus the TSC bin order), or the run records of order-2
-// fp64 tensorial grids (tsc_run_records).
+// tensorial grids (tsc_run_records), in the precision of the records.
 size_t record_bytes(int order, bool f32, bool tensorial, const GridDev& g);
 
 // Phase 2: M[g][o][c] (=|+=) sum of the records of the bins that hold both g and g+o,
@@ -64,10 +68,11 @@ struct RecSet {
 hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, const void* const* rec, int nrec,
                          int accumulate, void* M, hipStream_t s, bool canonical = false);
 
-// Phase 2 for run records (order 2, fp64, tensorial, tsc_run_records(g)):
-// the same sums as launch_gather, read from the records of x-runs of four bins.
+// Phase 2 for run records (order 2, tensorial, tsc_run_records(g)): the same
+// sums as launch_gather, read from the records of x-runs of four bins (fp32 or
+// fp64 records and output).
 hipError_t launch_gather_run(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
-                             hipStream_t s, bool canonical);
+                             hipStream_t s, bool canonical, bool f32);
 
 // The 2D problem (n2 == 1): per-bin fp64 records rec[bin][pair][comp] of the
 // (R+1)^2 support, and their fixed-order sum into M [nnodes][(2R+1)^2][comp]

@@ -80,7 +80,14 @@ constexpr int upper_block(int I, int J) { return I * NBLKR - (I * (I - 1)) / 2 +
 constexpr int block_slot(int bin, int a, int b) {
   return bin * BSTRIDE + 16 * upper_block(a / 4, b / 4) + 4 * (a % 4) + b % 4;
 }
-static_assert(upper_block(6, 6) == 27 && block_slot(0, 27, 27) == ZERO0 && block_slot(1, 27, 27) == ZERO1,
+// The same with each block stored transposed (entry (i, j) at 4 j + i): the
+// layout in which the fp32 4x4x1 instruction leaves a lane's four values of a
+// block (one column) contiguous, so a lane parks a block with one 16-byte store.
+constexpr int block_slot_t(int bin, int a, int b) {
+  return bin * BSTRIDE + 16 * upper_block(a / 4, b / 4) + 4 * (b % 4) + a % 4;
+}
+static_assert(upper_block(6, 6) == 27 && block_slot(0, 27, 27) == ZERO0 && block_slot(1, 27, 27) == ZERO1 &&
+                  block_slot_t(0, 27, 27) == ZERO0 && block_slot_t(1, 27, 27) == ZERO1,
               "the padding entries serve as zero slots");
 
 // Smallest dX of node column X (X + dX >= 0; dX >= 0 in the first row).
@@ -96,6 +103,7 @@ struct Tables {
   // left in each next bin: q0 (bits 0..10), q1 - ZERO0 (bits 11..21) and
   // q2 - ZERO1 (bits 22..31), q1 = ZERO0 when n < 2 and q2 = ZERO1 when n < 3
   unsigned contrib[NENT];
+  unsigned contrib_t[NENT];  // the same slots in the transposed block layout (block_slot_t)
   // per entry: the byte offset of its component 0 in the run record (bits
   // 0..16) and the plane stride of its slice in 128-byte lines (bits 17..21);
   // component c is stored c plane strides further on
@@ -126,13 +134,17 @@ constexpr Tables make_tables() {
         if (!ok) continue;
         for (int X = 0; X < UX; ++X)
           for (int dx = dx_min(X, row == ROW0); dx <= dx_max(X); ++dx, ++e) {
-            int q[3] = {0, ZERO0, ZERO1}, n = 0;
+            int q[3] = {0, ZERO0, ZERO1}, qt[3] = {0, ZERO0, ZERO1}, n = 0;
             for (int b = 0; b < RUN; ++b) {
               const int ax = X - b, bx = X + dx - b;
               if (ax < 0 || ax > 2 || bx < 0 || bx > 2) continue;
-              q[n++] = block_slot(b, ax + 3 * Y + 9 * Z, bx + 3 * (Y + dy) + 9 * (Z + dz));
+              const int na = ax + 3 * Y + 9 * Z, nb = bx + 3 * (Y + dy) + 9 * (Z + dz);
+              qt[n] = block_slot_t(b, na, nb);
+              q[n++] = block_slot(b, na, nb);
             }
             t.contrib[e] = (unsigned)q[0] | ((unsigned)(q[1] - ZERO0) << 11) | ((unsigned)(q[2] - ZERO1) << 22);
+            t.contrib_t[e] =
+                (unsigned)qt[0] | ((unsigned)(qt[1] - ZERO0) << 11) | ((unsigned)(qt[2] - ZERO1) << 22);
             t.nbins[e] = (unsigned char)n;
             const int sl = 3 * Z + Y;
             t.store_bytes[e] = (unsigned)(8 * (slice_base(sl) + e - slice_start(sl))) | ((unsigned)(slice_pad(sl) / 16) << 17);
