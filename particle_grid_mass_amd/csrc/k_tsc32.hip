@@ -265,9 +265,11 @@ __global__ __launch_bounds__(64) void k_tsc32(GridDev g, const float* __restrict
         const unsigned t = tb[q];
         const unsigned sb = ts[q];
         const float v = (sm[t & 2047u] + sm[((t >> 11) & 2047u) + run::ZERO0]) + sm[(t >> 22) + run::ZERO1];
-        // float offset = half the double offset of the same entry; comp planes of its slice
+        // float offset = half the double offset of the same entry; comp planes of
+        // its slice. Nontemporal, as in the fp64 kernel: the records are read
+        // again only by the deposit.
         const unsigned o = ((sb & 0x1ffffu) >> 1) + comp * 64u * (sb >> 17);
-        if (q < NIT - 1 || lane + 64 * q < run::NENT) *reinterpret_cast<float*>(dst + o) = v;
+        if (q < NIT - 1 || lane + 64 * q < run::NENT) __builtin_nontemporal_store(v, reinterpret_cast<float*>(dst + o));
       }
       wave_sync();
     }

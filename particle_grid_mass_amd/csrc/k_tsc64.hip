@@ -351,9 +351,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int q = 0; q < HB; ++q) {
           const double v = (x[q][0] + x[q][1]) + x[q][2];
           const int e = lane + 64 * (h + q);
-          // byte offset of the entry's component-0 value plus comp planes of its slice
+          // byte offset of the entry's component-0 value plus comp planes of its slice;
+          // nontemporal: the records are read again only by the deposit, and
+          // kept out of the way in L2 the particle lines that the group's other
+          // waves and its y neighbours read stay there (128^3 clustered:
+          // FETCH_SIZE 11.0M -> 8.2M KiB per launch, contraction 26.7 -> 26.2 ms)
           const unsigned o = (ts[h + q] & 0x1ffffu) + comp * 128u * (ts[h + q] >> 17);
-          if (h + q < NIT - 1 || e < run::NENT) *reinterpret_cast<double*>(dst + o) = v;
+          if (h + q < NIT - 1 || e < run::NENT) __builtin_nontemporal_store(v, reinterpret_cast<double*>(dst + o));
         }
       }
       wave_sync();
