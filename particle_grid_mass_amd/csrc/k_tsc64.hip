@@ -233,8 +233,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // dealt round the XCDs: a contiguous range per XCD put 1.3 times the mean
   // work on the XCDs whose range held a cluster of a clustered density
   const int lid = xcd_chunk_remap(blockIdx.x, gridDim.x, xch);
-  const int grp = lid / NQ, row = lid - grp * NQ;     // row of alpha: components CPW*row ..
-  if (grp >= ngroups) return;
+  const int vis = lid / NQ, row = lid - vis * NQ;     // row of alpha: components CPW*row ..
+  if (vis >= ngroups) return;
+  // Run records on a grid of an even number of planes: groups are visited by
+  // pairs of planes, row by row, the two planes' rows one after the other
+  // (the particles of a cell plane are read by the bins of two consecutive
+  // planes, which then run on one XCD close in time); otherwise in order.
+  int grp = vis;
+  if (RUNS && (g.n2 & 1) == 0) {
+    const int R = g.n0 / run::RUN, pr = 2 * R * g.n1;  // runs per row, per plane pair
+    const int pz = vis / pr, t = vis - pz * pr;
+    const int y = t / (2 * R), u = t - y * 2 * R;
+    const int zz = u / R, x = u - zz * R;
+    grp = x + R * (y + g.n1 * (2 * pz + zz));
+  }
   const Group G = load_group(bin_start, order, grp, nbins, np, lane);
   double* sF = smem + SMEM;
   if (GB) {
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // about 4% of the work as padding. Each bin's record depends only on its own
 // particles, so the records are the same in any order.
 constexpr int OWIN = 256;
-constexpr int XPLANES = 1;  // planes of runs per XCD chunk
+constexpr int XPLANES = 2;  // planes of runs per XCD chunk (the visit order pairs planes)
 
 __global__ __launch_bounds__(OWIN) void k_order_window(const int32_t* __restrict__ bin_start, int nbins,
                                                        int32_t* __restrict__ order) {
@@ -441,7 +453,7 @@ static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* b
   // particle data was fetched 4.5 times on a 128^3 grid); the planes dealt
   // round the XCDs still balance a clustered density. Per-bin records follow
   // the windowed bin order: chunks of 16 groups.
-  const int xch = RUNS ? NQ * XPLANES * (g.n0 / run::RUN) * g.n1 : 16 * NQ;
+  const int xch = RUNS ? NQ * XPLANES * (g.n0 / run::RUN) * g.n1 : 16 * NQ;  // a plane pair per chunk
   if (P.Bgrid)
     hipLaunchKernelGGL((k_tsc64<PT, true, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
                        (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch);
