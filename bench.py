@@ -147,12 +147,14 @@ def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
             + f", {case.name}" + ("_gridB" if field_on_grid else "") + ("_mix" if mix else ""))
 
 
-def workload_key(args) -> str:
+def workload_key(args, slab: int = 0) -> str:
+    """Key of the workload (and launch shape) in the committed counter table:
+    slab > 0 names the slab launches of the overlapped schedule."""
     return (f"config{args.config}" + (f"-{args.kind}" if args.kind else "") + f"-{args.dtype}"
             + ("-perspecies" if args.deposit_per_species else "")
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
             + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else "")
-            + ("-reorder" if getattr(args, "reorder", False) else ""))
+            + ("-reorder" if getattr(args, "reorder", False) else "") + (f"-slabs{slab}" if slab else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -351,6 +353,11 @@ def main():
                     help="skip the on-box peak measurements (matrix-instruction probe and a 1 GiB copy)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the extra pass that times steps with the MALL flushed before each")
+    ap.add_argument("--overlap", default="auto", choices=("auto", "off"),
+                    help="auto: on grids the library assembles by slabs of planes (mm_slab_planes), contract slab "
+                         "by slab and deposit each slab's completed node planes on a second stream meanwhile (the "
+                         "schedule of mm_assemble_ecsim, driven here through the plane-range entry points so that "
+                         "the contraction launches can be bracketed with events); off: the two phases in turn")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -434,8 +441,23 @@ def main():
     # species' matrices enter one field operator); --deposit-per-species
     # deposits each species' records on its own instead.
     multi = args.algo == "mfma" and len(spec) > 1 and args.dims == 3 and not args.deposit_per_species
+    # Slabs of planes: the contraction of slab k on the step's stream, then the
+    # node planes it completed deposited on a second stream while slab k + 1
+    # contracts (a node plane reads the records of its bin plane and the two
+    # before it; planes 0 and 1 wait for the last slab).
+    slab = 0
+    if (args.overlap == "auto" and args.algo == "mfma" and args.dims == 3 and tensorial and order == 2
+            and not on_grid and not multi and not args.canonical and not args.reorder):
+        slab = mm.slab_planes(case.grid, order)
+    overlap = slab > 0
+    zb = list(range(0, case.grid.n[2], slab)) + [case.grid.n[2]] if overlap else []
+    nslab = len(zb) - 1 if overlap else 1
+    side = torch.cuda.Stream(dev) if overlap else None
+    slab_ev = [torch.cuda.Event() for _ in range(nslab)] if overlap else []
     recs = []
-    if args.algo == "mfma":
+    if overlap:  # the record buffer only: every launch of the timed kernel is a slab launch
+        recs.append(torch.empty(mm.record_bytes(case.grid, order, tdt, True), dtype=torch.uint8, device=dev))
+    elif args.algo == "mfma":
         for s_ in (spec if multi else spec[:1]):
             bs_, perm_ = mm.bin_particles(case.grid, order, s_["pos"], s_["bs"], s_["perm"], mixed=mix)
             recs.append(mm.contract_bins(case.grid, order, s_["pos"], s_["w"], s_["B"], bs_, perm_, s_["beta"],
@@ -453,10 +475,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
     phases = ("bin", "contract", "deposit")
 
-    def step(evs, marks=(0, 1, 2, 3)):
+    def step(evs, marks=(0, 1, 2, 3), ovl=None):
         """One step over every species; records evs[si][k] for k in marks at the
         phase boundaries (0 before binning, 1 after binning, 2 after the
-        contraction, 3 after the deposit)."""
+        contraction, 3 after the deposit). With the slab overlap (ovl, default
+        as chosen above) mark 2 follows the last slab's contraction on the
+        step's stream and mark 3 the join with the second stream."""
+        ovl = overlap if ovl is None else ovl
         def mark(si, k):
             if evs is not None and k in marks:
                 evs[si][k].record(stream)
@@ -474,7 +499,22 @@ def main():
                 continue
             bs, perm = mm.bin_particles(case.grid, order, s["pos"], s["bs"], s["perm"], mixed=mix)
             mark(si, 1)
-            if args.algo == "mfma":
+            if args.algo == "mfma" and ovl:
+                rec = recs[0]
+                side.wait_stream(stream)
+                for k in range(nslab):
+                    mm.contract_bins_planes(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"],
+                                            case.sigma, zb[k], zb[k + 1], rec)
+                    slab_ev[k].record(stream)
+                    side.wait_event(slab_ev[k])
+                    with torch.cuda.stream(side):
+                        mm.deposit_records_planes(case.grid, order, rec, M, 2 if k == 0 else zb[k], zb[k + 1],
+                                                  accumulate=si > 0)
+                        if k == nslab - 1:
+                            mm.deposit_records_planes(case.grid, order, rec, M, 0, 2, accumulate=si > 0)
+                mark(si, 2)
+                stream.wait_stream(side)
+            elif args.algo == "mfma":
                 rec = recs[si] if multi else recs[0]
                 if args.reorder:
                     pidx = perm[:s["pos"].shape[0]]
@@ -593,16 +633,34 @@ def main():
                 "flush": "512 MiB device fill before each step, outside the events around the step"}
         print(f"[bench] cold pass done ({csteps} steps)", file=sys.stderr, flush=True)
 
+    # The contraction once more without the overlap (whole-grid launches, the
+    # phases in turn), untimed: the kernel's rate when it has the chip to
+    # itself, beside its rate in the overlapped steps.
+    solo_ms = None
+    if overlap:
+        ksteps = max(1, min(args.steps, 10))
+        kev = new_events(ksteps)
+        torch.cuda.synchronize()
+        for k in range(ksteps):
+            step(kev[k], (1, 2), ovl=False)
+        torch.cuda.synchronize()
+        solo_ms = sum(kev[k][si][1].elapsed_time(kev[k][si][2]) for k in range(ksteps)
+                      for si in range(len(spec))) / (ksteps * len(spec))
+        print(f"[bench] whole-grid contraction pass done ({ksteps} steps)", file=sys.stderr, flush=True)
+
     np_launch = np_total / len(spec)
+    # with the overlap the bracket holds the step's nslab slab launches
+    per = nslab if overlap and dom == "contract" else 1
+    launches *= per
     t_dom = dom_ms / launches * 1e-3
-    flops = flops_per_particle(order, tensorial, args.dims) * np_launch
+    flops = flops_per_particle(order, tensorial, args.dims) * np_launch / per
     # records as the library lays them out for this grid (run records, or one packed triangle per bin)
     rec_total = 0
     if args.algo == "mfma" and args.dims == 3 and order == 2 and tensorial:
         rec_total = mm.record_bytes(case.grid, order, tdt, True)
     run_records = rec_total > 0 and case.grid.n[0] % 4 == 0
     cbytes = contract_bytes(order, tensorial, elem, int(np_launch), nbins, on_grid, pelem, args.dims,
-                            8 if args.dims == 2 else 0, rec_total=rec_total)
+                            8 if args.dims == 2 else 0, rec_total=rec_total) / per
     # one deposition of every species' record sets, or the average over the
     # species' launches: the first overwrites M, the others accumulate into it
     # (read and write)
@@ -651,13 +709,27 @@ def main():
         roof["hbm_frac"] = cbytes / t_dom / PEAK_HBM
     roof["frac"] = roof["achieved"] / roof["peak"]
     khash = kernel_source_hash(kname)
-    traffic = pmc_traffic(kname, khash, workload_key(args))
+    traffic = pmc_traffic(kname, khash, workload_key(args, slab if overlap else 0))
     roof["traffic"] = traffic
     roof["traffic_note"] = ("rocprofv3 FETCH_SIZE x fetch_factor + WRITE_SIZE x write_factor per launch "
                             "(profiles/pmc_traffic.json)" if traffic is not None else
                             "no counter run on this kernel source and workload")
     roof["avg_launch_ms"] = t_dom * 1e3
     roof["launches_timed"] = launches  # launches of the timed steps bracketed by events (every mark_every-th step)
+    if per > 1:
+        roof["launch_note"] = (f"slab launches: the contraction of {slab} bin planes each, {nslab} per step, "
+                               f"with the deposition of earlier slabs running beside them on a second stream; "
+                               f"per-launch figures are the step's totals / {nslab}")
+    if solo_ms is not None and dom == "contract":
+        t_solo = solo_ms * 1e-3
+        if roof["bound"] == "mfma":
+            a_solo = flops * per / t_solo / 1e12
+        else:
+            a_solo = cbytes * per / t_solo / 1e9
+        roof["whole_grid_launch"] = {"avg_launch_ms": solo_ms, "achieved": a_solo, "frac": a_solo / roof["peak"],
+                                     "launches": ksteps * len(spec),
+                                     "note": "the whole-grid contraction with the chip to itself (phases in turn), "
+                                             "untimed pass after the timed one"}
     roof["kernel_source_hash"] = khash
     # the same achieved rate against the peak measured on this machine
     peaks = onbox_peaks(dev, stream) if not args.no_peaks else None
@@ -758,10 +830,15 @@ def main():
                    "np": np_total,
                    "species": len(spec), "algo": args.algo + ("+reorder" if args.reorder else ""), "stencil": "canonical half" if args.canonical else "full",
                    "step": ("bin + contract per species, one deposit of all species' records" if multi else
-                            "bin + contract + deposit per species") if args.algo == "mfma" else
+                            (f"bin + contract by slabs of {slab} planes, each slab's completed node planes "
+                             f"deposited on a second stream during the next slab's contraction" if overlap else
+                             "bin + contract + deposit per species")) if args.algo == "mfma" else
                    ("bin + assemble per species" if args.algo != "atomic" else "atomic scatter per species")},
         "phases_ms_per_launch": phase_per_launch_ms,
-        "phases_from": f"untimed pass of {psteps} steps with events at every phase boundary",
+        "phases_from": f"untimed pass of {psteps} steps with events at every phase boundary"
+                       + (": contract = the slab contractions on the step's stream (the deposits of earlier slabs "
+                          "run beside them), deposit = what remains of the deposition after the last slab"
+                          if overlap else ""),
         "assembly_only_particles_per_s": np_total / ((phase_ms["contract"] + phase_ms["deposit"]) / psteps * 1e-3)
         if args.algo != "atomic" else value,
         "roofline": roof,

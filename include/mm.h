@@ -153,6 +153,10 @@ mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_
  *  B [np][3]: magnetic field at each particle (dtype dt).
  *  M [nnodes][noff][3][3] output (dtype dt), row i of alpha first.
  *  Other arguments as for mm_assemble_scalar.
+ * With MM_ALGO_MFMA on large second-order grids (mm_slab_planes) the
+ * contraction and the deposition overlap by slabs of planes on two streams
+ * of the device; M is bit-identical to mm_contract_bins followed by
+ * mm_deposit_records, and the call stays ordered on `stream`.
  */
 mm_status mm_assemble_ecsim(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
                             const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
@@ -273,6 +277,58 @@ mm_status mm_deposit_records_canonical(const mm_grid* grid, int order, mm_dtype 
 #define MM_MAX_RECORD_SETS 4
 mm_status mm_deposit_records_multi(const mm_grid* grid, int order, mm_dtype dt, int tensorial, int canonical,
                                    int nrec, const void* const* recs, int accumulate, void* M, mm_stream_t stream);
+
+/*
+ * Slabs of planes. The two phases above restricted to planes of the grid, for
+ * callers that overlap them (mm_assemble_ecsim does so itself on large
+ * grids) or bound the work of one call. The split by planes is this
+ * library's; the page assembles the whole grid in one pass (Sec. 3). Only the
+ * run records apply (order 2 tensorial on a 3D grid whose n[0] is a multiple
+ * of 4; MM_F64 and MM_MIX, and MM_F32 with the field per particle); other
+ * grids, orders or a NULL B give MM_ERR_UNSUPPORTED.
+ *
+ * mm_contract_bins_planes - mm_contract_bins for the bins whose first support
+ * node lies in planes z0 <= z < z1 (0 <= z0 <= z1 <= n[2], else MM_ERR_ARG;
+ * z0 == z1 enqueues nothing): the run records of those planes' runs, each
+ * bit-identical to the one mm_contract_bins writes; the other runs' records
+ * are not touched.
+ *  rec        device buffer holding the records of the whole grid (rec_bytes
+ *             of them, at least mm_record_bytes for dt, else
+ *             MM_ERR_WORKSPACE), 16-byte aligned (else MM_ERR_ARG).
+ *  Other arguments as for mm_contract_bins; bin_start and perm cover all
+ *  particles (mm_bin_particles), the particles of other planes are not read.
+ *
+ * mm_deposit_records_planes - mm_deposit_records_multi for the nodes g of
+ * planes z0 <= z < z1 only: it computes M[g][o] for those nodes and the
+ * offsets o >= centre, and in the full stencil (canonical == 0) stores each
+ * also at its mirrored entry M[g + d(o)][-o], a node of planes z .. z + 2
+ * (periodic). Calls whose plane ranges partition 0 .. n[2] - 1 together
+ * write every entry of M once, bit-identical to one mm_deposit_records_multi
+ * call. The call reads the records of bin planes z0 - 2 .. z1 - 1 (periodic):
+ * those must be complete, the others may still be written meanwhile.
+ *  Arguments as for mm_deposit_records_multi, z0 and z1 as above.
+ */
+/*
+ * mm_slab_planes - the slab thickness mm_assemble_ecsim and
+ * mm_assemble_ecsim_gridB use with MM_ALGO_MFMA on this grid: on run-record
+ * grids of at least 8192 cells per plane and 16 planes they contract slabs of
+ * *planes bin planes in order (the last may be thinner) and deposit each
+ * slab's completed node planes on a second stream of the device while the
+ * next slab contracts (the library creates that stream and its events on the
+ * device's first such call and keeps them; calls that overlap on one device
+ * serialise their deposits on it). *planes = 0: the two phases run in turn.
+ * The results are bit-identical either way. Nothing is enqueued.
+ *  planes  host output; NULL -> MM_ERR_NULL. Grid and order errors as for
+ *          mm_assemble_ecsim.
+ */
+mm_status mm_slab_planes(const mm_grid* grid, int order, int* planes);
+mm_status mm_contract_bins_planes(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                  const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                                  double beta, double sigma, int z0, int z1, void* rec, size_t rec_bytes,
+                                  mm_stream_t stream);
+mm_status mm_deposit_records_planes(const mm_grid* grid, int order, mm_dtype dt, int canonical, int nrec,
+                                    const void* const* recs, int accumulate, int z0, int z1, void* M,
+                                    mm_stream_t stream);
 
 /*
  * mm_deposit_moments - deposition of per-particle quantities with the same

@@ -5,10 +5,11 @@ ABI of ``include/mm.h``); this package is its thin torch binding.
 """
 from .api import (MMError, assemble_ecsim, assemble_ecsim_gridB, assemble_ecsim_noalloc, assemble_scalar,  # noqa: F401
                   bin_particles,
-                  contract_bins, deposit_moments, deposit_records, noff, noff_canonical, noff_grid,
-                  probe_mfma_f64, record_bytes, stencil_matvec)
+                  contract_bins, contract_bins_planes, deposit_moments, deposit_records, deposit_records_planes,
+                  noff, noff_canonical, noff_grid,
+                  probe_mfma_f64, record_bytes, slab_planes, stencil_matvec)
 
 __all__ = ["bin_particles", "assemble_scalar", "assemble_ecsim", "assemble_ecsim_gridB", "assemble_ecsim_noalloc",
-           "contract_bins",
+           "contract_bins", "contract_bins_planes", "deposit_records_planes",
            "deposit_records", "deposit_moments", "stencil_matvec", "probe_mfma_f64", "noff", "noff_canonical",
-           "noff_grid", "record_bytes", "MMError"]
+           "noff_grid", "record_bytes", "slab_planes", "MMError"]

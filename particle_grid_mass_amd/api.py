@@ -287,6 +287,67 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     return rec
 
 
+def slab_planes(grid, order: int) -> int:
+    """Planes per slab with which the assembly overlaps contraction and
+    deposition on this grid (``mm_slab_planes``); 0 when it runs them in turn."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    out = ctypes.c_int(0)
+    _call(lib.mm_slab_planes, "mm_slab_planes", ctypes.byref(g), int(order), ctypes.byref(out))
+    return int(out.value)
+
+
+def contract_bins_planes(grid, order: int, pos, w, B, bin_start, perm, beta: float, sigma: float, z0: int, z1: int,
+                         rec: torch.Tensor) -> torch.Tensor:
+    """Phase 1 for the bins of planes ``z0 <= z < z1`` only (run records:
+    order 2, field per particle): writes those runs' records into ``rec``, a
+    buffer holding the records of the whole grid (``record_bytes``)."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    code, fdt, dt = _modes(pos, w)
+    _check_tensor(pos, "pos", fdt)
+    _check_tensor(w, "w", dt)
+    _check_tensor(B, "B", fdt)
+    _check_tensor(bin_start, "bin_start", torch.int32)
+    _check_tensor(perm, "perm", torch.int32)
+    npart = pos.numel() // 3
+    if w.numel() != npart or B.numel() != 3 * npart:
+        raise ValueError("pos, w and B disagree on the particle count")
+    _check_bins(bin_start, perm, _nnodes(g), npart)
+    if not isinstance(rec, torch.Tensor) or not rec.is_cuda or not rec.is_contiguous():
+        raise ValueError("rec must be a contiguous device tensor")
+    if B.numel() == 0:
+        B = torch.empty(1, dtype=B.dtype, device=B.device)  # tensorial marker; not read when np == 0
+    _call(lib.mm_contract_bins_planes, "mm_contract_bins_planes", ctypes.byref(g), int(order), code, npart,
+          _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm), float(beta), float(sigma), int(z0), int(z1),
+          _ptr(rec), rec.numel() * rec.element_size(), _stream(pos.device))
+    return rec
+
+
+def deposit_records_planes(grid, order: int, rec, M: torch.Tensor, z0: int, z1: int, accumulate: bool = False,
+                           canonical: bool = False) -> torch.Tensor:
+    """Phase 2 for the nodes of planes ``z0 <= z < z1`` (run records): ``rec`` is
+    one record buffer or a list of up to four, as for ``deposit_records``."""
+    lib = _lib.load()
+    recs = list(rec) if isinstance(rec, (list, tuple)) else [rec]
+    g = _grid_of(grid)
+    _check_tensor(M, "M", None)
+    if M.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {M.dtype}")
+    if not 1 <= len(recs) <= _lib.MM_MAX_RECORD_SETS:
+        raise ValueError(f"1 to {_lib.MM_MAX_RECORD_SETS} record sets, got {len(recs)}")
+    nof = noff_canonical(order) if canonical else noff_grid(order, g)
+    if M.numel() != _nnodes(g) * nof * 9:
+        raise ValueError("M has the wrong number of elements")
+    for r in recs:
+        _check_records(lib, g, order, M.dtype, True, r, M)
+    arr = (ctypes.c_void_p * len(recs))(*[r.data_ptr() for r in recs])
+    _call(lib.mm_deposit_records_planes, "mm_deposit_records_planes", ctypes.byref(g), int(order), _DT[M.dtype],
+          int(bool(canonical)), len(recs), arr, int(bool(accumulate)), int(z0), int(z1), _ptr(M),
+          _stream(M.device))
+    return M
+
+
 def record_bytes(grid, order: int, dtype: torch.dtype, tensorial: bool) -> int:
     """Bytes of the per-bin records that a deposition of this grid, order, output
     dtype and kind reads (the records mm_contract_bins writes first)."""

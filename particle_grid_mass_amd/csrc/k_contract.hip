@@ -510,6 +510,19 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
              : contract_t<double, MODE_ATOMIC>(g, order, P, bin_start, perm, beta, sigma, out, s);
 }
 
+bool contract_planes_apply(const GridDev& g, int order, bool f32, const Particles& P) {
+  if (order != 2 || !tsc_run_records(g)) return false;
+  return f32 ? (P.B && !P.Bgrid && !P.pos32) : (P.B || P.Bgrid);
+}
+
+hipError_t launch_contract_planes(const GridDev& g, bool f32, const Particles& P, const int32_t* bin_start,
+                                  const int32_t* perm, double beta, double sigma, void* rec, int z0, int z1,
+                                  hipStream_t s) {
+  if (!contract_planes_apply(g, 2, f32, P)) return hipErrorInvalidValue;
+  return f32 ? launch_tsc32(g, P, bin_start, perm, beta, sigma, (float*)rec, s, z0, z1)
+             : launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)rec, s, z0, z1);
+}
+
 bool contract_gathers_field(int order, bool f32, int mode) {
   return mode == MODE_RECORD && !f32 && (order == 1 || order == 2);  // k_cic64, k_tsc64
 }

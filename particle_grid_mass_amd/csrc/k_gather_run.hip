@@ -40,15 +40,16 @@ constexpr int PAIRS = 64;  // (node, offset) pairs per block, one per lane of ea
 
 template <typename T, bool CANON, int NR>
 __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<T> recs, int accumulate,
-                                                          T* __restrict__ M, int blocks_per_row) {
+                                                          T* __restrict__ M, int blocks_per_row, int rv0) {
   constexpr int NC = 9;
   constexpr int NOFF = 125;
   __shared__ T st[PAIRS * NC];
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int rv = blk / blocks_per_row;  // visit order of the node row
+  const int rl = blk / blocks_per_row;  // the launch's node rows start at row rv0 (plane rv0 / n1)
+  const int rv = rv0 + rl;              // visit order of the node row
   const int lane = threadIdx.x & 63, i = threadIdx.x >> 6;
   const int per = g.n0 * 5;             // pairs per (dY, dZ) row of offsets
-  const int p = (blk - rv * blocks_per_row) * PAIRS + lane;
+  const int p = (blk - rl * blocks_per_row) * PAIRS + lane;
   const int nfull = g.n2 / ZB;
   const int inb = g.n1 * ZB;
   int gy, gz;
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<T> r
 #pragma unroll
   for (int j = 0; j < 3; ++j) st[lane * NC + 3 * i + j] = sum[j];
   __syncthreads();
-  const int p0 = (blk - rv * blocks_per_row) * PAIRS;
+  const int p0 = (blk - rl * blocks_per_row) * PAIRS;
   for (int idx = threadIdx.x; idx < PAIRS * NC; idx += 3 * PAIRS) {
     const int l = idx / NC, c = idx - l * NC;
     const int pp = p0 + l;
@@ -140,34 +141,38 @@ __global__ __launch_bounds__(3 * PAIRS) void k_gather_run(GridDev g, RecSet<T> r
 }
 
 template <typename T, bool CANON, int NR>
-hipError_t go(const GridDev& g, const RecSet<T>& rs, int accumulate, void* M, hipStream_t s) {
+hipError_t go(const GridDev& g, const RecSet<T>& rs, int accumulate, void* M, hipStream_t s, int z0, int z1) {
   const size_t row_pairs = (size_t)run::NROW * 5 * g.n0;  // (dY, dZ) rows x dX x nodes of a node row
   const int bpr = (int)((row_pairs + PAIRS - 1) / PAIRS);
-  const size_t blocks = (size_t)bpr * g.n1 * g.n2;
+  const size_t blocks = (size_t)bpr * g.n1 * (z1 - z0);
   if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((k_gather_run<T, CANON, NR>), dim3((unsigned)blocks), dim3(3 * PAIRS), 0, s, g, rs, accumulate,
-                     (T*)M, bpr);
+                     (T*)M, bpr, z0 * g.n1);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t gather_run_t(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M, hipStream_t s,
-                        bool canonical) {
+                        bool canonical, int z0, int z1) {
   RecSet<T> rs{};
   for (int q = 0; q < nrec; ++q) rs.r[q] = (const T*)rec[q];
   rs.n = nrec;
   if (nrec > 1)
-    return canonical ? go<T, true, MAX_REC>(g, rs, accumulate, M, s) : go<T, false, MAX_REC>(g, rs, accumulate, M, s);
-  return canonical ? go<T, true, 1>(g, rs, accumulate, M, s) : go<T, false, 1>(g, rs, accumulate, M, s);
+    return canonical ? go<T, true, MAX_REC>(g, rs, accumulate, M, s, z0, z1)
+                     : go<T, false, MAX_REC>(g, rs, accumulate, M, s, z0, z1);
+  return canonical ? go<T, true, 1>(g, rs, accumulate, M, s, z0, z1) : go<T, false, 1>(g, rs, accumulate, M, s, z0, z1);
 }
 
 }  // namespace
 
 hipError_t launch_gather_run(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
-                             hipStream_t s, bool canonical, bool f32) {
+                             hipStream_t s, bool canonical, bool f32, int z0, int z1) {
   if (nrec < 1 || nrec > MAX_REC || !tsc_run_records(g)) return hipErrorInvalidValue;
-  return f32 ? gather_run_t<float>(g, rec, nrec, accumulate, M, s, canonical)
-             : gather_run_t<double>(g, rec, nrec, accumulate, M, s, canonical);
+  if (z1 < 0) z1 = g.n2;
+  if (z0 < 0 || z0 > z1 || z1 > g.n2) return hipErrorInvalidValue;
+  return f32 ? gather_run_t<float>(g, rec, nrec, accumulate, M, s, canonical, z0, z1)
+             : gather_run_t<double>(g, rec, nrec, accumulate, M, s, canonical, z0, z1);
 }
 
 }  // namespace mmk

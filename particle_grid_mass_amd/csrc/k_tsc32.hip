@@ -64,21 +64,21 @@ __device__ __forceinline__ int unit_swz(int b, int p) {
 
 static __constant__ run::Tables kRun32 = run::make_tables();
 
-// Bins 8g .. 8g+7. Prep lane l serves bin 8g + (l >> 3) (particles l & 7 and
-// 8 + (l & 7) of each chunk): start in perm and count; maxn (the largest
-// count of the group) is wave-uniform.
+// Bins b0 + 8g .. b0 + 8g + 7 below bend. Prep lane l serves bin b0 + 8g +
+// (l >> 3) (particles l & 7 and 8 + (l & 7) of each chunk): start in perm and
+// count; maxn (the largest count of the group) is wave-uniform.
 struct Group {
   int s, n;
   int maxn;
   int nchunks;
 };
 
-__device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int nbins, int np,
+__device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int b0, int bend, int np,
                                             int lane) {
   Group G;
-  const int bin = NBW * g + (lane >> 3);
+  const int bin = b0 + NBW * g + (lane >> 3);
   int s = 0, e = 0;
-  if (bin < nbins) {
+  if (bin < bend) {
     s = bin_start[bin];
     e = bin_start[bin + 1];
     s = s < 0 ? 0 : (s > np ? np : s);
@@ -174,19 +174,20 @@ __device__ __forceinline__ void wave_sync() {
 
 __global__ __launch_bounds__(64) void k_tsc32(GridDev g, const float* __restrict__ pos, const float* __restrict__ w,
                                               const float* __restrict__ Bf, const int32_t* __restrict__ bin_start,
-                                              const int32_t* __restrict__ perm, int np, int nbins, float beta,
-                                              float sigma, float* __restrict__ rec, int xch) {
+                                              const int32_t* __restrict__ perm, int np, int b0, int bend,
+                                              float beta, float sigma, float* __restrict__ rec, int xch) {
   __shared__ __attribute__((aligned(16))) float sm[SMEMF];
   const int lane = threadIdx.x;
-  const int ngroups = (nbins + NBW - 1) / NBW;
-  const int nruns = nbins / run::RUN;
+  // the launch covers bins b0 .. bend - 1 (whole runs)
+  const int ngroups = (bend - b0 + NBW - 1) / NBW;
+  const int r0 = b0 / run::RUN, rend = bend / run::RUN;
   // chunks of xch blocks (whole groups: the NQ waves of a group share an XCD
   // and its L2) dealt round the XCDs
   const int lid = xcd_chunk_remap(blockIdx.x, gridDim.x, xch);
   const int grp = lid / NQ, qw = lid - grp * NQ;
   if (grp >= ngroups) return;
   const int c0 = 2 * qw, c1 = 2 * qw + 1 < 9 ? 2 * qw + 1 : 8;  // this wave's components
-  const Group G = load_group(bin_start, grp, nbins, np, lane);
+  const Group G = load_group(bin_start, grp, b0, bend, np, lane);
 
   // MFMA lane roles: block blk (bin blk & 7, component slot blk >> 3), row /
   // column mr of the 4x4 block.
@@ -251,8 +252,8 @@ __global__ __launch_bounds__(64) void k_tsc32(GridDev g, const float* __restrict
     const unsigned comp = s2 == 0 ? c0 : c1;
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
-      const int r = 2 * grp + h;  // the run
-      if (r >= nruns) break;
+      const int r = r0 + 2 * grp + h;  // the run
+      if (r >= rend) break;
       if (cs == s2 && (bb >> 2) == h) {
         float* pl = sm + (bb & 3) * run::BSTRIDE + 4 * mr;
 #pragma unroll
@@ -277,16 +278,21 @@ __global__ __launch_bounds__(64) void k_tsc32(GridDev g, const float* __restrict
 }
 
 hipError_t launch_tsc32(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, float* rec, hipStream_t s) {
+                        double beta, double sigma, float* rec, hipStream_t s, int z0, int z1) {
   if (!P.B || P.Bgrid || P.pos32 || !tsc_run_records(g)) return hipErrorInvalidValue;
-  const int nbins = g.n0 * g.n1 * g.n2;
-  const int ngroups = (nbins + NBW - 1) / NBW;
-  // XCD chunks of a plane of groups: bins one row apart in y read the same
+  if (z1 < 0) z1 = g.n2;
+  if (z0 < 0 || z0 > z1 || z1 > g.n2) return hipErrorInvalidValue;
+  const int pl = g.n0 * g.n1;  // bins per plane
+  const int b0 = z0 * pl, bend = z1 * pl;
+  const int ngroups = (bend - b0 + NBW - 1) / NBW;
+  if (ngroups == 0) return hipSuccess;
+  // XCD chunks of a plane of groups (a launch of fewer than 8 planes: an
+  // eighth of its groups per chunk): bins one row apart in y read the same
   // cells' particles from one L2
-  const int plane = NQ * ((g.n0 * g.n1) / NBW);
-  const int xch = plane > NQ ? plane : NQ;
+  int xg = pl / NBW < ngroups / 8 ? pl / NBW : ngroups / 8;
+  xg = xg > 1 ? xg : 1;
   hipLaunchKernelGGL(k_tsc32, dim3(ngroups * NQ), dim3(64), 0, s, g, (const float*)P.pos, (const float*)P.w,
-                     (const float*)P.B, bin_start, perm, P.np, nbins, (float)beta, (float)sigma, rec, xch);
+                     (const float*)P.B, bin_start, perm, P.np, b0, bend, (float)beta, (float)sigma, rec, NQ * xg);
   return hipGetLastError();
 }
 

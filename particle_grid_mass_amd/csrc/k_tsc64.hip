@@ -224,7 +224,7 @@ template <typename PT, bool GB, bool RUNS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
     GridDev g, const PT* __restrict__ pos, const double* __restrict__ w, const PT* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
-    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order, int xch) {
+    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order, int xch, int z0, int nz) {
   __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
   double* sW = smem;
   const int lane = threadIdx.x;
@@ -234,18 +234,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // work on the XCDs whose range held a cluster of a clustered density
   const int lid = xcd_chunk_remap(blockIdx.x, gridDim.x, xch);
   const int vis = lid / NQ, row = lid - vis * NQ;     // row of alpha: components CPW*row ..
-  if (vis >= ngroups) return;
-  // Run records on a grid of an even number of planes: groups are visited by
-  // pairs of planes, row by row, the two planes' rows one after the other
-  // (the particles of a cell plane are read by the bins of two consecutive
-  // planes, which then run on one XCD close in time); otherwise in order.
+  // Run records: the launch covers the runs of the nz bin planes z0 .. z0 + nz - 1
+  if (vis >= (RUNS ? nz * (g.n0 / run::RUN) * g.n1 : ngroups)) return;
+  // Run records over an even number of planes: groups are visited by pairs of
+  // planes, row by row, the two planes' rows one after the other (the
+  // particles of a cell plane are read by the bins of two consecutive planes,
+  // which then run on one XCD close in time); otherwise in order.
   int grp = vis;
-  if (RUNS && (g.n2 & 1) == 0) {
-    const int R = g.n0 / run::RUN, pr = 2 * R * g.n1;  // runs per row, per plane pair
-    const int pz = vis / pr, t = vis - pz * pr;
-    const int y = t / (2 * R), u = t - y * 2 * R;
-    const int zz = u / R, x = u - zz * R;
-    grp = x + R * (y + g.n1 * (2 * pz + zz));
+  if (RUNS) {
+    const int R = g.n0 / run::RUN;  // runs per row
+    if ((nz & 1) == 0) {
+      const int pr = 2 * R * g.n1;  // runs per plane pair
+      const int pz = vis / pr, t = vis - pz * pr;
+      const int y = t / (2 * R), u = t - y * 2 * R;
+      const int zz = u / R, x = u - zz * R;
+      grp = x + R * (y + g.n1 * (z0 + 2 * pz + zz));
+    } else {
+      grp = vis + z0 * R * g.n1;
+    }
   }
   const Group G = load_group(bin_start, order, grp, nbins, np, lane);
   double* sF = smem + SMEM;
@@ -440,9 +446,12 @@ size_t tsc64_order_bytes(int64_t nbins) { return ((size_t)nbins * 4 + 255) / 256
 
 template <typename PT, bool RUNS>
 static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                          double beta, double sigma, double* rec, int32_t* order, hipStream_t s) {
+                          double beta, double sigma, double* rec, int32_t* order, hipStream_t s, int z0, int z1) {
   const int nbins = g.n0 * g.n1 * g.n2;
-  const int ngroups = (nbins + NB - 1) / NB;  // NQ single-wave workgroups per group of four bins
+  // NQ single-wave workgroups per group of four bins (for run records, the runs of planes z0 .. z1 - 1)
+  const int rp = (g.n0 / run::RUN) * g.n1;  // runs per plane
+  const int ngroups = RUNS ? (z1 - z0) * rp : (nbins + NB - 1) / NB;
+  if (ngroups == 0) return hipSuccess;
   // run records need the groups to be runs of consecutive x: no bin order
   if (!RUNS)
     hipLaunchKernelGGL(k_order_window, dim3((nbins + OWIN - 1) / OWIN), dim3(OWIN), 0, s, bin_start, nbins, order);
@@ -451,32 +460,45 @@ static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* b
   // plane apart in y, which read the same cells' particles, run on one XCD
   // and find them in its L2 (chunks of 16 runs put them on other XCDs and the
   // particle data was fetched 4.5 times on a 128^3 grid); the planes dealt
-  // round the XCDs still balance a clustered density. Per-bin records follow
-  // the windowed bin order: chunks of 16 groups.
-  const int xch = RUNS ? NQ * XPLANES * (g.n0 / run::RUN) * g.n1 : 16 * NQ;  // a plane pair per chunk
+  // round the XCDs still balance a clustered density (a launch of fewer than
+  // 16 planes: an eighth of its runs per chunk). Per-bin records follow the
+  // windowed bin order: chunks of 16 groups.
+  int xg = 16;
+  if (RUNS) {
+    xg = ngroups / 8 < XPLANES * rp ? ngroups / 8 : XPLANES * rp;
+    xg = xg > 1 ? xg : 1;
+  }
+  const int xch = NQ * xg;
+  const int nz = z1 - z0;
   if (P.Bgrid)
     hipLaunchKernelGGL((k_tsc64<PT, true, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch);
+                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
+                       z0, nz);
   else
     hipLaunchKernelGGL((k_tsc64<PT, false, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch);
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
+                       z0, nz);
   return hipGetLastError();
 }
 
 bool tsc_run_records(const GridDev& g) { return g.n2 > 1 && g.n0 % run::RUN == 0; }
 
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, double* rec, hipStream_t s) {
+                        double beta, double sigma, double* rec, hipStream_t s, int z0, int z1) {
   if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
-  if (tsc_run_records(g))
-    return P.pos32 ? tsc64_t<float, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s)
-                   : tsc64_t<double, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s);
+  if (z1 < 0) z1 = g.n2;
+  if (tsc_run_records(g)) {
+    if (z0 < 0 || z0 > z1 || z1 > g.n2) return hipErrorInvalidValue;
+    return P.pos32 ? tsc64_t<float, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s, z0, z1)
+                   : tsc64_t<double, true>(g, P, bin_start, perm, beta, sigma, rec, nullptr, s, z0, z1);
+  }
+  if (z0 != 0 || z1 != g.n2) return hipErrorInvalidValue;  // plane ranges: run records only
   // per-bin records; the bin order lives after them (record_bytes counts it)
   const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
   const size_t recb = (size_t)nbins * NPAIR * NC * 8;
   int32_t* order = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(rec) + (recb + 255) / 256 * 256);
-  return P.pos32 ? tsc64_t<float, false>(g, P, bin_start, perm, beta, sigma, rec, order, s)
-                 : tsc64_t<double, false>(g, P, bin_start, perm, beta, sigma, rec, order, s);
+  return P.pos32 ? tsc64_t<float, false>(g, P, bin_start, perm, beta, sigma, rec, order, s, 0, g.n2)
+                 : tsc64_t<double, false>(g, P, bin_start, perm, beta, sigma, rec, order, s, 0, g.n2);
 }
 
 }  // namespace mmk

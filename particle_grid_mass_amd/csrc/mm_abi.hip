@@ -178,6 +178,12 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     if (e == hipSuccess) e = launch_gather_2d(g, order, tensorial, ws, accumulate, M, s);
     return hip_status(e);
   }
+  // Large run-record grids: the two phases overlapped by slabs of planes
+  // (bit-identical results). Not in the allocation-free entry point, whose
+  // callers may not let the library create its second stream.
+  if (records && algo == MM_ALGO_MFMA && fixed_max == 0 && tensorial && order == 2 && overlap_slabs(g) >= 2 &&
+      contract_planes_apply(g, order, f32, P))
+    return hip_status(launch_assemble_overlapped(g, f32, P, bin_start, perm, beta, sigma, ws, accumulate, M, s));
   if (records) {
     e = algo == MM_ALGO_VALU ? launch_cic64_valu(g, P, bin_start, perm, beta, sigma, (double*)ws, s)
                              : launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
@@ -366,6 +372,57 @@ mm_status mm_deposit_records_multi(const mm_grid* grid, int order, mm_dtype dt, 
   if (is2d(grid)) return MM_ERR_UNSUPPORTED;
   return hip_status(launch_gather(to_dev(grid), order, dt == MM_F32, tensorial != 0, recs, nrec, accumulate, M,
                                   (hipStream_t)stream, canonical != 0));
+}
+
+mm_status mm_slab_planes(const mm_grid* grid, int order, int* planes) {
+  if (!planes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  *planes = order == 2 && !is2d(grid) ? overlap_slab_planes(to_dev(grid)) : 0;
+  return MM_OK;
+}
+
+mm_status mm_contract_bins_planes(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                  const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
+                                  double beta, double sigma, int z0, int z1, void* rec, size_t rec_bytes,
+                                  mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!rec || !bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
+  if (z0 < 0 || z0 > z1 || z1 > grid->n[2]) return MM_ERR_ARG;
+  const bool f32 = dt == MM_F32;
+  const GridDev g = to_dev(grid);
+  Particles P{pos, w, B, (int)np};
+  P.pos32 = dt == MM_MIX;
+  if (is2d(grid) || !B || !contract_planes_apply(g, order, f32, P)) return MM_ERR_UNSUPPORTED;
+  if (rec_bytes < record_bytes(order, f32, true, g)) return MM_ERR_WORKSPACE;
+  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
+  return hip_status(launch_contract_planes(g, f32, P, bin_start, perm, beta, sigma, rec, z0, z1,
+                                           (hipStream_t)stream));
+}
+
+mm_status mm_deposit_records_planes(const mm_grid* grid, int order, mm_dtype dt, int canonical, int nrec,
+                                    const void* const* recs, int accumulate, int z0, int z1, void* M,
+                                    mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (nrec < 1 || nrec > MM_MAX_RECORD_SETS) return MM_ERR_ARG;
+  if (!recs || !M) return MM_ERR_NULL;
+  for (int q = 0; q < nrec; ++q)
+    if (!recs[q]) return MM_ERR_NULL;
+  if (z0 < 0 || z0 > z1 || z1 > grid->n[2]) return MM_ERR_ARG;
+  const GridDev g = to_dev(grid);
+  if (is2d(grid) || order != 2 || !tsc_run_records(g)) return MM_ERR_UNSUPPORTED;
+  return hip_status(launch_gather_run(g, recs, nrec, accumulate, M, (hipStream_t)stream, canonical != 0,
+                                      dt == MM_F32, z0, z1));
 }
 
 mm_status mm_deposit_moments(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* Q,

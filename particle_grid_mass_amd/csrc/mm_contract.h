@@ -29,12 +29,15 @@ hipError_t launch_cic32(const GridDev& g, const Particles& P, const int32_t* bin
 
 // Phase 1 for TSC fp64 ECSIM (tensorial) records: 4x4x4 blocks, one bin per block, one wave
 // per (group of four bins, row of alpha).
+// Run records (tsc_run_records(g)): only the runs of bin planes z0 .. z1 - 1
+// (z1 < 0: all planes); other grids take the whole grid only.
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, double* rec, hipStream_t s);
+                        double beta, double sigma, double* rec, hipStream_t s, int z0 = 0, int z1 = -1);
 // Phase 1 for TSC fp32 ECSIM run records (tsc_run_records(g), field per
-// particle): 4x4x1 fp32 blocks, 8 bins and two components per wave.
+// particle): 4x4x1 fp32 blocks, 8 bins and two components per wave; the runs
+// of bin planes z0 .. z1 - 1 (z1 < 0: all planes).
 hipError_t launch_tsc32(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                        double beta, double sigma, float* rec, hipStream_t s);
+                        double beta, double sigma, float* rec, hipStream_t s, int z0 = 0, int z1 = -1);
 // Bytes k_tsc64 uses after its per-bin records (rounded up to 256) for the bin order.
 size_t tsc64_order_bytes(int64_t nbins);
 // Whether the order-2 tensorial records of this grid (fp64, and fp32 with the
@@ -71,8 +74,33 @@ hipError_t launch_gather(const GridDev& g, int order, bool f32, bool tensorial, 
 // Phase 2 for run records (order 2, tensorial, tsc_run_records(g)): the same
 // sums as launch_gather, read from the records of x-runs of four bins (fp32 or
 // fp64 records and output).
+// z0, z1: only the node rows of planes z0 .. z1 - 1 (z1 < 0: all), with their
+// mirrored entries (full stencil) in planes z .. z + 2; they read the records
+// of bin planes z0 - 2 .. z1 - 1 (periodic).
 hipError_t launch_gather_run(const GridDev& g, const void* const* rec, int nrec, int accumulate, void* M,
-                             hipStream_t s, bool canonical, bool f32);
+                             hipStream_t s, bool canonical, bool f32, int z0 = 0, int z1 = -1);
+
+// Run records by slabs of planes: whether this contraction takes plane ranges
+// (order 2, run records, fp64 or mixed with the field per particle or on the
+// grid, fp32 with the field per particle), and the contraction of bin planes
+// z0 .. z1 - 1 into rec (the full record layout; only those runs' records
+// are written).
+bool contract_planes_apply(const GridDev& g, int order, bool f32, const Particles& P);
+hipError_t launch_contract_planes(const GridDev& g, bool f32, const Particles& P, const int32_t* bin_start,
+                                  const int32_t* perm, double beta, double sigma, void* rec, int z0, int z1,
+                                  hipStream_t s);
+
+// The contraction and deposition of run records overlapped (mm_overlap.hip):
+// slabs of planes contracted in order on s, each slab's completed node planes
+// deposited on a second stream of the device while the next slab contracts.
+// overlap_slabs(g) is the number of slabs used (0: the grid is too small to
+// gain; the caller runs the two phases one after the other).
+int overlap_slabs(const GridDev& g);
+// Planes per slab of that schedule (the last slab may be thinner), 0 when it is not used.
+int overlap_slab_planes(const GridDev& g);
+hipError_t launch_assemble_overlapped(const GridDev& g, bool f32, const Particles& P, const int32_t* bin_start,
+                                      const int32_t* perm, double beta, double sigma, void* rec, int accumulate,
+                                      void* M, hipStream_t s);
 
 // The 2D problem (n2 == 1): per-bin fp64 records rec[bin][pair][comp] of the
 // (R+1)^2 support, and their fixed-order sum into M [nnodes][(2R+1)^2][comp]

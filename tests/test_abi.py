@@ -280,3 +280,74 @@ def test_valu_algo_validation():
     assert _ecsim(G8, dt=_lib.MM_F32, algo=3)[0] == _lib.MM_ERR_UNSUPPORTED
     assert _ecsim(_lib.make_grid((8, 8, 1)), algo=3)[0] == _lib.MM_ERR_UNSUPPORTED
     assert _ecsim(G8, algo=4)[0] == _lib.MM_ERR_ARG
+
+
+def test_slab_planes_query():
+    """mm_slab_planes: the slab thickness of the overlapped assembly, 0 where
+    the two phases run in turn (small planes, few slabs, first order, grids
+    without run records)."""
+    lib = _lib.load()
+
+    def q(n, order=2):
+        out = ctypes.c_int(-1)
+        st = lib.mm_slab_planes(ctypes.byref(_lib.make_grid(n)), order, ctypes.byref(out))
+        return st, out.value
+
+    assert q((128, 128, 128)) == (_lib.MM_OK, 4)
+    assert q((96, 96, 16)) == (_lib.MM_OK, 4)      # 9216 cells per plane, four slabs
+    assert q((96, 96, 12)) == (_lib.MM_OK, 0)      # three slabs
+    assert q((124, 64, 64)) == (_lib.MM_OK, 0)     # 7936 cells per plane
+    assert q((130, 128, 64)) == (_lib.MM_OK, 0)    # n0 not a multiple of 4: per-bin records
+    assert q((128, 128, 128), order=1) == (_lib.MM_OK, 0)
+    assert q((128, 128, 1)) == (_lib.MM_OK, 0)     # 2D
+    assert q((128, 128, 2048)) == (_lib.MM_OK, 8)  # at most 256 slabs
+    assert lib.mm_slab_planes(ctypes.byref(G8), 2, None) == _lib.MM_ERR_NULL
+    assert lib.mm_slab_planes(None, 2, ctypes.byref(ctypes.c_int())) == _lib.MM_ERR_NULL
+    assert q((8, 8, 8), order=3)[0] == _lib.MM_ERR_ARG
+
+
+def test_planes_validation():
+    """The plane-range contraction and deposition check the plane range, the
+    record buffer and the kind of records on the host."""
+    lib = _lib.load()
+    P = ctypes.c_void_p
+    g = _lib.make_grid((16, 8, 8))
+    need = 16 * 8 * 8 // 4 * 9360 * 8
+
+    def cp(grid=g, order=2, dt=_lib.MM_F64, np_=10, B=FAKE, z0=0, z1=8, rec=FAKE, nbytes=need):
+        return lib.mm_contract_bins_planes(ctypes.byref(grid) if grid is not None else None, order, dt, np_, FAKE,
+                                           FAKE, B, FAKE, FAKE, 0.5, 1.0, z0, z1, rec, nbytes, None)
+
+    assert cp(None) == _lib.MM_ERR_NULL
+    assert cp(rec=None) == _lib.MM_ERR_NULL
+    assert cp(z0=-1) == _lib.MM_ERR_ARG
+    assert cp(z0=3, z1=2) == _lib.MM_ERR_ARG
+    assert cp(z1=9) == _lib.MM_ERR_ARG
+    assert cp(dt=5) == _lib.MM_ERR_ARG
+    assert cp(np_=-1) == _lib.MM_ERR_ARG
+    assert cp(order=1) == _lib.MM_ERR_UNSUPPORTED
+    assert cp(B=None) == _lib.MM_ERR_UNSUPPORTED                          # scalar records are per bin
+    assert cp(grid=_lib.make_grid((18, 8, 8))) == _lib.MM_ERR_UNSUPPORTED  # n0 % 4 != 0
+    assert cp(grid=_lib.make_grid((16, 8, 1)), z1=1) == _lib.MM_ERR_UNSUPPORTED
+    assert cp(nbytes=need - 1) == _lib.MM_ERR_WORKSPACE
+    assert cp(dt=_lib.MM_F32, nbytes=need // 2 - 1) == _lib.MM_ERR_WORKSPACE
+    assert cp(rec=ctypes.c_void_p(0x1008)) == _lib.MM_ERR_ARG
+
+    def dp(grid=g, order=2, nrec=1, recs="ok", z0=0, z1=8, M=FAKE):
+        arr = (P * 4)(FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000))
+        if recs == "null_entry":
+            arr[0] = None
+        a = None if recs is None else arr
+        return lib.mm_deposit_records_planes(ctypes.byref(grid) if grid is not None else None, order, _lib.MM_F64, 0,
+                                             nrec, a, 0, z0, z1, M, None)
+
+    assert dp(None) == _lib.MM_ERR_NULL
+    assert dp(nrec=0) == _lib.MM_ERR_ARG
+    assert dp(nrec=5) == _lib.MM_ERR_ARG
+    assert dp(recs=None) == _lib.MM_ERR_NULL
+    assert dp(recs="null_entry") == _lib.MM_ERR_NULL
+    assert dp(M=None) == _lib.MM_ERR_NULL
+    assert dp(z0=5, z1=4) == _lib.MM_ERR_ARG
+    assert dp(z1=9) == _lib.MM_ERR_ARG
+    assert dp(order=1) == _lib.MM_ERR_UNSUPPORTED
+    assert dp(grid=_lib.make_grid((18, 8, 8))) == _lib.MM_ERR_UNSUPPORTED
