@@ -446,8 +446,10 @@ def main():
     # contracts (a node plane reads the records of its bin plane and the two
     # before it; planes 0 and 1 wait for the last slab).
     slab = 0
+    # (a field on the grid is gathered inside the fp64 contraction; fp32
+    # interpolates it in a pass of its own first and keeps the phases in turn)
     if (args.overlap == "auto" and args.algo == "mfma" and args.dims == 3 and tensorial and order == 2
-            and not on_grid and not multi and not args.canonical and not args.reorder):
+            and not (on_grid and case.dtype == "f32") and not multi and not args.canonical and not args.reorder):
         slab = mm.slab_planes(case.grid, order)
     overlap = slab > 0
     zb = list(range(0, case.grid.n[2], slab)) + [case.grid.n[2]] if overlap else []
@@ -504,7 +506,7 @@ def main():
                 side.wait_stream(stream)
                 for k in range(nslab):
                     mm.contract_bins_planes(case.grid, order, s["pos"], s["w"], s["B"], bs, perm, s["beta"],
-                                            case.sigma, zb[k], zb[k + 1], rec)
+                                            case.sigma, zb[k], zb[k + 1], rec, Bgrid=Fd)
                     slab_ev[k].record(stream)
                     side.wait_event(slab_ev[k])
                     with torch.cuda.stream(side):

@@ -326,6 +326,17 @@ mm_status mm_contract_bins_planes(const mm_grid* grid, int order, mm_dtype dt, i
                                   const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
                                   double beta, double sigma, int z0, int z1, void* rec, size_t rec_bytes,
                                   mm_stream_t stream);
+/*
+ * mm_contract_bins_planes_gridB - mm_contract_bins_planes with the field on
+ * the grid (Bgrid [nnodes][3], as for mm_contract_bins_gridB), gathered at
+ * each particle inside the contraction: MM_F64 and MM_MIX (MM_F32, which
+ * interpolates the field in a pass of its own first, gives
+ * MM_ERR_UNSUPPORTED). Bgrid == NULL is MM_ERR_NULL.
+ */
+mm_status mm_contract_bins_planes_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                        const void* w, const void* Bgrid, const int32_t* bin_start,
+                                        const int32_t* perm, double beta, double sigma, int z0, int z1, void* rec,
+                                        size_t rec_bytes, mm_stream_t stream);
 mm_status mm_deposit_records_planes(const mm_grid* grid, int order, mm_dtype dt, int canonical, int nrec,
                                     const void* const* recs, int accumulate, int z0, int z1, void* M,
                                     mm_stream_t stream);

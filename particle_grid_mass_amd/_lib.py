@@ -16,7 +16,8 @@ ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2, "valu": 3}
 # Every symbol the public header include/mm.h declares.
 EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_assemble_ecsim_gridB",
             "mm_contract_bins", "mm_contract_bins_gridB", "mm_deposit_records", "mm_deposit_records_canonical",
-            "mm_deposit_records_multi", "mm_slab_planes", "mm_contract_bins_planes", "mm_deposit_records_planes",
+            "mm_deposit_records_multi", "mm_slab_planes", "mm_contract_bins_planes", "mm_contract_bins_planes_gridB",
+            "mm_deposit_records_planes",
             "mm_record_bytes", "mm_deposit_moments", "mm_stencil_matvec", "mm_assemble_ecsim_noalloc",
             "mm_probe_mfma_f64", "mm_status_string", "mm_version")
 
@@ -65,13 +66,14 @@ def load():
     lib.mm_assemble_ecsim_noalloc.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, P, P]
     lib.mm_slab_planes.argtypes = [G, I, ctypes.POINTER(ctypes.c_int)]
     lib.mm_contract_bins_planes.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, ctypes.c_size_t, P]
+    lib.mm_contract_bins_planes_gridB.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, ctypes.c_size_t, P]
     lib.mm_deposit_records_planes.argtypes = [G, I, I, I, I, ctypes.POINTER(P), I, I, I, P, P]
     for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim, lib.mm_assemble_ecsim_gridB,
               lib.mm_contract_bins, lib.mm_contract_bins_gridB, lib.mm_deposit_records,
               lib.mm_deposit_records_canonical, lib.mm_deposit_records_multi, lib.mm_record_bytes,
               lib.mm_stencil_matvec, lib.mm_deposit_moments,
               lib.mm_probe_mfma_f64, lib.mm_assemble_ecsim_noalloc, lib.mm_slab_planes, lib.mm_contract_bins_planes,
-              lib.mm_deposit_records_planes):
+              lib.mm_contract_bins_planes_gridB, lib.mm_deposit_records_planes):
         f.restype = ctypes.c_int
     lib.mm_status_string.argtypes = [ctypes.c_int]
     lib.mm_status_string.restype = ctypes.c_char_p

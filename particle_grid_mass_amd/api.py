@@ -298,29 +298,42 @@ def slab_planes(grid, order: int) -> int:
 
 
 def contract_bins_planes(grid, order: int, pos, w, B, bin_start, perm, beta: float, sigma: float, z0: int, z1: int,
-                         rec: torch.Tensor) -> torch.Tensor:
+                         rec: torch.Tensor, Bgrid: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Phase 1 for the bins of planes ``z0 <= z < z1`` only (run records:
-    order 2, field per particle): writes those runs' records into ``rec``, a
-    buffer holding the records of the whole grid (``record_bytes``)."""
+    order 2): writes those runs' records into ``rec``, a buffer holding the
+    records of the whole grid (``record_bytes``). The field is per particle
+    (``B``) or on the grid nodes (``Bgrid`` ``[nnodes, 3]``; float64 or the
+    mixed layout)."""
     lib = _lib.load()
     g = _grid_of(grid)
     code, fdt, dt = _modes(pos, w)
     _check_tensor(pos, "pos", fdt)
     _check_tensor(w, "w", dt)
-    _check_tensor(B, "B", fdt)
+    if (B is None) == (Bgrid is None):
+        raise ValueError("give the field per particle (B) or on the grid (Bgrid)")
+    npart = pos.numel() // 3
+    if B is not None:
+        _check_tensor(B, "B", fdt)
+        if B.numel() != 3 * npart:
+            raise ValueError("pos and B disagree on the particle count")
+        field, fn, name = B, lib.mm_contract_bins_planes, "mm_contract_bins_planes"
+    else:
+        _check_tensor(Bgrid, "Bgrid", fdt)
+        if Bgrid.numel() != 3 * _nnodes(g):
+            raise ValueError(f"Bgrid has {Bgrid.numel()} elements, expected 3 * nnodes = {3 * _nnodes(g)}")
+        field, fn, name = Bgrid, lib.mm_contract_bins_planes_gridB, "mm_contract_bins_planes_gridB"
     _check_tensor(bin_start, "bin_start", torch.int32)
     _check_tensor(perm, "perm", torch.int32)
-    npart = pos.numel() // 3
-    if w.numel() != npart or B.numel() != 3 * npart:
-        raise ValueError("pos, w and B disagree on the particle count")
+    if w.numel() != npart:
+        raise ValueError("pos and w disagree on the particle count")
     _check_bins(bin_start, perm, _nnodes(g), npart)
     if not isinstance(rec, torch.Tensor) or not rec.is_cuda or not rec.is_contiguous():
         raise ValueError("rec must be a contiguous device tensor")
-    if B.numel() == 0:
-        B = torch.empty(1, dtype=B.dtype, device=B.device)  # tensorial marker; not read when np == 0
-    _call(lib.mm_contract_bins_planes, "mm_contract_bins_planes", ctypes.byref(g), int(order), code, npart,
-          _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm), float(beta), float(sigma), int(z0), int(z1),
-          _ptr(rec), rec.numel() * rec.element_size(), _stream(pos.device))
+    if field.numel() == 0:
+        field = torch.empty(1, dtype=field.dtype, device=field.device)  # tensorial marker; not read when np == 0
+    _call(fn, name, ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
+          _ptr(perm), float(beta), float(sigma), int(z0), int(z1), _ptr(rec), rec.numel() * rec.element_size(),
+          _stream(pos.device))
     return rec
 
 

@@ -246,6 +246,32 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   return hip_status(launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, s));
 }
 
+// mm_contract_bins_planes with the field per particle (B) or on the grid (Bgrid).
+mm_status contract_planes_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                 const void* w, const void* B, const void* Bgrid, const int32_t* bin_start,
+                                 const int32_t* perm, double beta, double sigma, int z0, int z1, void* rec,
+                                 size_t rec_bytes, mm_stream_t stream) {
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
+  if (np < 0) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!rec || !bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
+  if (z0 < 0 || z0 > z1 || z1 > grid->n[2]) return MM_ERR_ARG;
+  const bool f32 = dt == MM_F32;
+  const GridDev g = to_dev(grid);
+  Particles P{pos, w, B, (int)np};
+  P.pos32 = dt == MM_MIX;
+  P.Bgrid = Bgrid;
+  if (is2d(grid) || !(B || Bgrid) || !contract_planes_apply(g, order, f32, P)) return MM_ERR_UNSUPPORTED;
+  if (rec_bytes < record_bytes(order, f32, true, g)) return MM_ERR_WORKSPACE;
+  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
+  return hip_status(launch_contract_planes(g, f32, P, bin_start, perm, beta, sigma, rec, z0, z1,
+                                           (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -387,24 +413,17 @@ mm_status mm_contract_bins_planes(const mm_grid* grid, int order, mm_dtype dt, i
                                   const void* w, const void* B, const int32_t* bin_start, const int32_t* perm,
                                   double beta, double sigma, int z0, int z1, void* rec, size_t rec_bytes,
                                   mm_stream_t stream) {
-  int64_t nnodes = 0;
-  mm_status st = check_grid(grid, order, &nnodes);
-  if (st != MM_OK) return st;
-  if (!dtype_ok(dt)) return MM_ERR_ARG;
-  if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
-  if (np < 0) return MM_ERR_ARG;
-  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
-  if (!rec || !bin_start || (np > 0 && (!pos || !w || !perm))) return MM_ERR_NULL;
-  if (z0 < 0 || z0 > z1 || z1 > grid->n[2]) return MM_ERR_ARG;
-  const bool f32 = dt == MM_F32;
-  const GridDev g = to_dev(grid);
-  Particles P{pos, w, B, (int)np};
-  P.pos32 = dt == MM_MIX;
-  if (is2d(grid) || !B || !contract_planes_apply(g, order, f32, P)) return MM_ERR_UNSUPPORTED;
-  if (rec_bytes < record_bytes(order, f32, true, g)) return MM_ERR_WORKSPACE;
-  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
-  return hip_status(launch_contract_planes(g, f32, P, bin_start, perm, beta, sigma, rec, z0, z1,
-                                           (hipStream_t)stream));
+  return contract_planes_common(grid, order, dt, np, pos, w, B, nullptr, bin_start, perm, beta, sigma, z0, z1, rec,
+                                rec_bytes, stream);
+}
+
+mm_status mm_contract_bins_planes_gridB(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
+                                        const void* w, const void* Bgrid, const int32_t* bin_start,
+                                        const int32_t* perm, double beta, double sigma, int z0, int z1, void* rec,
+                                        size_t rec_bytes, mm_stream_t stream) {
+  if (!Bgrid) return MM_ERR_NULL;
+  return contract_planes_common(grid, order, dt, np, pos, w, nullptr, Bgrid, bin_start, perm, beta, sigma, z0, z1,
+                                rec, rec_bytes, stream);
 }
 
 mm_status mm_deposit_records_planes(const mm_grid* grid, int order, mm_dtype dt, int canonical, int nrec,

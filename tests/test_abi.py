@@ -333,6 +333,14 @@ def test_planes_validation():
     assert cp(dt=_lib.MM_F32, nbytes=need // 2 - 1) == _lib.MM_ERR_WORKSPACE
     assert cp(rec=ctypes.c_void_p(0x1008)) == _lib.MM_ERR_ARG
 
+    def cpg(dt=_lib.MM_F64, Bg=FAKE, z1=8):
+        return lib.mm_contract_bins_planes_gridB(ctypes.byref(g), 2, dt, 10, FAKE, FAKE, Bg, FAKE, FAKE, 0.5, 1.0, 0,
+                                                 z1, FAKE, need, None)
+
+    assert cpg(Bg=None) == _lib.MM_ERR_NULL
+    assert cpg(dt=_lib.MM_F32) == _lib.MM_ERR_UNSUPPORTED  # fp32 interpolates the field in a pass of its own
+    assert cpg(z1=9) == _lib.MM_ERR_ARG
+
     def dp(grid=g, order=2, nrec=1, recs="ok", z0=0, z1=8, M=FAKE):
         arr = (P * 4)(FAKE, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000))
         if recs == "null_entry":

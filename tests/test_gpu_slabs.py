@@ -175,6 +175,30 @@ def test_assemble_overlapped(mode):
     _sampled_rows_check(case, sp, M, mode, nodes)
 
 
+@pytest.mark.parametrize("mode", ["f64", "mix"])
+def test_contract_planes_grid_field(mode):
+    """With the field on the grid nodes (gathered inside the fp64 contraction),
+    records written plane range by plane range deposit to the same M as one
+    contraction, bit for bit."""
+    case = _case(46, (16, 12, 10), 30000, mode)
+    _print("contract planes gridB", case, mode)
+    sp = case.species[0]
+    beta, sigma = species_scalars(case, sp)
+    pos, w, _ = _dev(case, sp, mode)
+    Fg = torch.from_numpy(grid_field(case.grid, 11, "f64")).to("cuda", torch.float32 if mode == "mix" else torch.float64)
+    bs, perm = mm.bin_particles(case.grid, 2, pos, mixed=mode == "mix")
+    rec = mm.contract_bins(case.grid, 2, pos, w, None, bs, perm, beta, sigma, Bgrid=Fg)
+    M_full = torch.empty(case.grid.ncells * 125 * 9, dtype=torch.float64, device="cuda")
+    mm.deposit_records(case.grid, 2, rec, M_full, True)
+    rec_p = torch.full_like(rec, 0x5A)
+    for z0, z1 in PARTS[10]:
+        mm.contract_bins_planes(case.grid, 2, pos, w, None, bs, perm, beta, sigma, z0, z1, rec_p, Bgrid=Fg)
+    M_p = torch.full_like(M_full, float("nan"))
+    mm.deposit_records(case.grid, 2, rec_p, M_p, True)
+    torch.cuda.synchronize()
+    assert torch.equal(M_p, M_full)
+
+
 @pytest.mark.parametrize("mode", ["f64", "f32"])
 def test_assemble_overlapped_grid_field(mode):
     """The overlapped assembly with the field on the grid nodes (gathered in
