@@ -138,11 +138,12 @@ def _sampled_rows_check(case, sp, M, mode, nodes):
 
 
 @pytest.mark.parametrize("mode", ["f64", "f32", "mix"])
-def test_assemble_overlapped(mode):
+@pytest.mark.parametrize("n", [(96, 96, 18), (96, 88, 17)])
+def test_assemble_overlapped(mode, n):
     """mm_assemble_ecsim on a grid the library splits into slabs (96 x 96 x 18:
-    five slabs, the last of two planes) equals the two phases in turn bit for
-    bit, overwriting and accumulating, and matches the oracle on sampled rows."""
-    n = (96, 96, 18)
+    five slabs, the last of two planes; 96 x 88 x 17: the last of one plane,
+    visited in plain order) equals the two phases in turn bit for bit,
+    overwriting and accumulating, and matches the oracle on sampled rows."""
     case = _case(44, n, 400000, mode, spread=0.7)
     assert mm.slab_planes(case.grid, 2) == 4
     _print("assemble overlapped", case, mode)
@@ -170,7 +171,7 @@ def test_assemble_overlapped(mode):
     mm.assemble_ecsim(case.grid, 2, pos, w, B, bs, perm, beta, sigma, M=M, algo="mfma")
     rng = np.random.default_rng(5)
     nx, ny, nz = n
-    zs = np.array([0, 1, 3, 4, 8, 12, 15, 16, 17])
+    zs = np.array([0, 1, 3, 4, 8, 12, 15, 16, n[2] - 1])
     nodes = (rng.integers(0, nx, zs.size) + nx * (rng.integers(0, ny, zs.size) + ny * zs)).astype(np.int64)
     _sampled_rows_check(case, sp, M, mode, nodes)
 
