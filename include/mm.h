@@ -49,12 +49,17 @@
  *           (MM_ERR_UNSUPPORTED).
  *  Memory:  every array argument is a device pointer (hipMalloc or an
  *           allocator on top of it, e.g. torch) on the current device,
- *           owned by the caller. The library allocates nothing and keeps no
- *           mutable global state; calls are reentrant. The one exception is
- *           mm_assemble_ecsim_noalloc, which uses a fixed scratch array of the
- *           library per GPU (see there).
+ *           owned by the caller. The library allocates no device memory and
+ *           keeps no mutable global state; calls are reentrant. The
+ *           exceptions: mm_assemble_ecsim_noalloc uses a fixed scratch array
+ *           of the library per GPU (see there), and the overlapped assembly
+ *           (mm_slab_planes) creates a second stream and its events per GPU on
+ *           the first such call and keeps them.
  *  Streams: all work is enqueued asynchronously on `stream` (a hipStream_t,
- *           NULL = default stream); no call synchronizes the host.
+ *           NULL = default stream); no call synchronizes the host. The
+ *           overlapped assembly also enqueues on the GPU's second stream,
+ *           fenced by events: it starts after the work already on `stream`,
+ *           and `stream` waits for it before anything enqueued later.
  *  Workspace (CUB style): call with ws == NULL to receive the required byte
  *           count in *ws_bytes (nothing is enqueued, MM_OK is returned); then
  *           call again with a device buffer of at least that many bytes,

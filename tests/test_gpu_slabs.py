@@ -200,7 +200,7 @@ def test_contract_planes_grid_field(mode):
     assert torch.equal(M_p, M_full)
 
 
-@pytest.mark.parametrize("mode", ["f64", "f32"])
+@pytest.mark.parametrize("mode", ["f64", "f32", "mix"])
 def test_assemble_overlapped_grid_field(mode):
     """The overlapped assembly with the field on the grid nodes (gathered in
     the fp64 contraction, interpolated first for fp32) equals the two phases."""
@@ -212,8 +212,8 @@ def test_assemble_overlapped_grid_field(mode):
     beta, sigma = species_scalars(case, sp)
     pos, w, _ = _dev(case, sp, mode)
     dt = torch.float32 if mode == "f32" else torch.float64
-    Fg = torch.from_numpy(grid_field(case.grid, 9, case.dtype)).to("cuda", dt)
-    bs, perm = mm.bin_particles(case.grid, 2, pos)
+    Fg = torch.from_numpy(grid_field(case.grid, 9, case.dtype)).to("cuda", torch.float32 if mode == "mix" else dt)
+    bs, perm = mm.bin_particles(case.grid, 2, pos, mixed=mode == "mix")
     rec = mm.contract_bins(case.grid, 2, pos, w, None, bs, perm, beta, sigma, Bgrid=Fg)
     M_two = torch.empty(case.grid.ncells * 125 * 9, dtype=dt, device="cuda")
     mm.deposit_records(case.grid, 2, rec, M_two, True)
