@@ -65,14 +65,24 @@ hipError_t side_of(hipStream_t s, Side** out) {
     int cur = -1;
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-    e = hipStreamCreateWithFlags(&sd.st, hipStreamNonBlocking);
-    for (int i = 0; e == hipSuccess && i < kMaxSlabs + 2; ++i) e = hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming);
+    Side nw;
+    int nev = 0;
+    e = hipStreamCreateWithFlags(&nw.st, hipStreamNonBlocking);
+    for (; e == hipSuccess && nev < kMaxSlabs + 2; ++nev) e = hipEventCreateWithFlags(&nw.ev[nev], hipEventDisableTiming);
+    if (e != hipSuccess) {  // release what was created; a later call tries again
+      for (int i = 0; i < nev; ++i)
+        if (nw.ev[i]) (void)hipEventDestroy(nw.ev[i]);
+      if (nw.st) (void)hipStreamDestroy(nw.st);
+    }
+    if (e == hipSuccess) {
+      nw.ready = true;
+      sd = nw;
+    }
     if (cur != dev) {
       const hipError_t e2 = hipSetDevice(cur);
       if (e == hipSuccess) e = e2;
     }
-    if (e != hipSuccess) return e;  // what was created stays (and is reused by the next attempt's overwrite)
-    sd.ready = true;
+    if (e != hipSuccess) return e;
   }
   *out = &sd;
   return hipSuccess;
