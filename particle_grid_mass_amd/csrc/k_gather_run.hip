@@ -24,7 +24,9 @@
 // read once. Terms are added in a fixed order (z, y, then the run that starts
 // at or before the node's column, then the one before it), and several record
 // sets (species) are added term by term in set order: results are
-// deterministic.
+// deterministic. A launch covers the node rows of a range of planes (all of
+// them, or one slab's worth when the assembly overlaps the two phases); the
+// partition of the rows between launches does not change any sum.
 #include "mm_contract.h"
 #include "mm_run.h"
 

@@ -456,12 +456,13 @@ static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* b
   if (!RUNS)
     hipLaunchKernelGGL(k_order_window, dim3((nbins + OWIN - 1) / OWIN), dim3(OWIN), 0, s, bin_start, nbins, order);
   const int32_t* ord = RUNS ? nullptr : (const int32_t*)order;
-  // XCD chunks. Runs: whole planes of runs, so that the bins one row and one
-  // plane apart in y, which read the same cells' particles, run on one XCD
-  // and find them in its L2 (chunks of 16 runs put them on other XCDs and the
-  // particle data was fetched 4.5 times on a 128^3 grid); the planes dealt
-  // round the XCDs still balance a clustered density (a launch of fewer than
-  // 16 planes: an eighth of its runs per chunk). Per-bin records follow the
+  // XCD chunks. Runs: a pair of planes of runs per chunk, so that the bins one
+  // row and one plane apart, which read the same cells' particles, run on one
+  // XCD and find them in its L2 (chunks of 16 runs put them on other XCDs and
+  // the particle data was fetched 4.5 times on a 128^3 grid); the plane pairs
+  // dealt round the XCDs still balance a clustered density. A launch of fewer
+  // than 16 planes (a slab of the overlapped assembly) takes an eighth of its
+  // runs per chunk, so that every XCD gets a share. Per-bin records follow the
   // windowed bin order: chunks of 16 groups.
   int xg = 16;
   if (RUNS) {
