@@ -48,3 +48,31 @@ def test_deposit_bytes_several_sets(order):
         assert multi == one + (k - 1) * rec
         seq = one + (k - 1) * bench.deposit_bytes(order, True, 8, 1000, True)
         assert multi < seq
+
+
+def test_workload_key_names_slab_launches():
+    """The counter table keys the slab launches of the overlapped schedule apart
+    from the whole-grid launches of the same workload."""
+    import argparse
+    args = argparse.Namespace(config=5, kind=None, dtype="f64", deposit_per_species=False, shuffled=False,
+                              field="particle", canonical=False, dims=3, n2d=256, reorder=False)
+    assert bench.workload_key(args) == "config5-f64"
+    assert bench.workload_key(args, 4) == "config5-f64-slabs4"
+    args.field = "grid"
+    assert bench.workload_key(args, 4) == "config5-f64-gridB-slabs4"
+
+
+def test_traffic_table_entries_name_their_launch_grid():
+    """Every committed counter entry records the grid of the launches it was
+    averaged over, and the slab entries have smaller grids than the
+    whole-grid ones of the same workload."""
+    import json
+    with open(bench.PMC_FILE) as f:
+        d = json.load(f)
+    ents = d["kernels"]
+    for key, ent in ents.items():
+        assert ent["grid"] > 0, key
+        if key.endswith("-slabs4"):
+            whole = ents.get(key[: -len("-slabs4")])
+            if whole is not None:
+                assert ent["grid"] < whole["grid"], key
