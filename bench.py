@@ -137,14 +137,16 @@ def deposit_bytes(order: int, tensorial: bool, elem: int, nbins: int, accumulate
     return nrec * rec + out * (2 if accumulate else 1)
 
 
-def workload_name(case, field_on_grid: bool = False, mix: bool = False) -> str:
+def workload_name(case, field_on_grid: bool = False, mix: bool = False, records: bool = False) -> str:
     n = case.grid.n
     kind = "ECSIM 3x3" if case.kind == "ecsim" else "scalar"
     order = "CIC" if case.order == 1 else "TSC"
     dt = "f64 on fp32 positions and fields" if mix else case.dtype
     return (f"{order} {kind} {dt}, {n[0]}x{n[1]}x{n[2]} periodic cells, {case.np_total:,} particles "
             f"({len(case.species)} species)" + (", magnetic field on the grid nodes" if field_on_grid else "")
-            + f", {case.name}" + ("_gridB" if field_on_grid else "") + ("_mix" if mix else ""))
+            + (", one 64-byte record per particle" if records else "")
+            + f", {case.name}" + ("_gridB" if field_on_grid else "") + ("_mix" if mix else "")
+            + ("_records" if records else ""))
 
 
 def workload_key(args, slab: int = 0) -> str:
@@ -154,7 +156,8 @@ def workload_key(args, slab: int = 0) -> str:
             + ("-perspecies" if args.deposit_per_species else "")
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
             + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else "")
-            + ("-reorder" if getattr(args, "reorder", False) else "") + (f"-slabs{slab}" if slab else ""))
+            + ("-reorder" if getattr(args, "reorder", False) else "")
+            + ("-records" if getattr(args, "layout", "arrays") == "records" else "") + (f"-slabs{slab}" if slab else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -358,6 +361,10 @@ def main():
                          "by slab and deposit each slab's completed node planes on a second stream meanwhile (the "
                          "schedule of mm_assemble_ecsim, driven here through the plane-range entry points so that "
                          "the contraction launches can be bracketed with events); off: the two phases in turn")
+    ap.add_argument("--layout", default="arrays", choices=("arrays", "records"),
+                    help="particle storage: arrays (pos, w and B each dense, the default) or records (one 64-byte "
+                         "float64 record per particle, x y z w Bx By Bz and one unused value, read through the "
+                         "strided entry points; CIC fp64 ECSIM on the matrix-core path)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -395,6 +402,12 @@ def main():
     if args.reorder and (args.algo != "mfma" or args.dims != 3 or args.field == "grid"):
         print("bench.py: --reorder compares the matrix-core path with the field per particle (3D)", file=sys.stderr)
         sys.exit(2)
+    records = args.layout == "records"
+    if records and (case.order != 1 or case.kind != "ecsim" or case.dtype != "f64" or mix or args.algo != "mfma"
+                    or args.dims != 3 or args.field == "grid" or args.reorder):
+        print("bench.py: --layout records runs CIC fp64 ECSIM with the field per particle on the matrix-core path",
+              file=sys.stderr)
+        sys.exit(2)
     if args.canonical and args.algo != "mfma":
         print("bench.py: --canonical deposits the records of the matrix-core path (--algo mfma)", file=sys.stderr)
         sys.exit(2)
@@ -427,6 +440,11 @@ def main():
                          beta=sp.beta,
                          bs=torch.empty(nbins + 1, dtype=torch.int32, device=dev),
                          perm=torch.empty(max(sp.np, 1), dtype=torch.int32, device=dev)))
+        if records:  # one record per particle; the step reads it through views
+            d = spec[-1]
+            R = torch.zeros((sp.np, 8), dtype=torch.float64, device=dev)
+            R[:, 0:3], R[:, 3], R[:, 4:7] = d["pos"], d["w"], d["B"]
+            d["pos"], d["w"], d["B"] = R[:, 0:3], R[:, 3], R[:, 4:7]
         if args.reorder:  # bin-ordered copies and the identity permutation they are read through
             d = spec[-1]
             d["pos_r"], d["w_r"] = torch.empty_like(d["pos"]), torch.empty_like(d["w"])
@@ -441,6 +459,9 @@ def main():
     # species' matrices enter one field operator); --deposit-per-species
     # deposits each species' records on its own instead.
     multi = args.algo == "mfma" and len(spec) > 1 and args.dims == 3 and not args.deposit_per_species
+    # First order in fp64 arithmetic: the species share one record set, all
+    # contracted by one launch (mm_contract_bins_species) and deposited once.
+    one_set = multi and order == 1 and case.dtype == "f64" and not on_grid and not args.reorder
     # Slabs of planes: the contraction of slab k on the step's stream, then the
     # node planes it completed deposited on a second stream while slab k + 1
     # contracts (a node plane reads the records of its bin plane and the two
@@ -456,9 +477,16 @@ def main():
     nslab = len(zb) - 1 if overlap else 1
     side = torch.cuda.Stream(dev) if overlap else None
     slab_ev = [torch.cuda.Event() for _ in range(nslab)] if overlap else []
+    def species_set():
+        return [(s_["pos"], s_["w"], s_["B"], s_["bs"], s_["perm"][:s_["pos"].shape[0]], s_["beta"]) for s_ in spec]
+
     recs = []
     if overlap:  # the record buffer only: every launch of the timed kernel is a slab launch
         recs.append(torch.empty(mm.record_bytes(case.grid, order, tdt, True), dtype=torch.uint8, device=dev))
+    elif one_set:
+        for s_ in spec:
+            mm.bin_particles(case.grid, order, s_["pos"], s_["bs"], s_["perm"], mixed=mix)
+        recs.append(mm.contract_bins_species(case.grid, order, species_set(), case.sigma))
     elif args.algo == "mfma":
         for s_ in (spec if multi else spec[:1]):
             bs_, perm_ = mm.bin_particles(case.grid, order, s_["pos"], s_["bs"], s_["perm"], mixed=mix)
@@ -516,6 +544,12 @@ def main():
                             mm.deposit_records_planes(case.grid, order, rec, M, 0, 2, accumulate=si > 0)
                 mark(si, 2)
                 stream.wait_stream(side)
+            elif one_set:  # after the last species' binning: one contraction and one deposit for all
+                if si == len(spec) - 1:
+                    mm.contract_bins_species(case.grid, order, species_set(), case.sigma, rec=recs[0])
+                mark(si, 2)
+                if si == len(spec) - 1:
+                    mm.deposit_records(case.grid, order, recs[0], M, tensorial, canonical=args.canonical)
             elif args.algo == "mfma":
                 rec = recs[si] if multi else recs[0]
                 if args.reorder:
@@ -572,7 +606,7 @@ def main():
         for si in range(len(spec)):
             for pi, p in enumerate(phases):
                 phase_ms[p] += pev[k][si][pi].elapsed_time(pev[k][si][pi + 1])
-    nlaunch = {"bin": len(spec), "contract": len(spec), "deposit": 1 if multi else len(spec)}
+    nlaunch = {"bin": len(spec), "contract": 1 if one_set else len(spec), "deposit": 1 if multi else len(spec)}
     phase_per_launch_ms = {p: phase_ms[p] / (psteps * nlaunch[p]) for p in phases}
     if args.algo == "mfma":
         dom = max(("contract", "deposit"), key=lambda p: phase_per_launch_ms[p])
@@ -607,7 +641,8 @@ def main():
     ms_step = ms_total / args.steps
     # species whose launches the bracket holds (one deposition per step when
     # the species' records are deposited together)
-    dom_species = [len(spec) - 1] if (multi and dom == "deposit") else list(range(len(spec)))
+    dom_species = ([len(spec) - 1] if (multi and dom == "deposit") or (one_set and dom == "contract")
+                   else list(range(len(spec))))
     launches = len(marked) * len(dom_species)
     dom_ms = sum(ev[k][si][bracket[0]].elapsed_time(ev[k][si][bracket[1]])
                  for k in marked for si in dom_species)
@@ -650,7 +685,7 @@ def main():
                       for si in range(len(spec))) / (ksteps * len(spec))
         print(f"[bench] whole-grid contraction pass done ({ksteps} steps)", file=sys.stderr, flush=True)
 
-    np_launch = np_total / len(spec)
+    np_launch = np_total if one_set else np_total / len(spec)  # particles of one contraction launch
     # with the overlap the bracket holds the step's nslab slab launches
     per = nslab if overlap and dom == "contract" else 1
     launches *= per
@@ -668,7 +703,7 @@ def main():
     # (read and write)
     if multi:
         dbytes = deposit_bytes(order, tensorial, elem, nbins, accumulate=False, canonical=args.canonical,
-                               nrec=len(spec), rec_total=rec_total)
+                               nrec=1 if one_set else len(spec), rec_total=rec_total)
     else:
         dbytes = sum(deposit_bytes(order, tensorial, elem, nbins, accumulate=si > 0, canonical=args.canonical,
                                    dims=args.dims, rec_elem=8 if args.dims == 2 else 0, rec_total=rec_total)
@@ -826,12 +861,16 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_name(case, on_grid, mix), "config_id": args.config, "grid": list(case.grid.n),
-                   "order": order, "kind": case.kind, "field": args.field if tensorial else None,
+        "config": {"workload": workload_name(case, on_grid, mix, records), "config_id": args.config,
+                   "grid": list(case.grid.n), "layout": args.layout, "order": order, "kind": case.kind,
+                   "field": args.field if tensorial else None,
                    "storage": "fp32 positions and fields, fp64 weights and matrix" if mix else case.dtype,
                    "np": np_total,
-                   "species": len(spec), "algo": args.algo + ("+reorder" if args.reorder else ""), "stencil": "canonical half" if args.canonical else "full",
-                   "step": ("bin + contract per species, one deposit of all species' records" if multi else
+                   "species": len(spec), "algo": args.algo + ("+reorder" if args.reorder else ""),
+                   "stencil": "canonical half" if args.canonical else "full",
+                   "step": ("bin per species, one contraction of every species into one record set, one deposit"
+                            if one_set else
+                            "bin + contract per species, one deposit of all species' records" if multi else
                             (f"bin + contract by slabs of {slab} planes, each slab's completed node planes "
                              f"deposited on a second stream during the next slab's contraction" if overlap else
                              "bin + contract + deposit per species")) if args.algo == "mfma" else

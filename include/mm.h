@@ -235,6 +235,90 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
                              int accumulate, void* M, mm_stream_t stream);
 
 /*
+ * Strided particle arrays (fp64). The pages state the problem per particle
+ * (position x_p, weight w_p and field B_p, Sec. 2.1 Eq. 6) and leave their
+ * storage open; these entry points read them wherever the caller keeps them,
+ * for instance one record per particle (an array of structures): particle p's
+ * position is pos[p*pos_stride + 0..2], its weight w[p*w_stride] and its field
+ * B[p*B_stride + 0..2], strides counted in doubles. With pos_stride 3,
+ * w_stride 1 and B_stride 3 they are mm_bin_particles, mm_contract_bins and
+ * mm_assemble_ecsim with MM_F64. Out of cell order a particle whose values
+ * share one 64-byte record costs one random cache line of the contraction's
+ * gathers instead of one per array.
+ *
+ * mm_bin_particles_strided - mm_bin_particles (MM_F64) on positions
+ *   pos_stride doubles apart; bin_start and perm are bit for bit those of the
+ *   dense copy of the positions. Any order.
+ * mm_contract_bins_strided - mm_contract_bins (MM_F64, tensorial: B must not
+ *   be NULL, even when np == 0); records bit for bit those of the dense arrays.
+ * mm_assemble_ecsim_strided - mm_assemble_ecsim (MM_F64); M bit for bit that
+ *   of the dense arrays.
+ *  Strides other than the dense ones are read by the first-order (CIC)
+ *  matrix-core path on a 3D grid (MM_ALGO_MFMA; order 2, the other algorithms
+ *  and the 2D problem are MM_ERR_UNSUPPORTED with them). Each stride is at
+ *  least 3 (pos, B) or 1 (w) and below 2^31, else MM_ERR_ARG; the arrays may
+ *  overlap (they are only read). Other arguments, the workspace and the
+ *  errors as for the dense entry points.
+ */
+mm_status mm_bin_particles_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                   int64_t pos_stride, int32_t* bin_start, int32_t* perm, void* ws,
+                                   size_t* ws_bytes, mm_stream_t stream);
+mm_status mm_contract_bins_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                   int64_t pos_stride, const double* w, int64_t w_stride, const double* B,
+                                   int64_t B_stride, const int32_t* bin_start, const int32_t* perm, double beta,
+                                   double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream);
+mm_status mm_assemble_ecsim_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                    int64_t pos_stride, const double* w, int64_t w_stride, const double* B,
+                                    int64_t B_stride, const int32_t* bin_start, const int32_t* perm, double beta,
+                                    double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                                    size_t* ws_bytes, mm_stream_t stream);
+
+/*
+ * Several species in one call. The ECSIM operator sums over the particles of
+ * every species (Sec. 2.1 Eq. 6; Sec. 4.2 runs electrons and ions), each with
+ * its own beta = q dt / (2 m). One species of the set:
+ */
+#define MM_MAX_SPECIES 8
+typedef struct {
+  int64_t np;                 /* particles of the species (>= 0, < 2^31) */
+  const void* pos;            /* positions (dtype dt), particle p at pos[p*pos_stride + 0..2] */
+  const void* w;              /* weights, w[p*w_stride] */
+  const void* B;              /* field at each particle, B[p*B_stride + 0..2]; NULL: scalar records */
+  const int32_t* bin_start;   /* mm_bin_particles of these positions (never NULL) */
+  const int32_t* perm;        /* (may be NULL when np == 0) */
+  double beta;                /* q dt / (2 m) of the species */
+  int64_t pos_stride, w_stride, B_stride;  /* elements; 0 selects the dense 3, 1, 3 */
+} mm_species;
+
+/*
+ * mm_contract_bins_species - mm_contract_bins of every species into ONE set
+ * of records: each bin's record sums the particles of all species in it,
+ * contracted in one launch (the per-bin accumulators run on from species to
+ * species), so one record set is written and deposited instead of one per
+ * species. rec, rec_bytes and the layout are those of mm_contract_bins.
+ *  nspecies   1 .. MM_MAX_SPECIES (else MM_ERR_ARG); every species has a
+ *             field (tensorial) or none (scalar), else MM_ERR_ARG.
+ *  First order on a 3D grid with MM_F64 or MM_MIX only (other orders, MM_F32
+ *  and 2D: MM_ERR_UNSUPPORTED; contract those species one by one and deposit
+ *  with mm_deposit_records_multi). Strides as for the *_strided entry points
+ *  (other than dense: MM_F64, tensorial).
+ *
+ * mm_assemble_ecsim_species - mm_assemble_ecsim of every species into one M
+ * (accumulate as there, for the whole set). With MM_ALGO_MFMA where
+ * mm_contract_bins_species applies, the species share one record set;
+ * otherwise the species are assembled one after another into M, as by calls
+ * of mm_assemble_ecsim (mm_assemble_ecsim_strided) with accumulate after the
+ * first. Every species passes its field (B never NULL). The workspace query
+ * covers whichever of the two is taken.
+ */
+mm_status mm_contract_bins_species(const mm_grid* grid, int order, mm_dtype dt, int nspecies,
+                                   const mm_species* species, double sigma, void* rec, size_t* rec_bytes,
+                                   mm_stream_t stream);
+mm_status mm_assemble_ecsim_species(const mm_grid* grid, int order, mm_dtype dt, int nspecies,
+                                    const mm_species* species, double sigma, int accumulate, mm_algo algo, void* M,
+                                    void* ws, size_t* ws_bytes, mm_stream_t stream);
+
+/*
  * mm_record_bytes - size in bytes of the records that mm_deposit_records,
  * mm_deposit_records_canonical and mm_deposit_records_multi read for this
  * grid, order, dtype (of M) and kind: the first part of the buffer that

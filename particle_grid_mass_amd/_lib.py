@@ -17,13 +17,24 @@ ALGOS = {"mfma": 0, "atomic": 1, "mfma_atomic": 2, "valu": 3}
 EXPORTED = ("mm_bin_particles", "mm_assemble_scalar", "mm_assemble_ecsim", "mm_assemble_ecsim_gridB",
             "mm_contract_bins", "mm_contract_bins_gridB", "mm_deposit_records", "mm_deposit_records_canonical",
             "mm_deposit_records_multi", "mm_slab_planes", "mm_contract_bins_planes", "mm_contract_bins_planes_gridB",
-            "mm_deposit_records_planes",
+            "mm_deposit_records_planes", "mm_bin_particles_strided", "mm_contract_bins_strided",
+            "mm_assemble_ecsim_strided", "mm_contract_bins_species", "mm_assemble_ecsim_species",
             "mm_record_bytes", "mm_deposit_moments", "mm_stencil_matvec", "mm_assemble_ecsim_noalloc",
             "mm_probe_mfma_f64", "mm_status_string", "mm_version")
 
 
 class MMGrid(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32 * 3), ("origin", ctypes.c_double * 3), ("h", ctypes.c_double * 3)]
+
+
+MAX_SPECIES = 8
+
+
+class MMSpecies(ctypes.Structure):
+    """One species of the multi-species entry points (mm_species)."""
+    _fields_ = [("np", ctypes.c_int64), ("pos", ctypes.c_void_p), ("w", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("bin_start", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("beta", ctypes.c_double),
+                ("pos_stride", ctypes.c_int64), ("w_stride", ctypes.c_int64), ("B_stride", ctypes.c_int64)]
 
 
 class MMError(RuntimeError):
@@ -68,12 +79,20 @@ def load():
     lib.mm_contract_bins_planes.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, ctypes.c_size_t, P]
     lib.mm_contract_bins_planes_gridB.argtypes = [G, I, I, I64, P, P, P, P, P, D, D, I, I, P, ctypes.c_size_t, P]
     lib.mm_deposit_records_planes.argtypes = [G, I, I, I, I, ctypes.POINTER(P), I, I, I, P, P]
+    lib.mm_bin_particles_strided.argtypes = [G, I, I64, P, I64, P, P, P, SZ, P]
+    lib.mm_contract_bins_strided.argtypes = [G, I, I64, P, I64, P, I64, P, I64, P, P, D, D, P, SZ, P]
+    lib.mm_assemble_ecsim_strided.argtypes = [G, I, I64, P, I64, P, I64, P, I64, P, P, D, D, I, I, P, P, SZ, P]
+    SP = ctypes.POINTER(MMSpecies)
+    lib.mm_contract_bins_species.argtypes = [G, I, I, I, SP, D, P, SZ, P]
+    lib.mm_assemble_ecsim_species.argtypes = [G, I, I, I, SP, D, I, I, P, P, SZ, P]
     for f in (lib.mm_bin_particles, lib.mm_assemble_scalar, lib.mm_assemble_ecsim, lib.mm_assemble_ecsim_gridB,
               lib.mm_contract_bins, lib.mm_contract_bins_gridB, lib.mm_deposit_records,
               lib.mm_deposit_records_canonical, lib.mm_deposit_records_multi, lib.mm_record_bytes,
               lib.mm_stencil_matvec, lib.mm_deposit_moments,
               lib.mm_probe_mfma_f64, lib.mm_assemble_ecsim_noalloc, lib.mm_slab_planes, lib.mm_contract_bins_planes,
-              lib.mm_contract_bins_planes_gridB, lib.mm_deposit_records_planes):
+              lib.mm_contract_bins_planes_gridB, lib.mm_deposit_records_planes, lib.mm_bin_particles_strided,
+              lib.mm_contract_bins_strided, lib.mm_assemble_ecsim_strided, lib.mm_contract_bins_species,
+              lib.mm_assemble_ecsim_species):
         f.restype = ctypes.c_int
     lib.mm_status_string.argtypes = [ctypes.c_int]
     lib.mm_status_string.restype = ctypes.c_char_p

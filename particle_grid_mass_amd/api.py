@@ -64,6 +64,36 @@ def _check_tensor(t: torch.Tensor, name: str, dtype, shape_tail=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _row_strides(pos: torch.Tensor, w: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None):
+    """Element strides (pos, w, B) of particle arrays that are views into
+    larger storage, such as one float64 record per particle (``part[:, 0:3]``,
+    ``part[:, 3]``, ``part[:, 4:7]``), for the ``*_strided`` entry points;
+    None when every given array is contiguous (the dense entry points)."""
+    arrs = [t for t in (pos, w, B) if t is not None]
+    for name, t in zip(("pos", "w", "B"), (pos, w, B)):
+        if t is not None and not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+    if all(t.is_contiguous() for t in arrs):
+        return None
+    for name, t, rows in (("pos", pos, True), ("w", w, False), ("B", B, True)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must live on a GPU device")
+        if t.dtype != torch.float64:
+            raise ValueError(f"{name} must be contiguous (strided particle arrays are float64)")
+        if rows and (t.dim() != 2 or t.shape[1] != 3 or (t.shape[0] > 1 and t.stride(1) != 1)):
+            raise ValueError(f"{name} must be contiguous or a [np, 3] view with unit stride along its rows")
+        if not rows and t.dim() != 1:
+            raise ValueError(f"{name} must be contiguous or a one-dimensional view")
+
+    def rs(t, dense):
+        if t is None or t.shape[0] <= 1:
+            return dense
+        return int(t.stride(0))
+    return rs(pos, 3), rs(w, 1), rs(B, 3)
+
+
 def _check_bins(bin_start: torch.Tensor, perm: torch.Tensor, nnodes: int, npart: int):
     """The binning arrays must match the grid and the particles they index:
     bin_start holds nnodes + 1 entries and perm at least one per particle
@@ -113,7 +143,9 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
         raise TypeError(f"unsupported dtype {dt}")
     if mixed and dt != torch.float32:
         raise TypeError("mixed binning takes float32 positions")
-    _check_tensor(pos, "pos", dt)
+    strides = _row_strides(pos)
+    if strides is None:
+        _check_tensor(pos, "pos", dt)
     npart = pos.numel() // 3
     dev = pos.device
     if bin_start is None:
@@ -124,10 +156,15 @@ def bin_particles(grid, order: int, pos: torch.Tensor, bin_start: Optional[torch
     _check_tensor(perm, "perm", torch.int32)
     _check_bins(bin_start, perm, _nnodes(g), npart)
     s = _stream(dev)
-    head = (ctypes.byref(g), int(order), _lib.MM_MIX if mixed else _DT[dt], npart, _ptr(pos), _ptr(bin_start),
-            _ptr(perm))
-    ws, nbytes = _workspace(lib.mm_bin_particles, "mm_bin_particles", head, dev, s)
-    _call(lib.mm_bin_particles, "mm_bin_particles", *head, _ptr(ws), ctypes.byref(nbytes), s)
+    if strides is not None:
+        fn, name = lib.mm_bin_particles_strided, "mm_bin_particles_strided"
+        head = (ctypes.byref(g), int(order), npart, _ptr(pos), strides[0], _ptr(bin_start), _ptr(perm))
+    else:
+        fn, name = lib.mm_bin_particles, "mm_bin_particles"
+        head = (ctypes.byref(g), int(order), _lib.MM_MIX if mixed else _DT[dt], npart, _ptr(pos), _ptr(bin_start),
+                _ptr(perm))
+    ws, nbytes = _workspace(fn, name, head, dev, s)
+    _call(fn, name, *head, _ptr(ws), ctypes.byref(nbytes), s)
     return bin_start, perm[:npart]
 
 
@@ -135,10 +172,12 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
     lib = _lib.load()
     g = _grid_of(grid)
     code, fdt, dt = _modes(pos, w)
-    _check_tensor(pos, "pos", fdt)
-    _check_tensor(w, "w", dt)
-    if B is not None:
-        _check_tensor(B, "B", fdt)
+    strides = _row_strides(pos, w, B) if kind == "ecsim" and Bgrid is None else None
+    if strides is None:
+        _check_tensor(pos, "pos", fdt)
+        _check_tensor(w, "w", dt)
+        if B is not None:
+            _check_tensor(B, "B", fdt)
     if Bgrid is not None:
         _check_tensor(Bgrid, "Bgrid", fdt)
         if Bgrid.numel() != 3 * _nnodes(g):
@@ -170,6 +209,10 @@ def _assemble(kind, grid, order, pos, w, B, bin_start, perm, beta, sigma, M, acc
         fn, name = lib.mm_assemble_ecsim_gridB, "mm_assemble_ecsim_gridB"
         head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(Bgrid), _ptr(bin_start),
                 _ptr(perm), float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
+    elif kind == "ecsim" and strides is not None:
+        fn, name = lib.mm_assemble_ecsim_strided, "mm_assemble_ecsim_strided"
+        head = (ctypes.byref(g), int(order), npart, _ptr(pos), strides[0], _ptr(w), strides[1], _ptr(B), strides[2],
+                _ptr(bin_start), _ptr(perm), float(beta), float(sigma), int(bool(accumulate)), a, _ptr(M))
     elif kind == "ecsim":
         fn, name = lib.mm_assemble_ecsim, "mm_assemble_ecsim"
         head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(B), _ptr(bin_start), _ptr(perm),
@@ -246,12 +289,14 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
     lib = _lib.load()
     g = _grid_of(grid)
     code, fdt, dt = _modes(pos, w)
-    _check_tensor(pos, "pos", fdt)
-    _check_tensor(w, "w", dt)
     if B is not None and Bgrid is not None:
         raise ValueError("give the field per particle (B) or on the grid (Bgrid), not both")
-    if B is not None:
-        _check_tensor(B, "B", fdt)
+    strides = _row_strides(pos, w, B) if B is not None else None
+    if strides is None:
+        _check_tensor(pos, "pos", fdt)
+        _check_tensor(w, "w", dt)
+        if B is not None:
+            _check_tensor(B, "B", fdt)
     if Bgrid is not None:
         _check_tensor(Bgrid, "Bgrid", fdt)
         if Bgrid.numel() != 3 * _nnodes(g):
@@ -275,8 +320,13 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
         # the field when np == 0, so a one-element stand-in marks the call
         # as tensorial
         field = torch.empty(1, dtype=field.dtype, device=field.device)
-    head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
-            _ptr(perm), float(beta), float(sigma))
+    if strides is not None:
+        fn, name = lib.mm_contract_bins_strided, "mm_contract_bins_strided"
+        head = (ctypes.byref(g), int(order), npart, _ptr(pos), strides[0], _ptr(w), strides[1], _ptr(field),
+                strides[2], _ptr(bin_start), _ptr(perm), float(beta), float(sigma))
+    else:
+        head = (ctypes.byref(g), int(order), code, npart, _ptr(pos), _ptr(w), _ptr(field), _ptr(bin_start),
+                _ptr(perm), float(beta), float(sigma))
     nbytes = ctypes.c_size_t(0)
     _call(fn, name + " (size query)", *head, None, ctypes.byref(nbytes), s)
     if rec is None:
@@ -285,6 +335,92 @@ def contract_bins(grid, order: int, pos, w, B, bin_start, perm, beta: float = 0.
         nbytes = ctypes.c_size_t(rec.numel() * rec.element_size())
     _call(fn, name, *head, _ptr(rec), ctypes.byref(nbytes), s)
     return rec
+
+
+def _species_array(g, species):
+    """ctypes mm_species array for (pos, w, B, bin_start, perm, beta) tuples, one
+    per species (dense or strided views as for the single-species calls).
+    Returns the array, the dtype code, the output dtype, the device and the
+    tensors that must outlive the call."""
+    if not 1 <= len(species) <= _lib.MAX_SPECIES:
+        raise ValueError(f"between 1 and {_lib.MAX_SPECIES} species, got {len(species)}")
+    arr = (_lib.MMSpecies * len(species))()
+    keep = []
+    code0 = dt0 = dev = None
+    for i, sp in enumerate(species):
+        pos, w, B, bin_start, perm, beta = sp
+        code, fdt, dt = _modes(pos, w)
+        if code0 is None:
+            code0, dt0, dev = code, dt, pos.device
+        elif code != code0:
+            raise TypeError("every species must use the same dtypes")
+        strides = _row_strides(pos, w, B)
+        if strides is None:
+            _check_tensor(pos, "pos", fdt)
+            _check_tensor(w, "w", dt)
+            if B is not None:
+                _check_tensor(B, "B", fdt)
+            strides = (0, 0, 0)
+        npart = pos.numel() // 3
+        if w.numel() != npart or (B is not None and B.numel() != 3 * npart):
+            raise ValueError(f"species {i}: pos, w and B disagree on the particle count")
+        _check_tensor(bin_start, "bin_start", torch.int32)
+        _check_tensor(perm, "perm", torch.int32)
+        _check_bins(bin_start, perm, _nnodes(g), npart)
+        if B is not None and B.numel() == 0:  # no particles: a stand-in address marks the species tensorial
+            B = torch.empty(1, dtype=B.dtype, device=B.device)
+            keep.append(B)
+        arr[i] = _lib.MMSpecies(npart, pos.data_ptr() or None, w.data_ptr() or None,
+                                None if B is None else B.data_ptr(), bin_start.data_ptr(), perm.data_ptr() or None,
+                                float(beta), strides[0], strides[1], strides[2])
+    return arr, code0, dt0, dev, keep
+
+
+def contract_bins_species(grid, order: int, species, sigma: float = 1.0,
+                          rec: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Phase 1 of every species into one record set (``mm_contract_bins_species``):
+    each bin's record sums all species' particles in it. ``species`` holds
+    ``(pos, w, B, bin_start, perm, beta)`` per species (B None for scalar records)."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    arr, code, _, dev, keep = _species_array(g, species)
+    s = _stream(dev)
+    nbytes = ctypes.c_size_t(0)
+    head = (ctypes.byref(g), int(order), code, len(species), arr, float(sigma))
+    _call(lib.mm_contract_bins_species, "mm_contract_bins_species (size query)", *head, None, ctypes.byref(nbytes),
+          s)
+    if rec is None:
+        rec = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
+    else:
+        nbytes = ctypes.c_size_t(rec.numel() * rec.element_size())
+    _call(lib.mm_contract_bins_species, "mm_contract_bins_species", *head, _ptr(rec), ctypes.byref(nbytes), s)
+    del keep
+    return rec
+
+
+def assemble_ecsim_species(grid, order: int, species, sigma: float = 1.0, M: Optional[torch.Tensor] = None,
+                           accumulate: bool = False, algo: str = "mfma") -> torch.Tensor:
+    """3x3 ECSIM mass matrix of several species into one ``M`` (``mm_assemble_ecsim_species``);
+    ``species`` holds ``(pos, w, B, bin_start, perm, beta)`` per species."""
+    lib = _lib.load()
+    g = _grid_of(grid)
+    arr, code, dt, dev, keep = _species_array(g, species)
+    if algo not in _lib.ALGOS:
+        raise ValueError(f"unknown algo {algo!r}; expected one of {sorted(_lib.ALGOS)}")
+    nof = noff_grid(order, g)
+    if M is None:
+        M = torch.empty((_nnodes(g), nof, 9), dtype=dt, device=dev)
+        accumulate = False
+    _check_tensor(M, "M", dt)
+    if M.numel() != _nnodes(g) * nof * 9:
+        raise ValueError(f"M has {M.numel()} elements, expected {_nnodes(g) * nof * 9}")
+    s = _stream(dev)
+    head = (ctypes.byref(g), int(order), code, len(species), arr, float(sigma), int(bool(accumulate)),
+            _lib.ALGOS[algo], _ptr(M))
+    ws, nbytes = _workspace(lib.mm_assemble_ecsim_species, "mm_assemble_ecsim_species", head, dev, s)
+    _call(lib.mm_assemble_ecsim_species, "mm_assemble_ecsim_species", *head, _ptr(ws), ctypes.byref(nbytes), s)
+    del keep
+    return M
 
 
 def slab_planes(grid, order: int) -> int:

@@ -90,7 +90,7 @@ __device__ __forceinline__ void count_digit_runs(int* h, int d, bool valid, int 
 // otherwise.
 // T: arithmetic of the key; PT: type of the stored positions (T, or fp32 read into fp64).
 template <typename T, int R, typename PT>
-__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restrict__ pos, int np, int nbins,
+__global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restrict__ pos, int64_t ps, int np, int nbins,
                                                   uint32_t* __restrict__ keys, int32_t* __restrict__ ghist,
                                                   int ntiles, int32_t* __restrict__ tile_unsorted,
                                                   int32_t* __restrict__ bin_start, int32_t* __restrict__ perm) {
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restric
       size_t idx = base + (size_t)i * BT + tid;
       idx = idx < (size_t)np ? idx : (size_t)np - 1;  // clamped: loads are unconditional
 #pragma unroll
-      for (int d = 0; d < 3; ++d) x[i][d] = (T)pos[3 * idx + d];
+      for (int d = 0; d < 3; ++d) x[i][d] = (T)pos[ps * idx + d];
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -132,7 +132,8 @@ __global__ __launch_bounds__(BT) void k_keys_hist(GridDev g, const PT* __restric
   if (tid == 0) {  // key of the last particle of the previous tile
     int kb = -1;
     if (base > 0) {
-      const T xb[3] = {(T)pos[3 * (base - 1)], (T)pos[3 * (base - 1) + 1], (T)pos[3 * (base - 1) + 2]};
+      const size_t pb = ps * (base - 1);
+      const T xb[3] = {(T)pos[pb], (T)pos[pb + 1], (T)pos[pb + 2]};
       kb = particle_key<R>(xb, g);
     }
     kbefore = kb;
@@ -207,54 +208,86 @@ __global__ __launch_bounds__(BT) void k_hist(const uint32_t* __restrict__ keys, 
 // One block per digit column: exclusive scan over the tiles in place, column
 // total to totals[digit]. In the first pass (tile_unsorted != NULL) every
 // block reduces the per-tile descent records itself and block 0 stores the
-// result in *unsorted for the kernels after it.
+// result in *unsorted for the kernels after it. With one block per column
+// the latency of each round of loads is exposed, so the loads are
+// unconditional (clamped indices; np > 0, so ntiles >= 1), the column is
+// taken in batches of SB chunks of 2048 tiles loaded before any is scanned,
+// and the first batch is in flight while the order flag is found (in key
+// order the values are then not used).
 __global__ __launch_bounds__(256) void k_scan_cols(int32_t* __restrict__ ghist, int ntiles,
                                                    int32_t* __restrict__ totals,
                                                    const int32_t* __restrict__ tile_unsorted,
                                                    int32_t* __restrict__ unsorted) {
-  __shared__ int wsum[4];
+  constexpr int SI = 8, SB = 4;  // tiles per thread per chunk, chunks per batch
+  __shared__ int wsum[SB][4];
+  const int col = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* c = ghist + (size_t)col * ntiles;
+  int v[SB][SI];
+  auto load_batch = [&](int b0) {
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+#pragma unroll
+      for (int i = 0; i < SI; ++i) {
+        const int idx = b0 + k * 256 * SI + tid * SI + i;
+        const int x = c[idx < ntiles ? idx : ntiles - 1];
+        v[k][i] = idx < ntiles ? x : 0;
+      }
+    }
+  };
+  load_batch(0);
   if (tile_unsorted) {
     bool any = false;
-    for (int t = threadIdx.x; t < ntiles; t += 256) any |= tile_unsorted[t] != 0;
+    for (int t0 = 0; t0 < ntiles; t0 += 256 * 8) {
+      int f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i * 256 + tid;
+        f[i] = tile_unsorted[t < ntiles ? t : ntiles - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) any |= f[i] != 0;  // a clamped index repeats a real tile's record
+    }
     any = __syncthreads_or(any);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *unsorted = any ? 1 : 0;
+    if (col == 0 && tid == 0) *unsorted = any ? 1 : 0;
     if (!any) return;  // already in key order
   } else if (*unsorted == 0) {
     return;
   }
-  const int col = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t* c = ghist + (size_t)col * ntiles;
   int carry = 0;
-  for (int b0 = 0; b0 < ntiles; b0 += 256 * 8) {
-    int v[8], run = 0;
+  for (int b0 = 0; b0 < ntiles; b0 += 256 * SI * SB) {
+    if (b0 > 0) load_batch(b0);
+    int run[SB], incl[SB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = b0 + tid * 8 + i;
-      v[i] = idx < ntiles ? c[idx] : 0;
-      run += v[i];
-    }
-    int incl = run;
+    for (int k = 0; k < SB; ++k) {
+      run[k] = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
+      for (int i = 0; i < SI; ++i) run[k] += v[k][i];
+      incl[k] = run[k];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl[k], off);
+        if (lane >= off) incl[k] += y;
+      }
+      if (lane == 63) wsum[k][wave] = incl[k];
     }
-    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int wbase = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) wbase += wsum[w];
-      total += wsum[w];
-    }
-    int excl = carry + wbase + incl - run;
+    for (int k = 0; k < SB; ++k) {
+      int wbase = 0, total = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = b0 + tid * 8 + i;
-      if (idx < ntiles) c[idx] = excl;
-      excl += v[i];
+      for (int w = 0; w < 4; ++w) {
+        if (w < wave) wbase += wsum[k][w];
+        total += wsum[k][w];
+      }
+      int excl = carry + wbase + incl[k] - run[k];
+#pragma unroll
+      for (int i = 0; i < SI; ++i) {
+        const int idx = b0 + k * 256 * SI + tid * SI + i;
+        if (idx < ntiles) c[idx] = excl;
+        excl += v[k][i];
+      }
+      carry += total;
     }
-    carry += total;
     __syncthreads();
   }
   if (tid == 0) totals[col] = carry;
@@ -500,19 +533,19 @@ static BinWs bin_layout(void* base, int64_t np, int64_t nbins) {
 size_t bin_workspace_bytes(int64_t np, int64_t nbins) { return bin_layout(nullptr, np, nbins).bytes; }
 
 template <typename T, typename PT>
-static hipError_t keys_t(const GridDev& g, int order, const void* pos, int np, int nbins, const BinWs& w, int ntiles,
-                         int32_t* bin_start, int32_t* perm, hipStream_t s) {
+static hipError_t keys_t(const GridDev& g, int order, const void* pos, int64_t ps, int np, int nbins, const BinWs& w,
+                         int ntiles, int32_t* bin_start, int32_t* perm, hipStream_t s) {
   if (order == 1)
-    hipLaunchKernelGGL((k_keys_hist<T, 1, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, np, nbins, w.keysA,
-                       w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
+    hipLaunchKernelGGL((k_keys_hist<T, 1, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, ps, np, nbins,
+                       w.keysA, w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   else
-    hipLaunchKernelGGL((k_keys_hist<T, 2, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, np, nbins, w.keysA,
-                       w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
+    hipLaunchKernelGGL((k_keys_hist<T, 2, PT>), dim3(ntiles), dim3(BT), 0, s, g, (const PT*)pos, ps, np, nbins,
+                       w.keysA, w.ghist, ntiles, w.tile_unsorted, bin_start, perm);
   return hipGetLastError();
 }
 
 hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, int np, int nbins, int32_t* bin_start,
-                      int32_t* perm, void* ws, hipStream_t s, bool pos32) {
+                      int32_t* perm, void* ws, hipStream_t s, bool pos32, int64_t ps) {
   if (np == 0) {
     hipLaunchKernelGGL(k_fill_i32, dim3((nbins + 1 + 255) / 256), dim3(256), 0, s, bin_start, nbins + 1, 0);
     return hipGetLastError();
@@ -522,8 +555,8 @@ hipError_t launch_bin(const GridDev& g, int order, bool f32, const void* pos, in
   const int ntiles = (np + TILE - 1) / TILE;
   // fp32 positions (MM_F32 and the mixed layout) are read exactly into fp64:
   // the key is found in fp64 arithmetic, as every kernel finds the support
-  hipError_t e = (f32 || pos32) ? keys_t<double, float>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s)
-                                : keys_t<double, double>(g, order, pos, np, nbins, w, ntiles, bin_start, perm, s);
+  hipError_t e = (f32 || pos32) ? keys_t<double, float>(g, order, pos, ps, np, nbins, w, ntiles, bin_start, perm, s)
+                                : keys_t<double, double>(g, order, pos, ps, np, nbins, w, ntiles, bin_start, perm, s);
   if (e != hipSuccess) return e;
   uint32_t* kin = w.keysA;
   uint32_t* kout = w.keysB;

@@ -29,6 +29,13 @@
 //  * A finished group stages its packed upper-triangle records in LDS, two
 //    bins at a time, and writes them with 16-byte stores (the records of
 //    consecutive bins are contiguous).
+//  * One launch may contract several species (each with its own arrays,
+//    binning and beta): a group's accumulators run on from one species'
+//    particles to the next, so their records are written once, summed.
+//  * The particle arrays may have any element stride (ST), as when each
+//    particle is one record of its position, weight and field: out of cell
+//    order a particle then costs one random cache line instead of one per
+//    array.
 #include "mm_contract.h"
 
 namespace mmk {
@@ -105,24 +112,47 @@ struct Raw {
   bool valid;
 };
 
+// Element strides of the particle arrays (used when the kernel's ST is set).
+struct Strides {
+  int64_t ps, wst, bst;
+};
+
+// The species contracted by one launch: each bin's records sum the particles
+// of every species in it, each with its own arrays, binning and beta.
+template <typename PT>
+struct SpeciesSet {
+  const PT* pos[MAX_SPECIES];
+  const double* w[MAX_SPECIES];
+  const PT* B[MAX_SPECIES];  // per-particle field (NULL when scalar or on the grid)
+  const int32_t* bin_start[MAX_SPECIES];
+  const int32_t* perm[MAX_SPECIES];
+  double beta[MAX_SPECIES];
+  int64_t ps[MAX_SPECIES], wst[MAX_SPECIES], bst[MAX_SPECIES];
+  int np[MAX_SPECIES];
+  int n;
+};
+
 // GB: the field is on the grid (gathered in stage), not per particle.
 // PT: type of the stored positions and field (fp64, or fp32 read into fp64).
-template <typename PT, int NC, bool GB>
+// ST: particle values st.ps, st.wst and st.bst elements apart (say records of
+// several values per particle) instead of the dense 3, 1 and 3.
+template <typename PT, int NC, bool GB, bool ST>
 __device__ __forceinline__ Raw load_raw(const PT* __restrict__ pos, const double* __restrict__ w,
-                                        const PT* __restrict__ Bf, int p, int np) {
+                                        const PT* __restrict__ Bf, int p, int np, const Strides& st) {
   // unconditional loads (particle 0 stands in for a lane without a particle;
   // np > 0 here) keep the number of loads in flight the same on every path
   Raw r;
   r.valid = (unsigned)p < (unsigned)np;
   const size_t q = r.valid ? (size_t)p : 0;
-  r.x = pos[3 * q];
-  r.y = pos[3 * q + 1];
-  r.z = pos[3 * q + 2];
-  r.w = w[q];
+  const size_t qp = ST ? st.ps * q : 3 * q, qw = ST ? st.wst * q : q, qb = ST ? st.bst * q : 3 * q;
+  r.x = pos[qp];
+  r.y = pos[qp + 1];
+  r.z = pos[qp + 2];
+  r.w = w[qw];
   if (NC == 9 && !GB) {
-    r.bx = Bf[3 * q];
-    r.by = Bf[3 * q + 1];
-    r.bz = Bf[3 * q + 2];
+    r.bx = Bf[qb];
+    r.by = Bf[qb + 1];
+    r.bz = Bf[qb + 2];
   } else {
     r.bx = r.by = r.bz = 0.0;
   }
@@ -201,18 +231,14 @@ struct Acc {
 
 }  // namespace
 
-template <typename PT, int NC, bool GB>
-__global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ pos,
-                                              const double* __restrict__ w, const PT* __restrict__ Bf,
-                                              const int32_t* __restrict__ bin_start,
-                                              const int32_t* __restrict__ perm, int np, int nbins, double beta,
-                                              double sigma, double* __restrict__ rec) {
+template <typename PT, int NC, bool GB, bool ST>
+__global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S, const PT* __restrict__ Bgrid,
+                                              int nbins, double sigma, double* __restrict__ rec) {
   __shared__ __attribute__((aligned(16))) double sm[GB ? Cfg<NC>::SMEM_GB : Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
   const int ngroups = (nbins + NB - 1) / NB;
   const int grp = blockIdx.x;
   if (grp >= ngroups) return;
-  const Group G = load_group(bin_start, grp, nbins, np, lane);
   double* sB = sm + Cfg<NC>::STAGE;
   if (GB && lane < NB * 8) {
     // Bf is the grid field [nnodes][3]: node a of bin 4 grp + (lane >> 3) is
@@ -224,7 +250,7 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ 
       const int x = kx + (a & 1) < g.n0 ? kx + (a & 1) : 0;
       const int y = ky + ((a >> 1) & 1) < g.n1 ? ky + ((a >> 1) & 1) : 0;
       const int z = kz + (a >> 2) < g.n2 ? kz + (a >> 2) : 0;
-      const PT* f = Bf + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
+      const PT* f = Bgrid + 3 * ((size_t)x + (size_t)g.n0 * ((size_t)y + (size_t)g.n1 * z));
       f0 = f[0];
       f1 = f[1];
       f2 = f[2];
@@ -242,7 +268,16 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ 
 
   Acc<NC> acc;
   acc.zero();
-  if (np > 0) {
+  for (int sp = 0; sp < S.n; ++sp) {  // the accumulators run on over the species
+    const PT* __restrict__ pos = S.pos[sp];
+    const double* __restrict__ w = S.w[sp];
+    const PT* __restrict__ Bf = S.B[sp];
+    const int32_t* __restrict__ perm = S.perm[sp];
+    const int np = S.np[sp];
+    if (np == 0) continue;
+    const double beta = S.beta[sp];
+    const Strides str{S.ps[sp], S.wst[sp], S.bst[sp]};
+    const Group G = load_group(S.bin_start[sp], grp, nbins, np, lane);
     // Two chunks of particle data in flight ahead of the one being contracted.
     // The loop is unrolled by two so that each register set is reloaded right
     // after its chunk is staged (no copies, which would wait for the loads).
@@ -258,7 +293,7 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ 
         stage<NC, GB>(r, g, beta, sigma, sm, sB, lane);
         __syncthreads();
       }
-      r = load_raw<PT, NC, GB>(pos, w, Bf, perm_index(pr), np);  // chunk j + 2
+      r = load_raw<PT, NC, GB, ST>(pos, w, Bf, perm_index(pr), np, str);  // chunk j + 2
       pr = chunk_perm(perm, G, j + 4, lane);
       const int left = G.maxn - j * CH;
       const int nr = j < 0 ? 0 : (left >= CH ? CH / 4 : (left > 0 ? (left + 3) / 4 : 0));
@@ -328,27 +363,69 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const PT* __restrict__ 
   }
 }
 
-template <typename PT>
-static hipError_t cic64_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
-                          double beta, double sigma, double* rec, hipStream_t s) {
+template <typename PT, bool ST>
+static hipError_t cic64_t(const GridDev& g, const SpeciesSet<PT>& S, const PT* Bgrid, bool tensorial, double sigma,
+                          double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
   const int ngroups = (nbins + NB - 1) / NB;  // one single-wave workgroup per group of four bins
-  if (P.Bgrid)
-    hipLaunchKernelGGL((k_cic64<PT, 9, true>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos, (const double*)P.w,
-                       (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec);
-  else if (P.B)
-    hipLaunchKernelGGL((k_cic64<PT, 9, false>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  if (Bgrid)
+    hipLaunchKernelGGL((k_cic64<PT, 9, true, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
+  else if (tensorial)
+    hipLaunchKernelGGL((k_cic64<PT, 9, false, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
   else
-    hipLaunchKernelGGL((k_cic64<PT, 1, false>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 1, false, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
   return hipGetLastError();
+}
+
+template <typename PT>
+static hipError_t cic64_species(const GridDev& g, int ns, const Particles* P, const int32_t* const* bin_start,
+                                const int32_t* const* perm, const double* beta, double sigma, double* rec,
+                                hipStream_t s) {
+  SpeciesSet<PT> S = {};
+  S.n = ns;
+  bool strided = false;
+  for (int i = 0; i < ns; ++i) {
+    S.pos[i] = (const PT*)P[i].pos;
+    S.w[i] = (const double*)P[i].w;
+    S.B[i] = (const PT*)P[i].B;
+    S.bin_start[i] = bin_start[i];
+    S.perm[i] = perm[i];
+    S.beta[i] = beta[i];
+    S.ps[i] = P[i].ps;
+    S.wst[i] = P[i].wst;
+    S.bst[i] = P[i].bst;
+    S.np[i] = P[i].np;
+    strided = strided || P[i].strided();
+  }
+  const PT* Bgrid = (const PT*)P[0].Bgrid;
+  const bool tensorial = P[0].B != nullptr || Bgrid;
+  if (strided) {
+    // strided arrays: fp64 values with the field per particle
+    if (Bgrid || !tensorial) return hipErrorInvalidValue;
+    return cic64_t<PT, true>(g, S, Bgrid, true, sigma, rec, s);
+  }
+  return cic64_t<PT, false>(g, S, Bgrid, tensorial, sigma, rec, s);
+}
+
+hipError_t launch_cic64_species(const GridDev& g, int ns, const Particles* P, const int32_t* const* bin_start,
+                                const int32_t* const* perm, const double* beta, double sigma, double* rec,
+                                hipStream_t s) {
+  if (ns < 1 || ns > MAX_SPECIES) return hipErrorInvalidValue;
+  // one kind of storage, field and records for the whole set
+  for (int i = 1; i < ns; ++i)
+    if (P[i].pos32 != P[0].pos32 || P[i].Bgrid != P[0].Bgrid || (P[i].B != nullptr) != (P[0].B != nullptr))
+      return hipErrorInvalidValue;
+  if (P[0].pos32) {
+    for (int i = 0; i < ns; ++i)
+      if (P[i].strided()) return hipErrorInvalidValue;
+    return cic64_species<float>(g, ns, P, bin_start, perm, beta, sigma, rec, s);
+  }
+  return cic64_species<double>(g, ns, P, bin_start, perm, beta, sigma, rec, s);
 }
 
 hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s) {
-  return P.pos32 ? cic64_t<float>(g, P, bin_start, perm, beta, sigma, rec, s)
-                 : cic64_t<double>(g, P, bin_start, perm, beta, sigma, rec, s);
+  return launch_cic64_species(g, 1, &P, &bin_start, &perm, &beta, sigma, rec, s);
 }
 
 }  // namespace mmk

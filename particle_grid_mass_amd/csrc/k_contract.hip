@@ -496,6 +496,7 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
                            const int32_t* perm, double beta, double sigma, int mode, void* out, hipStream_t s) {
   if (mode == MODE_RECORD && order == 1 && !f32)
     return launch_cic64(g, P, bin_start, perm, beta, sigma, (double*)out, s);
+  if (P.strided()) return hipErrorInvalidValue;  // only the fp64 CIC record kernel reads strided arrays
   if (mode == MODE_RECORD && order == 1 && f32 && !P.Bgrid)
     return launch_cic32(g, P, bin_start, perm, beta, sigma, (float*)out, s);
   if (mode == MODE_RECORD && order == 2 && !f32 && (P.B || P.Bgrid))
@@ -511,7 +512,7 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
 }
 
 bool contract_planes_apply(const GridDev& g, int order, bool f32, const Particles& P) {
-  if (order != 2 || !tsc_run_records(g)) return false;
+  if (order != 2 || !tsc_run_records(g) || P.strided()) return false;
   return f32 ? (P.B && !P.Bgrid && !P.pos32) : (P.B || P.Bgrid);
 }
 

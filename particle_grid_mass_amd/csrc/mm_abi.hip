@@ -9,6 +9,7 @@
 #include "mm_contract.h"
 
 static_assert(MM_MAX_RECORD_SETS == mmk::MAX_REC, "record set limit of the ABI and the gather");
+static_assert(MM_MAX_SPECIES == mmk::MAX_SPECIES, "species limit of the ABI and the contraction");
 
 using namespace mmk;
 
@@ -65,6 +66,24 @@ bool is2d(const mm_grid* g) { return g->n[2] == 1; }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Element strides of the particle arrays: position p at pos[ps p + 0..2],
+// weight at w[wst p], field at B[bst p + 0..2]. Dense arrays are 3, 1, 3.
+struct Strides {
+  int64_t ps = 3, wst = 1, bst = 3;
+  bool dense() const { return ps == 3 && wst == 1 && bst == 3; }
+  bool valid() const { return ps >= 3 && wst >= 1 && bst >= 3 && ps <= kMaxI32 && wst <= kMaxI32 && bst <= kMaxI32; }
+};
+
+// Other strides than the dense ones are read by the fp64 CIC record
+// contraction (3D, field per particle) only.
+mm_status check_strides(const Strides& st, const mm_grid* grid, int order, mm_dtype dt, bool tensorial,
+                        const void* Bgrid) {
+  if (st.dense()) return MM_OK;
+  if (!st.valid()) return MM_ERR_ARG;
+  if (dt != MM_F64 || order != 1 || is2d(grid) || Bgrid || !tensorial) return MM_ERR_UNSUPPORTED;
+  return MM_OK;
+}
+
 // ------------------------------------------------------------ fixed scratch
 // Device scratch of the allocation-free entry point mm_assemble_ecsim_noalloc:
 // the per-bin records of the two-phase assembly live here instead of in a
@@ -108,7 +127,8 @@ mm_status scratch_of_current_device(void** out) {
 mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
                           const void* B, const void* Bgrid, bool tensorial, const int32_t* bin_start,
                           const int32_t* perm, double beta, double sigma, mm_algo algo, void* M, void* ws,
-                          size_t* ws_bytes, mm_stream_t stream, int accumulate, size_t fixed_max = 0) {
+                          size_t* ws_bytes, mm_stream_t stream, int accumulate, size_t fixed_max = 0,
+                          const Strides& str = Strides()) {
   if (!ws_bytes && fixed_max == 0) return MM_ERR_NULL;
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
@@ -116,6 +136,8 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC && algo != MM_ALGO_VALU)
     return MM_ERR_ARG;
+  if ((st = check_strides(str, grid, order, dt, tensorial, Bgrid)) != MM_OK) return st;
+  if (!str.dense() && algo != MM_ALGO_MFMA) return MM_ERR_UNSUPPORTED;
   if (algo == MM_ALGO_ATOMIC && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
   // the vector-FMA comparison contraction: CIC, fp64 arithmetic, 3D, field per particle
   if (algo == MM_ALGO_VALU && (order != 1 || dt == MM_F32 || is2d(grid) || Bgrid)) return MM_ERR_UNSUPPORTED;
@@ -163,6 +185,9 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   hipError_t e = hipSuccess;
   Particles P{pos, w, tensorial ? B : nullptr, (int)np};
   P.pos32 = dt == MM_MIX;
+  P.ps = str.ps;
+  P.wst = str.wst;
+  P.bst = str.bst;
   if (Bgrid && np > 0) {
     if (interp) {
       void* bp = (char*)ws + rec_need;
@@ -205,12 +230,14 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
 // mm_contract_bins with the field per particle (B) or on the grid (Bgrid).
 mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, const void* w,
                           const void* B, const void* Bgrid, const int32_t* bin_start, const int32_t* perm,
-                          double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream) {
+                          double beta, double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream,
+                          const Strides& str = Strides()) {
   if (!rec_bytes) return MM_ERR_NULL;
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if ((st = check_strides(str, grid, order, dt, B != nullptr || Bgrid != nullptr, Bgrid)) != MM_OK) return st;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -232,6 +259,9 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   hipStream_t s = (hipStream_t)stream;
   Particles P{pos, w, B, (int)np};
   P.pos32 = dt == MM_MIX;
+  P.ps = str.ps;
+  P.wst = str.wst;
+  P.bst = str.bst;
   if (Bgrid) {
     if (interp) {
       void* bp = (char*)rec + align256(rec_need);
@@ -272,6 +302,83 @@ mm_status contract_planes_common(const mm_grid* grid, int order, mm_dtype dt, in
                                            (hipStream_t)stream));
 }
 
+// ----------------------------------------------------------- species sets
+// Strides of one species (0 selects the dense value).
+Strides species_strides(const mm_species& sp) {
+  Strides st;
+  st.ps = sp.pos_stride ? sp.pos_stride : 3;
+  st.wst = sp.w_stride ? sp.w_stride : 1;
+  st.bst = sp.B_stride ? sp.B_stride : 3;
+  return st;
+}
+
+// Whether one launch contracts the whole set: first order, 3D, fp64 arithmetic.
+bool species_fused(const mm_grid* grid, int order, mm_dtype dt) {
+  return order == 1 && !is2d(grid) && dt != MM_F32;
+}
+
+// Checks shared by the species entry points; *tensorial is the kind of the set.
+mm_status check_species(const mm_grid* grid, int order, mm_dtype dt, int ns, const mm_species* sp,
+                        bool* tensorial) {
+  if (ns < 1 || ns > MM_MAX_SPECIES) return MM_ERR_ARG;
+  if (!sp) return MM_ERR_NULL;
+  *tensorial = sp[0].B != nullptr;
+  for (int i = 0; i < ns; ++i) {
+    const mm_species& s = sp[i];
+    if (s.np < 0 || !is_finite_d(s.beta)) return MM_ERR_ARG;
+    if (s.np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+    if ((s.B != nullptr) != *tensorial) return MM_ERR_ARG;
+    if (!s.bin_start) return MM_ERR_NULL;
+    if (s.np > 0 && (!s.pos || !s.w || !s.perm)) return MM_ERR_NULL;
+    const mm_status st = check_strides(species_strides(s), grid, order, dt, *tensorial, nullptr);
+    if (st != MM_OK) return st;
+  }
+  return MM_OK;
+}
+
+// The set as the contraction's particle descriptors.
+struct SpeciesArgs {
+  Particles P[MM_MAX_SPECIES];
+  const int32_t* bin_start[MM_MAX_SPECIES];
+  const int32_t* perm[MM_MAX_SPECIES];
+  double beta[MM_MAX_SPECIES];
+};
+void species_args(mm_dtype dt, int ns, const mm_species* sp, SpeciesArgs* a) {
+  for (int i = 0; i < ns; ++i) {
+    a->P[i] = Particles{sp[i].pos, sp[i].w, sp[i].B, (int)sp[i].np};
+    a->P[i].pos32 = dt == MM_MIX;
+    const Strides st = species_strides(sp[i]);
+    a->P[i].ps = st.ps;
+    a->P[i].wst = st.wst;
+    a->P[i].bst = st.bst;
+    a->bin_start[i] = sp[i].bin_start;
+    a->perm[i] = sp[i].perm;
+    a->beta[i] = sp[i].beta;
+  }
+}
+
+// mm_bin_particles with the positions ps elements apart (3 when dense).
+mm_status bin_common(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos, int64_t ps,
+                     int32_t* bin_start, int32_t* perm, void* ws, size_t* ws_bytes, mm_stream_t stream) {
+  if (!ws_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt)) return MM_ERR_ARG;
+  if (np < 0 || ps < 3 || ps > kMaxI32) return MM_ERR_ARG;
+  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
+  if (!bin_start) return MM_ERR_NULL;
+  if (np > 0 && (!pos || !perm)) return MM_ERR_NULL;
+  const size_t need = np > 0 ? bin_workspace_bytes(np, nnodes) : 0;
+  if (!ws) {
+    *ws_bytes = need;
+    return MM_OK;
+  }
+  if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+  return hip_status(launch_bin(to_dev(grid), order, dt == MM_F32, pos, (int)np, (int)nnodes, bin_start, perm, ws,
+                               (hipStream_t)stream, dt == MM_MIX, ps));
+}
+
 }  // namespace
 
 extern "C" {
@@ -286,23 +393,122 @@ mm_status mm_assemble_ecsim_noalloc(const mm_grid* grid, int order, mm_dtype dt,
 
 mm_status mm_bin_particles(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,
                            int32_t* bin_start, int32_t* perm, void* ws, size_t* ws_bytes, mm_stream_t stream) {
+  return bin_common(grid, order, dt, np, pos, 3, bin_start, perm, ws, ws_bytes, stream);
+}
+
+mm_status mm_bin_particles_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                   int64_t pos_stride, int32_t* bin_start, int32_t* perm, void* ws,
+                                   size_t* ws_bytes, mm_stream_t stream) {
+  return bin_common(grid, order, MM_F64, np, pos, pos_stride, bin_start, perm, ws, ws_bytes, stream);
+}
+
+mm_status mm_contract_bins_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                   int64_t pos_stride, const double* w, int64_t w_stride, const double* B,
+                                   int64_t B_stride, const int32_t* bin_start, const int32_t* perm, double beta,
+                                   double sigma, void* rec, size_t* rec_bytes, mm_stream_t stream) {
+  if (!B) return MM_ERR_NULL;  // the records are tensorial, also when np == 0
+  Strides st;
+  st.ps = pos_stride;
+  st.wst = w_stride;
+  st.bst = B_stride;
+  return contract_common(grid, order, MM_F64, np, pos, w, B, nullptr, bin_start, perm, beta, sigma, rec, rec_bytes,
+                         stream, st);
+}
+
+mm_status mm_assemble_ecsim_strided(const mm_grid* grid, int order, int64_t np, const double* pos,
+                                    int64_t pos_stride, const double* w, int64_t w_stride, const double* B,
+                                    int64_t B_stride, const int32_t* bin_start, const int32_t* perm, double beta,
+                                    double sigma, int accumulate, mm_algo algo, void* M, void* ws,
+                                    size_t* ws_bytes, mm_stream_t stream) {
+  Strides st;
+  st.ps = pos_stride;
+  st.wst = w_stride;
+  st.bst = B_stride;
+  return assemble_common(grid, order, MM_F64, np, pos, w, B, nullptr, true, bin_start, perm, beta, sigma, algo, M,
+                         ws, ws_bytes, stream, accumulate, 0, st);
+}
+
+mm_status mm_contract_bins_species(const mm_grid* grid, int order, mm_dtype dt, int nspecies,
+                                   const mm_species* species, double sigma, void* rec, size_t* rec_bytes,
+                                   mm_stream_t stream) {
+  if (!rec_bytes) return MM_ERR_NULL;
+  int64_t nnodes = 0;
+  mm_status st = check_grid(grid, order, &nnodes);
+  if (st != MM_OK) return st;
+  if (!dtype_ok(dt) || !is_finite_d(sigma)) return MM_ERR_ARG;
+  bool tensorial = false;
+  if ((st = check_species(grid, order, dt, nspecies, species, &tensorial)) != MM_OK) return st;
+  if (!species_fused(grid, order, dt)) return MM_ERR_UNSUPPORTED;
+  const GridDev g = to_dev(grid);
+  const size_t need = record_bytes(order, false, tensorial, g);
+  if (!rec) {
+    *rec_bytes = need;
+    return MM_OK;
+  }
+  if (*rec_bytes < need) return MM_ERR_WORKSPACE;
+  if (((uintptr_t)rec & 15) != 0) return MM_ERR_ARG;
+  SpeciesArgs a;
+  species_args(dt, nspecies, species, &a);
+  return hip_status(launch_cic64_species(g, nspecies, a.P, a.bin_start, a.perm, a.beta, sigma, (double*)rec,
+                                         (hipStream_t)stream));
+}
+
+mm_status mm_assemble_ecsim_species(const mm_grid* grid, int order, mm_dtype dt, int nspecies,
+                                    const mm_species* species, double sigma, int accumulate, mm_algo algo, void* M,
+                                    void* ws, size_t* ws_bytes, mm_stream_t stream) {
   if (!ws_bytes) return MM_ERR_NULL;
   int64_t nnodes = 0;
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
-  if (!dtype_ok(dt)) return MM_ERR_ARG;
-  if (np < 0) return MM_ERR_ARG;
-  if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
-  if (!bin_start) return MM_ERR_NULL;
-  if (np > 0 && (!pos || !perm)) return MM_ERR_NULL;
-  const size_t need = np > 0 ? bin_workspace_bytes(np, nnodes) : 0;
+  if (!dtype_ok(dt) || !is_finite_d(sigma)) return MM_ERR_ARG;
+  if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC && algo != MM_ALGO_VALU)
+    return MM_ERR_ARG;
+  bool tensorial = false;
+  if ((st = check_species(grid, order, dt, nspecies, species, &tensorial)) != MM_OK) return st;
+  if (!tensorial) return MM_ERR_NULL;
+  if (!M) return MM_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  if (algo == MM_ALGO_MFMA && species_fused(grid, order, dt)) {  // one record set for the whole set
+    const GridDev g = to_dev(grid);
+    const size_t need = align256(record_bytes(order, false, true, g));
+    if (!ws) {
+      *ws_bytes = need;
+      return MM_OK;
+    }
+    if (*ws_bytes < need) return MM_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 15) != 0) return MM_ERR_ARG;
+    SpeciesArgs a;
+    species_args(dt, nspecies, species, &a);
+    hipError_t e = launch_cic64_species(g, nspecies, a.P, a.bin_start, a.perm, a.beta, sigma, (double*)ws, s);
+    if (e == hipSuccess) {
+      const void* recs[1] = {ws};
+      e = launch_gather(g, order, false, true, recs, 1, accumulate, M, s);
+    }
+    return hip_status(e);
+  }
+  // species after species, accumulating into M
+  size_t need = 0;
+  for (int i = 0; i < nspecies; ++i) {
+    const mm_species& sp = species[i];
+    size_t b = 0;
+    st = assemble_common(grid, order, dt, sp.np, sp.pos, sp.w, sp.B, nullptr, true, sp.bin_start, sp.perm, sp.beta,
+                         sigma, algo, M, nullptr, &b, stream, 1, 0, species_strides(sp));
+    if (st != MM_OK) return st;
+    need = b > need ? b : need;
+  }
   if (!ws) {
     *ws_bytes = need;
     return MM_OK;
   }
   if (*ws_bytes < need) return MM_ERR_WORKSPACE;
-  return hip_status(launch_bin(to_dev(grid), order, dt == MM_F32, pos, (int)np, (int)nnodes, bin_start, perm, ws,
-                               (hipStream_t)stream, dt == MM_MIX));
+  for (int i = 0; i < nspecies; ++i) {
+    const mm_species& sp = species[i];
+    size_t b = *ws_bytes;
+    st = assemble_common(grid, order, dt, sp.np, sp.pos, sp.w, sp.B, nullptr, true, sp.bin_start, sp.perm, sp.beta,
+                         sigma, algo, M, ws, &b, stream, accumulate || i > 0, 0, species_strides(sp));
+    if (st != MM_OK) return st;
+  }
+  return MM_OK;
 }
 
 mm_status mm_assemble_scalar(const mm_grid* grid, int order, mm_dtype dt, int64_t np, const void* pos,

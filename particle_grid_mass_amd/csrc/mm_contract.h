@@ -17,6 +17,13 @@ hipError_t launch_contract(const GridDev& g, int order, bool f32, const Particle
 // Phase 1 for CIC fp64 records: four bins per wave, one per 4x4x4 block.
 hipError_t launch_cic64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s);
+// The same for ns (1 .. MAX_SPECIES) species in one launch: each bin's record
+// sums the particles of every species (P[i] with bin_start[i], perm[i] and
+// beta[i]); all species share the storage type, field placement and kind.
+constexpr int MAX_SPECIES = 8;
+hipError_t launch_cic64_species(const GridDev& g, int ns, const Particles* P, const int32_t* const* bin_start,
+                                const int32_t* const* perm, const double* beta, double sigma, double* rec,
+                                hipStream_t s);
 
 // Phase 1 for CIC fp64 records on vector FMAs (the comparison kernel of MM_ALGO_VALU):
 // 16 bins per wave, four lanes per bin splitting its 36 pairs.

@@ -359,3 +359,129 @@ def test_planes_validation():
     assert dp(z1=9) == _lib.MM_ERR_ARG
     assert dp(order=1) == _lib.MM_ERR_UNSUPPORTED
     assert dp(grid=_lib.make_grid((18, 8, 8))) == _lib.MM_ERR_UNSUPPORTED
+
+
+def test_strided_validation():
+    """The strided entry points check their strides and the combinations that
+    read them on the host (size queries only: nothing is launched). Dense
+    strides are the dense entry points and answer the same sizes."""
+    lib = _lib.load()
+    g = _lib.make_grid((8, 8, 8))
+    g2 = _lib.make_grid((8, 8, 1))
+    sz = ctypes.c_size_t(0)
+
+    def bp(stride=8, np_=10, order=1, pos=FAKE, perm=FAKE, bs=FAKE):
+        return lib.mm_bin_particles_strided(ctypes.byref(g), order, np_, pos, stride, bs, perm, None,
+                                            ctypes.byref(sz), None)
+
+    assert bp() == _lib.MM_OK
+    assert bp(order=2) == _lib.MM_OK
+    assert bp(stride=2) == _lib.MM_ERR_ARG
+    assert bp(stride=1 << 31) == _lib.MM_ERR_ARG
+    assert bp(np_=-1) == _lib.MM_ERR_ARG
+    assert bp(pos=None) == _lib.MM_ERR_NULL
+    assert bp(bs=None) == _lib.MM_ERR_NULL
+    assert bp(np_=0, pos=None, perm=None) == _lib.MM_OK
+    want = ctypes.c_size_t(0)
+    assert lib.mm_bin_particles(ctypes.byref(g), 1, _lib.MM_F64, 10, FAKE, FAKE, FAKE, None, ctypes.byref(want),
+                                None) == _lib.MM_OK
+    assert bp() == _lib.MM_OK and sz.value == want.value
+
+    def cb(grid=g, order=1, ps=8, ws_=8, bs_=8, B=FAKE, np_=10):
+        return lib.mm_contract_bins_strided(ctypes.byref(grid), order, np_, FAKE, ps, FAKE, ws_, B, bs_, FAKE, FAKE,
+                                            0.5, 1.0, None, ctypes.byref(sz), None)
+
+    assert cb() == _lib.MM_OK
+    rec_want = ctypes.c_size_t(0)
+    assert lib.mm_record_bytes(ctypes.byref(g), 1, _lib.MM_F64, 1, ctypes.byref(rec_want)) == _lib.MM_OK
+    assert sz.value == rec_want.value
+    assert cb(ps=2) == _lib.MM_ERR_ARG
+    assert cb(ws_=0) == _lib.MM_ERR_ARG
+    assert cb(bs_=2) == _lib.MM_ERR_ARG
+    assert cb(B=None) == _lib.MM_ERR_NULL
+    assert cb(B=None, np_=0) == _lib.MM_ERR_NULL  # the records are tensorial
+    assert cb(order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert cb(order=2, ps=3, ws_=1, bs_=3) == _lib.MM_OK  # dense strides: the dense entry point
+    assert cb(grid=g2) == _lib.MM_ERR_UNSUPPORTED
+
+    def ae(grid=g, order=1, algo=_lib.ALGOS["mfma"], ps=8, ws_=8, bs_=8):
+        return lib.mm_assemble_ecsim_strided(ctypes.byref(grid), order, 10, FAKE, ps, FAKE, ws_, FAKE, bs_, FAKE,
+                                             FAKE, 0.5, 1.0, 0, algo, FAKE, None, ctypes.byref(sz), None)
+
+    assert ae() == _lib.MM_OK
+    dense = ctypes.c_size_t(0)
+    assert lib.mm_assemble_ecsim(ctypes.byref(g), 1, _lib.MM_F64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 0.5, 1.0, 0,
+                                 _lib.ALGOS["mfma"], FAKE, None, ctypes.byref(dense), None) == _lib.MM_OK
+    assert ae() == _lib.MM_OK and sz.value == dense.value
+    assert ae(ps=2) == _lib.MM_ERR_ARG
+    assert ae(ws_=-1) == _lib.MM_ERR_ARG
+    for algo in ("atomic", "mfma_atomic", "valu"):
+        assert ae(algo=_lib.ALGOS[algo]) == _lib.MM_ERR_UNSUPPORTED
+        assert ae(algo=_lib.ALGOS[algo], ps=3, ws_=1, bs_=3) == _lib.MM_OK
+    assert ae(order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert ae(grid=g2) == _lib.MM_ERR_UNSUPPORTED
+
+
+def test_species_validation():
+    """The multi-species entry points check the set on the host (size queries
+    only: nothing is launched)."""
+    lib = _lib.load()
+    g = _lib.make_grid((8, 8, 8))
+    sz = ctypes.c_size_t(0)
+    F = 0x1000
+
+    def sp(np_=10, B=F, beta=0.5, bs=F, perm=F, pos=F, strides=(0, 0, 0)):
+        return _lib.MMSpecies(np_, pos, F, B, bs, perm, beta, *strides)
+
+    def arr(*items):
+        a = (_lib.MMSpecies * max(len(items), 1))()
+        for i, s in enumerate(items):
+            a[i] = s
+        return a
+
+    def cb(items, order=1, dt=_lib.MM_F64, ns=None, grid=g):
+        a = arr(*items)
+        return lib.mm_contract_bins_species(ctypes.byref(grid), order, dt, len(items) if ns is None else ns, a, 1.0,
+                                            None, ctypes.byref(sz), None)
+
+    rec_t = ctypes.c_size_t(0)
+    assert lib.mm_record_bytes(ctypes.byref(g), 1, _lib.MM_F64, 1, ctypes.byref(rec_t)) == _lib.MM_OK
+    assert cb([sp(), sp(beta=-0.2)]) == _lib.MM_OK and sz.value == rec_t.value
+    assert cb([sp(), sp()], dt=_lib.MM_MIX) == _lib.MM_OK and sz.value == rec_t.value  # fp64 records
+    rec_s = ctypes.c_size_t(0)
+    assert lib.mm_record_bytes(ctypes.byref(g), 1, _lib.MM_F64, 0, ctypes.byref(rec_s)) == _lib.MM_OK
+    assert cb([sp(B=None), sp(B=None)]) == _lib.MM_OK and sz.value == rec_s.value     # scalar records
+    assert cb([sp()] * 8) == _lib.MM_OK
+    assert cb([sp()] * 2, ns=9) == _lib.MM_ERR_ARG
+    assert cb([sp()], ns=0) == _lib.MM_ERR_ARG
+    assert cb([sp(), sp(B=None)]) == _lib.MM_ERR_ARG      # a tensorial and a scalar species
+    assert cb([sp(np_=-1)]) == _lib.MM_ERR_ARG
+    assert cb([sp(beta=float("nan"))]) == _lib.MM_ERR_ARG
+    assert cb([sp(bs=None)]) == _lib.MM_ERR_NULL
+    assert cb([sp(perm=None)]) == _lib.MM_ERR_NULL
+    assert cb([sp(np_=0, perm=None, pos=None)]) == _lib.MM_OK
+    assert cb([sp(strides=(8, 8, 8))]) == _lib.MM_OK
+    assert cb([sp(strides=(2, 0, 0))]) == _lib.MM_ERR_ARG
+    assert cb([sp(strides=(8, 8, 8))], dt=_lib.MM_MIX) == _lib.MM_ERR_UNSUPPORTED
+    assert cb([sp()], order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert cb([sp()], dt=_lib.MM_F32) == _lib.MM_ERR_UNSUPPORTED
+    assert cb([sp()], grid=_lib.make_grid((8, 8, 1))) == _lib.MM_ERR_UNSUPPORTED
+    assert lib.mm_contract_bins_species(ctypes.byref(g), 1, _lib.MM_F64, 1, None, 1.0, None, ctypes.byref(sz),
+                                        None) == _lib.MM_ERR_NULL
+
+    def ae(items, order=1, dt=_lib.MM_F64, algo="mfma", M=F):
+        a = arr(*items)
+        return lib.mm_assemble_ecsim_species(ctypes.byref(g), order, dt, len(items), a, 1.0, 0, _lib.ALGOS[algo],
+                                             M, None, ctypes.byref(sz), None)
+
+    assert ae([sp(), sp()]) == _lib.MM_OK and sz.value >= rec_t.value     # one record set
+    for algo in ("atomic", "mfma_atomic", "valu"):                         # species one by one
+        assert ae([sp(), sp()], algo=algo) == _lib.MM_OK
+    one = ctypes.c_size_t(0)
+    assert lib.mm_assemble_ecsim(ctypes.byref(g), 2, _lib.MM_F64, 10, F, F, F, F, F, 0.5, 1.0, 0, _lib.ALGOS["mfma"],
+                                 F, None, ctypes.byref(one), None) == _lib.MM_OK
+    assert ae([sp(), sp()], order=2) == _lib.MM_OK and sz.value == one.value
+    assert ae([sp(B=None)]) == _lib.MM_ERR_NULL
+    assert ae([sp()], M=None) == _lib.MM_ERR_NULL
+    assert ae([sp(strides=(8, 8, 8))], algo="atomic") == _lib.MM_ERR_UNSUPPORTED
+    assert ae([sp(strides=(8, 8, 8))], order=2) == _lib.MM_ERR_UNSUPPORTED

@@ -76,3 +76,13 @@ def test_traffic_table_entries_name_their_launch_grid():
             whole = ents.get(key[: -len("-slabs4")])
             if whole is not None:
                 assert ent["grid"] < whole["grid"], key
+
+
+def test_workload_key_names_record_layout():
+    """Counters taken on particle records are not read for the dense arrays."""
+    import argparse
+    args = argparse.Namespace(config=3, kind=None, dtype="f64", deposit_per_species=False, shuffled=True,
+                              field="particle", canonical=False, dims=3, n2d=256, reorder=False, layout="records")
+    assert bench.workload_key(args) == "config3-f64-shuffled-records"
+    args.layout = "arrays"
+    assert bench.workload_key(args) == "config3-f64-shuffled"

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import particle_grid_mass_amd as mm
-from tests.gpu_util import TOL, TDT, oracle_assemble, rel_fro, require_gpu, to_dev
+from tests.gpu_util import TOL, TDT, assert_match, oracle_assemble, rel_fro, require_gpu, to_dev
 from workloads import make_config, random_case
 
 pytestmark = pytest.mark.gpu
@@ -150,3 +150,93 @@ def test_mirrored_deposit_exact_symmetry(kind, dtype):
         assert np.array_equal(Mn[:, c:, :], Mc.view(cshape).cpu().numpy()), (order, counts)
         ref = oracle_assemble(case).reshape(shape)
         assert rel_fro(Mn, ref) <= TOL[dtype]
+
+
+# ------------------------------------------------ every species in one record set
+def _widen32(case):
+    """The case with positions and fields rounded to fp32 (the mixed layout's
+    stored values), as the oracle must see them."""
+    sp = [dataclasses.replace(s, pos=s.pos.astype(np.float32).astype(np.float64),
+                              B=None if s.B is None else s.B.astype(np.float32).astype(np.float64))
+          for s in case.species]
+    return dataclasses.replace(case, species=sp)
+
+
+def species_tuples(case, layout="dense", mixed=False):
+    """(pos, w, B, bin_start, perm, beta) per species on the device: dense
+    arrays, fp32 positions and fields (mixed), or for layout "record8" one
+    64-byte float64 record per particle on every other species."""
+    out = []
+    for k, sp in enumerate(case.species):
+        tens = sp.B is not None and case.kind == "ecsim"
+        if mixed:
+            pos, w = to_dev(sp.pos, torch.float32), to_dev(sp.w, torch.float64)
+            B = to_dev(sp.B, torch.float32) if tens else None
+        elif layout == "record8" and k % 2 == 0 and tens:
+            R = torch.full((sp.pos.shape[0], 8), float("nan"), dtype=torch.float64, device="cuda")
+            R[:, 0:3], R[:, 3], R[:, 4:7] = to_dev(sp.pos, torch.float64), to_dev(sp.w, torch.float64), \
+                to_dev(sp.B, torch.float64)
+            pos, w, B = R[:, 0:3], R[:, 3], R[:, 4:7]
+        else:
+            pos, w = to_dev(sp.pos, torch.float64), to_dev(sp.w, torch.float64)
+            B = to_dev(sp.B, torch.float64) if tens else None
+        bs, perm = mm.bin_particles(case.grid, case.order, pos, mixed=mixed)
+        out.append((pos, w, B, bs, perm, sp.beta))
+    return out
+
+
+SET_CASES = [(401, (5, 6, 7), (3000, 1200)), (402, (6, 5, 5), (0, 800)), (403, (9, 8, 7), (20000, 7000, 3, 500)),
+             (404, (7, 6, 8), (900, 0, 1, 2000, 37, 4000, 5, 800)),  # the most species a set takes
+             (405, (16, 12, 10), (60000, 60000))]
+
+
+@pytest.mark.parametrize("mode", ["dense", "record8", "mixed"])
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+@pytest.mark.parametrize("seed,n,counts", SET_CASES)
+def test_contract_species_one_set(seed, n, counts, kind, mode):
+    """First order: one contraction launch for every species, one record set,
+    one deposit; the oracle sums the species' matrices."""
+    if mode == "record8" and kind == "scalar":
+        pytest.skip("strided arrays are read by the tensorial path")
+    case = species_case(seed, 1, n, counts, kind, "f64")
+    if mode == "mixed":
+        case = _widen32(case)
+    print(f"[case] species set n={n} counts={counts} {kind} {mode}", flush=True)
+    tens = kind == "ecsim"
+    rec = mm.contract_bins_species(case.grid, 1, species_tuples(case, mode, mode == "mixed"), case.sigma)
+    M, shape = new_M(case, False)
+    mm.deposit_records(case.grid, 1, rec, M, tens)
+    torch.cuda.synchronize()
+    assert rec.numel() == mm.record_bytes(case.grid, 1, torch.float64, tens)
+    assert_match(M.view(shape).cpu().numpy(), oracle_assemble(case).reshape(shape), "f64")
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("algo", ["mfma", "atomic"])
+@pytest.mark.parametrize("order,n", [(1, (7, 6, 5)), (2, (7, 6, 5)), (2, (8, 6, 5))])
+def test_assemble_ecsim_species(order, n, algo, accumulate):
+    """The whole set in one call: one record set (first order, matrix cores)
+    or species after species (otherwise), into M or added to it."""
+    case = species_case(500 + order, order, n, (5000, 2100, 0), "ecsim", "f64")
+    print(f"[case] assemble species order={order} n={n} {algo} accumulate={accumulate}", flush=True)
+    shape = (case.grid.ncells, mm.noff(order), 9)
+    base = np.random.default_rng(9).standard_normal(shape) if accumulate else np.zeros(shape)
+    M = torch.from_numpy(base).cuda()
+    mm.assemble_ecsim_species(case.grid, order, species_tuples(case), case.sigma, M=M, accumulate=accumulate,
+                              algo=algo)
+    torch.cuda.synchronize()
+    assert_match(M.cpu().numpy() - base, oracle_assemble(case).reshape(shape), "f64")
+
+
+def test_config3_one_set():
+    """Config 3 (64^3 cells, 125 per cell, two species) as one record set,
+    sorted and shuffled, with one 64-byte record per particle."""
+    for shuffled in (False, True):
+        case = make_config(3, shuffled=shuffled)
+        print(f"[case] c3 one set shuffled={shuffled}", flush=True)
+        M = mm.assemble_ecsim_species(case.grid, 1, species_tuples(case, "record8" if shuffled else "dense"),
+                                      case.sigma)
+        torch.cuda.synchronize()
+        shape = (case.grid.ncells, 27, 9)
+        assert_match(M.cpu().numpy().reshape(shape), oracle_assemble(case).reshape(shape), "f64")
+        del M
