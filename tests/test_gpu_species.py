@@ -190,14 +190,15 @@ SET_CASES = [(401, (5, 6, 7), (3000, 1200)), (402, (6, 5, 5), (0, 800)), (403, (
              (405, (16, 12, 10), (60000, 60000))]
 
 
-@pytest.mark.parametrize("mode", ["dense", "record8", "mixed"])
-@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+# (kind, storage): strided records are read by the tensorial path only
+SET_MODES = [("scalar", "dense"), ("scalar", "mixed"), ("ecsim", "dense"), ("ecsim", "record8"), ("ecsim", "mixed")]
+
+
+@pytest.mark.parametrize("kind,mode", SET_MODES)
 @pytest.mark.parametrize("seed,n,counts", SET_CASES)
 def test_contract_species_one_set(seed, n, counts, kind, mode):
     """First order: one contraction launch for every species, one record set,
     one deposit; the oracle sums the species' matrices."""
-    if mode == "record8" and kind == "scalar":
-        pytest.skip("strided arrays are read by the tensorial path")
     case = species_case(seed, 1, n, counts, kind, "f64")
     if mode == "mixed":
         case = _widen32(case)
