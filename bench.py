@@ -382,7 +382,7 @@ def main():
     import numpy as np
     import torch
     import particle_grid_mass_amd as mm
-    from workloads import grid_field, make_2d, make_config
+    from workloads import grid_field, make_2d, make_config, positions_f32
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -396,7 +396,7 @@ def main():
         case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled)
     if mix:  # the stored fp32 positions and fields, seen by the oracle as the same values in fp64
         for sp in case.species:
-            sp.pos = sp.pos.astype(np.float32).astype(np.float64)
+            sp.pos = positions_f32(sp.pos, case.grid).astype(np.float64)
             if sp.B is not None:
                 sp.B = sp.B.astype(np.float32).astype(np.float64)
     if args.reorder and (args.algo != "mfma" or args.dims != 3 or args.field == "grid"):

@@ -13,7 +13,7 @@ particles stored cell by cell. The named configurations extend it to two
 species, shuffled order and a clustered density.
 """
 from .gen import (Grid, Species, Case, WORKLOAD_NOTES, make_config, uniform_species, random_case,
-                  clustered_counts, species_from_counts, grid_field, make_2d)
+                  clustered_counts, species_from_counts, grid_field, make_2d, positions_f32)
 
 __all__ = ["Grid", "Species", "Case", "WORKLOAD_NOTES", "make_config", "uniform_species", "random_case",
-           "clustered_counts", "species_from_counts", "grid_field", "make_2d"]
+           "clustered_counts", "species_from_counts", "grid_field", "make_2d", "positions_f32"]

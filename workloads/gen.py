@@ -68,6 +68,21 @@ def _round(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
     return a.astype(np.float32)
 
 
+def positions_f32(pos: np.ndarray, grid: "Grid") -> np.ndarray:
+    """Positions rounded to float32 without leaving the cell they were drawn
+    in. Rounding to nearest can put a value drawn just below a cell's upper
+    face onto that face, i.e. into the next cell (a few particles per
+    million), which would break the cell order of a cell-sorted draw; such a
+    value takes the float32 just below the face instead."""
+    p32 = pos.astype(np.float32)
+    for d in range(3):
+        o, h = grid.origin[d], grid.h[d]
+        face = np.floor((pos[:, d] - o) / h) + 1.0  # upper face of the drawn cell, in cells
+        over = (p32[:, d].astype(np.float64) - o) / h >= face
+        p32[over, d] = np.nextafter(p32[over, d], np.float32(-np.inf))
+    return p32
+
+
 def species_from_counts(grid: Grid, counts: np.ndarray, rng_pos, rng_w, rng_b, with_B: bool, beta: float,
                         name: str, w_range=(0.5, 1.5)) -> Species:
     """Particles cell by cell with ``counts[cell]`` per cell, uniform inside each cell."""
@@ -158,7 +173,7 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
         sp = uniform_species(g, 64, seed, with_B=True, beta=0.5)
         sp = Species(sp.pos, sp.w, sp.B, 0.5, "electrons")
-        return Case("c2_cic_ecsim", g, 1, "ecsim", [_cast(sp, dtype)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[2])
+        return Case("c2_cic_ecsim", g, 1, "ecsim", [_cast(sp, dtype, g)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[2])
     if cid == 3:
         g = Grid((64, 64, 64) if scale is None else (scale,) * 3)
         ppc = 125
@@ -171,27 +186,30 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
             sel = idx[idx % 2 == parity]
             if shuffled:
                 sel = sel[rperm.permutation(sel.shape[0])]
-            species.append(_cast(Species(allp.pos[sel], allp.w[sel], allp.B[sel], beta, name), dtype))
+            species.append(_cast(Species(allp.pos[sel], allp.w[sel], allp.B[sel], beta, name), dtype, g))
         return Case("c3_cic_ecsim_2sp" + ("_shuffled" if shuffled else "_sorted"), g, 1, "ecsim", species,
                     dtype=dtype, seed=seed, note=WORKLOAD_NOTES[3])
     if cid == 4:
         kind = kind or "ecsim"
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
         sp = uniform_species(g, 64, seed, with_B=(kind == "ecsim"), beta=0.5)
-        return Case(f"c4_tsc_{kind}", g, 2, kind, [_cast(sp, dtype)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[4])
+        return Case(f"c4_tsc_{kind}", g, 2, kind, [_cast(sp, dtype, g)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[4])
     if cid == 5:
         n = 128 if scale is None else scale
         g = Grid((n, n, n))
         counts = clustered_counts(n, 64.0, seed, sigma_cells=16.0 * n / 128.0)
         rp, rw, rb = _streams(seed, 3)
         sp = species_from_counts(g, counts, rp, rw, rb, True, 0.5, "electrons")
-        return Case(f"c5_tsc_ecsim_clustered_{dtype}", g, 2, "ecsim", [_cast(sp, dtype)], dtype=dtype, seed=seed,
+        return Case(f"c5_tsc_ecsim_clustered_{dtype}", g, 2, "ecsim", [_cast(sp, dtype, g)], dtype=dtype, seed=seed,
                     note=WORKLOAD_NOTES[5])
     raise ValueError(f"unknown config {cid}")
 
 
-def _cast(sp: Species, dtype: str) -> Species:
-    return Species(_round(sp.pos, dtype), _round(sp.w, dtype), _round(sp.B, dtype), sp.beta, sp.name)
+def _cast(sp: Species, dtype: str, grid: Optional["Grid"] = None) -> Species:
+    """The species in the storage dtype; with a grid, float32 positions stay
+    in the cells they were drawn in (positions_f32)."""
+    pos = positions_f32(sp.pos, grid) if (dtype == "f32" and grid is not None) else _round(sp.pos, dtype)
+    return Species(pos, _round(sp.w, dtype), _round(sp.B, dtype), sp.beta, sp.name)
 
 
 def random_case(seed: int, order: int, n: Tuple[int, int, int], npart: int, kind: str = "ecsim",
