@@ -157,7 +157,9 @@ def workload_key(args, slab: int = 0) -> str:
             + ("-shuffled" if args.shuffled else "") + ("-gridB" if args.field == "grid" else "")
             + ("-canonical" if args.canonical else "") + (f"-2d{args.n2d}" if args.dims == 2 else "")
             + ("-reorder" if getattr(args, "reorder", False) else "")
-            + ("-records" if getattr(args, "layout", "arrays") == "records" else "") + (f"-slabs{slab}" if slab else ""))
+            + ("-records" if getattr(args, "layout", "arrays") == "records" else "")
+            + (f"-n{args.n}" if getattr(args, "n", 0) else "") + (f"-ppc{args.ppc}" if getattr(args, "ppc", 0) else "")
+            + (f"-slabs{slab}" if slab else ""))
 
 
 def pmc_traffic(kernel: str, khash: str, wkey: str):
@@ -365,6 +367,11 @@ def main():
                     help="particle storage: arrays (pos, w and B each dense, the default) or records (one 64-byte "
                          "float64 record per particle, x y z w Bx By Bz and one unused value, read through the "
                          "strided entry points; CIC fp64 ECSIM on the matrix-core path)")
+    ap.add_argument("--n", type=int, default=0,
+                    help="grid edge replacing the config's (a sweep over the grid size)")
+    ap.add_argument("--ppc", type=int, default=0,
+                    help="particles per cell replacing those of the uniform configs 1, 2 and 4 (a sweep over the "
+                         "particle density)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (untimed), the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -393,7 +400,11 @@ def main():
                          5: (2, "ecsim")}[args.config]
         case = make_2d(args.n2d, 64, order2, kind2, dtype="f64" if mix else args.dtype, seed=2000 + args.config)
     else:
-        case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled)
+        if args.ppc and args.config not in (1, 2, 4):
+            print("bench.py: --ppc applies to the uniform configs 1, 2 and 4", file=sys.stderr)
+            sys.exit(2)
+        case = make_config(args.config, kind=args.kind, dtype="f64" if mix else args.dtype, shuffled=args.shuffled,
+                           scale=args.n or None, ppc=args.ppc or None)
     if mix:  # the stored fp32 positions and fields, seen by the oracle as the same values in fp64
         for sp in case.species:
             sp.pos = positions_f32(sp.pos, case.grid).astype(np.float64)

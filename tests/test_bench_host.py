@@ -86,3 +86,22 @@ def test_workload_key_names_record_layout():
     assert bench.workload_key(args) == "config3-f64-shuffled-records"
     args.layout = "arrays"
     assert bench.workload_key(args) == "config3-f64-shuffled"
+
+
+def test_sweep_options_name_their_workload():
+    """--n and --ppc replace the grid edge and the density of a uniform config,
+    and the counter table keys such runs apart from the named configs."""
+    import argparse
+    from workloads import make_config
+    case = make_config(2, scale=4, ppc=3)
+    assert case.grid.n == (4, 4, 4) and case.np_total == 4 ** 3 * 3
+    args = argparse.Namespace(config=2, kind=None, dtype="f64", deposit_per_species=False, shuffled=False,
+                              field="particle", canonical=False, dims=3, n2d=256, reorder=False, layout="arrays",
+                              n=16, ppc=256)
+    assert bench.workload_key(args) == "config2-f64-n16-ppc256"
+    try:
+        make_config(3, ppc=8)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("config 3 has a fixed density")

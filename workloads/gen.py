@@ -158,20 +158,24 @@ WORKLOAD_NOTES = {
 
 
 def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffled: bool = False,
-                scale: Optional[int] = None) -> Case:
+                scale: Optional[int] = None, ppc: Optional[int] = None) -> Case:
     """Build named configuration ``cid`` (1..5).
 
     ``kind`` picks scalar/ecsim where a config offers both (config 4);
-    ``scale`` replaces the grid edge (same ppc and constants) for reduced runs.
+    ``scale`` replaces the grid edge (same ppc and constants) for reduced runs;
+    ``ppc`` replaces the particles per cell of the uniform configurations
+    (1, 2 and 4), for sweeps over the particle density.
     """
+    if ppc is not None and cid not in (1, 2, 4):
+        raise ValueError("ppc applies to the uniform configurations 1, 2 and 4")
     seed = 1000 + cid
     if cid == 1:
         g = Grid((8, 8, 8) if scale is None else (scale,) * 3)
-        sp = uniform_species(g, 64, seed, with_B=False, beta=0.0)
+        sp = uniform_species(g, ppc or 64, seed, with_B=False, beta=0.0)
         return Case("c1_cic_scalar", g, 1, "scalar", [sp], dtype="f64", seed=seed, note=WORKLOAD_NOTES[1])
     if cid == 2:
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
-        sp = uniform_species(g, 64, seed, with_B=True, beta=0.5)
+        sp = uniform_species(g, ppc or 64, seed, with_B=True, beta=0.5)
         sp = Species(sp.pos, sp.w, sp.B, 0.5, "electrons")
         return Case("c2_cic_ecsim", g, 1, "ecsim", [_cast(sp, dtype, g)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[2])
     if cid == 3:
@@ -192,7 +196,7 @@ def make_config(cid: int, kind: Optional[str] = None, dtype: str = "f64", shuffl
     if cid == 4:
         kind = kind or "ecsim"
         g = Grid((32, 32, 32) if scale is None else (scale,) * 3)
-        sp = uniform_species(g, 64, seed, with_B=(kind == "ecsim"), beta=0.5)
+        sp = uniform_species(g, ppc or 64, seed, with_B=(kind == "ecsim"), beta=0.5)
         return Case(f"c4_tsc_{kind}", g, 2, kind, [_cast(sp, dtype, g)], dtype=dtype, seed=seed, note=WORKLOAD_NOTES[4])
     if cid == 5:
         n = 128 if scale is None else scale
