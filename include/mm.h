@@ -253,9 +253,10 @@ mm_status mm_deposit_records(const mm_grid* grid, int order, mm_dtype dt, int te
  *   be NULL, even when np == 0); records bit for bit those of the dense arrays.
  * mm_assemble_ecsim_strided - mm_assemble_ecsim (MM_F64); M bit for bit that
  *   of the dense arrays.
- *  Strides other than the dense ones are read by the first-order (CIC)
- *  matrix-core path on a 3D grid (MM_ALGO_MFMA; order 2, the other algorithms
- *  and the 2D problem are MM_ERR_UNSUPPORTED with them). Each stride is at
+ *  Strides other than the dense ones are read by the matrix-core path
+ *  (MM_ALGO_MFMA) on a 3D grid, CIC and TSC (the other algorithms and the 2D
+ *  problem are MM_ERR_UNSUPPORTED with them; at order 2 the strided assembly
+ *  runs its two phases in turn, without the slab overlap). Each stride is at
  *  least 3 (pos, B) or 1 (w) and below 2^31, else MM_ERR_ARG; the arrays may
  *  overlap (they are only read). Other arguments, the workspace and the
  *  errors as for the dense entry points.

@@ -28,6 +28,8 @@
 //  * Records rec[bin][pair][comp] are staged in LDS one bin at a time; the
 //    three components a wave owns per pair are written as one 24-byte piece
 //    (the three waves of a group fill the 72 bytes of a pair in the XCD's L2).
+//  * The particle arrays may have any element stride (ST), as when each
+//    particle is one record of its position, weight and field.
 #include "mm_contract.h"
 #include "mm_run.h"
 
@@ -98,22 +100,29 @@ struct Raw {
   bool valid;
 };
 
+// Element strides of the particle arrays (read when the kernel's ST is set).
+struct ArrStrides {
+  int64_t ps, wst, bst;
+};
+
 // GB: the field is on the grid (gathered in stage), not per particle. PT: type
-// of the stored positions and field (fp64, or fp32 read into fp64).
-template <typename PT, bool GB>
+// of the stored positions and field (fp64, or fp32 read into fp64). ST: the
+// particle values st.ps, st.wst and st.bst elements apart instead of 3, 1, 3.
+template <typename PT, bool GB, bool ST>
 __device__ __forceinline__ Raw load_raw(const PT* __restrict__ pos, const double* __restrict__ w,
-                                        const PT* __restrict__ Bf, int p, int np) {
+                                        const PT* __restrict__ Bf, int p, int np, const ArrStrides& st) {
   Raw r{0, 0, 0, 0, 0, 0, 0, false};
   if ((unsigned)p < (unsigned)np) {
     r.valid = true;
-    r.x = pos[3 * (size_t)p];
-    r.y = pos[3 * (size_t)p + 1];
-    r.z = pos[3 * (size_t)p + 2];
-    r.w = w[p];
+    const size_t qp = ST ? (size_t)st.ps * p : 3 * (size_t)p, qb = ST ? (size_t)st.bst * p : 3 * (size_t)p;
+    r.x = pos[qp];
+    r.y = pos[qp + 1];
+    r.z = pos[qp + 2];
+    r.w = w[ST ? (size_t)st.wst * p : (size_t)p];
     if (!GB) {
-      r.bx = Bf[3 * (size_t)p];
-      r.by = Bf[3 * (size_t)p + 1];
-      r.bz = Bf[3 * (size_t)p + 2];
+      r.bx = Bf[qb];
+      r.by = Bf[qb + 1];
+      r.bz = Bf[qb + 2];
     }
   }
   return r;
@@ -220,11 +229,12 @@ __device__ __forceinline__ void wave_sync() {
 // the component's nine line-aligned stretches of the run record.
 static __constant__ run::Tables kRun = run::make_tables();
 
-template <typename PT, bool GB, bool RUNS>
+template <typename PT, bool GB, bool RUNS, bool ST>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_tsc64(
     GridDev g, const PT* __restrict__ pos, const double* __restrict__ w, const PT* __restrict__ Bf,
     const int32_t* __restrict__ bin_start, const int32_t* __restrict__ perm, int np, int nbins, double beta,
-    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order, int xch, int z0, int nz) {
+    double sigma, double* __restrict__ rec, const int32_t* __restrict__ order, int xch, int z0, int nz,
+    ArrStrides str) {
   __shared__ __attribute__((aligned(16))) double smem[GB ? SMEM + FIELD : SMEM];
   double* sW = smem;
   const int lane = threadIdx.x;
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // lane's constant part taken out of the loop
   const int wl = (CH * mb + mk) * (WSLOT / 2), wx = mb ^ mk;
 
-  Raw raw = load_raw<PT, GB>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
+  Raw raw = load_raw<PT, GB, ST>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np, str);
   int pnext = chunk_perm(perm, G, 1, lane);
   double acc[CPW][NBP];
 #pragma unroll
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   for (int j = 0; j < G.nchunks; ++j) {
     stage<GB>(raw, g, beta, sigma, row, sW, sF, lane);
     wave_sync();
-    raw = load_raw<PT, GB>(pos, w, Bf, pnext, np);  // next chunk, in flight during the rounds
+    raw = load_raw<PT, GB, ST>(pos, w, Bf, pnext, np, str);  // next chunk, in flight during the rounds
     pnext = chunk_perm(perm, G, j + 2, lane);
 
     const int left = G.maxn - j * CH;
@@ -471,14 +481,19 @@ static hipError_t tsc64_t(const GridDev& g, const Particles& P, const int32_t* b
   }
   const int xch = NQ * xg;
   const int nz = z1 - z0;
-  if (P.Bgrid)
-    hipLaunchKernelGGL((k_tsc64<PT, true, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
-                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
-                       z0, nz);
-  else
-    hipLaunchKernelGGL((k_tsc64<PT, false, RUNS>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+  const ArrStrides str{P.ps, P.wst, P.bst};
+  if (P.strided())  // fp64 values with the field per particle (checked by the caller)
+    hipLaunchKernelGGL((k_tsc64<PT, false, RUNS, true>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
                        (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
-                       z0, nz);
+                       z0, nz, str);
+  else if (P.Bgrid)
+    hipLaunchKernelGGL((k_tsc64<PT, true, RUNS, false>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.Bgrid, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
+                       z0, nz, str);
+  else
+    hipLaunchKernelGGL((k_tsc64<PT, false, RUNS, false>), dim3(ngroups * NQ), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec, ord, xch,
+                       z0, nz, str);
   return hipGetLastError();
 }
 
@@ -487,6 +502,7 @@ bool tsc_run_records(const GridDev& g) { return g.n2 > 1 && g.n0 % run::RUN == 0
 hipError_t launch_tsc64(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                         double beta, double sigma, double* rec, hipStream_t s, int z0, int z1) {
   if (!P.B && !P.Bgrid) return hipErrorInvalidValue;  // tensorial (ECSIM) records only
+  if (P.strided() && (P.pos32 || P.Bgrid || !P.B)) return hipErrorInvalidValue;  // strided: fp64, field per particle
   if (z1 < 0) z1 = g.n2;
   if (tsc_run_records(g)) {
     if (z0 < 0 || z0 > z1 || z1 > g.n2) return hipErrorInvalidValue;

@@ -74,14 +74,23 @@ struct Strides {
   bool valid() const { return ps >= 3 && wst >= 1 && bst >= 3 && ps <= kMaxI32 && wst <= kMaxI32 && bst <= kMaxI32; }
 };
 
-// Other strides than the dense ones are read by the fp64 CIC record
-// contraction (3D, field per particle) only.
+// Other strides than the dense ones are read by the fp64 3x3 record
+// contractions (CIC and TSC, 3D, field per particle) only.
 mm_status check_strides(const Strides& st, const mm_grid* grid, int order, mm_dtype dt, bool tensorial,
                         const void* Bgrid) {
+  (void)order;
   if (st.dense()) return MM_OK;
   if (!st.valid()) return MM_ERR_ARG;
-  if (dt != MM_F64 || order != 1 || is2d(grid) || Bgrid || !tensorial) return MM_ERR_UNSUPPORTED;
+  if (dt != MM_F64 || is2d(grid) || Bgrid || !tensorial) return MM_ERR_UNSUPPORTED;
   return MM_OK;
+}
+
+// The record contraction of the two-phase path; strided second-order arrays
+// go to the fp64 TSC kernel directly (the generic dispatch takes dense ones).
+hipError_t contract_records(const GridDev& g, int order, bool f32, const Particles& P, const int32_t* bin_start,
+                            const int32_t* perm, double beta, double sigma, void* rec, hipStream_t s) {
+  if (P.strided() && order == 2) return launch_tsc64(g, P, bin_start, perm, beta, sigma, (double*)rec, s);
+  return launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, s);
 }
 
 // ------------------------------------------------------------ fixed scratch
@@ -211,7 +220,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     return hip_status(launch_assemble_overlapped(g, f32, P, bin_start, perm, beta, sigma, ws, accumulate, M, s));
   if (records) {
     e = algo == MM_ALGO_VALU ? launch_cic64_valu(g, P, bin_start, perm, beta, sigma, (double*)ws, s)
-                             : launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, ws, s);
+                             : contract_records(g, order, f32, P, bin_start, perm, beta, sigma, ws, s);
     if (e == hipSuccess) {
       const void* recs[1] = {ws};
       e = launch_gather(g, order, f32, tensorial, recs, 1, accumulate, M, s);
@@ -273,7 +282,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
     }
   }
   if (is2d(grid)) return hip_status(launch_contract_2d(g, order, P, bin_start, perm, beta, sigma, rec, s));
-  return hip_status(launch_contract(g, order, f32, P, bin_start, perm, beta, sigma, MODE_RECORD, rec, s));
+  return hip_status(contract_records(g, order, f32, P, bin_start, perm, beta, sigma, rec, s));
 }
 
 // mm_contract_bins_planes with the field per particle (B) or on the grid (Bgrid).

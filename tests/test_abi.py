@@ -400,7 +400,7 @@ def test_strided_validation():
     assert cb(bs_=2) == _lib.MM_ERR_ARG
     assert cb(B=None) == _lib.MM_ERR_NULL
     assert cb(B=None, np_=0) == _lib.MM_ERR_NULL  # the records are tensorial
-    assert cb(order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert cb(order=2) == _lib.MM_OK                      # the fp64 TSC contraction reads strides too
     assert cb(order=2, ps=3, ws_=1, bs_=3) == _lib.MM_OK  # dense strides: the dense entry point
     assert cb(grid=g2) == _lib.MM_ERR_UNSUPPORTED
 
@@ -418,7 +418,8 @@ def test_strided_validation():
     for algo in ("atomic", "mfma_atomic", "valu"):
         assert ae(algo=_lib.ALGOS[algo]) == _lib.MM_ERR_UNSUPPORTED
         assert ae(algo=_lib.ALGOS[algo], ps=3, ws_=1, bs_=3) == _lib.MM_OK
-    assert ae(order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert ae(order=2) == _lib.MM_OK
+    assert ae(order=2, algo=_lib.ALGOS["atomic"]) == _lib.MM_ERR_UNSUPPORTED
     assert ae(grid=g2) == _lib.MM_ERR_UNSUPPORTED
 
 
@@ -484,4 +485,5 @@ def test_species_validation():
     assert ae([sp(B=None)]) == _lib.MM_ERR_NULL
     assert ae([sp()], M=None) == _lib.MM_ERR_NULL
     assert ae([sp(strides=(8, 8, 8))], algo="atomic") == _lib.MM_ERR_UNSUPPORTED
-    assert ae([sp(strides=(8, 8, 8))], order=2) == _lib.MM_ERR_UNSUPPORTED
+    assert ae([sp(strides=(8, 8, 8))], order=2) == _lib.MM_OK  # species one by one, each strided
+    assert ae([sp(strides=(8, 8, 8))], order=2, dt=_lib.MM_MIX) == _lib.MM_ERR_UNSUPPORTED

@@ -122,6 +122,39 @@ def test_strided_assembly(seed, n, npart, layout):
     assert torch.equal(M, Md)
 
 
+SMALL2 = [
+    # seed, n, npart: an x extent of 8 or 12 gives run records, 7 per-bin records
+    (51, (8, 6, 5), 3),
+    (52, (7, 6, 5), 1500),
+    (53, (12, 7, 6), 20000),
+    (54, (9, 8, 7), 20000),
+]
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("seed,n,npart", SMALL2)
+def test_strided_assembly_tsc(seed, n, npart, layout):
+    """Second order: the fp64 TSC contraction reads the strides (run records
+    and per-bin records), matching the oracle and the dense path bit for bit."""
+    case = random_case(seed, 2, n, npart, kind="ecsim", beta=0.7, sigma=1.3, origin=(0.25, -2.0, 1.0),
+                       h=(0.5, 1.0, 0.75), spread=0.8)
+    print(f"[case] strided TSC assembly {layout} n={n} np={npart}", flush=True)
+    M = assemble(case, lambda sp: strided_views(sp, layout))
+    assert_match(as_numpy_M(M, case), oracle_assemble(case), "f64")
+    Md = assemble(case, dense)
+    assert torch.equal(M, Md)
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("n", [(8, 6, 8), (7, 6, 8)])
+def test_strided_edge_assembly_tsc(n, layout):
+    """Particles on nodes, at the TSC tie and on the periodic boundary."""
+    case = edge_case(410, 2, "ecsim", "f64", "dyadic", n=n)
+    print(f"[case] strided TSC edge assembly {case.name} n={n} {layout}", flush=True)
+    M = assemble(case, lambda sp: strided_views(sp, layout))
+    assert_match(as_numpy_M(M, case), oracle_assemble(case), "f64")
+
+
 @pytest.mark.parametrize("layout", sorted(LAYOUTS))
 @pytest.mark.parametrize("spacing", ["pow2", "dyadic", "inexact"])
 def test_strided_edge_assembly(spacing, layout):
@@ -149,6 +182,20 @@ def test_strided_records_bitwise(layout):
     torch.cuda.synchronize()
     assert torch.equal(rec, rec_d)
     assert_match(as_numpy_M(M, case), oracle_assemble(case), "f64")
+    # second order, run records
+    case2 = random_case(22, 2, (12, 10, 9), 30000, kind="ecsim", beta=0.4, sigma=0.9)
+    sp2 = case2.species[0]
+    pos, w, B = strided_views(sp2, layout)
+    bs, perm = mm.bin_particles(case2.grid, 2, pos)
+    nrec = mm.record_bytes(case2.grid, 2, torch.float64, True)
+    # zero-filled buffers: the padding slots of run records are never written
+    rec = mm.contract_bins(case2.grid, 2, pos, w, B, bs, perm, sp2.beta, case2.sigma,
+                           rec=torch.zeros(nrec, dtype=torch.uint8, device="cuda"))
+    pd, wd, Bd = dense(sp2)
+    rec_d = mm.contract_bins(case2.grid, 2, pd, wd, Bd, bs, perm, sp2.beta, case2.sigma,
+                             rec=torch.zeros(nrec, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(rec, rec_d)
 
 
 def test_strided_two_species_and_empty():
@@ -188,13 +235,13 @@ def test_strided_config3_shuffled():
 
 
 def test_strided_unsupported():
-    """Strides reach the first-order matrix-core path only; fp32 storage must be dense."""
+    """Strides reach the fp64 matrix-core path only; fp32 storage must be dense."""
     case = random_case(41, 2, (8, 6, 5), 100, kind="ecsim")
     sp = case.species[0]
     pos, w, B = strided_views(sp, "record8")
     bs, perm = mm.bin_particles(case.grid, 2, pos)
     with pytest.raises(mm.MMError):
-        mm.assemble_ecsim(case.grid, 2, pos, w, B, bs, perm, beta=0.5)
+        mm.assemble_ecsim(case.grid, 2, pos, w, B, bs, perm, beta=0.5, algo="atomic")
     case1 = random_case(42, 1, (8, 6, 5), 100, kind="ecsim")
     pos, w, B = strided_views(case1.species[0], "record8")
     bs, perm = mm.bin_particles(case1.grid, 1, pos)
