@@ -68,10 +68,12 @@ struct Group {
   int nchunks;
 };
 
+// Split-K form (SK): the group is the single bin g, and every lane serves it.
+template <bool SK>
 __device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int nbins, int np,
                                             int lane) {
   Group G;
-  const int bin = NB * g + (lane >> 4);
+  const int bin = SK ? g : NB * g + (lane >> 4);
   int s = 0, e = 0;
   if (bin < nbins) {
     s = bin_start[bin];
@@ -86,7 +88,8 @@ __device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_star
   m = max(m, __builtin_amdgcn_readlane(G.n, 32));
   m = max(m, __builtin_amdgcn_readlane(G.n, 48));
   G.maxn = m;
-  G.nchunks = m > 0 ? (m + CH - 1) / CH : 1;  // an empty group still writes zero records
+  // an empty group still writes zero records; SK chunks hold 4 CH particles of its bin
+  G.nchunks = m > 0 ? (m + (SK ? 4 * CH : CH) - 1) / (SK ? 4 * CH : CH) : 1;
   return G;
 }
 
@@ -98,8 +101,9 @@ struct PermRef {
   int v;
   bool ok;
 };
+template <bool SK>
 __device__ __forceinline__ PermRef chunk_perm(const int32_t* __restrict__ perm, const Group& G, int j, int lane) {
-  const int q = j * CH + (lane & 15);
+  const int q = SK ? j * 4 * CH + lane : j * CH + (lane & 15);
   PermRef r;
   r.ok = q < G.n;
   r.v = perm[r.ok ? G.s + q : 0];
@@ -173,7 +177,7 @@ __device__ __forceinline__ int t_base(int s) { return WREG + s * Cfg<NC>::ST + (
 // for a lane without a particle). With GB the field at the particle is
 // gathered from sB, the grid field at the 8 support nodes of each bin of the
 // group (node a = ax + 2 ay + 4 az, 3 components), with the particle's weights.
-template <int NC, bool GB>
+template <int NC, bool GB, bool SK>
 __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double beta, double sigma, double* sm,
                                       const double* sB, int lane) {
   double wx[2] = {0, 0}, wy[2] = {0, 0}, wz[2] = {0, 0}, t[NC];
@@ -186,7 +190,7 @@ __device__ __forceinline__ void stage(const Raw& r, const GridDev& g, double bet
     const double f = sigma * r.w;
     double bx = r.bx, by = r.by, bz = r.bz;
     if (NC == 9 && GB) {
-      const double* fb = sB + (lane >> 4) * 24;
+      const double* fb = sB + (SK ? 0 : (lane >> 4)) * 24;
       bx = by = bz = 0.0;
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
@@ -231,19 +235,23 @@ struct Acc {
 
 }  // namespace
 
-template <typename PT, int NC, bool GB, bool ST>
+// SK (split K, for grids of few bins): one bin per wave, the four blocks of
+// the instruction taking different particles of it (16 per block and chunk);
+// their four partial matrices are summed across lanes before the record is
+// written. Four times as many waves, for the same matrix work.
+template <typename PT, int NC, bool GB, bool ST, bool SK>
 __global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S, const PT* __restrict__ Bgrid,
                                               int nbins, double sigma, double* __restrict__ rec) {
   __shared__ __attribute__((aligned(16))) double sm[GB ? Cfg<NC>::SMEM_GB : Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
-  const int ngroups = (nbins + NB - 1) / NB;
+  const int ngroups = SK ? nbins : (nbins + NB - 1) / NB;
   const int grp = blockIdx.x;
   if (grp >= ngroups) return;
   double* sB = sm + Cfg<NC>::STAGE;
-  if (GB && lane < NB * 8) {
+  if (GB && lane < (SK ? 8 : NB * 8)) {
     // Bf is the grid field [nnodes][3]: node a of bin 4 grp + (lane >> 3) is
     // the bin's own node (its first support node) shifted by (ax, ay, az).
-    const int bin = NB * grp + (lane >> 3), a = lane & 7;
+    const int bin = SK ? grp : NB * grp + (lane >> 3), a = lane & 7;
     double f0 = 0.0, f1 = 0.0, f2 = 0.0;
     if (bin < nbins) {
       const int kx = bin % g.n0, ky = (bin / g.n0) % g.n1, kz = bin / (g.n0 * g.n1);
@@ -277,25 +285,27 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S,
     if (np == 0) continue;
     const double beta = S.beta[sp];
     const Strides str{S.ps[sp], S.wst[sp], S.bst[sp]};
-    const Group G = load_group(S.bin_start[sp], grp, nbins, np, lane);
+    const Group G = load_group<SK>(S.bin_start[sp], grp, nbins, np, lane);
     // Two chunks of particle data in flight ahead of the one being contracted.
     // The loop is unrolled by two so that each register set is reloaded right
     // after its chunk is staged (no copies, which would wait for the loads).
     // The loop starts two steps early (j = -2, -1) with only the loads, so
     // that every load is issued by the loop body in one order.
     Raw ra, rb;
-    PermRef pa = chunk_perm(perm, G, 0, lane), pb = chunk_perm(perm, G, 1, lane);
+    PermRef pa = chunk_perm<SK>(perm, G, 0, lane), pb = chunk_perm<SK>(perm, G, 1, lane);
     // resolved here, so that the loop is entered with no load in flight
     pa.v = perm_index(pa);
     pb.v = perm_index(pb);
     auto step = [&](Raw& r, PermRef& pr, int j) {
       if (j >= 0) {
-        stage<NC, GB>(r, g, beta, sigma, sm, sB, lane);
+        stage<NC, GB, SK>(r, g, beta, sigma, sm, sB, lane);
         __syncthreads();
       }
       r = load_raw<PT, NC, GB, ST>(pos, w, Bf, perm_index(pr), np, str);  // chunk j + 2
-      pr = chunk_perm(perm, G, j + 4, lane);
-      const int left = G.maxn - j * CH;
+      pr = chunk_perm<SK>(perm, G, j + 4, lane);
+      // rounds with particles: slot 16 mb + 4 rd + mk; with SK every block's
+      // first 4 nr slots, so that a prefix of the chunk's 64 is covered
+      const int left = G.maxn - j * (SK ? 4 * CH : CH);
       const int nr = j < 0 ? 0 : (left >= CH ? CH / 4 : (left > 0 ? (left + 3) / 4 : 0));
       for (int rd = 0; rd < nr; ++rd) {
         // slot = 16 mb + 4 rd + mk: w_unit(slot, mr) and t_base(slot) with the
@@ -331,6 +341,38 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S,
     }
   }
 
+  if (SK) {
+    // the four blocks hold partial sums of the one bin: add them (lanes that
+    // differ in the block bits 2 and 3), then write its record
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        double v = acc.q[c][k];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        acc.q[c][k] = v;
+      }
+    const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
+    const int p00 = di * 8 - (di * (di - 1)) / 2 + (dj - di);
+    const int p01 = di * 8 - (di * (di - 1)) / 2 + (4 + dj - di);
+    const int a1 = 4 + di;
+    const int p11 = a1 * 8 - (a1 * (a1 - 1)) / 2 + (dj - di);
+    if (db == 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (di <= dj) sm[p00 * NC + c] = acc.q[c][0];
+        sm[p01 * NC + c] = acc.q[c][1];
+        if (di <= dj) sm[p11 * NC + c] = acc.q[c][2];
+      }
+    }
+    __syncthreads();
+    double2* dst = reinterpret_cast<double2*>(rec + (size_t)grp * NPAIR * NC);
+    const double2* src = reinterpret_cast<const double2*>(sm);
+    for (int i = lane; i < NPAIR * NC / 2; i += 64) dst[i] = src[i];
+    return;
+  }
+
   // D_blk[i][j] sits in lane (i << 4) | (blk << 2) | j. Stage the packed
   // records rec[bin][pair(a, b)][c] (a <= b, pair(a, b) = 8a - a(a-1)/2 + b - a)
   // two bins at a time in LDS and write them with 16-byte stores (the records
@@ -363,18 +405,30 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S,
   }
 }
 
-template <typename PT, bool ST>
+template <typename PT, bool ST, bool SK>
 static hipError_t cic64_t(const GridDev& g, const SpeciesSet<PT>& S, const PT* Bgrid, bool tensorial, double sigma,
                           double* rec, hipStream_t s) {
   const int nbins = g.n0 * g.n1 * g.n2;
-  const int ngroups = (nbins + NB - 1) / NB;  // one single-wave workgroup per group of four bins
+  // one single-wave workgroup per group of four bins, or per bin (SK)
+  const int ngroups = SK ? nbins : (nbins + NB - 1) / NB;
   if (Bgrid)
-    hipLaunchKernelGGL((k_cic64<PT, 9, true, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 9, true, ST, SK>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma,
+                       rec);
   else if (tensorial)
-    hipLaunchKernelGGL((k_cic64<PT, 9, false, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 9, false, ST, SK>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma,
+                       rec);
   else
-    hipLaunchKernelGGL((k_cic64<PT, 1, false, ST>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma, rec);
+    hipLaunchKernelGGL((k_cic64<PT, 1, false, ST, SK>), dim3(ngroups), dim3(64), 0, s, g, S, Bgrid, nbins, sigma,
+                       rec);
   return hipGetLastError();
+}
+
+// Split K when groups of four bins would leave the SIMDs with fewer than
+// three waves each and the bins hold at least a chunk of 16 particles on
+// average (below that the chunks of 64 would be mostly empty).
+static bool use_split_k(const GridDev& g, int64_t np_total) {
+  const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
+  return (nbins + NB - 1) / NB < 3072 && np_total >= 16 * nbins;
 }
 
 template <typename PT>
@@ -399,12 +453,17 @@ static hipError_t cic64_species(const GridDev& g, int ns, const Particles* P, co
   }
   const PT* Bgrid = (const PT*)P[0].Bgrid;
   const bool tensorial = P[0].B != nullptr || Bgrid;
+  int64_t np_total = 0;
+  for (int i = 0; i < ns; ++i) np_total += P[i].np;
+  const bool sk = use_split_k(g, np_total);
   if (strided) {
     // strided arrays: fp64 values with the field per particle
     if (Bgrid || !tensorial) return hipErrorInvalidValue;
-    return cic64_t<PT, true>(g, S, Bgrid, true, sigma, rec, s);
+    return sk ? cic64_t<PT, true, true>(g, S, Bgrid, true, sigma, rec, s)
+              : cic64_t<PT, true, false>(g, S, Bgrid, true, sigma, rec, s);
   }
-  return cic64_t<PT, false>(g, S, Bgrid, tensorial, sigma, rec, s);
+  return sk ? cic64_t<PT, false, true>(g, S, Bgrid, tensorial, sigma, rec, s)
+            : cic64_t<PT, false, false>(g, S, Bgrid, tensorial, sigma, rec, s);
 }
 
 hipError_t launch_cic64_species(const GridDev& g, int ns, const Particles* P, const int32_t* const* bin_start,
