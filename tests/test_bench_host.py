@@ -114,13 +114,13 @@ def test_positions_f32_keep_their_cells():
     from workloads import Grid, positions_f32
     g = Grid((4, 4, 4))
     eps = np.finfo(np.float64).eps
-    pos = np.array([[0.5, 1.0 - eps, 2.25],          # rounds up onto the face x = 1 in plain fp32
-                    [3.0 - 1e-12, 0.0, 1.5],         # rounds up onto x = 3
-                    [1.25, 2.0, 3.999999999]])       # rounds onto z = 4, the periodic end
+    pos = np.array([[0.5, 1.0 - eps, 2.25],          # y rounds up onto the face y = 1 in plain fp32
+                    [3.0 - 1e-12, 0.0, 1.5],         # x rounds up onto x = 3
+                    [1.25, 2.0, 3.999999999]])       # z rounds onto z = 4, the periodic end
     plain = pos.astype(np.float32)
     got = positions_f32(pos, g)
     assert got.dtype == np.float32
     assert np.array_equal(np.floor(got.astype(np.float64)), np.floor(pos))
     moved = plain != got
-    assert moved.sum() == 3 and moved[0, 0] and moved[1, 0] and moved[2, 2]
+    assert moved.sum() == 3 and moved[0, 1] and moved[1, 0] and moved[2, 2]
     assert np.all(got[moved] == np.nextafter(plain[moved], np.float32(-np.inf)))
