@@ -76,9 +76,7 @@ struct Strides {
 
 // Other strides than the dense ones are read by the fp64 3x3 record
 // contractions (CIC and TSC, 3D, field per particle) only.
-mm_status check_strides(const Strides& st, const mm_grid* grid, int order, mm_dtype dt, bool tensorial,
-                        const void* Bgrid) {
-  (void)order;
+mm_status check_strides(const Strides& st, const mm_grid* grid, mm_dtype dt, bool tensorial, const void* Bgrid) {
   if (st.dense()) return MM_OK;
   if (!st.valid()) return MM_ERR_ARG;
   if (dt != MM_F64 || is2d(grid) || Bgrid || !tensorial) return MM_ERR_UNSUPPORTED;
@@ -145,7 +143,7 @@ mm_status assemble_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   if (!dtype_ok(dt)) return MM_ERR_ARG;
   if (algo != MM_ALGO_MFMA && algo != MM_ALGO_ATOMIC && algo != MM_ALGO_MFMA_ATOMIC && algo != MM_ALGO_VALU)
     return MM_ERR_ARG;
-  if ((st = check_strides(str, grid, order, dt, tensorial, Bgrid)) != MM_OK) return st;
+  if ((st = check_strides(str, grid, dt, tensorial, Bgrid)) != MM_OK) return st;
   if (!str.dense() && algo != MM_ALGO_MFMA) return MM_ERR_UNSUPPORTED;
   if (algo == MM_ALGO_ATOMIC && dt == MM_MIX) return MM_ERR_UNSUPPORTED;
   // the vector-FMA comparison contraction: CIC, fp64 arithmetic, 3D, field per particle
@@ -246,7 +244,7 @@ mm_status contract_common(const mm_grid* grid, int order, mm_dtype dt, int64_t n
   mm_status st = check_grid(grid, order, &nnodes);
   if (st != MM_OK) return st;
   if (!dtype_ok(dt)) return MM_ERR_ARG;
-  if ((st = check_strides(str, grid, order, dt, B != nullptr || Bgrid != nullptr, Bgrid)) != MM_OK) return st;
+  if ((st = check_strides(str, grid, dt, B != nullptr || Bgrid != nullptr, Bgrid)) != MM_OK) return st;
   if (!is_finite_d(sigma) || !is_finite_d(beta)) return MM_ERR_ARG;
   if (np < 0) return MM_ERR_ARG;
   if (np >= kMaxI32) return MM_ERR_UNSUPPORTED;
@@ -339,7 +337,7 @@ mm_status check_species(const mm_grid* grid, int order, mm_dtype dt, int ns, con
     if ((s.B != nullptr) != *tensorial) return MM_ERR_ARG;
     if (!s.bin_start) return MM_ERR_NULL;
     if (s.np > 0 && (!s.pos || !s.w || !s.perm)) return MM_ERR_NULL;
-    const mm_status st = check_strides(species_strides(s), grid, order, dt, *tensorial, nullptr);
+    const mm_status st = check_strides(species_strides(s), grid, dt, *tensorial, nullptr);
     if (st != MM_OK) return st;
   }
   return MM_OK;
