@@ -343,17 +343,23 @@ __global__ __launch_bounds__(64) void k_cic64(GridDev g, const SpeciesSet<PT> S,
 
   if (SK) {
     // the four blocks hold partial sums of the one bin: add them (lanes that
-    // differ in the block bits 2 and 3), then write its record
+    // differ in the block bits 2 and 3) through LDS, one component at a time
+    // (all at once in registers would cost a wave per SIMD), then write its
+    // record
+    const int db = (lane >> 2) & 3;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        double v = acc.q[c][k];
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        acc.q[c][k] = v;
+      for (int k = 0; k < 3; ++k) sm[3 * lane + k] = acc.q[c][k];
+      __syncthreads();
+      if (db == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          acc.q[c][k] = ((sm[3 * lane + k] + sm[3 * (lane + 4) + k]) + sm[3 * (lane + 8) + k]) + sm[3 * (lane + 12) + k];
       }
-    const int di = lane >> 4, db = (lane >> 2) & 3, dj = lane & 3;
+      __syncthreads();
+    }
+    const int di = lane >> 4, dj = lane & 3;
     const int p00 = di * 8 - (di * (di - 1)) / 2 + (dj - di);
     const int p01 = di * 8 - (di * (di - 1)) / 2 + (4 + dj - di);
     const int a1 = 4 + di;

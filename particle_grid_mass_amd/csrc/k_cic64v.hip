@@ -21,6 +21,10 @@
 // multiply-adds per particle, the diagonal blocks in full) in k_cic64. The
 // next chunk's particle data is in flight during the steps. Each lane writes
 // its nine pairs' record values, contiguous in rec[bin][pair][comp].
+// On grids of few bins (SK) a wave owns 4 bins and each bin 16 lanes: four
+// slices of four, each slice taking every fourth particle of the bin's chunks
+// of 16, and the slices' sums are added across lanes before the record is
+// written (four times the waves, the same FMAs per particle).
 #include "mm_contract.h"
 
 namespace mmk {
@@ -46,10 +50,11 @@ struct Group {
   int nchunks;
 };
 
+template <bool SK>
 __device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_start, int g, int nbins, int np,
                                             int lane) {
   Group G;
-  const int bin = NB * g + (lane >> 2);
+  const int bin = SK ? 4 * g + (lane >> 4) : NB * g + (lane >> 2);
   int s = 0, e = 0;
   if (bin < nbins) {
     s = bin_start[bin];
@@ -63,12 +68,13 @@ __device__ __forceinline__ Group load_group(const int32_t* __restrict__ bin_star
 #pragma unroll
   for (int off = 4; off < 64; off <<= 1) m = max(m, __shfl_xor(m, off));
   G.maxn = __builtin_amdgcn_readfirstlane(m);
-  G.nchunks = G.maxn > 0 ? (G.maxn + CH - 1) / CH : 1;
+  G.nchunks = G.maxn > 0 ? (G.maxn + (SK ? 4 * CH : CH) - 1) / (SK ? 4 * CH : CH) : 1;
   return G;
 }
 
+template <bool SK>
 __device__ __forceinline__ int chunk_perm(const int32_t* __restrict__ perm, const Group& G, int j, int lane) {
-  const int q = j * CH + (lane & 3);
+  const int q = SK ? j * 4 * CH + (lane & 15) : j * CH + (lane & 3);
   return q < G.n ? perm[G.s + q] : -1;
 }
 
@@ -136,18 +142,20 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
-template <typename PT, int NC>
+template <typename PT, int NC, bool SK>
 __global__ __launch_bounds__(64) void k_cic64v(GridDev g, const PT* __restrict__ pos, const double* __restrict__ w,
                                                const PT* __restrict__ Bf, const int32_t* __restrict__ bin_start,
                                                const int32_t* __restrict__ perm, int np, int nbins, double beta,
                                                double sigma, double* __restrict__ rec) {
   __shared__ __attribute__((aligned(16))) double sm[Cfg<NC>::SMEM];
   const int lane = threadIdx.x;
-  const int ngroups = (nbins + NB - 1) / NB;
+  constexpr int NBW = SK ? 4 : NB;  // bins per wave
+  const int ngroups = (nbins + NBW - 1) / NBW;
   const int grp = xcd_chunk_remap(blockIdx.x, gridDim.x, 16);  // chunks of groups dealt round the XCDs
   if (grp >= ngroups) return;
-  const Group G = load_group(bin_start, grp, nbins, np, lane);
-  const int bl = lane >> 2, q = lane & 3;  // the lane's bin in the group and quarter of its pairs
+  const Group G = load_group<SK>(bin_start, grp, nbins, np, lane);
+  // the lane's bin in the group, slice of the bin's particles (SK) and quarter of its pairs
+  const int bl = SK ? lane >> 4 : lane >> 2, sl = SK ? (lane >> 2) & 3 : 0, q = lane & 3;
 
   double acc[PPL][NC];
 #pragma unroll
@@ -155,17 +163,18 @@ __global__ __launch_bounds__(64) void k_cic64v(GridDev g, const PT* __restrict__
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[k][c] = 0.0;
 
-  Raw raw = load_raw<PT, NC>(pos, w, Bf, chunk_perm(perm, G, 0, lane), np);
-  int pnext = chunk_perm(perm, G, 1, lane);
+  Raw raw = load_raw<PT, NC>(pos, w, Bf, chunk_perm<SK>(perm, G, 0, lane), np);
+  int pnext = chunk_perm<SK>(perm, G, 1, lane);
   for (int j = 0; j < G.nchunks; ++j) {
     stage<NC>(raw, g, beta, sigma, sm, lane);
     wave_sync();
     raw = load_raw<PT, NC>(pos, w, Bf, pnext, np);  // next chunk, in flight during the steps
-    pnext = chunk_perm(perm, G, j + 2, lane);
-    const int left = G.maxn - j * CH;
-    const int nr = left >= CH ? CH : left;
+    pnext = chunk_perm<SK>(perm, G, j + 2, lane);
+    // steps with particles; with SK step rd takes particle 4 rd + sl of the bin's 16
+    const int left = G.maxn - j * (SK ? 4 * CH : CH);
+    const int nr = SK ? (left >= 4 * CH ? CH : (left + 3) / 4) : (left >= CH ? CH : left);
     for (int rd = 0; rd < nr; ++rd) {
-      const double* s = sm + (CH * bl + rd) * Cfg<NC>::SLOT;
+      const double* s = sm + (SK ? 4 * CH * bl + 4 * rd + sl : CH * bl + rd) * Cfg<NC>::SLOT;
       const double* sp = s + q * Cfg<NC>::PS;
       double ww[PPL + 1], t[NC];
 #pragma unroll
@@ -188,7 +197,26 @@ __global__ __launch_bounds__(64) void k_cic64v(GridDev g, const PT* __restrict__
     }
     wave_sync();
   }
-  const int bin = NB * grp + bl;
+  const int bin = NBW * grp + bl;
+  if (SK) {
+    // add the four slices' sums through LDS, one pair at a time (all at once
+    // in registers would take a hundred more), in slice order
+    double* dst = rec + ((size_t)bin * NPAIR + PPL * q) * NC;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sm[lane * NC + c] = acc[k][c];
+      wave_sync();
+      if (sl == 0 && bin < nbins) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          dst[k * NC + c] = ((sm[lane * NC + c] + sm[(lane + 4) * NC + c]) + sm[(lane + 8) * NC + c]) +
+                            sm[(lane + 12) * NC + c];
+      }
+      wave_sync();
+    }
+    return;
+  }
   if (bin < nbins) {
     double* dst = rec + ((size_t)bin * NPAIR + PPL * q) * NC;
 #pragma unroll
@@ -198,18 +226,30 @@ __global__ __launch_bounds__(64) void k_cic64v(GridDev g, const PT* __restrict__
   }
 }
 
+template <typename PT, bool SK>
+static hipError_t cic64v_launch(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
+                                double beta, double sigma, double* rec, hipStream_t s) {
+  const int nbins = g.n0 * g.n1 * g.n2;
+  const int ngroups = (nbins + (SK ? 4 : NB) - 1) / (SK ? 4 : NB);
+  if (P.B)
+    hipLaunchKernelGGL((k_cic64v<PT, 9, SK>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  else
+    hipLaunchKernelGGL((k_cic64v<PT, 1, SK>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos,
+                       (const double*)P.w, (const PT*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
+  return hipGetLastError();
+}
+
+// Split K when groups of 16 bins would leave the SIMDs with fewer than two
+// waves each (the kernel runs two per SIMD) and the bins average at least 16
+// particles.
 template <typename PT>
 static hipError_t cic64v_t(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
                            double beta, double sigma, double* rec, hipStream_t s) {
-  const int nbins = g.n0 * g.n1 * g.n2;
-  const int ngroups = (nbins + NB - 1) / NB;
-  if (P.B)
-    hipLaunchKernelGGL((k_cic64v<PT, 9>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos, (const double*)P.w,
-                       (const PT*)P.B, bin_start, perm, P.np, nbins, beta, sigma, rec);
-  else
-    hipLaunchKernelGGL((k_cic64v<PT, 1>), dim3(ngroups), dim3(64), 0, s, g, (const PT*)P.pos, (const double*)P.w,
-                       (const PT*)nullptr, bin_start, perm, P.np, nbins, beta, sigma, rec);
-  return hipGetLastError();
+  const int64_t nbins = (int64_t)g.n0 * g.n1 * g.n2;
+  const bool sk = (nbins + NB - 1) / NB < 2048 && (int64_t)P.np >= 16 * nbins;
+  return sk ? cic64v_launch<PT, true>(g, P, bin_start, perm, beta, sigma, rec, s)
+            : cic64v_launch<PT, false>(g, P, bin_start, perm, beta, sigma, rec, s);
 }
 
 hipError_t launch_cic64_valu(const GridDev& g, const Particles& P, const int32_t* bin_start, const int32_t* perm,
