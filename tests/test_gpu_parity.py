@@ -312,6 +312,21 @@ def test_valu_contraction_small(seed, order, n, npart, kind):
     assert_match(as_numpy_M(gpu_assemble(case, "valu"), case), oracle_assemble(case), "f64")
 
 
+@pytest.mark.parametrize("algo", ["mfma", "valu"])
+@pytest.mark.parametrize("kind", ["scalar", "ecsim"])
+def test_split_k_many_chunks(algo, kind):
+    """A grid of few bins (210) holding about 250 particles per occupied bin
+    takes the split-K contraction of either algorithm (one bin per wave on the
+    matrix cores, four per wave on vector FMAs); the bins are ragged and span
+    several chunks of the slices."""
+    case = random_case(21, 1, (6, 5, 7), 42000, kind=kind, dtype="f64", beta=0.7, sigma=1.3,
+                       origin=(0.25, -2.0, 1.0), h=(0.5, 1.0, 0.75), spread=0.8)
+    nb = 6 * 5 * 7
+    assert (nb + 3) // 4 < 3072 and (nb + 15) // 16 < 2048 and 42000 >= 16 * nb  # both split-K rules hold
+    _print_case(f"splitk/{algo}", case)
+    assert_match(as_numpy_M(gpu_assemble(case, algo), case), oracle_assemble(case), "f64")
+
+
 def test_valu_contraction_config2():
     case = make_config(2)
     _print_case("c2/valu", case)
